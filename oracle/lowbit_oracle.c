@@ -1,0 +1,561 @@
+/*
+ * lowbit_oracle.c -- plain, slow CPU oracle for the block-scaled FP4 hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
+ * calls this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark load it.  It shares no source, header, table or helper
+ * with the HIP kernels.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC
+ * (no FMA contraction, IEEE binary32/binary64 with subnormals).
+ *
+ * What it computes, and where each step comes from:
+ *   - The fused producer follows the FlashInfer page "cute_dsl/add_rmsnorm_fp4quant.py",
+ *     AddRMSNormFP4QuantKernel.kernel, phases 1-3 (add + residual write-back,
+ *     sum of squares / rstd, per-block scale, FP4 quantize-and-pack), with the
+ *     readings listed under each function below.
+ *   - The FP4 GEMM follows the FlashRT "fp4-gemm" README: "Tensor Contract"
+ *     (A (M,K/2), B (N,K/2) packed, out (M,N) = alpha * A . B^T) and its
+ *     "Validation" paragraph (dequantize exactly the bytes the kernel used,
+ *     then a high-precision matmul of the dequantized low-bit values).
+ *   - Element formats are written from their definitions: FP4 E2M1 (max 6),
+ *     FP8 E4M3 "FN" (bias 7, max 448, no infinities), UE8M0 (2^(b-127)), as
+ *     the FlashInfer page's constants FLOAT4_E2M1_MAX = 6 and
+ *     FLOAT8_E4M3_MAX = 448 state; rounding is round-to-nearest, ties to the
+ *     even code, saturating at the format maximum.
+ *
+ * Every function is a direct transcription of the definition, not a faster
+ * equivalent: encoders scan the value grid, the GEMM is a triple loop in fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1 };
+enum { ORC_SF_LINEAR = 0, ORC_SF_TILED = 1 };
+enum { ORC_EPI_NONE = 0, ORC_EPI_BIAS = 1, ORC_EPI_RESIDUAL = 2, ORC_EPI_BIAS_RESIDUAL = 3,
+       ORC_EPI_BIAS_GELU = 4 };
+
+/* ------------------------------------------------------------------------- */
+/* bf16 <-> fp32                                                              */
+/* ------------------------------------------------------------------------- */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* bf16 is the upper half of a binary32; widening is exact. */
+float orc_bf16_to_f32(uint16_t b) { return bits_f32((uint32_t)b << 16); }
+
+/* Round a binary32 to bf16, nearest-even, written as "pick the nearer of the
+ * two truncation neighbours" (inputs here are always finite). */
+uint16_t orc_f32_to_bf16(float f) {
+    uint32_t u = f32_bits(f);
+    uint16_t lo = (uint16_t)(u >> 16);          /* truncation toward zero */
+    uint32_t rest = u & 0xFFFFu;                /* discarded low half */
+    if (rest > 0x8000u) return (uint16_t)(lo + 1);
+    if (rest < 0x8000u) return lo;
+    return (lo & 1u) ? (uint16_t)(lo + 1) : lo; /* exact tie: keep the even one */
+}
+
+/* ------------------------------------------------------------------------- */
+/* FP4 E2M1                                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* Magnitudes of codes 0..7: exponent bias 1, one mantissa bit, code 1 is the
+ * subnormal 0.5.  Bit 3 is the sign. */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(uint8_t code) {
+    double m = E2M1_MAG[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* Nearest E2M1 magnitude to |v|, ties to the code with mantissa bit 0 (the
+ * even code), saturating at 6.  The sign of v is kept, so -0.1 gives 0x8. */
+uint8_t orc_e2m1_encode(float v) {
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    if (a >= 6.0) return (uint8_t)(sign | 7);
+    /* a lies in [E2M1_MAG[c], E2M1_MAG[c+1]) for exactly one c in 0..6 */
+    int c = 0;
+    while (!(a < E2M1_MAG[c + 1])) c++;
+    double mid = 0.5 * (E2M1_MAG[c] + E2M1_MAG[c + 1]); /* exact in binary64 */
+    int code;
+    if (a < mid) code = c;
+    else if (a > mid) code = c + 1;
+    else code = (c % 2 == 0) ? c : c + 1;
+    return (uint8_t)(sign | code);
+}
+
+/* ------------------------------------------------------------------------- */
+/* FP8 E4M3 (OCP "FN": bias 7, no infinities, S.1111.111 is NaN, max 448)      */
+/* ------------------------------------------------------------------------- */
+
+double orc_e4m3_value(uint8_t b) {
+    int s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);      /* subnormal: 0.mmm * 2^-6 */
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest E4M3 value, ties to the even code, saturating at 448.  Scans the
+ * 127 non-negative finite codes in increasing order. */
+uint8_t orc_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int c = 0;                                   /* codes 0x00..0x7E increase */
+    while (!(a < orc_e4m3_value((uint8_t)(c + 1)))) c++;
+    double lo = orc_e4m3_value((uint8_t)c), hi = orc_e4m3_value((uint8_t)(c + 1));
+    double mid = 0.5 * (lo + hi);               /* exact: few significant bits */
+    int code;
+    if (a < mid) code = c;
+    else if (a > mid) code = c + 1;
+    else code = (c % 2 == 0) ? c : c + 1;
+    return (uint8_t)(sign | code);
+}
+
+/* ------------------------------------------------------------------------- */
+/* UE8M0: byte b encodes 2^(b-127); 255 is NaN and is never produced           */
+/* ------------------------------------------------------------------------- */
+
+double orc_ue8m0_value(uint8_t b) {
+    if (b == 255) return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Scale-factor layouts                                                       */
+/* ------------------------------------------------------------------------- */
+/*
+ * LINEAR: row-major (rows, K/B) bytes, the FlashInfer page's unswizzled
+ *         layout mS[row, sf_idx].
+ * TILED:  rows are grouped by 32 and scale blocks by 8.  Each 32 x 8 group is
+ *         256 contiguous bytes laid out as 64 little-endian 32-bit words;
+ *         word w = ((kb%8)/4)*32 + row%32 holds the four consecutive blocks
+ *         4*((kb%8)/4) .. +3 of that row, block kb in byte kb%4.
+ *         Groups are ordered row-group major.  Padding bytes are zero.
+ */
+static int64_t block_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
+
+int64_t orc_sf_bytes(int64_t rows, int64_t k, int fmt, int layout) {
+    int64_t nblk = k / block_of(fmt);
+    if (layout == ORC_SF_LINEAR) return rows * nblk;
+    return ((rows + 31) / 32) * ((nblk + 7) / 8) * 256;
+}
+
+int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int layout) {
+    if (layout == ORC_SF_LINEAR) return row * nblk + kb;
+    int64_t ktiles = (nblk + 7) / 8;
+    int64_t tile = (row / 32) * ktiles + kb / 8;
+    int64_t j = kb % 8;
+    return tile * 256 + ((j / 4) * 32 + row % 32) * 4 + j % 4;
+}
+
+/* ------------------------------------------------------------------------- */
+/* One quantization block (FlashInfer page, kernel Phase 3)                    */
+/* ------------------------------------------------------------------------- */
+/*
+ * Input: the block's fp32 values y[0..B).  Output: the scale byte, the codes,
+ * and (optional) the pre-rounding values the parity checker needs.
+ *
+ * NVFP4 (B = 16, E4M3 scale, global scale gs folded into the block scale --
+ * the page's code multiplies gs into the scale and "not applied to input"):
+ *     s_pre = min(fl32(fl32(gs * amax) / 6), 448);  sbyte = E4M3(s_pre)
+ *     inv   = sdec == 0 ? 0 : fl32(fl32(1 / sdec) * gs)
+ *     v_i   = fl32(y_i * inv);  code_i = E2M1(v_i)
+ * MXFP4 (B = 32, UE8M0 scale, OCP MX rule, gs unused):
+ *     e = clamp(floor(log2 amax) - 2, -127, 127)  (amax == 0 gives -127)
+ *     sbyte = e + 127;  v_i = y_i * 2^-e (exact);  code_i = E2M1(v_i)
+ */
+static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes, uint8_t* sbyte,
+                        float* amax_out, float* spre_out, float* v_out) {
+    float amax = 0.0f;
+    for (int i = 0; i < B; i++) {
+        float a = fabsf(y[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax_out) *amax_out = amax;
+    if (fmt == ORC_NVFP4) {
+        volatile float t = gs * amax;            /* fl32(gs * amax) */
+        volatile float s_pre = t / 6.0f;         /* fl32(. / 6) */
+        float sp = s_pre;
+        if (sp > 448.0f) sp = 448.0f;
+        if (spre_out) *spre_out = sp;
+        uint8_t sb = orc_e4m3_encode(sp);
+        *sbyte = sb;
+        float sdec = (float)orc_e4m3_value(sb);  /* exact in fp32 */
+        float inv;
+        if (sdec == 0.0f) {
+            inv = 0.0f;
+        } else {
+            volatile float r = 1.0f / sdec;      /* fl32(1 / sdec) */
+            inv = r * gs;                        /* fl32(. * gs) */
+        }
+        for (int i = 0; i < B; i++) {
+            volatile float v = y[i] * inv;
+            if (v_out) v_out[i] = v;
+            codes[i] = orc_e2m1_encode(v);
+        }
+    } else {
+        int e;
+        if (amax == 0.0f) {
+            e = -127;
+        } else {
+            int E;
+            (void)frexp((double)amax, &E);       /* amax = f * 2^E, f in [0.5, 1) */
+            e = (E - 1) - 2;                     /* floor(log2 amax) - emax(E2M1) */
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+        }
+        if (spre_out) *spre_out = amax;          /* the value whose binade decides e */
+        *sbyte = (uint8_t)(e + 127);
+        for (int i = 0; i < B; i++) {
+            float v = ldexpf(y[i], -e);          /* exact unless it underflows */
+            if (v_out) v_out[i] = v;
+            codes[i] = orc_e2m1_encode(v);
+        }
+    }
+}
+
+/* Re-encode a block from a given scale byte (used by the parity checker when
+ * the device's scale byte differs inside the tolerance window). */
+void orc_encode_with_scale(const float* y, int B, int fmt, float gs, uint8_t sbyte, uint8_t* codes) {
+    if (fmt == ORC_NVFP4) {
+        float sdec = (float)orc_e4m3_value(sbyte);
+        float inv;
+        if (sdec == 0.0f) {
+            inv = 0.0f;
+        } else {
+            volatile float r = 1.0f / sdec;
+            inv = r * gs;
+        }
+        for (int i = 0; i < B; i++) {
+            volatile float v = y[i] * inv;
+            codes[i] = orc_e2m1_encode(v);
+        }
+    } else {
+        int e = (int)sbyte - 127;
+        for (int i = 0; i < B; i++) codes[i] = orc_e2m1_encode(ldexpf(y[i], -e));
+    }
+}
+
+/* Pack codes two per byte: element 2j in the low nibble, 2j+1 in the high. */
+static void pack_row(const uint8_t* codes, int64_t n, uint8_t* out) {
+    for (int64_t j = 0; j < n / 2; j++)
+        out[j] = (uint8_t)((codes[2 * j] & 15) | ((codes[2 * j + 1] & 15) << 4));
+}
+
+/* Quantize one row of n fp32 values and write codes + scales in the layout. */
+static void quant_row(const float* y, int64_t row, int64_t n, int fmt, float gs, int layout,
+                      uint8_t* packed_row, uint8_t* sf, uint8_t* codes_tmp,
+                      float* amax_row, float* spre_row, float* v_row) {
+    int B = (int)block_of(fmt);
+    int64_t nblk = n / B;
+    for (int64_t b = 0; b < nblk; b++) {
+        uint8_t sb;
+        quant_block(y + b * B, B, fmt, gs, codes_tmp + b * B, &sb,
+                    amax_row ? amax_row + b : NULL, spre_row ? spre_row + b : NULL,
+                    v_row ? v_row + b * B : NULL);
+        sf[orc_sf_offset(row, b, nblk, layout)] = sb;
+    }
+    pack_row(codes_tmp, n, packed_row);
+}
+
+static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
+    if (rows < 0 || k <= 0) return 1;
+    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return 1;
+    if (layout != ORC_SF_LINEAR && layout != ORC_SF_TILED) return 1;
+    if (k % block_of(fmt) != 0) return 1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Fused producer (FlashInfer page, AddRMSNormFP4QuantKernel)                  */
+/* ------------------------------------------------------------------------- */
+/*
+ * For each row m (H elements; x, r, w are bf16 bit patterns):
+ *  1. h_i = fl32(x_i + r_i); residual_i <- bf16(h_i)     (Phase 2, in place)
+ *  2. S = sum_i h_i^2 over the fp32 h (the page squares the unrounded h),
+ *     accumulated in binary64 (each h_i^2 is exact there);
+ *     rstd = fl32(1 / sqrt(S / H + eps))  -- a correctly rounded reading of
+ *     the page's rsqrt(mean_sq + eps)
+ *  3. y_i = fl32(fl32(bf16(h_i) * rstd) * w_i)  (the page reads h back from its
+ *     bf16 shared-memory copy and computes h * rstd * w)
+ *  4. per block: quant_block above; scales go to out_sf in the layout.
+ * gs: the global scale value (NVFP4; ignored for MXFP4).
+ * Optional diagnostics (NULL to skip): y (M*H fp32), v (M*H fp32),
+ * amax and s_pre (M*H/B fp32 each), rstd (M fp32).
+ */
+int orc_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w,
+                          int64_t M, int64_t H, float eps, int fmt, int layout, float gs,
+                          uint8_t* out_packed, uint8_t* out_sf,
+                          float* diag_y, float* diag_v, float* diag_amax, float* diag_spre,
+                          float* diag_rstd) {
+    if (check_common(M, H, fmt, layout)) return 1;
+    int64_t B = block_of(fmt), nblk = H / B;
+    memset(out_sf, 0, (size_t)orc_sf_bytes(M, H, fmt, layout)); /* padding is zero */
+    int err = 0;
+#pragma omp parallel
+    {
+        float* h = (float*)malloc(sizeof(float) * H);
+        float* y = (float*)malloc(sizeof(float) * H);
+        uint8_t* codes = (uint8_t*)malloc((size_t)H);
+        if (!h || !y || !codes) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < M; m++) {
+                const uint16_t* xr = x + m * H;
+                uint16_t* rr = residual + m * H;
+                /* step 1 */
+                for (int64_t i = 0; i < H; i++) {
+                    volatile float s = orc_bf16_to_f32(xr[i]) + orc_bf16_to_f32(rr[i]);
+                    h[i] = s;
+                }
+                /* step 2 */
+                double S = 0.0;
+                for (int64_t i = 0; i < H; i++) S += (double)h[i] * (double)h[i];
+                double denom = sqrt(S / (double)H + (double)eps);
+                float rstd = (float)(1.0 / denom);
+                if (diag_rstd) diag_rstd[m] = rstd;
+                /* residual write-back, then step 3 from the bf16 copy */
+                for (int64_t i = 0; i < H; i++) {
+                    uint16_t hb = orc_f32_to_bf16(h[i]);
+                    rr[i] = hb;
+                    volatile float t = orc_bf16_to_f32(hb) * rstd;
+                    volatile float yi = t * orc_bf16_to_f32(w[i]);
+                    y[i] = yi;
+                }
+                if (diag_y) memcpy(diag_y + m * H, y, sizeof(float) * H);
+                /* step 4 */
+                quant_row(y, m, H, fmt, gs, layout, out_packed + m * (H / 2), out_sf, codes,
+                          diag_amax ? diag_amax + m * nblk : NULL,
+                          diag_spre ? diag_spre + m * nblk : NULL,
+                          diag_v ? diag_v + m * H : NULL);
+            }
+        }
+        free(h); free(y); free(codes);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Quantize (FlashRT README: quantize_fp4_sfa_bf16)                            */
+/* ------------------------------------------------------------------------- */
+/* y_i = f32(x_i) (exact), then the per-block rule above.  This makes every
+ * GEMM operand: activations and the prepacked weights alike. */
+int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout, float gs,
+                 uint8_t* out_packed, uint8_t* out_sf, float* diag_spre) {
+    if (check_common(rows, K, fmt, layout)) return 1;
+    int64_t nblk = K / block_of(fmt);
+    memset(out_sf, 0, (size_t)orc_sf_bytes(rows, K, fmt, layout));
+    int err = 0;
+#pragma omp parallel
+    {
+        float* y = (float*)malloc(sizeof(float) * K);
+        uint8_t* codes = (uint8_t*)malloc((size_t)K);
+        if (!y || !codes) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < rows; m++) {
+                for (int64_t i = 0; i < K; i++) y[i] = orc_bf16_to_f32(x[m * K + i]);
+                quant_row(y, m, K, fmt, gs, layout, out_packed + m * (K / 2), out_sf, codes, NULL,
+                          diag_spre ? diag_spre + m * nblk : NULL, NULL);
+            }
+        }
+        free(y); free(codes);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dequantize (FlashRT README: dequantize_fp4_sfa_fp16, here to bf16)          */
+/* ------------------------------------------------------------------------- */
+/* x_hat = fl32(E2M1(code) * scale / gs) for NVFP4 (gs divides: it was folded
+ * into the block scale on the way in), E2M1(code) * 2^(b-127) for MXFP4, then
+ * stored as bf16 (nearest-even).  Also returns the binary64 values when
+ * out_f64 is non-NULL. */
+int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
+                   int layout, float gs, uint16_t* out_bf16, double* out_f64) {
+    if (check_common(rows, K, fmt, layout)) return 1;
+    int64_t B = block_of(fmt), nblk = K / B;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < rows; m++) {
+        for (int64_t i = 0; i < K; i++) {
+            uint8_t byte = packed[m * (K / 2) + i / 2];
+            uint8_t code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+            uint8_t sb = sf[orc_sf_offset(m, i / B, nblk, layout)];
+            /* q * scale is exact in binary64 (and in binary32) */
+            double v = orc_e2m1_value(code) *
+                       ((fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb));
+            /* NVFP4: one division by gs; the binary64 quotient rounded to
+             * binary32 equals the correctly rounded binary32 quotient */
+            if (fmt == ORC_NVFP4) v = v / (double)gs;
+            if (out_f64) out_f64[m * K + i] = v;
+            if (out_bf16) out_bf16[m * K + i] = orc_f32_to_bf16((float)v);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* GEMM (FlashRT README: nvfp4_gemm_* family and its validation method)        */
+/* ------------------------------------------------------------------------- */
+/*
+ * D[m,n] = alpha * sum_k Ahat[m,k] * Bhat[n,k], Ahat/Bhat dequantized exactly
+ * (no global scale: the caller folds 1/(gsA*gsB) into alpha), then
+ *   bias:          + bias[n]
+ *   residual:      + residual[m,n]
+ *   bias+residual: + bias[n] + residual[m,n]
+ *   bias+gelu:     GELU(z + bias[n]), GELU(t) = 0.5 t (1 + erf(t / sqrt 2))
+ * all in binary64.  out_ref receives the unrounded value; out_l1 receives
+ * |alpha| * sum_k |Ahat * Bhat| (the accumulation budget of the tolerance).
+ */
+static double dq(const uint8_t* packed, const uint8_t* sf, int64_t row, int64_t k, int64_t K,
+                 int fmt, int layout) {
+    int64_t B = block_of(fmt), nblk = K / B;
+    uint8_t byte = packed[row * (K / 2) + k / 2];
+    uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+    uint8_t sb = sf[orc_sf_offset(row, k / B, nblk, layout)];
+    double s = (fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb);
+    return orc_e2m1_value(code) * s;
+}
+
+static double gelu_erf(double t) { return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); }
+
+static double epilogue(double acc, double alpha, int epi, const uint16_t* bias,
+                       const uint16_t* residual, int64_t m, int64_t n, int64_t N) {
+    double z = alpha * acc;
+    if (epi == ORC_EPI_BIAS || epi == ORC_EPI_BIAS_RESIDUAL || epi == ORC_EPI_BIAS_GELU)
+        z += (double)orc_bf16_to_f32(bias[n]);
+    if (epi == ORC_EPI_RESIDUAL || epi == ORC_EPI_BIAS_RESIDUAL)
+        z += (double)orc_bf16_to_f32(residual[m * N + n]);
+    if (epi == ORC_EPI_BIAS_GELU) z = gelu_erf(z);
+    return z;
+}
+
+/* Dequantize both operands once (fp64, exact), then a plain triple loop. */
+int orc_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+             int64_t M, int64_t N, int64_t K, int fmt, int layout_a, int layout_b, double alpha,
+             int epi, const uint16_t* bias, const uint16_t* residual,
+             double* out_ref, double* out_l1) {
+    if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    double* A = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    double* Bm = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    if (!A || !Bm) { free(A); free(Bm); return 2; }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k = 0; k < K; k++) A[m * K + k] = dq(a, sfa, m, k, K, fmt, layout_a);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) Bm[n * K + k] = dq(b, sfb, n, k, K, fmt, layout_b);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0, l1 = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = A[m * K + k] * Bm[n * K + k];
+                acc += p;
+                l1 += fabs(p);
+            }
+            out_ref[m * N + n] = epilogue(acc, alpha, epi, bias, residual, m, n, N);
+            if (out_l1) out_l1[m * N + n] = fabs(alpha) * l1;
+        }
+    }
+    free(A); free(Bm);
+    return 0;
+}
+
+/* The same definition evaluated only at the listed (m, n) entries, for sampled
+ * checks at sizes where the full product is too slow on the CPU. */
+int orc_gemm_entries(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                     int64_t M, int64_t N, int64_t K, int fmt, int layout_a, int layout_b,
+                     double alpha, int epi, const uint16_t* bias, const uint16_t* residual,
+                     int64_t count, const int64_t* idx_m, const int64_t* idx_n,
+                     double* out_ref, double* out_l1) {
+    if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    for (int64_t t = 0; t < count; t++)
+        if (idx_m[t] < 0 || idx_m[t] >= M || idx_n[t] < 0 || idx_n[t] >= N) return 1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; t++) {
+        int64_t m = idx_m[t], n = idx_n[t];
+        double acc = 0.0, l1 = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double p = dq(a, sfa, m, k, K, fmt, layout_a) * dq(b, sfb, n, k, K, fmt, layout_b);
+            acc += p;
+            l1 += fabs(p);
+        }
+        out_ref[t] = epilogue(acc, alpha, epi, bias, residual, m, n, N);
+        if (out_l1) out_l1[t] = fabs(alpha) * l1;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* GEMM with bias + GELU epilogue emitting NVFP4 (FlashRT README:              */
+/* nvfp4_gemm_bias_gelu_nvfp4 -- packed FP4 plus scales for the next GEMM)     */
+/* ------------------------------------------------------------------------- */
+/* t = alpha * acc + bias[n]; y = fl32(GELU(t)) (binary64 GELU rounded once);
+ * then each 16-run of y along n is quantized with the NVFP4 block rule and
+ * global scale gs_out, written as an (M, N) GEMM-A operand: packed (M, N/2)
+ * and scales in out_layout.  Diagnostics (optional): y, v (M*N), l1 (M*N),
+ * s_pre and amax (M*N/16). */
+int orc_gemm_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                      int64_t M, int64_t N, int64_t K, int fmt, int layout_a, int layout_b,
+                      double alpha, const uint16_t* bias, float gs_out, int out_layout,
+                      uint8_t* out_packed, uint8_t* out_sf,
+                      float* diag_y, float* diag_v, double* diag_l1, float* diag_spre,
+                      float* diag_amax) {
+    if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    if (N % 16 != 0) return 1;
+    double* ref = (double*)malloc(sizeof(double) * (size_t)(M * N));
+    double* l1 = (double*)malloc(sizeof(double) * (size_t)(M * N));
+    if (!ref || !l1) { free(ref); free(l1); return 2; }
+    int rc = orc_gemm(a, b, sfa, sfb, M, N, K, fmt, layout_a, layout_b, alpha, ORC_EPI_BIAS_GELU,
+                      bias, NULL, ref, l1);
+    if (rc) { free(ref); free(l1); return rc; }
+    int64_t nblk = N / 16;
+    memset(out_sf, 0, (size_t)orc_sf_bytes(M, N, ORC_NVFP4, out_layout));
+    int err = 0;
+#pragma omp parallel
+    {
+        float* y = (float*)malloc(sizeof(float) * N);
+        uint8_t* codes = (uint8_t*)malloc((size_t)N);
+        if (!y || !codes) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < M; m++) {
+                for (int64_t n = 0; n < N; n++) y[n] = (float)ref[m * N + n];
+                if (diag_y) memcpy(diag_y + m * N, y, sizeof(float) * N);
+                quant_row(y, m, N, ORC_NVFP4, gs_out, out_layout, out_packed + m * (N / 2), out_sf,
+                          codes, diag_amax ? diag_amax + m * nblk : NULL,
+                          diag_spre ? diag_spre + m * nblk : NULL, diag_v ? diag_v + m * N : NULL);
+            }
+        }
+        free(y); free(codes);
+    }
+    if (diag_l1) memcpy(diag_l1, l1, sizeof(double) * (size_t)(M * N));
+    free(ref); free(l1);
+    return err;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
