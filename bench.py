@@ -1,0 +1,287 @@
+"""Benchmark of the low-bit linear hot path on one MI355X.
+
+One step = one pass of every stage of the path over one batch of resident,
+seeded synthetic input:
+  1. fused add + RMSNorm + NVFP4 quant, 4096 x 4096 (outlier channels, global
+     scale 6*448/amax)                                   -- HBM-bound
+  2. MXFP4 prefill GEMM + bias + residual, (8192, 14336, 4096)
+  3. MXFP4 prefill GEMM + bias + residual, (8192, 4096, 14336)   -- MFMA-bound
+  4. NVFP4 chain at M = 2048: producer (H = 5120) -> GEMM N = 17408 with
+     bias + GELU emitting NVFP4 -> GEMM N = 5120 (K = 17408) to bf16
+
+value = 100 * (sum of the stages' roofline times) / (measured step time): the
+step's throughput as a percentage of the one-GPU roofline (HBM 8 TB/s for
+the producer, dense FP4 MFMA 10.1 PFLOP/s for the GEMMs).  Per-kernel GB/s and
+TFLOP/s are printed on stderr and carried in "kernels".
+
+Prints ONE JSON line on stdout.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_scaled_fp4_add_amd as lb  # noqa: E402
+from block_scaled_fp4_add_amd import synth  # noqa: E402
+
+HBM_PEAK = 8.0e12          # B/s, MI355X published
+FP4_PEAK = 10.1e15         # FLOP/s dense FP4/FP6 MFMA, published
+FP16_PEAK = 2.5e15         # FLOP/s dense fp16/bf16 MFMA, published
+EPS = 1e-6
+METRIC = "fused add-RMSNorm-FP4 quant GB/s + FP4 GEMM TFLOPS, as % of 1-GPU roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def producer_bytes(M, H, B):
+    # x read, r read, r written (bf16) + FP4 codes + one scale byte per block
+    # + the weight row and the global scale once per launch
+    return M * H * 6 + M * H // 2 + M * H // B + 2 * H + 4
+
+
+def gemm_bytes(M, N, K, B, epi_bias=False, epi_res=False, out_fp4=False):
+    b = (M + N) * (K // 2 + K // B)
+    b += 2 * N if epi_bias else 0
+    b += 2 * M * N if epi_res else 0
+    b += (M * N // 2 + M * N // 16) if out_fp4 else 2 * M * N
+    return b
+
+
+class Stage:
+    """A kernel launch with its per-launch HIP-event timing on torch's stream
+    (the stream every lowbit call is launched on)."""
+
+    def __init__(self, name, fn, bound, work, unit_work, roof):
+        self.name, self.fn, self.bound, self.work, self.unit_work, self.roof = name, fn, bound, work, unit_work, roof
+        self.times = []
+
+    def __call__(self, timed):
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            self.fn()
+            e1.record()
+            self.times.append((e0, e1))
+        else:
+            self.fn()
+
+    def mean_s(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.times])) * 1e-3
+
+    def ideal_s(self):
+        return self.work / self.roof
+
+
+def build_stages():
+    dev = "cuda"
+    stages = []
+
+    # 1. producer, NVFP4 4096 x 4096, rotated over 4 input sets (256 MiB) so
+    #    that the 256 MiB last-level cache cannot hold the step's inputs
+    c = synth.NVFP4_PRODUCER
+    M, H = c["M"], c["H"]
+    sets = []
+    for i in range(4):
+        x, r, w = synth.producer_inputs(M, H, c["seed"] + 100 * i, outliers=True)
+        sets.append((x.to(dev), r.to(dev), w.to(dev)))
+    # global scale 6*448/amax(y): a calibration input, measured once with the
+    # path itself at gs = 1 via dequantization of its own output
+    x0, r0, w0 = synth.producer_inputs(M, H, c["seed"], outliers=True)
+    p, s = lb.lowbit_add_rmsnorm_quant(x0.to(dev), r0.to(dev), w0.to(dev), EPS, lb.NVFP4, lb.LINEAR)
+    amax = lb.lowbit_dequantize(p, s, lb.NVFP4, lb.LINEAR).float().abs().max().item()
+    gs = torch.tensor([2688.0 / amax], dtype=torch.float32, device=dev)
+    pk = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lb.LINEAR), dtype=torch.uint8, device=dev)
+    it = {"i": 0}
+
+    def producer():
+        x, r, w = sets[it["i"] % 4]
+        it["i"] += 1
+        lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.NVFP4, lb.LINEAR, global_scale=gs, out_packed=pk,
+                                    out_sf=sf)
+
+    stages.append(Stage("add_rmsnorm_nvfp4_4096x4096", producer, "hbm", producer_bytes(M, H, 16),
+                        "B", HBM_PEAK))
+
+    # 2-3. MXFP4 prefill GEMMs with bias + residual (operands quantized by the path itself)
+    c = synth.MXFP4_PREFILL
+    for (M, N, K) in c["shapes"]:
+        A = synth.activation(M, K, c["seed"], outliers=True).to(dev)
+        Wt = synth.weight(N, K, c["seed"]).to(dev)
+        a, sfa = lb.lowbit_quantize(A, lb.MXFP4, lb.TILED)
+        b, sfb = lb.lowbit_quantize(Wt, lb.MXFP4, lb.TILED)
+        del A, Wt
+        bias = synth.bias(N, c["seed"]).to(dev)
+        res = synth.residual(M, N, c["seed"]).to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def gemm(a=a, b=b, sfa=sfa, sfb=sfb, bias=bias, res=res, out=out):
+            lb.lowbit_gemm_bias_residual_bf16(a, b, sfa, sfb, bias, res, fmt=lb.MXFP4, sfa_layout=lb.TILED,
+                                              sfb_layout=lb.TILED, out=out)
+
+        stages.append(Stage(f"mxfp4_gemm_bias_residual_{M}x{N}x{K}", gemm, "mfma", 2.0 * M * N * K, "FLOP",
+                            FP4_PEAK))
+
+    # 4. NVFP4 chain at M = 2048
+    c = synth.NVFP4_CHAIN
+    H, N1, M = c["H"], c["N1"], 2048
+    x, r, w = (t.to(dev) for t in synth.producer_inputs(M, H, c["seed"] + M, outliers=True))
+    W1 = synth.weight(N1, H, c["seed"], index=10).to(dev)
+    W2 = synth.weight(H, N1, c["seed"], index=11).to(dev)
+    bias1 = synth.bias(N1, c["seed"], index=12).to(dev)
+    gs1 = torch.tensor([2688.0 / W1.float().abs().max().item()], device=dev)
+    gs2 = torch.tensor([2688.0 / W2.float().abs().max().item()], device=dev)
+    b1, sfb1 = lb.lowbit_quantize(W1, lb.NVFP4, lb.TILED, global_scale=gs1)
+    b2, sfb2 = lb.lowbit_quantize(W2, lb.NVFP4, lb.TILED, global_scale=gs2)
+    del W1, W2
+    p, s = lb.lowbit_add_rmsnorm_quant(x, r.clone(), w, EPS, lb.NVFP4, lb.TILED)
+    amax = lb.lowbit_dequantize(p, s, lb.NVFP4, lb.TILED).float().abs().max().item()
+    gsA = torch.tensor([2688.0 / amax], dtype=torch.float32, device=dev)
+    alpha1 = 1.0 / (gsA.item() * gs1.item())
+    alpha2 = 1.0 / gs2.item()
+    a1 = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    sa1 = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lb.TILED), dtype=torch.uint8, device=dev)
+    a2 = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
+    sa2 = torch.empty(lb.lowbit_sf_bytes(M, N1, lb.NVFP4, lb.TILED), dtype=torch.uint8, device=dev)
+    out2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+
+    def chain_producer():
+        lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.NVFP4, lb.TILED, global_scale=gsA, out_packed=a1,
+                                    out_sf=sa1)
+
+    def chain_gemm1():
+        lb.lowbit_gemm_bias_gelu_fp4(a1, b1, sa1, sfb1, bias1, fmt=lb.NVFP4, sfa_layout=lb.TILED,
+                                     sfb_layout=lb.TILED, alpha=alpha1, out_packed=a2, out_sf=sa2,
+                                     out_layout=lb.TILED)
+
+    def chain_gemm2():
+        lb.lowbit_gemm_bf16(a2, b2, sa2, sfb2, fmt=lb.NVFP4, sfa_layout=lb.TILED, sfb_layout=lb.TILED,
+                            alpha=alpha2, out=out2)
+
+    stages.append(Stage(f"chain_add_rmsnorm_nvfp4_{M}x{H}", chain_producer, "hbm",
+                        producer_bytes(M, H, 16), "B", HBM_PEAK))
+    stages.append(Stage(f"chain_nvfp4_gemm_gelu_fp4_{M}x{N1}x{H}", chain_gemm1, "mfma",
+                        2.0 * M * N1 * H, "FLOP", FP4_PEAK))
+    stages.append(Stage(f"chain_nvfp4_gemm_{M}x{H}x{N1}", chain_gemm2, "mfma", 2.0 * M * H * N1, "FLOP",
+                        FP4_PEAK))
+    return stages
+
+
+def cpu_baseline(stages, step_ideal_s):
+    """Time the CPU oracle, as it stands, on a bounded sample of the same
+    workload and extrapolate to one step (a reported baseline, not a target)."""
+    from oracle import oracle as orc
+
+    L = orc.lib()
+    threads = orc.num_threads()
+    t_total = 0.0
+    parts = []
+    # producer: 256 of the 4096 rows
+    c = synth.NVFP4_PRODUCER
+    rows = 256
+    x, r, w = synth.producer_inputs(rows, c["H"], c["seed"], outliers=True)
+    t0 = time.perf_counter()
+    orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4, orc.LINEAR, gs=1.0)
+    dt = time.perf_counter() - t0
+    prod_s = dt * (c["M"] / rows)
+    t_total += prod_s * (1 + 2048 * 5120 / (c["M"] * c["H"]))   # the chain's producer scales by elements
+    parts.append(f"producer {rows}x{c['H']} rows ({dt:.2f} s)")
+    # GEMM: 1024 output entries of the (8192, 14336, 4096) GEMM, rate in MAC/s
+    M, N, K = synth.MXFP4_PREFILL["shapes"][0]
+    Msub, Nsub = 8, 128
+    A = synth.activation(Msub, K, 1)
+    Wt = synth.weight(Nsub, K, 1)
+    a, sfa = orc.quantize(synth.bits(A), orc.MXFP4, orc.LINEAR)
+    b, sfb = orc.quantize(synth.bits(Wt), orc.MXFP4, orc.LINEAR)
+    t0 = time.perf_counter()
+    orc.gemm(a, b, sfa, sfb, Msub, Nsub, K, orc.MXFP4, orc.LINEAR, orc.LINEAR)
+    dt = time.perf_counter() - t0
+    mac_rate = Msub * Nsub * K / dt
+    gemm_macs = sum(s.work / 2 for s in stages if s.unit_work == "FLOP")
+    t_total += gemm_macs / mac_rate
+    parts.append(f"gemm {Msub}x{Nsub}x{K} ({dt:.2f} s, {mac_rate / 1e9:.2f} GMAC/s)")
+    value = 100.0 * step_ideal_s / t_total
+    return {"value": value, "unit": "% of 1-GPU roofline", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(parts) + f"; extrapolated step time {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lb.lib()
+    log("[bench] building inputs")
+    stages = build_stages()
+    torch.cuda.synchronize()
+    log("[bench] warmup")
+    for _ in range(args.warmup):
+        for s in stages:
+            s(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for s in stages:
+            s(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    ideal = sum(s.ideal_s() for s in stages)
+    value = 100.0 * ideal / (wall / args.steps)
+    kernels = {}
+    for s in stages:
+        t = s.mean_s()
+        rate = s.work / t
+        frac = s.ideal_s() / t
+        kernels[s.name] = {"us": round(t * 1e6, 2),
+                           ("GB/s" if s.unit_work == "B" else "TFLOP/s"):
+                               round(rate / (1e9 if s.unit_work == "B" else 1e12), 1),
+                           "roofline_frac": round(frac, 4)}
+        log(f"[bench] {s.name}: {t * 1e6:.1f} us, "
+            f"{rate / (1e9 if s.unit_work == 'B' else 1e12):.1f} {'GB/s' if s.unit_work == 'B' else 'TFLOP/s'}, "
+            f"{100 * frac:.1f}% of roofline")
+    # dominant kernel: the one with the largest share of the step
+    dom = max(stages, key=lambda s: s.mean_s())
+    t = dom.mean_s()
+    roof = {"bound": dom.bound, "achieved": round(dom.work / t / (1e9 if dom.bound == "hbm" else 1e12), 2),
+            "peak": (HBM_PEAK / 1e9) if dom.bound == "hbm" else (FP4_PEAK / 1e12),
+            "unit": "GB/s" if dom.bound == "hbm" else "TFLOP/s",
+            "frac": round(dom.ideal_s() / t, 4), "traffic": None, "kernel": dom.name}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(stages, ideal)
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "% of 1-GPU roofline", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4_e2m1",
+            "data": "synthetic",
+            "config": {"workload": "nvfp4_add_rmsnorm_quant_m4096_h4096 + "
+                                   "mxfp4_prefill_gemm_bias_residual (8192,14336,4096),(8192,4096,14336) + "
+                                   "nvfp4_chain_m2048_h5120_n17408",
+                       "parallelism": "none (1 GPU)"},
+            "roofline": roof, "cpu_baseline": cpu, "kernels": kernels}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+"""Python binding of liblowbit.so, the MI355X (gfx950) low-bit linear hot path.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of liblowbit.so (see include/lowbit.h for the contract of each call).
+PyTorch supplies device memory and the current stream.  Outputs may be passed
+in; when omitted they are allocated here (the C ABI itself never allocates).
+
+If the native library is missing, every call raises: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+NVFP4, MXFP4 = 0, 1
+LINEAR, TILED = 0, 1
+VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = -1, 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowbit.so")
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "misaligned pointer", 3: "unsupported shape",
+           4: "device is not gfx950", 5: "HIP runtime error"}
+
+# exported symbols (the entry points of include/lowbit.h)
+EXPORTS = (
+    "lowbit_status_str", "lowbit_sf_bytes", "lowbit_add_rmsnorm_quant", "lowbit_quantize",
+    "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
+    "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
+    "lowbit_gemm_pick_variant",
+)
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS.get(status, 'unknown status')} (status {status})")
+
+
+_lib = None
+_vp, _i64, _int, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+
+
+def lib():
+    """The loaded liblowbit.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"liblowbit.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.lowbit_status_str.restype = ctypes.c_char_p
+        L.lowbit_status_str.argtypes = [_int]
+        L.lowbit_sf_bytes.restype = ctypes.c_size_t
+        L.lowbit_sf_bytes.argtypes = [_i64, _i64, _int, _int]
+        L.lowbit_add_rmsnorm_quant.restype = _int
+        L.lowbit_add_rmsnorm_quant.argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _vp, _vp, _vp]
+        L.lowbit_quantize.restype = _int
+        L.lowbit_quantize.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]
+        L.lowbit_dequantize.restype = _int
+        L.lowbit_dequantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
+        head = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f32]
+        L.lowbit_gemm_bf16.argtypes = head + [_vp, _int, _vp]
+        L.lowbit_gemm_bias_bf16.argtypes = head + [_vp, _vp, _int, _vp]
+        L.lowbit_gemm_residual_bf16.argtypes = head + [_vp, _vp, _int, _vp]
+        L.lowbit_gemm_bias_residual_bf16.argtypes = head + [_vp, _vp, _vp, _int, _vp]
+        L.lowbit_gemm_bias_gelu_bf16.argtypes = head + [_vp, _vp, _int, _vp]
+        L.lowbit_gemm_bias_gelu_fp4.argtypes = head + [_vp, _vp, _vp, _vp, _int, _int, _vp]
+        for n in ("lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
+                  "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16",
+                  "lowbit_gemm_bias_gelu_fp4"):
+            getattr(L, n).restype = _int
+        L.lowbit_gemm_pick_variant.restype = _int
+        L.lowbit_gemm_pick_variant.argtypes = [_i64, _i64, _i64, _int, _int]
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise LowbitError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def block_size(fmt):
+    return 16 if fmt == NVFP4 else 32
+
+
+def lowbit_sf_bytes(rows, k, fmt, layout):
+    return int(lib().lowbit_sf_bytes(rows, k, fmt, layout))
+
+
+def _alloc_q(rows, k, fmt, layout, device, out_packed, out_sf):
+    if out_packed is None:
+        out_packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=device)
+    if out_sf is None:
+        out_sf = torch.empty(lowbit_sf_bytes(rows, k, fmt, layout), dtype=torch.uint8, device=device)
+    return out_packed, out_sf
+
+
+def lowbit_add_rmsnorm_quant(input, residual, weight, eps=1e-6, fmt=NVFP4, layout=LINEAR,
+                             global_scale=None, out_packed=None, out_sf=None, stream=None):
+    """residual += input (in place); y = RMSNorm(residual) * weight; y -> FP4.
+    Returns (packed (M, H/2) uint8, scales uint8)."""
+    _need(input, torch.bfloat16, "input")
+    _need(residual, torch.bfloat16, "residual")
+    _need(weight, torch.bfloat16, "weight")
+    if global_scale is not None:
+        _need(global_scale, torch.float32, "global_scale")
+    M, H = input.shape
+    out_packed, out_sf = _alloc_q(M, H, fmt, layout, input.device, out_packed, out_sf)
+    _check("lowbit_add_rmsnorm_quant", lib().lowbit_add_rmsnorm_quant(
+        _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, layout, _ptr(global_scale),
+        _ptr(out_packed), _ptr(out_sf), _stream(stream)))
+    return out_packed, out_sf
+
+
+def lowbit_quantize(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=None, out_sf=None,
+                    stream=None):
+    _need(x, torch.bfloat16, "x")
+    if global_scale is not None:
+        _need(global_scale, torch.float32, "global_scale")
+    rows, K = x.shape
+    out_packed, out_sf = _alloc_q(rows, K, fmt, layout, x.device, out_packed, out_sf)
+    _check("lowbit_quantize", lib().lowbit_quantize(
+        _ptr(x), rows, K, fmt, layout, _ptr(global_scale), _ptr(out_packed), _ptr(out_sf),
+        _stream(stream)))
+    return out_packed, out_sf
+
+
+def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):
+    _need(packed, torch.uint8, "packed")
+    _need(sf, torch.uint8, "sf")
+    rows, K = packed.shape[0], packed.shape[1] * 2
+    if out is None:
+        out = torch.empty((rows, K), dtype=torch.bfloat16, device=packed.device)
+    _check("lowbit_dequantize", lib().lowbit_dequantize(
+        _ptr(packed), _ptr(sf), rows, K, fmt, layout, _ptr(global_scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha):
+    for t, n in ((a, "a"), (b, "b"), (sfa, "sfa"), (sfb, "sfb")):
+        _need(t, torch.uint8, n)
+    M, N, K = a.shape[0], b.shape[0], a.shape[1] * 2
+    if b.shape[1] * 2 != K:
+        raise ValueError("a and b disagree on K")
+    return M, N, K, [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), M, N, K, fmt, sfa_layout, sfb_layout,
+                     float(alpha)]
+
+
+def _out_bf16(out, M, N, dev):
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out")
+    return out
+
+
+def lowbit_gemm_bf16(a, b, sfa, sfb, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR, alpha=1.0,
+                     out=None, variant=VARIANT_AUTO, stream=None):
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    out = _out_bf16(out, M, N, a.device)
+    _check("lowbit_gemm_bf16", lib().lowbit_gemm_bf16(*head, _ptr(out), variant, _stream(stream)))
+    return out
+
+
+def lowbit_gemm_bias_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
+                          alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    _need(bias, torch.bfloat16, "bias")
+    out = _out_bf16(out, M, N, a.device)
+    _check("lowbit_gemm_bias_bf16",
+           lib().lowbit_gemm_bias_bf16(*head, _ptr(bias), _ptr(out), variant, _stream(stream)))
+    return out
+
+
+def lowbit_gemm_residual_bf16(a, b, sfa, sfb, residual, fmt=NVFP4, sfa_layout=LINEAR,
+                              sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    _need(residual, torch.bfloat16, "residual")
+    out = _out_bf16(out, M, N, a.device)
+    _check("lowbit_gemm_residual_bf16",
+           lib().lowbit_gemm_residual_bf16(*head, _ptr(residual), _ptr(out), variant, _stream(stream)))
+    return out
+
+
+def lowbit_gemm_bias_residual_bf16(a, b, sfa, sfb, bias, residual, fmt=NVFP4, sfa_layout=LINEAR,
+                                   sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO,
+                                   stream=None):
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    _need(bias, torch.bfloat16, "bias")
+    _need(residual, torch.bfloat16, "residual")
+    out = _out_bf16(out, M, N, a.device)
+    _check("lowbit_gemm_bias_residual_bf16", lib().lowbit_gemm_bias_residual_bf16(
+        *head, _ptr(bias), _ptr(residual), _ptr(out), variant, _stream(stream)))
+    return out
+
+
+def lowbit_gemm_bias_gelu_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
+                               alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    _need(bias, torch.bfloat16, "bias")
+    out = _out_bf16(out, M, N, a.device)
+    _check("lowbit_gemm_bias_gelu_bf16",
+           lib().lowbit_gemm_bias_gelu_bf16(*head, _ptr(bias), _ptr(out), variant, _stream(stream)))
+    return out
+
+
+def lowbit_gemm_bias_gelu_fp4(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
+                              alpha=1.0, out_global_scale=None, out_packed=None, out_sf=None,
+                              out_layout=LINEAR, variant=VARIANT_AUTO, stream=None):
+    """GELU(alpha * A.B^T + bias) quantized to NVFP4 along N.  Returns (packed, scales)."""
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    _need(bias, torch.bfloat16, "bias")
+    if out_global_scale is not None:
+        _need(out_global_scale, torch.float32, "out_global_scale")
+    out_packed, out_sf = _alloc_q(M, N, NVFP4, out_layout, a.device, out_packed, out_sf)
+    _check("lowbit_gemm_bias_gelu_fp4", lib().lowbit_gemm_bias_gelu_fp4(
+        *head, _ptr(bias), _ptr(out_global_scale), _ptr(out_packed), _ptr(out_sf), out_layout, variant,
+        _stream(stream)))
+    return out_packed, out_sf
+
+
+def lowbit_gemm_pick_variant(M, N, K, fmt=NVFP4, variant=VARIANT_AUTO):
+    return int(lib().lowbit_gemm_pick_variant(M, N, K, fmt, variant))

@@ -1,0 +1,263 @@
+// api.cpp -- the extern "C" entry points of liblowbit.so: argument checks,
+// device check, schedule choice, launch.  Declared and documented in
+// include/lowbit.h.
+//
+// Checks run in a fixed order -- enums and pointers (EINVAL), sizes (ESHAPE),
+// alignment (EALIGN), then the device (EDEVICE) -- and nothing is launched
+// unless all pass.  The device query happens last, so every argument error is
+// reported the same way with or without a GPU present.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "lowbit.h"
+
+namespace {
+
+using lowbit::GemmArgs;
+
+constexpr int64_t kMaxRowElems = 32768;  // 4 waves x 64 lanes x 128 elements per lane
+
+bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }
+bool layout_ok(int l) { return l == LOWBIT_SF_LINEAR || l == LOWBIT_SF_TILED; }
+int64_t block_of(int f) { return f == LOWBIT_NVFP4 ? 16 : 32; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// gfx950 check, cached per device ordinal.
+lowbit_status device_check() {
+  static std::mutex mu;
+  static int cached[64];  // 0 unknown, 1 ok, 2 not gfx950
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return LOWBIT_EDEVICE;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return LOWBIT_EDEVICE;
+    }
+    cached[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return cached[dev] == 1 ? LOWBIT_OK : LOWBIT_EDEVICE;
+}
+
+lowbit_status from_hip(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_EHIP; }
+
+lowbit_status check_sf_ptr(const void* sf, int layout) {
+  if (layout == LOWBIT_SF_TILED && !aligned(sf, 4)) return LOWBIT_EALIGN;
+  return LOWBIT_OK;
+}
+
+lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                          int64_t M, int64_t N, int64_t K, int fmt, int la, int lb, float alpha,
+                          int epi, const void* bias, const void* residual, void* out,
+                          const float* gs_out, uint8_t* out_packed, uint8_t* out_sf, int out_layout,
+                          int variant, hipStream_t stream) {
+  const bool fp4_out = epi == lowbit::kEpiBiasGeluFp4;
+  // EINVAL: enums and pointers
+  if (!fmt_ok(fmt) || !layout_ok(la) || !layout_ok(lb)) return LOWBIT_EINVAL;
+  if (fp4_out && !layout_ok(out_layout)) return LOWBIT_EINVAL;
+  if (variant < -1 || variant > 1) return LOWBIT_EINVAL;
+  if (M < 0 || N < 0 || K < 0) return LOWBIT_ESHAPE;
+  const bool empty = (M == 0 || N == 0);
+  if (!empty) {
+    if (!a || !b || !sfa || !sfb) return LOWBIT_EINVAL;
+    const bool needs_bias = epi == lowbit::kEpiBias || epi == lowbit::kEpiBiasResidual ||
+                            epi == lowbit::kEpiBiasGelu || fp4_out;
+    const bool needs_res = epi == lowbit::kEpiResidual || epi == lowbit::kEpiBiasResidual;
+    if (needs_bias && !bias) return LOWBIT_EINVAL;
+    if (needs_res && !residual) return LOWBIT_EINVAL;
+    if (fp4_out ? (!out_packed || !out_sf) : !out) return LOWBIT_EINVAL;
+  }
+  // ESHAPE
+  const int64_t B = block_of(fmt);
+  if (K < B || K % B != 0) return LOWBIT_ESHAPE;
+  if (fp4_out && N % 16 != 0) return LOWBIT_ESHAPE;
+  const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant);
+  if (v < 0) return LOWBIT_ESHAPE;
+  if (empty) return LOWBIT_OK;
+  // EALIGN
+  if (!aligned(a, 16) || !aligned(b, 16)) return LOWBIT_EALIGN;
+  if (check_sf_ptr(sfa, la) || check_sf_ptr(sfb, lb)) return LOWBIT_EALIGN;
+  if (bias && !aligned(bias, 16)) return LOWBIT_EALIGN;
+  if (residual && !aligned(residual, 16)) return LOWBIT_EALIGN;
+  if (fp4_out) {
+    if (!aligned(out_packed, 8) || (out_layout == LOWBIT_SF_TILED && !aligned(out_sf, 4)))
+      return LOWBIT_EALIGN;
+    if (gs_out && !aligned(gs_out, 4)) return LOWBIT_EALIGN;
+  } else if (!aligned(out, 16)) {
+    return LOWBIT_EALIGN;
+  }
+  // EDEVICE
+  if (lowbit_status d = device_check()) return d;
+  GemmArgs g{};
+  g.a = a;
+  g.b = b;
+  g.sfa = sfa;
+  g.sfb = sfb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.fmt = fmt;
+  g.la = la;
+  g.lb = lb;
+  g.alpha = alpha;
+  g.epi = epi;
+  g.bias = static_cast<const uint16_t*>(bias);
+  g.residual = static_cast<const uint16_t*>(residual);
+  g.out = static_cast<uint16_t*>(out);
+  g.gs_out = gs_out;
+  g.out_packed = out_packed;
+  g.out_sf = out_sf;
+  g.out_layout = out_layout;
+  if (getenv("LOWBIT_LOG"))
+    fprintf(stderr, "[lowbit] gemm M=%lld N=%lld K=%lld fmt=%d epi=%d variant=%d\n", (long long)M,
+            (long long)N, (long long)K, fmt, epi, v);
+  return from_hip(lowbit::launch_gemm(g, v, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lowbit_status_str(lowbit_status s) {
+  switch (s) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_EINVAL: return "invalid argument";
+    case LOWBIT_EALIGN: return "misaligned pointer";
+    case LOWBIT_ESHAPE: return "unsupported shape";
+    case LOWBIT_EDEVICE: return "device is not gfx950";
+    case LOWBIT_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t lowbit_sf_bytes(int64_t rows, int64_t k, lowbit_format fmt, lowbit_sf_layout layout) {
+  if (!fmt_ok(fmt) || !layout_ok(layout) || rows < 0 || k < 0 || k % block_of(fmt) != 0) return 0;
+  return (size_t)lowbit::sf_bytes_of(layout, rows, k / block_of(fmt));
+}
+
+lowbit_status lowbit_add_rmsnorm_quant(const void* input, void* residual, const void* weight, int64_t M,
+                                       int64_t H, float eps, lowbit_format fmt, lowbit_sf_layout layout,
+                                       const float* global_scale, uint8_t* out_packed, uint8_t* out_sf,
+                                       hipStream_t stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
+  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (M < 0) return LOWBIT_ESHAPE;
+  if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
+  if (H < 64 || H % block_of(fmt) != 0 || H > kMaxRowElems) return LOWBIT_ESHAPE;
+  if (M == 0) return LOWBIT_OK;
+  if (!aligned(input, 16) || !aligned(residual, 16) || !aligned(weight, 16) || !aligned(out_packed, 16))
+    return LOWBIT_EALIGN;
+  if (check_sf_ptr(out_sf, layout) || (global_scale && !aligned(global_scale, 4))) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_add_rmsnorm_quant(
+      static_cast<const uint16_t*>(input), static_cast<uint16_t*>(residual),
+      static_cast<const uint16_t*>(weight), M, H, eps, fmt, layout, global_scale, out_packed, out_sf,
+      stream));
+}
+
+lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
+                              lowbit_sf_layout layout, const float* global_scale, uint8_t* out_packed,
+                              uint8_t* out_sf, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
+  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (rows < 0) return LOWBIT_ESHAPE;
+  if (rows > 0 && (!x || !out_packed || !out_sf)) return LOWBIT_EINVAL;
+  if (K < block_of(fmt) || K % block_of(fmt) != 0 || K > kMaxRowElems) return LOWBIT_ESHAPE;
+  if (rows == 0) return LOWBIT_OK;
+  if (!aligned(x, 16) || !aligned(out_packed, 16)) return LOWBIT_EALIGN;
+  if (check_sf_ptr(out_sf, layout) || (global_scale && !aligned(global_scale, 4))) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_quantize(static_cast<const uint16_t*>(x), rows, K, fmt, layout,
+                                          global_scale, out_packed, out_sf, stream));
+}
+
+lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
+                                lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
+                                void* out, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
+  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (rows < 0) return LOWBIT_ESHAPE;
+  if (rows > 0 && (!packed || !sf || !out)) return LOWBIT_EINVAL;
+  if (K < block_of(fmt) || K % block_of(fmt) != 0) return LOWBIT_ESHAPE;
+  if (rows == 0) return LOWBIT_OK;
+  if (!aligned(packed, 16) || !aligned(out, 16)) return LOWBIT_EALIGN;
+  if (global_scale && !aligned(global_scale, 4)) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_dequantize(packed, sf, rows, K, fmt, layout, global_scale,
+                                            static_cast<uint16_t*>(out), stream));
+}
+
+lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                               int64_t M, int64_t N, int64_t K, lowbit_format fmt,
+                               lowbit_sf_layout sfa_layout, lowbit_sf_layout sfb_layout, float alpha,
+                               void* out, int variant, hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiNone,
+                     nullptr, nullptr, out, nullptr, nullptr, nullptr, 0, variant, stream);
+}
+
+lowbit_status lowbit_gemm_bias_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                    const uint8_t* sfb, int64_t M, int64_t N, int64_t K, lowbit_format fmt,
+                                    lowbit_sf_layout sfa_layout, lowbit_sf_layout sfb_layout, float alpha,
+                                    const void* bias, void* out, int variant, hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiBias, bias,
+                     nullptr, out, nullptr, nullptr, nullptr, 0, variant, stream);
+}
+
+lowbit_status lowbit_gemm_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                        const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                        lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                        lowbit_sf_layout sfb_layout, float alpha, const void* residual,
+                                        void* out, int variant, hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiResidual,
+                     nullptr, residual, out, nullptr, nullptr, nullptr, 0, variant, stream);
+}
+
+lowbit_status lowbit_gemm_bias_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                             const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                             lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                             lowbit_sf_layout sfb_layout, float alpha, const void* bias,
+                                             const void* residual, void* out, int variant,
+                                             hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha,
+                     lowbit::kEpiBiasResidual, bias, residual, out, nullptr, nullptr, nullptr, 0, variant,
+                     stream);
+}
+
+lowbit_status lowbit_gemm_bias_gelu_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                         const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                         lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                         lowbit_sf_layout sfb_layout, float alpha, const void* bias,
+                                         void* out, int variant, hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiBiasGelu,
+                     bias, nullptr, out, nullptr, nullptr, nullptr, 0, variant, stream);
+}
+
+lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                        const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                        lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                        lowbit_sf_layout sfb_layout, float alpha, const void* bias,
+                                        const float* out_global_scale, uint8_t* out_packed,
+                                        uint8_t* out_sf, lowbit_sf_layout out_layout, int variant,
+                                        hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha,
+                     lowbit::kEpiBiasGeluFp4, bias, nullptr, nullptr, out_global_scale, out_packed, out_sf,
+                     out_layout, variant, stream);
+}
+
+int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant) {
+  if (!fmt_ok(fmt) || M < 0 || N < 0 || K < block_of(fmt) || K % block_of(fmt) != 0) return -1;
+  return lowbit::gemm_pick_variant(M, N, K, fmt, variant);
+}
+
+}  // extern "C"

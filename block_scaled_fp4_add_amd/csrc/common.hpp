@@ -1,0 +1,149 @@
+// common.hpp -- device-side building blocks of liblowbit (gfx950 only).
+//
+// Element formats (FP4 E2M1, FP8 E4M3 "FN", UE8M0), the two scale layouts,
+// and wave-level helpers.  Everything here is written for CDNA4: wave64,
+// the hardware FP4 packing conversion and bf16 conversion of gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+constexpr int kWave = 64;
+
+enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1 };
+enum Layout : int { kLinear = 0, kTiled = 1 };
+enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual = 3, kEpiBiasGelu = 4,
+                 kEpiBiasGeluFp4 = 5 };
+
+template <int FMT> struct FmtTraits;
+template <> struct FmtTraits<kNVFP4> { static constexpr int B = 16; };
+template <> struct FmtTraits<kMXFP4> { static constexpr int B = 32; };
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// FP4 E2M1: two fp32 -> one byte (first value in the low nibble).  The gfx950
+// conversion rounds to nearest-even, saturates at +-6 and keeps the sign of a
+// value that rounds to zero; it is applied with a unit scale so that the
+// quantizer's own product v = fl32(y * inv) is what gets rounded.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1x2(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+// Eight fp32 -> 32 bits (element i in nibble i).
+__device__ __forceinline__ uint32_t e2m1x8(const float* v) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
+  return r;
+}
+
+// E2M1 code -> value (sign bit 3): exponent field e (bias 1), mantissa bit m;
+// normal values are (2 + m) * 2^(e-2), the subnormal one is 0.5 * m.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t code) {
+  uint32_t e = (code >> 1) & 3, m = code & 1;
+  float mag = (e == 0) ? 0.5f * (float)m : (float)(2 + m) * __uint_as_float((uint32_t)(125 + e) << 23);
+  return (code & 8) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 E4M3 "FN" (bias 7, max 448, no infinities): encode non-negative finite
+// x with round-to-nearest-even and saturation at 448.  With e = max(floor(
+// log2 x), -6) the grid step there is 2^(e-3); q = rint(x / step) counts
+// steps, and code = (e + 7) * 8 + q - 8 is right both for normals (q in
+// [8, 16], q == 16 carrying into the exponent) and for subnormals (e = -6).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float x) {
+  if (!(x < 448.0f)) return 0x7Eu;
+  int eb = (int)((__float_as_uint(x) >> 23) & 0xFF);
+  int e = eb - 127;
+  if (e < -6) e = -6;
+  float inv_step = __uint_as_float((uint32_t)(127 + 3 - e) << 23);  // 2^(3-e), exact
+  float q = __builtin_rintf(x * inv_step);                           // exact scaling, RNE
+  int code = (e + 7) * 8 + (int)q - 8;
+  return code > 0x7E ? 0x7Eu : (uint32_t)code;
+}
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 15, m = b & 7;
+  float v = (e == 0) ? (float)m * 0x1p-9f : (float)(8 + m) * __uint_as_float((e + 117u) << 23);
+  return (b & 0x80) ? -v : v;
+}
+// UE8M0 byte -> 2^(b-127) for b in [1, 254]; b == 0 gives 2^-127 (subnormal).
+__device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
+  return b == 0 ? 0x1p-127f : __uint_as_float(b << 23);
+}
+
+// ---------------------------------------------------------------------------
+// Scale layouts.  LINEAR: row * nblk + kb.  TILED: 32-row x 8-block groups of
+// 256 bytes; word ((kb%8)/4)*32 + row%32 holds blocks 4*((kb%8)/4)..+3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t sf_offset(int layout, int64_t row, int64_t kb, int64_t nblk) {
+  if (layout == kLinear) return row * nblk + kb;
+  int64_t ktiles = (nblk + 7) >> 3;
+  int64_t j = kb & 7;
+  return (((row >> 5) * ktiles + (kb >> 3)) << 8) + ((((j >> 2) << 5) + (row & 31)) << 2) + (j & 3);
+}
+__host__ __device__ inline int64_t sf_bytes_of(int layout, int64_t rows, int64_t nblk) {
+  if (layout == kLinear) return rows * nblk;
+  return ((rows + 31) / 32) * ((nblk + 7) / 8) * 256;
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (wave64, butterfly over all lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// GELU with the exact erf form, fp32.
+__device__ __forceinline__ float gelu_erf(float t) {
+  return 0.5f * t * (1.0f + erff(t * 0.70710678118654752440f));
+}
+
+// NVFP4 block scale from a block amax (E4M3 byte and the fp32 inverse used
+// to scale the block's values), global scale gs folded in:
+//   s = E4M3(min(fl32(fl32(gs * amax) / 6), 448)), inv = s ? fl32(fl32(1/s) * gs) : 0
+__device__ __forceinline__ uint32_t nv_block_scale(float amax, float gs, float* inv) {
+  float t = __fmul_rn(gs, amax);
+  float s_pre = fminf(__fdiv_rn(t, 6.0f), 448.0f);
+  uint32_t sb = e4m3_encode_nonneg(s_pre);
+  float sdec = e4m3_to_f32(sb);
+  *inv = (sdec == 0.0f) ? 0.0f : __fmul_rn(__fdiv_rn(1.0f, sdec), gs);
+  return sb;
+}
+// MXFP4 block scale (OCP MX): e = clamp(floor(log2 amax) - 2, -127, 127);
+// returns the byte e + 127 and the exact power of two 2^-e.
+__device__ __forceinline__ uint32_t mx_block_scale(float amax, float* inv) {
+  int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);  // amax >= 0, finite
+  int sb = eb - 2;
+  if (sb < 0) sb = 0;                                     // e = -127 (also amax == 0 / subnormal)
+  *inv = __uint_as_float((uint32_t)(254 - sb) << 23);     // 2^(127 - sb) = 2^-e
+  return (uint32_t)sb;
+}
+
+}  // namespace lowbit

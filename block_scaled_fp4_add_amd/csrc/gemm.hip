@@ -1,0 +1,538 @@
+// gemm.hip -- block-scaled A4W4 GEMM for gfx950, out = epilogue(alpha * A . B^T)
+// (FlashRT fp4-gemm README: nvfp4_gemm_bf16 and its epilogue family, the
+// "Tensor Contract": A (M, K/2) and B (N, K/2) packed FP4 plus block scales).
+//
+// Contraction unit.  K is walked in "supersteps" of 256 elements (128 packed
+// bytes per row).  Inside a superstep, lane (r, c) of a wave (r = lane % 32,
+// c = lane / 32) owns 64 contiguous bytes of row r: elements 128c .. 128c+127.
+// Because a sum over K may be taken in any order as long as A and B agree,
+// both operands use this same assignment:
+//   MXFP4: four v_mfma_scale_f32_32x32x64_f8f6f4 per superstep; slice s feeds
+//          the lane's bytes 16s..16s+15, i.e. the 32-element block 4c + s of
+//          the superstep, whose UE8M0 scale is byte s of the lane's scale word
+//          (selected by the instruction's op_sel).  One 32-bit word per lane
+//          therefore feeds the four MFMAs -- the TILED scale layout stores
+//          exactly these words contiguously per 32-row group.
+//   NVFP4: E4M3 16-block scales have no native MFMA form, so each FP4 value
+//          is multiplied by its block scale in fp16 -- exact, since E2M1 times
+//          E4M3 has at most 6 significant bits and lies in [2^-10, 2688] --
+//          and sixteen v_mfma_f32_32x32x16_f16 consume the superstep, step t
+//          using the lane's dword t (block 8c + t/2).
+// Accumulation is fp32 in the MFMA accumulators.
+//
+// Schedules:
+//   prefill: 128x128 macro tiles, 4 waves of 64x64; A and B supersteps are
+//            staged through LDS (two buffers, 16-byte chunks XOR-swizzled by
+//            row so the 32-row fragment reads are bank-conflict free); tiles
+//            are mapped so that consecutive tiles share an XCD's L2.
+//   decode:  the weights are the MFMA row operand (32 weight rows per
+//            workgroup, all <= 128 tokens as the column operand, so each weight
+//            byte is read once); the K supersteps are dealt round-robin to the
+//            workgroup's waves and the partial tiles summed through LDS.
+// Epilogues run per 32x32 tile through LDS so that every global access is a
+// contiguous 16-element run of a row: bf16 out with alpha, bias, residual,
+// GELU; or GELU followed by NVFP4 quantization along N (FP4 output for the
+// next GEMM).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lowbit {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSSBytes = 128;   // packed bytes per row per superstep (256 elements)
+constexpr int kEpiPitch = 36;   // fp32 pitch of a 32x32 epilogue tile in LDS
+
+// 64 bytes of one row held by one lane for one superstep.
+struct Frag {
+  u32x4 q[4];
+};
+
+// A lane's scale bytes for one superstep: MXFP4 4 bytes (blocks 4c..4c+3 of
+// the superstep's 8), NVFP4 8 bytes (blocks 8c..8c+7 of its 16).
+template <int FMT> struct SfWord;
+template <> struct SfWord<kMXFP4> { uint32_t w; };
+template <> struct SfWord<kNVFP4> { uint32_t w[2]; };
+
+template <int FMT>
+__device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int layout, int64_t row,
+                                        int64_t R, int64_t nblk, int64_t ss, int c) {
+  constexpr int NB = (FMT == kMXFP4) ? 4 : 8;
+  // absent rows / blocks carry no data; give them a harmless finite scale
+  constexpr uint32_t kPad = (FMT == kMXFP4) ? 0x7F7F7F7Fu : 0u;
+  uint32_t w[NB / 4];
+#pragma unroll
+  for (int i = 0; i < NB / 4; i++) w[i] = kPad;
+  if (row < R) {
+    const int64_t ktiles = (nblk + 7) >> 3;
+    if (layout == kTiled) {
+      if constexpr (FMT == kMXFP4) {
+        w[0] = *reinterpret_cast<const uint32_t*>(sf + (((row >> 5) * ktiles + ss) << 8) +
+                                                  ((c * 32 + (row & 31)) << 2));
+      } else {
+        const int64_t tile = 2 * ss + c;
+        if (tile < ktiles) {
+          const uint8_t* p = sf + (((row >> 5) * ktiles + tile) << 8) + ((row & 31) << 2);
+          w[0] = *reinterpret_cast<const uint32_t*>(p);
+          w[1] = *reinterpret_cast<const uint32_t*>(p + 128);
+        }
+      }
+    } else {
+      const int64_t kb0 = ss * (2 * NB) + c * NB;
+      const uint8_t* p = sf + row * nblk;
+#pragma unroll
+      for (int j = 0; j < NB; j++) {
+        const int64_t kb = kb0 + j;
+        const uint32_t byte = (kb < nblk) ? (uint32_t)p[kb] : (kPad & 0xFF);
+        w[j >> 2] = (w[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | (byte << (8 * (j & 3)));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NB / 4; i++) {
+    if constexpr (FMT == kMXFP4) out.w = w[0];
+    else out.w[i] = w[i];
+  }
+}
+
+// 64 packed bytes of `row` for superstep ss, lane half c; zero outside.
+__device__ __forceinline__ void load_frag_global(Frag& f, const uint8_t* base, int64_t row, int64_t R,
+                                                 int64_t kbytes, int64_t off) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const int64_t o = off + 16 * s;
+    if (row < R && o + 16 <= kbytes)
+      f.q[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + row * kbytes + o));
+    else
+      f.q[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ v8i as_v8i(u32x4 q) {
+  return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+}
+
+// Scaled FP4 MFMA, slice S of a superstep (op_sel must be a constant).
+template <int S>
+__device__ __forceinline__ v16f mfma_mx(u32x4 a, u32x4 b, v16f acc, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i(a), as_v8i(b), acc, 4, 4, S, (int)sa, S,
+                                                         (int)sb);
+}
+
+// Eight E2M1 codes (one dword, element i in nibble i) times an fp16 block
+// scale -> eight fp16.  The E2M1 magnitudes are fp16 values whose low byte is
+// zero, so a v_perm byte lookup builds their high bytes; the sign bit is moved
+// in, and one packed fp16 multiply per pair applies the scale (exact).
+__device__ __forceinline__ v8h dq8(uint32_t w, v2h s2) {
+  constexpr uint32_t kLutLo = 0x3E3C3800u;  // 0, 0.5, 1, 1.5
+  constexpr uint32_t kLutHi = 0x46444240u;  // 2, 3, 4, 6
+  const uint32_t ev = __builtin_amdgcn_perm(kLutHi, kLutLo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  const uint32_t od = __builtin_amdgcn_perm(kLutHi, kLutLo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+  const v2h p0 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x040C000Cu)) * s2;
+  const v2h p1 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x050C010Cu)) * s2;
+  const v2h p2 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x060C020Cu)) * s2;
+  const v2h p3 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x070C030Cu)) * s2;
+  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ v2h nv_scale2(const SfWord<kNVFP4>& sw, int blk) {
+  const uint32_t b = (sw.w[blk >> 2] >> (8 * (blk & 3))) & 0xFF;
+  const _Float16 h = (_Float16)e4m3_to_f32(b);
+  return v2h{h, h};
+}
+
+__device__ __forceinline__ uint32_t frag_dword(const Frag& f, int t) {
+  const u32x4 q = f.q[t >> 2];
+  switch (t & 3) {
+    case 0: return q.x;
+    case 1: return q.y;
+    case 2: return q.z;
+    default: return q.w;
+  }
+}
+
+// acc[i][j] += A-frag i x B-frag j over one superstep.
+template <int FMT, int TI, int TJ>
+__device__ __forceinline__ void superstep_mma(v16f (&acc)[TI][TJ], const Frag (&fa)[TI], const Frag (&fb)[TJ],
+                                              const SfWord<FMT> (&sa)[TI], const SfWord<FMT> (&sb)[TJ]) {
+  if constexpr (FMT == kMXFP4) {
+#define LB_SLICE(S)                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < TI; i++)                                                   \
+    _Pragma("unroll") for (int j = 0; j < TJ; j++)                                                   \
+      acc[i][j] = mfma_mx<S>(fa[i].q[S], fb[j].q[S], acc[i][j], sa[i].w, sb[j].w);
+    LB_SLICE(0) LB_SLICE(1) LB_SLICE(2) LB_SLICE(3)
+#undef LB_SLICE
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; t++) {
+      v8h va[TI], vb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; i++) va[i] = dq8(frag_dword(fa[i], t), nv_scale2(sa[i], t >> 1));
+#pragma unroll
+      for (int j = 0; j < TJ; j++) vb[j] = dq8(frag_dword(fb[j], t), nv_scale2(sb[j], t >> 1));
+#pragma unroll
+      for (int i = 0; i < TI; i++)
+#pragma unroll
+        for (int j = 0; j < TJ; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue on one 16-element run of output row m (columns n .. n+15), values
+// from LDS.  n is a multiple of 16.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__device__ __forceinline__ void epi_run16(const float* t, int64_t m, int64_t n, const GemmArgs& g) {
+  if (m >= g.M || n >= g.N) return;
+  const float alpha = g.alpha;
+  if constexpr (EPI == kEpiBiasGeluFp4) {
+    // N % 16 == 0, so the whole block is in range
+    float y[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      const float z = alpha * t[k] + bf16_to_f32(g.bias[n + k]);
+      y[k] = gelu_erf(z);
+      amax = fmaxf(amax, fabsf(y[k]));
+    }
+    float inv;
+    const float gs = g.gs_out ? *g.gs_out : 1.0f;
+    const uint32_t sb = nv_block_scale(amax, gs, &inv);
+#pragma unroll
+    for (int k = 0; k < 16; k++) y[k] = __fmul_rn(y[k], inv);
+    uint2 p;
+    p.x = e2m1x8(y);
+    p.y = e2m1x8(y + 8);
+    *reinterpret_cast<uint2*>(g.out_packed + m * (g.N / 2) + n / 2) = p;
+    g.out_sf[sf_offset(g.out_layout, m, n / 16, g.N / 16)] = (uint8_t)sb;
+  } else {
+    const bool vec = (g.N % 8) == 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int64_t nn = n + 8 * h;
+      if (nn >= g.N) break;
+      float z[8];
+#pragma unroll
+      for (int k = 0; k < 8; k++) z[k] = alpha * t[8 * h + k];
+      if (vec && nn + 8 <= g.N) {
+        if constexpr (EPI == kEpiBias || EPI == kEpiBiasResidual || EPI == kEpiBiasGelu) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(g.bias + nn);
+          const uint32_t* bw = reinterpret_cast<const uint32_t*>(&bv);
+#pragma unroll
+          for (int k = 0; k < 4; k++) { z[2 * k] += bf16_lo(bw[k]); z[2 * k + 1] += bf16_hi(bw[k]); }
+        }
+        if constexpr (EPI == kEpiResidual || EPI == kEpiBiasResidual) {
+          const uint4 rv = *reinterpret_cast<const uint4*>(g.residual + m * g.N + nn);
+          const uint32_t* rw = reinterpret_cast<const uint32_t*>(&rv);
+#pragma unroll
+          for (int k = 0; k < 4; k++) { z[2 * k] += bf16_lo(rw[k]); z[2 * k + 1] += bf16_hi(rw[k]); }
+        }
+        if constexpr (EPI == kEpiBiasGelu) {
+#pragma unroll
+          for (int k = 0; k < 8; k++) z[k] = gelu_erf(z[k]);
+        }
+        uint4 o;
+        o.x = pack_bf16x2(z[0], z[1]);
+        o.y = pack_bf16x2(z[2], z[3]);
+        o.z = pack_bf16x2(z[4], z[5]);
+        o.w = pack_bf16x2(z[6], z[7]);
+        *reinterpret_cast<uint4*>(g.out + m * g.N + nn) = o;
+      } else {
+        for (int k = 0; k < 8 && nn + k < g.N; k++) {
+          float v = z[k];
+          if constexpr (EPI == kEpiBias || EPI == kEpiBiasResidual || EPI == kEpiBiasGelu)
+            v += bf16_to_f32(g.bias[nn + k]);
+          if constexpr (EPI == kEpiResidual || EPI == kEpiBiasResidual)
+            v += bf16_to_f32(g.residual[m * g.N + nn + k]);
+          if constexpr (EPI == kEpiBiasGelu) v = gelu_erf(v);
+          g.out[m * g.N + nn + k] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+// Zero the TILED padding of the FP4 output scales that this workgroup owns:
+// rows [max(M, r0), min(rows_pad, r1)) x blocks [b0, b1), and, for the
+// workgroup holding the last column block, blocks [nblk, nblk_pad) of rows
+// [r0, min(rows_pad, r1)).
+__device__ __forceinline__ void fp4_out_padding(const GemmArgs& g, int64_t r0, int64_t r1, int64_t b0,
+                                                int64_t b1, bool last_col_tile, int tid, int nthreads) {
+  if (g.out_layout != kTiled) return;
+  const int64_t nblk = g.N / 16;
+  const int64_t nblk_pad = (nblk + 7) / 8 * 8;
+  const int64_t rows_pad = (g.M + 31) / 32 * 32;
+  const int64_t re = r1 < rows_pad ? r1 : rows_pad;
+  const int64_t be = b1 < nblk ? b1 : nblk;
+  const int64_t rs = r0 > g.M ? r0 : g.M;
+  if (rs < re && b0 < be) {
+    const int64_t cnt = (re - rs) * (be - b0);
+    for (int64_t i = tid; i < cnt; i += nthreads)
+      g.out_sf[sf_offset(kTiled, rs + i / (be - b0), b0 + i % (be - b0), nblk)] = 0;
+  }
+  if (last_col_tile && nblk_pad > nblk && r0 < re) {
+    const int64_t w = nblk_pad - nblk;
+    const int64_t cnt = (re - r0) * w;
+    for (int64_t i = tid; i < cnt; i += nthreads)
+      g.out_sf[sf_offset(kTiled, r0 + i / w, nblk + i % w, nblk)] = 0;
+  }
+}
+
+// ===========================================================================
+// Prefill schedule
+// ===========================================================================
+constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 2;
+constexpr int kPThreads = kPWM * kPWN * 64;
+constexpr int kPStage = (kPBM + kPBN) * kSSBytes;        // 32 KiB per LDS buffer
+constexpr int kPLoads = (kPBM + kPBN) * 8 / kPThreads;   // 16-byte chunks per thread per superstep
+
+// 16-byte chunk position of (row, chunk) in an LDS stage: rows of 128 bytes,
+// chunk index XOR-ed with a row function so that the 32 rows read by one
+// fragment load spread over all banks (8- and 16-lane groups alike).
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  const int f = (row & 7) ^ ((row >> 3) & 1);
+  return row * kSSBytes + ((chunk ^ f) << 4);
+}
+
+template <int FMT, int EPI>
+__global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(GemmArgs g) {
+  constexpr int TI = kPBM / kPWM / 32, TJ = kPBN / kPWN / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPStage];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, c = lane >> 5;
+  const int wm = wave / kPWN, wn = wave % kPWN;
+
+  // tile mapping: consecutive tiles on one XCD (workgroups are dealt to the 8
+  // XCDs round-robin), then a grouped raster of 8 tile-rows
+  const int64_t tiles_m = (g.M + kPBM - 1) / kPBM, tiles_n = (g.N + kPBN - 1) / kPBN;
+  const int64_t T = tiles_m * tiles_n;
+  int64_t t = blockIdx.x;
+  if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
+  const int64_t group = 8 * tiles_n;
+  const int64_t first_m = (t / group) * 8;
+  const int64_t gsz = (tiles_m - first_m) < 8 ? (tiles_m - first_m) : 8;
+  const int64_t tm = first_m + (t % group) % gsz;
+  const int64_t tn = (t % group) / gsz;
+  const int64_t m0 = tm * kPBM, n0 = tn * kPBN;
+
+  const int64_t kbytes = g.K / 2;
+  const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
+  const int64_t nss = (g.K + 255) / 256;
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; i++)
+#pragma unroll
+    for (int j = 0; j < TJ; j++) acc[i][j] = v16f{};
+
+  u32x4 stage[kPLoads];
+  SfWord<FMT> sa[TI], sb[TJ], sa_n[TI], sb_n[TJ];
+
+  auto gload = [&](int64_t ss) {
+#pragma unroll
+    for (int i = 0; i < kPLoads; i++) {
+      const int q = tid + i * kPThreads;
+      const int row = q >> 3, ch = q & 7;
+      const int64_t o = ss * kSSBytes + ch * 16;
+      const uint8_t* src;
+      bool ok;
+      if (row < kPBM) {
+        ok = (m0 + row < g.M) && (o + 16 <= kbytes);
+        src = g.a + (m0 + row) * kbytes + o;
+      } else {
+        ok = (n0 + row - kPBM < g.N) && (o + 16 <= kbytes);
+        src = g.b + (n0 + row - kPBM) * kbytes + o;
+      }
+      stage[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sload = [&](int64_t ss, SfWord<FMT> (&xa)[TI], SfWord<FMT> (&xb)[TJ]) {
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+      load_sf<FMT>(xa[i], g.sfa, g.la, m0 + wm * TI * 32 + i * 32 + r, g.M, nblk, ss, c);
+#pragma unroll
+    for (int j = 0; j < TJ; j++)
+      load_sf<FMT>(xb[j], g.sfb, g.lb, n0 + wn * TJ * 32 + j * 32 + r, g.N, nblk, ss, c);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPLoads; i++) {
+      const int q = tid + i * kPThreads;
+      *reinterpret_cast<u32x4*>(smem + buf * kPStage + lds_off(q >> 3, q & 7)) = stage[i];
+    }
+  };
+  auto compute = [&](int buf) {
+    Frag fa[TI], fb[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+      const int row = wm * TI * 32 + i * 32 + r;
+#pragma unroll
+      for (int s = 0; s < 4; s++)
+        fa[i].q[s] = *reinterpret_cast<const u32x4*>(smem + buf * kPStage + lds_off(row, 4 * c + s));
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; j++) {
+      const int row = kPBM + wn * TJ * 32 + j * 32 + r;
+#pragma unroll
+      for (int s = 0; s < 4; s++)
+        fb[j].q[s] = *reinterpret_cast<const u32x4*>(smem + buf * kPStage + lds_off(row, 4 * c + s));
+    }
+    superstep_mma<FMT, TI, TJ>(acc, fa, fb, sa, sb);
+  };
+
+  if (nss > 0) {
+    gload(0);
+    sload(0, sa, sb);
+    lstore(0);
+    __syncthreads();
+    for (int64_t ss = 0; ss < nss; ss++) {
+      const int buf = (int)(ss & 1);
+      const bool more = ss + 1 < nss;
+      if (more) {
+        gload(ss + 1);
+        sload(ss + 1, sa_n, sb_n);
+      }
+      compute(buf);
+      if (more) {
+        lstore(buf ^ 1);
+#pragma unroll
+        for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
+#pragma unroll
+        for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue: each wave stages its 32x32 tiles through its own LDS slice
+  float* et = reinterpret_cast<float*>(smem) + wave * 32 * kEpiPitch;
+  const int er = lane >> 1, ec = (lane & 1) * 16;
+#pragma unroll
+  for (int i = 0; i < TI; i++) {
+#pragma unroll
+    for (int j = 0; j < TJ; j++) {
+#pragma unroll
+      for (int k = 0; k < 16; k++) et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiPitch + r] = acc[i][j][k];
+      __syncthreads();
+      epi_run16<EPI>(et + er * kEpiPitch + ec, m0 + wm * TI * 32 + i * 32 + er,
+                     n0 + wn * TJ * 32 + j * 32 + ec, g);
+      __syncthreads();
+    }
+  }
+  if constexpr (EPI == kEpiBiasGeluFp4)
+    fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
+}
+
+// ===========================================================================
+// Decode schedule (weights as the MFMA row operand, K split across waves)
+// ===========================================================================
+template <int FMT, int MT, int W, int EPI>
+__global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) float red[W * MT * 64 * 16];
+  __shared__ __attribute__((aligned(16))) float tile[MT * 32 * kEpiPitch];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, c = lane >> 5;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t kbytes = g.K / 2;
+  const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
+  const int64_t nss = (g.K + 255) / 256;
+
+  v16f acc[1][MT];
+#pragma unroll
+  for (int i = 0; i < MT; i++) acc[0][i] = v16f{};
+
+  for (int64_t ss = wave; ss < nss; ss += W) {
+    Frag fw[1], fx[MT];
+    SfWord<FMT> sw[1], sx[MT];
+    load_frag_global(fw[0], g.b, n0 + r, g.N, kbytes, ss * kSSBytes + 64 * c);
+    load_sf<FMT>(sw[0], g.sfb, g.lb, n0 + r, g.N, nblk, ss, c);
+#pragma unroll
+    for (int i = 0; i < MT; i++) {
+      load_frag_global(fx[i], g.a, 32 * i + r, g.M, kbytes, ss * kSSBytes + 64 * c);
+      load_sf<FMT>(sx[i], g.sfa, g.la, 32 * i + r, g.M, nblk, ss, c);
+    }
+    superstep_mma<FMT, 1, MT>(acc, fw, fx, sw, sx);
+  }
+
+  // cross-wave sum of the partial C^T tiles
+#pragma unroll
+  for (int i = 0; i < MT; i++)
+#pragma unroll
+    for (int k = 0; k < 16; k++) red[((wave * MT + i) * 64 + lane) * 16 + k] = acc[0][i][k];
+  __syncthreads();
+  for (int e = tid; e < MT * 64 * 16; e += W * 64) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; w++) s += red[w * MT * 64 * 16 + e];
+    // e = (i * 64 + l) * 16 + k: C^T row n = (k/4)*8 + (l/32)*4 + k%4, column m = l % 32
+    const int i = e / 1024, l = (e / 16) % 64, k = e % 16;
+    const int nl = (k >> 2) * 8 + (l >> 5) * 4 + (k & 3), ml = l & 31;
+    tile[(i * 32 + ml) * kEpiPitch + nl] = s;
+  }
+  __syncthreads();
+  if (wave < MT) {
+    const int er = lane >> 1, ec = (lane & 1) * 16;
+    epi_run16<EPI>(tile + (wave * 32 + er) * kEpiPitch + ec, wave * 32 + er, n0 + ec, g);
+  }
+  if constexpr (EPI == kEpiBiasGeluFp4)
+    fp4_out_padding(g, 0, (g.M + 31) / 32 * 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, tid, W * 64);
+}
+
+template <int FMT, int EPI>
+hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
+  if (variant == 0) {
+    const unsigned grid = (unsigned)((g.N + 31) / 32);
+    const int mt = (int)((g.M + 31) / 32);
+#define LB_DEC(MT, W)                                                                          \
+    if (mt == MT) {                                                                            \
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, MT, W, EPI>), dim3(grid), dim3(W * 64), 0, s, g); \
+      return hipGetLastError();                                                                \
+    }
+    LB_DEC(1, 8) LB_DEC(2, 8) LB_DEC(3, 4) LB_DEC(4, 4)
+#undef LB_DEC
+    return hipErrorInvalidValue;
+  }
+  const int64_t T = ((g.M + kPBM - 1) / kPBM) * ((g.N + kPBN - 1) / kPBN);
+  hipLaunchKernelGGL((gemm_prefill_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const GemmArgs& g, int variant, hipStream_t s) {
+  switch (g.epi) {
+    case kEpiNone: return launch_fmt_epi<FMT, kEpiNone>(g, variant, s);
+    case kEpiBias: return launch_fmt_epi<FMT, kEpiBias>(g, variant, s);
+    case kEpiResidual: return launch_fmt_epi<FMT, kEpiResidual>(g, variant, s);
+    case kEpiBiasResidual: return launch_fmt_epi<FMT, kEpiBiasResidual>(g, variant, s);
+    case kEpiBiasGelu: return launch_fmt_epi<FMT, kEpiBiasGelu>(g, variant, s);
+    case kEpiBiasGeluFp4: return launch_fmt_epi<FMT, kEpiBiasGeluFp4>(g, variant, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant) {
+  (void)N; (void)K; (void)fmt;
+  if (variant == -1) return M <= 128 ? 0 : 1;
+  if (variant == 0) return M <= 128 ? 0 : -1;   // the decode tile holds at most 128 tokens
+  if (variant == 1) return 1;
+  return -1;
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int variant, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  return g.fmt == kMXFP4 ? launch_fmt<kMXFP4>(g, variant, s) : launch_fmt<kNVFP4>(g, variant, s);
+}
+
+}  // namespace lowbit

@@ -1,0 +1,43 @@
+// launch.hpp -- internal launchers behind the C ABI (arguments already
+// validated by api.cpp; every pointer is a device pointer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w, int64_t M,
+                                    int64_t H, float eps, int fmt, int layout, const float* gs,
+                                    uint8_t* out_packed, uint8_t* out_sf, hipStream_t s);
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
+                           const float* gs, uint8_t* out_packed, uint8_t* out_sf, hipStream_t s);
+
+hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
+                             int layout, const float* gs, uint16_t* out, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* a;
+  const uint8_t* b;
+  const uint8_t* sfa;
+  const uint8_t* sfb;
+  int64_t M, N, K;
+  int fmt;
+  int la, lb;                 // scale layouts of A and B
+  float alpha;
+  int epi;                    // Epi
+  const uint16_t* bias;       // (N) or nullptr
+  const uint16_t* residual;   // (M, N) or nullptr
+  uint16_t* out;              // bf16 (M, N)
+  const float* gs_out;        // FP4 output: global scale or nullptr
+  uint8_t* out_packed;        // FP4 output: (M, N/2)
+  uint8_t* out_sf;            // FP4 output scales
+  int out_layout;
+};
+
+// Schedule resolution shared by the launcher and lowbit_gemm_pick_variant.
+int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant);
+hipError_t launch_gemm(const GemmArgs& g, int variant, hipStream_t s);
+
+}  // namespace lowbit

@@ -1,0 +1,177 @@
+/*
+ * lowbit.h -- C ABI of liblowbit.so, the MI355X (gfx950) low-bit linear hot path:
+ *   - a fused producer: residual += input; y = RMSNorm(residual) * weight;
+ *     y quantized to FP4 E2M1 with per-block scales;
+ *   - standalone FP4 quantize / dequantize of bf16 tensors;
+ *   - a block-scaled A4W4 GEMM, out = epilogue(alpha * A . B^T), with BF16 or
+ *     NVFP4 output.
+ *
+ * Sources of the operations (web pages):
+ *   [FI]  FlashInfer, cute_dsl/add_rmsnorm_fp4quant.py: AddRMSNormFP4QuantKernel
+ *         and add_rmsnorm_fp4quant() (operation list in the module docstring,
+ *         kernel phases 1-3, API asserts and output allocation).
+ *   [FRT] FlashRT fp4-gemm README: "Available Functions", "Tensor Contract",
+ *         the variant list, and the "Validation" paragraph.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees memory, never synchronizes the device, and
+ *     launches only on `stream` (NULL = the null stream).
+ *   - bf16 tensors are row-major uint16 bit patterns.  Packed FP4 tensors are
+ *     row-major uint8 of shape (rows, K/2): element 2j of a row sits in the low
+ *     nibble of byte j, element 2j+1 in the high nibble.
+ *   - Formats: LOWBIT_NVFP4 = 16-element blocks with FP8 E4M3 scales and an
+ *     optional fp32 global scale gs (folded into the block scale on the way
+ *     in: dequant = E2M1 * scale / gs); LOWBIT_MXFP4 = 32-element blocks with
+ *     UE8M0 scales 2^(b-127) (OCP MX: e = floor(log2 amax) - 2).
+ *     Rounding is to nearest, ties to the even code, saturating at 6 (E2M1)
+ *     and 448 (E4M3); the sign of a value that rounds to zero is kept.
+ *   - Scale layouts (per operand, `rows` x `K/B` scale bytes):
+ *       LOWBIT_SF_LINEAR: row-major bytes, offset = row*(K/B) + kb.
+ *       LOWBIT_SF_TILED : rows grouped by 32, blocks by 8; each group is 256
+ *         bytes = 64 little-endian words, word ((kb%8)/4)*32 + row%32 holds
+ *         blocks 4*((kb%8)/4)..+3 of that row (block kb in byte kb%4);
+ *         groups ordered row-group major; size ceil(rows/32)*ceil((K/B)/8)*256;
+ *         padding bytes are written as zero by every producer.  One word per
+ *         MFMA lane feeds four scaled-MFMA K-steps through the byte select.
+ *   - Alignment: packed/bf16 tensor pointers 16 bytes; scale pointers 4 bytes
+ *     (TILED) or 1 byte (LINEAR); global scales 4 bytes.
+ *   - Errors are returned, never raised; on any error nothing is launched and
+ *     no output is touched.  Asynchronous launch failures surface as
+ *     LOWBIT_EHIP.  The device must be gfx950 (LOWBIT_EDEVICE otherwise).
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOWBIT_OK = 0,
+  LOWBIT_EINVAL = 1,      /* bad enum, NULL pointer, format/argument combination */
+  LOWBIT_EALIGN = 2,      /* pointer alignment */
+  LOWBIT_ESHAPE = 3,      /* sizes: K % B, H < 64, rows < 0, variant invalid for the shape */
+  LOWBIT_EDEVICE = 4,     /* current device is not gfx950 */
+  LOWBIT_EHIP = 5,        /* a HIP runtime call or launch failed */
+} lowbit_status;
+
+typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1 } lowbit_format;
+typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1 } lowbit_sf_layout;
+
+/* GEMM schedule: -1 picks by shape; 0 = decode (weights as the MFMA row
+ * operand, K split across the waves of a workgroup, for small M); 1 = prefill
+ * (LDS-staged macro tiles, for large M).  Cf. [FRT] `variant`. */
+#define LOWBIT_VARIANT_AUTO (-1)
+#define LOWBIT_VARIANT_DECODE 0
+#define LOWBIT_VARIANT_PREFILL 1
+
+/* Human-readable name of a status. */
+const char* lowbit_status_str(lowbit_status s);
+
+/* Bytes of the scale buffer for a (rows, k) operand in the given format and
+ * layout (cf. [FRT] sfa_size_bytes).  Returns 0 for invalid arguments. */
+size_t lowbit_sf_bytes(int64_t rows, int64_t k, lowbit_format fmt, lowbit_sf_layout layout);
+
+/* Fused add + RMSNorm + FP4 quantization ([FI] AddRMSNormFP4QuantKernel).
+ * For each of the M rows of H elements:
+ *   h = fl32(input + residual); residual <- bf16(h)            (in place)
+ *   rstd = fl32(1 / sqrt(sum(h^2) / H + eps))   (sum of the fp32 h, in fp64)
+ *   y = fl32(fl32(bf16(h) * rstd) * weight)
+ *   per block: NVFP4 s = E4M3(min(fl32(fl32(gs*amax)/6), 448)),
+ *              inv = fl32(fl32(1/s)*gs) (0 if s == 0), code = E2M1(fl32(y*inv));
+ *              MXFP4 e = clamp(floor(log2 amax) - 2, -127, 127), byte e+127,
+ *              code = E2M1(y * 2^-e).
+ * input, residual: bf16 (M, H); weight: bf16 (H); out_packed: uint8 (M, H/2);
+ * out_sf: lowbit_sf_bytes(M, H, fmt, layout) bytes.
+ * global_scale: NVFP4 only, device fp32[1] or NULL (= 1.0); must be NULL for
+ * MXFP4.  Requires H % B == 0 and H >= 64 ([FI] asserts), M >= 0 (M == 0 is
+ * a no-op).  `input` must not alias `residual`. */
+lowbit_status lowbit_add_rmsnorm_quant(const void* input, void* residual, const void* weight,
+                                       int64_t M, int64_t H, float eps, lowbit_format fmt,
+                                       lowbit_sf_layout layout, const float* global_scale,
+                                       uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
+
+/* Quantize a bf16 (rows, K) tensor: the per-block rule above with y = x
+ * ([FRT] quantize_fp4_sfa_bf16; used for activations and prepacked weights).
+ * Requires K % B == 0, rows >= 0. */
+lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
+                              lowbit_sf_layout layout, const float* global_scale,
+                              uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
+
+/* Dequantize to bf16: x = bf16(fl32(E2M1 * scale / gs)) (NVFP4, gs from
+ * global_scale or 1.0) or bf16(E2M1 * 2^(b-127)) (MXFP4; global_scale NULL)
+ * ([FRT] dequantize_fp4_sfa_fp16, here with bf16 output). */
+lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
+                                lowbit_format fmt, lowbit_sf_layout layout,
+                                const float* global_scale, void* out, hipStream_t stream);
+
+/* Block-scaled A4W4 GEMM ([FRT] nvfp4_gemm_bf16 and its epilogue family).
+ * a: packed (M, K/2); b: packed (N, K/2) (the weight, "B^T" row-major);
+ * sfa / sfb: their scales in sfa_layout / sfb_layout; both operands use `fmt`.
+ * acc[m,n] = sum_k Ahat[m,k] * Bhat[n,k] with Ahat = E2M1 * scale (no global
+ * scale: pass alpha = 1/(gsA*gsB) for NVFP4 operands), accumulated in fp32.
+ * out: bf16 (M, N) = bf16(alpha*acc [+ bias[n]] [+ residual[m,n]]) or
+ * bf16(GELU(alpha*acc + bias[n])), GELU(t) = 0.5 t (1 + erf(t/sqrt 2)).
+ * bias: bf16 (N); residual: bf16 (M, N) (may alias out).
+ * Requires K % B == 0, K >= B, M, N >= 0 (empty is a no-op).
+ * variant: LOWBIT_VARIANT_*; an explicit variant that cannot run the shape
+ * returns LOWBIT_ESHAPE instead of silently picking another schedule. */
+lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                               const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                               lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                               lowbit_sf_layout sfb_layout, float alpha, void* out, int variant,
+                               hipStream_t stream);
+lowbit_status lowbit_gemm_bias_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                    const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                    lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                    lowbit_sf_layout sfb_layout, float alpha, const void* bias,
+                                    void* out, int variant, hipStream_t stream);
+lowbit_status lowbit_gemm_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                        const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                        lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                        lowbit_sf_layout sfb_layout, float alpha,
+                                        const void* residual, void* out, int variant,
+                                        hipStream_t stream);
+lowbit_status lowbit_gemm_bias_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                             const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                             lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                             lowbit_sf_layout sfb_layout, float alpha,
+                                             const void* bias, const void* residual, void* out,
+                                             int variant, hipStream_t stream);
+lowbit_status lowbit_gemm_bias_gelu_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                         const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                         lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                         lowbit_sf_layout sfb_layout, float alpha,
+                                         const void* bias, void* out, int variant,
+                                         hipStream_t stream);
+
+/* GEMM + bias + GELU emitting NVFP4 for the next projection ([FRT]
+ * nvfp4_gemm_bias_gelu_nvfp4: packed FP4 plus scales, no bf16 tensor in
+ * between).  y = fl32(GELU(alpha*acc + bias[n])) is quantized along N in
+ * 16-blocks with E4M3 scales and global scale out_global_scale (device
+ * fp32[1] or NULL = 1.0).  out_packed: uint8 (M, N/2); out_sf:
+ * lowbit_sf_bytes(M, N, LOWBIT_NVFP4, out_layout) bytes.  Requires N % 16 == 0. */
+lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                        const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                        lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                        lowbit_sf_layout sfb_layout, float alpha,
+                                        const void* bias, const float* out_global_scale,
+                                        uint8_t* out_packed, uint8_t* out_sf,
+                                        lowbit_sf_layout out_layout, int variant,
+                                        hipStream_t stream);
+
+/* Which schedule a GEMM call with these sizes would run (-1 auto resolved),
+ * or -1 if the sizes are invalid.  Host-only, launches nothing. */
+int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

@@ -226,8 +226,10 @@ static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes
 }
 
 /* Re-encode a block from a given scale byte (used by the parity checker when
- * the device's scale byte differs inside the tolerance window). */
-void orc_encode_with_scale(const float* y, int B, int fmt, float gs, uint8_t sbyte, uint8_t* codes) {
+ * the device's scale byte differs inside the tolerance window).  v_out
+ * (optional) receives the pre-rounding values. */
+void orc_encode_with_scale(const float* y, int B, int fmt, float gs, uint8_t sbyte, uint8_t* codes,
+                           float* v_out) {
     if (fmt == ORC_NVFP4) {
         float sdec = (float)orc_e4m3_value(sbyte);
         float inv;
@@ -239,11 +241,16 @@ void orc_encode_with_scale(const float* y, int B, int fmt, float gs, uint8_t sby
         }
         for (int i = 0; i < B; i++) {
             volatile float v = y[i] * inv;
+            if (v_out) v_out[i] = v;
             codes[i] = orc_e2m1_encode(v);
         }
     } else {
         int e = (int)sbyte - 127;
-        for (int i = 0; i < B; i++) codes[i] = orc_e2m1_encode(ldexpf(y[i], -e));
+        for (int i = 0; i < B; i++) {
+            float v = ldexpf(y[i], -e);
+            if (v_out) v_out[i] = v;
+            codes[i] = orc_e2m1_encode(v);
+        }
     }
 }
 

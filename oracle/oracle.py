@@ -63,7 +63,7 @@ def lib():
     L.orc_sf_offset.restype = _i64
     L.orc_sf_offset.argtypes = [_i64, _i64, _i64, _int]
     L.orc_encode_with_scale.restype = None
-    L.orc_encode_with_scale.argtypes = [_f32p, _int, _int, ctypes.c_float, ctypes.c_uint8, _u8p]
+    L.orc_encode_with_scale.argtypes = [_f32p, _int, _int, ctypes.c_float, ctypes.c_uint8, _u8p, _vp]
     L.orc_add_rmsnorm_quant.restype = _int
     L.orc_add_rmsnorm_quant.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, ctypes.c_float, _int, _int,
                                         ctypes.c_float, _u8p, _u8p, _vp, _vp, _vp, _vp, _vp]
@@ -133,11 +133,13 @@ def sf_offset(row: int, kb: int, nblk: int, layout: int) -> int:
     return lib().orc_sf_offset(row, kb, nblk, layout)
 
 
-def encode_with_scale(y, fmt: int, gs: float, sbyte: int):
+def encode_with_scale(y, fmt: int, gs: float, sbyte: int, with_v: bool = False):
+    """Codes of the block y under a given scale byte (and the pre-rounding v)."""
     y = _c(y, np.float32)
     out = np.zeros(y.size, dtype=np.uint8)
-    lib().orc_encode_with_scale(y, y.size, fmt, gs, sbyte, out)
-    return out
+    v = np.zeros(y.size, dtype=np.float32)
+    lib().orc_encode_with_scale(y, y.size, fmt, gs, sbyte, out, _ptr(v))
+    return (out, v) if with_v else out
 
 
 # --- tensor entry points --------------------------------------------------------------------

@@ -1,0 +1,183 @@
+"""GPU parity of the memory-bound kernels against the CPU oracle: the fused
+add + RMSNorm + FP4 producer, the quantizer and the dequantizer.  Calls go
+through the C ABI (ctypes binding); inputs are seeded and synthetic."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_add_amd as lb
+from block_scaled_fp4_add_amd import synth
+
+from . import checkers
+from .gpu_util import banner, dev_bf16, dev_f32, dev_u8, host_bits, host_u8
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gs_for(orc, x, r, w, M, H):
+    """NVFP4 global scale 6*448/amax(y), amax from the oracle's own y."""
+    d = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4, orc.LINEAR,
+                              diag=True)
+    return float(np.float32(2688.0 / np.abs(d["y"]).max()))
+
+
+def run_producer(orc, M, H, fmt, layout, seed, outliers=False, use_gs=False):
+    banner(f"producer M={M} H={H} fmt={fmt} layout={layout} seed={seed} gs={use_gs}")
+    x, r, w = synth.producer_inputs(M, H, seed, outliers=outliers)
+    gs = _gs_for(orc, x, r, w, M, H) if (use_gs and fmt == orc.NVFP4) else 1.0
+    ref = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, fmt, layout,
+                                gs=gs, diag=True)
+    xd, rd, wd = dev_bf16(x), dev_bf16(r), dev_bf16(w)
+    sf_n = lb.lowbit_sf_bytes(M, H, fmt, layout)
+    packed = torch.full((M, H // 2), 0xAA, dtype=torch.uint8, device="cuda")
+    sf = torch.full((sf_n,), 0xAA, dtype=torch.uint8, device="cuda")
+    lb.lowbit_add_rmsnorm_quant(xd, rd, wd, EPS, fmt, layout,
+                                global_scale=dev_f32(gs) if (use_gs and fmt == lb.NVFP4) else None,
+                                out_packed=packed, out_sf=sf)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(rd), ref["residual"]), "residual must be bf16(x + r) bit-exact"
+    spre = ref["spre"] if fmt == orc.NVFP4 else ref["amax"]
+    rep = checkers.compare_quantized(orc, fmt, gs, host_u8(packed), host_u8(sf), ref["packed"], ref["sf"],
+                                     ref["y"], ref["v"], spre, M, H, layout)
+    banner(f"  report {dict(rep)}")
+    assert rep.ok(), rep
+    if layout == orc.TILED:
+        assert checkers.tiled_padding_is_zero(orc, host_u8(sf), M, H // (16 if fmt == 0 else 32))
+    return rep
+
+
+SMALL = [(8, 256), (1, 64), (3, 320), (33, 1024), (5, 5120), (1, 5120), (17, 17408), (2, 32768),
+         (70, 4096)]
+
+
+@pytest.mark.parametrize("M,H", SMALL)
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_producer_small(orc, M, H, fmt, layout):
+    run_producer(orc, M, H, fmt, layout, seed=M * 7 + H, outliers=True, use_gs=(fmt == 0))
+
+
+def test_producer_tiny_mxfp4_workload(orc):
+    """8 rows x 256, MXFP4, linear scales (the tiny end-to-end workload)."""
+    c = synth.TINY_MXFP4
+    run_producer(orc, c["M"], c["H"], orc.MXFP4, orc.LINEAR, seed=c["seed"])
+
+
+def test_producer_nvfp4_4096x4096_full(orc):
+    """The memory-bound benchmark workload in full: 4096 x 4096, NVFP4 with
+    1% outlier channels and the global scale 6*448/amax."""
+    c = synth.NVFP4_PRODUCER
+    rep = run_producer(orc, c["M"], c["H"], orc.NVFP4, orc.LINEAR, seed=c["seed"], outliers=True,
+                       use_gs=True)
+    # in-window differences must stay rare
+    assert rep["code_diff_in_window"] + rep["scale_diff_in_window"] <= 0.001 * rep["blocks"]
+
+
+def test_producer_chain_rows(orc):
+    """Producer rows of the NVFP4 chain workload (H = 5120) at M = 1, 128, 2048, TILED scales."""
+    c = synth.NVFP4_CHAIN
+    for M in c["Ms"]:
+        run_producer(orc, M, c["H"], orc.NVFP4, orc.TILED, seed=c["seed"] + M, outliers=True, use_gs=True)
+
+
+def test_producer_constant_rows(orc):
+    with open(os.path.join(GOLDEN, "producer_constant_rows.json")) as f:
+        rows = json.load(f)["rows"]
+    for row in rows:
+        H = row["H"]
+        for fmt in (0, 1):
+            x = torch.full((1, H), row["c"], dtype=torch.bfloat16)
+            r = torch.zeros((1, H), dtype=torch.bfloat16)
+            w = torch.ones((H,), dtype=torch.bfloat16)
+            packed, sf = lb.lowbit_add_rmsnorm_quant(dev_bf16(x), dev_bf16(r), dev_bf16(w), EPS, fmt, 0)
+            want = row["nv"] if fmt == 0 else row["mx"]
+            assert (host_u8(sf) == want["scale_byte"]).all()
+            assert (checkers.unpack_codes(host_u8(packed)) == want["code"]).all()
+
+
+def test_producer_empty_is_noop(orc):
+    z = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(256, dtype=torch.bfloat16, device="cuda")
+    p, s = lb.lowbit_add_rmsnorm_quant(z, z.clone(), w, EPS, 1, 0)
+    assert p.numel() == 0
+
+
+# --- quantize / dequantize ------------------------------------------------------------------
+
+QSHAPES = [(1, 64), (7, 160), (41, 1536), (128, 5120), (5, 17408), (33, 256), (100, 96)]
+
+
+@pytest.mark.parametrize("rows,K", QSHAPES)
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_quantize_bit_exact(orc, rows, K, fmt, layout):
+    if K % (16 if fmt == 0 else 32):
+        pytest.skip("K not a multiple of the block")
+    banner(f"quantize rows={rows} K={K} fmt={fmt} layout={layout}")
+    x = synth.activation(rows, K, seed=rows + K, outliers=True)
+    gs = 3.25 if fmt == 0 else 1.0
+    ref_p, ref_s = orc.quantize(synth.bits(x), fmt, layout, gs=gs)
+    p, s = lb.lowbit_quantize(dev_bf16(x), fmt, layout, global_scale=dev_f32(gs) if fmt == 0 else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(p), ref_p)
+    assert np.array_equal(host_u8(s), ref_s)
+
+
+def test_quantize_hand_blocks(orc):
+    with open(os.path.join(GOLDEN, "hand_blocks.json")) as f:
+        blocks = json.load(f)["blocks"]
+    for blk in blocks:
+        fmt = 0 if blk["fmt"] == "nvfp4" else 1
+        x = torch.tensor(blk["x"], dtype=torch.float32).to(torch.bfloat16).reshape(1, -1)
+        p, s = lb.lowbit_quantize(dev_bf16(x), fmt, 0,
+                                  global_scale=dev_f32(blk["gs"]) if fmt == 0 else None)
+        torch.cuda.synchronize()
+        assert int(host_u8(s)[0]) == blk["scale_byte"], blk["name"]
+        assert checkers.unpack_codes(host_u8(p))[0].tolist() == blk["codes"], blk["name"]
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_dequantize_bit_exact(orc, fmt, layout):
+    rows, K = 37, 512
+    rng = np.random.default_rng(fmt * 2 + layout)
+    packed = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    nb = orc.sf_bytes(rows, K, fmt, layout)
+    if fmt == 0:
+        sf = rng.integers(0, 0x7F, nb, dtype=np.uint8)       # finite E4M3 (no NaN code)
+        gs = 0.75
+    else:
+        sf = rng.integers(100, 150, nb, dtype=np.uint8)
+        gs = 1.0
+    want, _ = orc.dequantize(packed, sf, rows, K, fmt, layout, gs=gs)
+    out = lb.lowbit_dequantize(dev_u8(packed), dev_u8(sf), fmt, layout,
+                               global_scale=dev_f32(gs) if fmt == 0 else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), want)
+
+
+def test_argument_errors_on_device():
+    x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
+    p = torch.empty((4, 50), dtype=torch.uint8, device="cuda")
+    s = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_quantize(x, 1, 0, out_packed=p, out_sf=s)          # K % 32 != 0
+    assert e.value.status == 3
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_quantize(x, 1, 0)          # no scale buffer can be sized: NULL -> invalid argument
+    assert e.value.status == 1
+    w = torch.ones(48, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_add_rmsnorm_quant(x, x.clone(), w, EPS, 0, 0)   # H < 64
+    assert e.value.status == 3
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_add_rmsnorm_quant(x, x.clone(), w, EPS, 1, 0, global_scale=dev_f32(1.0))
+    assert e.value.status == 1
