@@ -84,6 +84,9 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   if (fp4_out && N % 16 != 0) return LOWBIT_ESHAPE;
   const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant);
   if (v < 0) return LOWBIT_ESHAPE;
+  // the prefill schedule addresses each operand through a 32-bit buffer offset
+  if (v == 1 && (M * (K / 2) >= (int64_t(1) << 30) || N * (K / 2) >= (int64_t(1) << 30)))
+    return LOWBIT_ESHAPE;
   if (empty) return LOWBIT_OK;
   // EALIGN
   if (!aligned(a, 16) || !aligned(b, 16)) return LOWBIT_EALIGN;

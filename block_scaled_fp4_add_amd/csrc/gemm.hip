@@ -21,10 +21,11 @@
 // Accumulation is fp32 in the MFMA accumulators.
 //
 // Schedules:
-//   prefill: 128x128 macro tiles, 4 waves of 64x64; A and B supersteps are
-//            staged through LDS (two buffers, 16-byte chunks XOR-swizzled by
-//            row so the 32-row fragment reads are bank-conflict free); tiles
-//            are mapped so that consecutive tiles share an XCD's L2.
+//   prefill: 256x256 macro tiles, 4 waves of 128x128; A and B supersteps are
+//            copied to LDS by buffer loads that write LDS directly (two
+//            buffers, 16-byte chunks XOR-swizzled by row so the 32-row
+//            fragment reads are bank-conflict free); tiles are mapped so that
+//            consecutive tiles share an XCD's L2.
 //   decode:  the weights are the MFMA row operand (32 weight rows per
 //            workgroup, all <= 128 tokens as the column operand, so each weight
 //            byte is read once); the K supersteps are dealt round-robin to the
@@ -185,6 +186,34 @@ __device__ __forceinline__ void superstep_mma(v16f (&acc)[TI][TJ], const Frag (&
   }
 }
 
+// acc[i][j] += quarter S (bytes 16S..16S+15 of each lane's 64) of a superstep:
+// MXFP4 one scaled MFMA per tile pair (op_sel S picks the block's scale
+// byte); NVFP4 four fp16 MFMA steps (block 8c + 2S + t/2).
+template <int FMT, int S, int TI, int TJ>
+__device__ __forceinline__ void quarter_mma(v16f (&acc)[TI][TJ], const u32x4 (&qa)[TI], const u32x4 (&qb)[TJ],
+                                            const SfWord<FMT> (&sa)[TI], const SfWord<FMT> (&sb)[TJ]) {
+  if constexpr (FMT == kMXFP4) {
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+      for (int j = 0; j < TJ; j++) acc[i][j] = mfma_mx<S>(qa[i], qb[j], acc[i][j], sa[i].w, sb[j].w);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      v8h va[TI], vb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][t], nv_scale2(sa[i], 2 * S + (t >> 1)));
+#pragma unroll
+      for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][t], nv_scale2(sb[j], 2 * S + (t >> 1)));
+#pragma unroll
+      for (int i = 0; i < TI; i++)
+#pragma unroll
+        for (int j = 0; j < TJ; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue on one 16-element run of output row m (columns n .. n+15), values
 // from LDS.  n is a multiple of 16.
@@ -289,10 +318,23 @@ __device__ __forceinline__ void fp4_out_padding(const GemmArgs& g, int64_t r0, i
 // ===========================================================================
 // Prefill schedule
 // ===========================================================================
-constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 2;
+// 256 x 256 macro tile, 4 waves of 128 x 128 (16 accumulator tiles of 32 x 32
+// per wave, 256 accumulator registers), one workgroup per CU.  A superstep's
+// A and B rows (512 rows x 128 bytes = 64 KiB) are copied HBM -> LDS by the
+// buffer-load-to-LDS path (no VGPR staging); two LDS buffers double-buffer
+// the K loop.  Out-of-range rows and the K tail are fetched with an
+// out-of-range buffer offset, which the hardware returns as zeros.
+// At 128 x 128 per wave the fragment reads need 64 B/clk/CU of LDS bandwidth
+// at the full MFMA rate, plus 32 B/clk for the stage writes: within the
+// 128 B/clk the CU delivers.
+constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 2;
 constexpr int kPThreads = kPWM * kPWN * 64;
-constexpr int kPStage = (kPBM + kPBN) * kSSBytes;        // 32 KiB per LDS buffer
-constexpr int kPLoads = (kPBM + kPBN) * 8 / kPThreads;   // 16-byte chunks per thread per superstep
+constexpr int kPStage = (kPBM + kPBN) * kSSBytes;         // 64 KiB per LDS buffer
+constexpr int kPUnits = (kPBM + kPBN) * kSSBytes / 16;    // 16-byte units per stage
+constexpr int kPLoads = kPUnits / kPThreads;              // 16 per thread per superstep
+constexpr int kOOB = 0x7FFFFFF0;                          // offset beyond any operand buffer
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 16-byte chunk position of (row, chunk) in an LDS stage: rows of 128 bytes,
 // chunk index XOR-ed with a row function so that the 32 rows read by one
@@ -302,8 +344,10 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * kSSBytes + ((chunk ^ f) << 4);
 }
 
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 template <int FMT, int EPI>
-__global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) {
   constexpr int TI = kPBM / kPWM / 32, TJ = kPBN / kPWN / 32;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPStage];
 
@@ -327,6 +371,10 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(GemmArgs g) {
   const int64_t kbytes = g.K / 2;
   const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
   const int64_t nss = (g.K + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.M * kbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, (int)(g.N * kbytes), 0x00020000);
 
   v16f acc[TI][TJ];
 #pragma unroll
@@ -334,25 +382,36 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TJ; j++) acc[i][j] = v16f{};
 
-  u32x4 stage[kPLoads];
   SfWord<FMT> sa[TI], sb[TJ], sa_n[TI], sb_n[TJ];
 
-  auto gload = [&](int64_t ss) {
+  // Global -> LDS copy of superstep ss into buffer buf.  Unit u = i*256 + tid
+  // lands at byte 16u of the stage (the DMA writes lane l of a wave at base +
+  // 16 l); unit u is position u%8 of row u/8 and holds global chunk
+  // (u%8) ^ f(row).  Absent rows get a base offset past the end of the
+  // buffer, and chunks past K an offset past the end too, so both read as 0.
+  constexpr int kAbsent = 0x40000000;   // > any operand buffer (checked by the host)
+  int base_off[kPLoads];
+  int chunk_off[kPLoads];
+#pragma unroll
+  for (int i = 0; i < kPLoads; i++) {
+    const int u = i * kPThreads + tid;
+    const int row = u >> 3;
+    const int f = (row & 7) ^ ((row >> 3) & 1);
+    chunk_off[i] = ((u & 7) ^ f) * 16;
+    const int64_t gr = (i < kPLoads / 2) ? m0 + row : n0 + row - kPBM;
+    const int64_t R = (i < kPLoads / 2) ? g.M : g.N;
+    base_off[i] = (gr < R) ? (int)(gr * kbytes) + chunk_off[i] : kAbsent;
+  }
+  auto gload = [&](int64_t ss, int buf) {
+    const int so = (int)(ss * kSSBytes);
 #pragma unroll
     for (int i = 0; i < kPLoads; i++) {
-      const int q = tid + i * kPThreads;
-      const int row = q >> 3, ch = q & 7;
-      const int64_t o = ss * kSSBytes + ch * 16;
-      const uint8_t* src;
-      bool ok;
-      if (row < kPBM) {
-        ok = (m0 + row < g.M) && (o + 16 <= kbytes);
-        src = g.a + (m0 + row) * kbytes + o;
-      } else {
-        ok = (n0 + row - kPBM < g.N) && (o + 16 <= kbytes);
-        src = g.b + (n0 + row - kPBM) * kbytes + o;
-      }
-      stage[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)) : u32x4{0u, 0u, 0u, 0u};
+      const int voff = (so + chunk_off[i] + 16 <= (int)kbytes) ? base_off[i] + so : kAbsent;
+      lds_ptr_t dst = (lds_ptr_t)(smem + buf * kPStage + (i * kPThreads + wave * 64) * 16);
+      if (i < kPLoads / 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, voff, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, voff, 0, 0, 0);
     }
   };
   auto sload = [&](int64_t ss, SfWord<FMT> (&xa)[TI], SfWord<FMT> (&xb)[TJ]) {
@@ -363,57 +422,76 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(GemmArgs g) {
     for (int j = 0; j < TJ; j++)
       load_sf<FMT>(xb[j], g.sfb, g.lb, n0 + wn * TJ * 32 + j * 32 + r, g.N, nblk, ss, c);
   };
-  auto lstore = [&](int buf) {
+  // fragment quarter q (bytes 16q..16q+15 of each lane's 64) of buffer buf
+  auto frags = [&](int buf, int q, u32x4 (&qa)[TI], u32x4 (&qb)[TJ]) {
+    const uint8_t* base = smem + buf * kPStage;
 #pragma unroll
-    for (int i = 0; i < kPLoads; i++) {
-      const int q = tid + i * kPThreads;
-      *reinterpret_cast<u32x4*>(smem + buf * kPStage + lds_off(q >> 3, q & 7)) = stage[i];
-    }
+    for (int i = 0; i < TI; i++)
+      qa[i] = *reinterpret_cast<const u32x4*>(base + lds_off(wm * TI * 32 + i * 32 + r, 4 * c + q));
+#pragma unroll
+    for (int j = 0; j < TJ; j++)
+      qb[j] = *reinterpret_cast<const u32x4*>(base + lds_off(kPBM + wn * TJ * 32 + j * 32 + r, 4 * c + q));
   };
-  auto compute = [&](int buf) {
-    Frag fa[TI], fb[TJ];
+  // interleave the next quarter's LDS reads with this quarter's MFMAs
+  auto interleave = [&]() {
+    if constexpr (FMT == kMXFP4) {
 #pragma unroll
-    for (int i = 0; i < TI; i++) {
-      const int row = wm * TI * 32 + i * 32 + r;
-#pragma unroll
-      for (int s = 0; s < 4; s++)
-        fa[i].q[s] = *reinterpret_cast<const u32x4*>(smem + buf * kPStage + lds_off(row, 4 * c + s));
+      for (int k = 0; k < TI + TJ; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - (TI + TJ), 0);
     }
-#pragma unroll
-    for (int j = 0; j < TJ; j++) {
-      const int row = kPBM + wn * TJ * 32 + j * 32 + r;
-#pragma unroll
-      for (int s = 0; s < 4; s++)
-        fb[j].q[s] = *reinterpret_cast<const u32x4*>(smem + buf * kPStage + lds_off(row, 4 * c + s));
-    }
-    superstep_mma<FMT, TI, TJ>(acc, fa, fb, sa, sb);
   };
 
   if (nss > 0) {
-    gload(0);
+    u32x4 qa[TI], qb[TJ], na[TI], nb[TJ];
+    gload(0, 0);
     sload(0, sa, sb);
-    lstore(0);
+    wait_vm_all();
     __syncthreads();
+    frags(0, 0, qa, qb);
     for (int64_t ss = 0; ss < nss; ss++) {
       const int buf = (int)(ss & 1);
-      const bool more = ss + 1 < nss;
-      if (more) {
-        gload(ss + 1);
-        sload(ss + 1, sa_n, sb_n);
-      }
-      compute(buf);
-      if (more) {
-        lstore(buf ^ 1);
-#pragma unroll
-        for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
-#pragma unroll
-        for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
-      }
+      // superstep ss+1 streams into the other buffer while ss is multiplied
+      // (past the end of K it reads zeros into a buffer nobody reads)
+      gload(ss + 1, buf ^ 1);
+      sload(ss + 1 < nss ? ss + 1 : ss, sa_n, sb_n);
+      __builtin_amdgcn_sched_barrier(0);
+      frags(buf, 1, na, nb);
+      quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      frags(buf, 2, qa, qb);
+      quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      frags(buf, 3, na, nb);
+      quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // every wave has read all of buffer buf; superstep ss+1 must have landed
+      wait_vm_all();
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      frags(buf ^ 1, 0, qa, qb);
+      quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
+#pragma unroll
+      for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
     }
+    // the last gload wrote zeros into the other buffer; it lands before the
+    // LDS is reused by the epilogue
+    wait_vm_all();
+    __syncthreads();
   }
 
-  // epilogue: each wave stages its 32x32 tiles through its own LDS slice
+  // epilogue: each wave stages its 32x32 tiles through its own LDS slice;
+  // LDS instructions of one wave execute in order, so a wave-level barrier
+  // (no workgroup barrier) orders the writes before the reads
   float* et = reinterpret_cast<float*>(smem) + wave * 32 * kEpiPitch;
   const int er = lane >> 1, ec = (lane & 1) * 16;
 #pragma unroll
@@ -422,10 +500,14 @@ __global__ __launch_bounds__(kPThreads) void gemm_prefill_kernel(GemmArgs g) {
     for (int j = 0; j < TJ; j++) {
 #pragma unroll
       for (int k = 0; k < 16; k++) et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiPitch + r] = acc[i][j][k];
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       epi_run16<EPI>(et + er * kEpiPitch + ec, m0 + wm * TI * 32 + i * 32 + er,
                      n0 + wn * TJ * 32 + j * 32 + ec, g);
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
   if constexpr (EPI == kEpiBiasGeluFp4)
