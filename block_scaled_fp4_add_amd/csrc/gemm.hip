@@ -3,21 +3,22 @@
 // "Tensor Contract": A (M, K/2) and B (N, K/2) packed FP4 plus block scales).
 //
 // Contraction unit.  K is walked in "supersteps" of 256 elements (128 packed
-// bytes per row).  Inside a superstep, lane (r, c) of a wave (r = lane % 32,
-// c = lane / 32) owns 64 contiguous bytes of row r: elements 128c .. 128c+127.
-// Because a sum over K may be taken in any order as long as A and B agree,
-// both operands use this same assignment:
-//   MXFP4: four v_mfma_scale_f32_32x32x64_f8f6f4 per superstep; slice s feeds
-//          the lane's bytes 16s..16s+15, i.e. the 32-element block 4c + s of
-//          the superstep, whose UE8M0 scale is byte s of the lane's scale word
-//          (selected by the instruction's op_sel).  One 32-bit word per lane
-//          therefore feeds the four MFMAs -- the TILED scale layout stores
-//          exactly these words contiguously per 32-row group.
+// bytes per row), each made of two 128-element stages h = 0, 1.  Lane (r, c)
+// of a wave (r = lane % 32, c = lane / 32) owns, of row r, bytes
+// 64h + 32c .. 64h + 32c + 31 of every superstep; its quarter Q = 2h + s is
+// the 16 bytes at 64h + 32c + 16s.  A sum over K may be taken in any order as
+// long as A and B agree, so both operands use this same assignment:
+//   MXFP4: four v_mfma_scale_f32_32x32x64_f8f6f4 per superstep; quarter Q
+//          feeds the lane's 32-element block 4h + 2c + s of the superstep,
+//          whose UE8M0 scale is byte Q of the lane's scale word (selected by
+//          the instruction's op_sel).  One 32-bit word per lane therefore
+//          feeds the four MFMAs -- the TILED scale layout stores exactly
+//          these words, 32 rows x 2 lane halves per 256-byte group.
 //   NVFP4: E4M3 16-block scales have no native MFMA form, so each FP4 value
 //          is multiplied by its block scale in fp16 -- exact, since E2M1 times
 //          E4M3 has at most 6 significant bits and lies in [2^-10, 2688] --
-//          and sixteen v_mfma_f32_32x32x16_f16 consume the superstep, step t
-//          using the lane's dword t (block 8c + t/2).
+//          and sixteen v_mfma_f32_32x32x16_f16 consume the superstep; dword t'
+//          of quarter Q is one step, block 8h + 4c + 2s + t'/2.
 // Accumulation is fp32 in the MFMA accumulators.
 //
 // Schedules:
@@ -55,21 +56,25 @@ struct Frag {
   u32x4 q[4];
 };
 
-// A lane's scale bytes for one superstep: MXFP4 4 bytes (blocks 4c..4c+3 of
-// the superstep's 8), NVFP4 8 bytes (blocks 8c..8c+7 of its 16).
+// A lane's scale bytes for one superstep: MXFP4 4 bytes (blocks 2c, 2c+1,
+// 2c+4, 2c+5 of the superstep's 8, byte Q for quarter Q); NVFP4 8 bytes
+// (blocks 4c..4c+3 then 8+4c..8+4c+3 of its 16, byte 2Q + t'/2).
 template <int FMT> struct SfWord;
 template <> struct SfWord<kMXFP4> { uint32_t w; };
 template <> struct SfWord<kNVFP4> { uint32_t w[2]; };
 
+// byte-select pattern of v_perm picking bytes {2c, 2c+1} of two words
+__device__ __forceinline__ uint32_t pair_sel(int c) { return c ? 0x07060302u : 0x05040100u; }
+
 template <int FMT>
 __device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int layout, int64_t row,
                                         int64_t R, int64_t nblk, int64_t ss, int c) {
-  constexpr int NB = (FMT == kMXFP4) ? 4 : 8;
   // absent rows / blocks carry no data; give them a harmless finite scale
   constexpr uint32_t kPad = (FMT == kMXFP4) ? 0x7F7F7F7Fu : 0u;
-  uint32_t w[NB / 4];
+  constexpr int NW = (FMT == kMXFP4) ? 1 : 2;
+  uint32_t w[NW];
 #pragma unroll
-  for (int i = 0; i < NB / 4; i++) w[i] = kPad;
+  for (int i = 0; i < NW; i++) w[i] = kPad;
   if (row < R) {
     const int64_t ktiles = (nblk + 7) >> 3;
     if (layout == kTiled) {
@@ -77,37 +82,46 @@ __device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int
         w[0] = *reinterpret_cast<const uint32_t*>(sf + (((row >> 5) * ktiles + ss) << 8) +
                                                   ((c * 32 + (row & 31)) << 2));
       } else {
-        const int64_t tile = 2 * ss + c;
-        if (tile < ktiles) {
-          const uint8_t* p = sf + (((row >> 5) * ktiles + tile) << 8) + ((row & 31) << 2);
-          w[0] = *reinterpret_cast<const uint32_t*>(p);
-          w[1] = *reinterpret_cast<const uint32_t*>(p + 128);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int64_t tile = 2 * ss + h;
+          if (tile < ktiles) {
+            const uint8_t* p = sf + (((row >> 5) * ktiles + tile) << 8) + ((row & 31) << 2);
+            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(p);
+            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(p + 128);
+            w[h] = __builtin_amdgcn_perm(w1, w0, pair_sel(c));
+          }
         }
       }
     } else {
-      const int64_t kb0 = ss * (2 * NB) + c * NB;
       const uint8_t* p = sf + row * nblk;
 #pragma unroll
-      for (int j = 0; j < NB; j++) {
-        const int64_t kb = kb0 + j;
+      for (int j = 0; j < 4 * NW; j++) {
+        // MXFP4 byte j <-> block 8ss + 2c + (j&1) + 4(j>>1); NVFP4 byte j <-> 16ss + 8(j/4) + 4c + j%4
+        const int64_t kb = (FMT == kMXFP4) ? 8 * ss + 2 * c + (j & 1) + 4 * (j >> 1)
+                                           : 16 * ss + 8 * (j >> 2) + 4 * c + (j & 3);
         const uint32_t byte = (kb < nblk) ? (uint32_t)p[kb] : (kPad & 0xFF);
         w[j >> 2] = (w[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | (byte << (8 * (j & 3)));
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < NB / 4; i++) {
-    if constexpr (FMT == kMXFP4) out.w = w[0];
-    else out.w[i] = w[i];
+  if constexpr (FMT == kMXFP4) {
+    out.w = w[0];
+  } else {
+    out.w[0] = w[0];
+    out.w[1] = w[1];
   }
 }
 
-// 64 packed bytes of `row` for superstep ss, lane half c; zero outside.
+// byte offset of quarter Q of lane half c inside a superstep's 128 bytes
+__device__ __forceinline__ int quarter_off(int Q, int c) { return 64 * (Q >> 1) + 32 * c + 16 * (Q & 1); }
+
+// the 64 packed bytes lane half c owns of `row` in superstep ss; zero outside.
 __device__ __forceinline__ void load_frag_global(Frag& f, const uint8_t* base, int64_t row, int64_t R,
-                                                 int64_t kbytes, int64_t off) {
+                                                 int64_t kbytes, int64_t ss, int c) {
 #pragma unroll
   for (int s = 0; s < 4; s++) {
-    const int64_t o = off + 16 * s;
+    const int64_t o = ss * kSSBytes + quarter_off(s, c);
     if (row < R && o + 16 <= kbytes)
       f.q[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + row * kbytes + o));
     else
@@ -427,10 +441,11 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
     const uint8_t* base = smem + buf * kPStage;
 #pragma unroll
     for (int i = 0; i < TI; i++)
-      qa[i] = *reinterpret_cast<const u32x4*>(base + lds_off(wm * TI * 32 + i * 32 + r, 4 * c + q));
+      qa[i] = *reinterpret_cast<const u32x4*>(base + lds_off(wm * TI * 32 + i * 32 + r, quarter_off(q, c) >> 4));
 #pragma unroll
     for (int j = 0; j < TJ; j++)
-      qb[j] = *reinterpret_cast<const u32x4*>(base + lds_off(kPBM + wn * TJ * 32 + j * 32 + r, 4 * c + q));
+      qb[j] = *reinterpret_cast<const u32x4*>(
+          base + lds_off(kPBM + wn * TJ * 32 + j * 32 + r, quarter_off(q, c) >> 4));
   };
   // interleave the next quarter's LDS reads with this quarter's MFMAs
   auto interleave = [&]() {
@@ -536,11 +551,11 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
   for (int64_t ss = wave; ss < nss; ss += W) {
     Frag fw[1], fx[MT];
     SfWord<FMT> sw[1], sx[MT];
-    load_frag_global(fw[0], g.b, n0 + r, g.N, kbytes, ss * kSSBytes + 64 * c);
+    load_frag_global(fw[0], g.b, n0 + r, g.N, kbytes, ss, c);
     load_sf<FMT>(sw[0], g.sfb, g.lb, n0 + r, g.N, nblk, ss, c);
 #pragma unroll
     for (int i = 0; i < MT; i++) {
-      load_frag_global(fx[i], g.a, 32 * i + r, g.M, kbytes, ss * kSSBytes + 64 * c);
+      load_frag_global(fx[i], g.a, 32 * i + r, g.M, kbytes, ss, c);
       load_sf<FMT>(sx[i], g.sfa, g.la, 32 * i + r, g.M, nblk, ss, c);
     }
     superstep_mma<FMT, 1, MT>(acc, fw, fx, sw, sx);

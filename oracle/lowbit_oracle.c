@@ -138,9 +138,10 @@ double orc_ue8m0_value(uint8_t b) {
  * LINEAR: row-major (rows, K/B) bytes, the FlashInfer page's unswizzled
  *         layout mS[row, sf_idx].
  * TILED:  rows are grouped by 32 and scale blocks by 8.  Each 32 x 8 group is
- *         256 contiguous bytes laid out as 64 little-endian 32-bit words;
- *         word w = ((kb%8)/4)*32 + row%32 holds the four consecutive blocks
- *         4*((kb%8)/4) .. +3 of that row, block kb in byte kb%4.
+ *         256 contiguous bytes laid out as 64 little-endian 32-bit words.
+ *         With j = kb % 8, block kb of a row sits in word
+ *         ((j / 2) % 2) * 32 + row % 32, byte (j % 2) + 2 * (j / 4): word
+ *         h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of row r.
  *         Groups are ordered row-group major.  Padding bytes are zero.
  */
 static int64_t block_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
@@ -156,7 +157,7 @@ int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int layout) {
     int64_t ktiles = (nblk + 7) / 8;
     int64_t tile = (row / 32) * ktiles + kb / 8;
     int64_t j = kb % 8;
-    return tile * 256 + ((j / 4) * 32 + row % 32) * 4 + j % 4;
+    return tile * 256 + (((j / 2) % 2) * 32 + row % 32) * 4 + (j % 2) + 2 * (j / 4);
 }
 
 /* ------------------------------------------------------------------------- */

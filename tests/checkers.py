@@ -38,7 +38,7 @@ def gather_scales(orc, sf, rows, nblk, layout):
     kb = np.arange(nblk)[None, :]
     ktiles = (nblk + 7) // 8
     j = kb % 8
-    off = ((r // 32) * ktiles + kb // 8) * 256 + ((j // 4) * 32 + r % 32) * 4 + j % 4
+    off = ((r // 32) * ktiles + kb // 8) * 256 + (((j // 2) % 2) * 32 + r % 32) * 4 + (j % 2) + 2 * (j // 4)
     return sf[off]
 
 
@@ -49,7 +49,7 @@ def tiled_padding_is_zero(orc, sf, rows, nblk):
     kb = np.arange(nblk)[None, :]
     ktiles = (nblk + 7) // 8
     j = kb % 8
-    off = ((r // 32) * ktiles + kb // 8) * 256 + ((j // 4) * 32 + r % 32) * 4 + j % 4
+    off = ((r // 32) * ktiles + kb // 8) * 256 + (((j // 2) % 2) * 32 + r % 32) * 4 + (j % 2) + 2 * (j // 4)
     used[off.ravel()] = True
     return not np.any(sf[~used])
 

@@ -167,16 +167,22 @@ def test_tiled_layout_is_a_bijection(orc, rows, nblk):
             seen.add(off)
 
 
-def test_tiled_layout_word_holds_four_consecutive_blocks(orc):
+def test_tiled_layout_word_holds_the_blocks_of_one_lane(orc):
+    """Word h*32 + r of a group holds blocks 2h, 2h+1, 2h+4, 2h+5 of row r in
+    bytes 0..3 (the four blocks one MFMA lane consumes over 256 elements)."""
     nblk = 24
     for r in (0, 5, 31, 32, 63):
-        for kb in range(0, nblk, 4):
-            offs = [orc.sf_offset(r, kb + j, nblk, 1) for j in range(4)]
-            assert offs[0] % 4 == 0 and offs == [offs[0] + j for j in range(4)]
+        for t in range(nblk // 8):
+            for h in (0, 1):
+                blocks = [8 * t + 2 * h, 8 * t + 2 * h + 1, 8 * t + 2 * h + 4, 8 * t + 2 * h + 5]
+                offs = [orc.sf_offset(r, kb, nblk, 1) for kb in blocks]
+                assert offs[0] % 4 == 0 and offs == [offs[0] + j for j in range(4)]
+                assert (offs[0] % 256) // 4 == h * 32 + r % 32
     # a 32-row x 8-block tile is 256 contiguous bytes, rows adjacent per word
     assert orc.sf_offset(0, 0, 8, 1) == 0
     assert orc.sf_offset(1, 0, 8, 1) == 4
-    assert orc.sf_offset(0, 4, 8, 1) == 128
+    assert orc.sf_offset(0, 2, 8, 1) == 128
+    assert orc.sf_offset(0, 4, 8, 1) == 2
     assert orc.sf_offset(31, 7, 8, 1) == 255
     assert orc.sf_offset(32, 0, 8, 1) == 256
     assert orc.sf_offset(0, 8, 16, 1) == 256
