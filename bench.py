@@ -17,6 +17,7 @@ TFLOP/s are printed on stderr and carried in "kernels".
 Prints ONE JSON line on stdout.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +36,8 @@ HBM_PEAK = 8.0e12          # B/s, MI355X published
 FP4_PEAK = 10.1e15         # FLOP/s dense FP4/FP6 MFMA, published
 FP16_PEAK = 2.5e15         # FLOP/s dense fp16/bf16 MFMA, published
 EPS = 1e-6
+COPY_PROBE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 METRIC = "fused add-RMSNorm-FP4 quant GB/s + FP4 GEMM TFLOPS, as % of 1-GPU roofline"
 
 
@@ -60,8 +63,12 @@ class Stage:
     """A kernel launch with its per-launch HIP-event timing on torch's stream
     (the stream every lowbit call is launched on)."""
 
-    def __init__(self, name, fn, bound, work, unit_work, roof):
+    def __init__(self, name, fn, bound, work, unit_work, roof, own_peak=None, own_dtype=None):
         self.name, self.fn, self.bound, self.work, self.unit_work, self.roof = name, fn, bound, work, unit_work, roof
+        # the peak of the arithmetic the kernel executes (the NVFP4 GEMM runs fp16
+        # MFMAs on exactly dequantized operands); the step value prices every GEMM at FP4
+        self.own_peak = roof if own_peak is None else own_peak
+        self.own_dtype = own_dtype
         self.times = []
 
     def __call__(self, timed):
@@ -171,48 +178,98 @@ def build_stages():
     stages.append(Stage(f"chain_add_rmsnorm_nvfp4_{M}x{H}", chain_producer, "hbm",
                         producer_bytes(M, H, 16), "B", HBM_PEAK))
     stages.append(Stage(f"chain_nvfp4_gemm_gelu_fp4_{M}x{N1}x{H}", chain_gemm1, "mfma",
-                        2.0 * M * N1 * H, "FLOP", FP4_PEAK))
+                        2.0 * M * N1 * H, "FLOP", FP4_PEAK, FP16_PEAK, "fp16"))
     stages.append(Stage(f"chain_nvfp4_gemm_{M}x{H}x{N1}", chain_gemm2, "mfma", 2.0 * M * H * N1, "FLOP",
-                        FP4_PEAK))
+                        FP4_PEAK, FP16_PEAK, "fp16"))
     return stages
 
 
 def cpu_baseline(stages, step_ideal_s):
-    """Time the CPU oracle, as it stands, on a bounded sample of the same
-    workload and extrapolate to one step (a reported baseline, not a target)."""
+    """Time the CPU oracle, as it stands, on a bounded sample of every stage
+    of the step and extrapolate each stage by its share of the work (bytes
+    for the producers, multiply-accumulates for the GEMMs).  The sample is
+    the full 4096 x 4096 producer plus a block of rows x columns (full K) of
+    each GEMM, about 60 GMAC in all.  A reported baseline, not a target."""
     from oracle import oracle as orc
 
-    L = orc.lib()
+    orc.lib()
     threads = orc.num_threads()
-    t_total = 0.0
     parts = []
-    # producer: 256 of the 4096 rows
+    t_step = 0.0
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # producers: the full NVFP4 4096 x 4096 workload, rate in bytes/s
     c = synth.NVFP4_PRODUCER
-    rows = 256
-    x, r, w = synth.producer_inputs(rows, c["H"], c["seed"], outliers=True)
-    t0 = time.perf_counter()
-    orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4, orc.LINEAR, gs=1.0)
-    dt = time.perf_counter() - t0
-    prod_s = dt * (c["M"] / rows)
-    t_total += prod_s * (1 + 2048 * 5120 / (c["M"] * c["H"]))   # the chain's producer scales by elements
-    parts.append(f"producer {rows}x{c['H']} rows ({dt:.2f} s)")
-    # GEMM: 1024 output entries of the (8192, 14336, 4096) GEMM, rate in MAC/s
-    M, N, K = synth.MXFP4_PREFILL["shapes"][0]
-    Msub, Nsub = 8, 128
-    A = synth.activation(Msub, K, 1)
-    Wt = synth.weight(Nsub, K, 1)
-    a, sfa = orc.quantize(synth.bits(A), orc.MXFP4, orc.LINEAR)
-    b, sfb = orc.quantize(synth.bits(Wt), orc.MXFP4, orc.LINEAR)
-    t0 = time.perf_counter()
-    orc.gemm(a, b, sfa, sfb, Msub, Nsub, K, orc.MXFP4, orc.LINEAR, orc.LINEAR)
-    dt = time.perf_counter() - t0
-    mac_rate = Msub * Nsub * K / dt
-    gemm_macs = sum(s.work / 2 for s in stages if s.unit_work == "FLOP")
-    t_total += gemm_macs / mac_rate
-    parts.append(f"gemm {Msub}x{Nsub}x{K} ({dt:.2f} s, {mac_rate / 1e9:.2f} GMAC/s)")
-    value = 100.0 * step_ideal_s / t_total
+    x, r, w = synth.producer_inputs(c["M"], c["H"], c["seed"], outliers=True)
+    xb, rb, wb = synth.bits(x), synth.bits(r), synth.bits(w)
+    dt = timed(lambda: orc.add_rmsnorm_quant(xb, rb, wb, EPS, orc.NVFP4, orc.LINEAR, gs=1.0))
+    rate_b = producer_bytes(c["M"], c["H"], 16) / dt
+    t_step += sum(s.work for s in stages if s.unit_work == "B") / rate_b
+    parts.append(f"producer {c['M']}x{c['H']} nvfp4 full ({dt:.2f} s)")
+
+    def gemm_rate(M, N, K, fmt, Msub, Nsub, seed, gelu_fp4=False):
+        A = synth.activation(Msub, K, seed, outliers=True)
+        Wt = synth.weight(Nsub, K, seed)
+        gs = 1.0
+        a, sfa = orc.quantize(synth.bits(A), fmt, orc.TILED, gs=gs)
+        b, sfb = orc.quantize(synth.bits(Wt), fmt, orc.TILED, gs=gs)
+        bias = synth.bits(synth.bias(Nsub, seed))
+        if gelu_fp4:
+            fn = lambda: orc.gemm_gelu_fp4(a, b, sfa, sfb, Msub, Nsub, K, fmt, orc.TILED, orc.TILED, 1.0,
+                                           bias, 1.0, orc.TILED)
+        else:
+            res = synth.bits(synth.residual(Msub, Nsub, seed))
+            fn = lambda: orc.gemm(a, b, sfa, sfb, Msub, Nsub, K, fmt, orc.TILED, orc.TILED, 1.0,
+                                  orc.EPI_BIAS_RESIDUAL, bias, res)
+        dt = timed(fn)
+        parts.append(f"{'nvfp4' if fmt == orc.NVFP4 else 'mxfp4'} gemm{'-gelu-fp4' if gelu_fp4 else ''} "
+                     f"{Msub}x{Nsub} of ({M},{N},{K}) ({dt:.2f} s)")
+        return Msub * Nsub * K / dt
+
+    gemm_stages = [s for s in stages if s.unit_work == "FLOP"]
+    (M1, N1, K1), (M2, N2, K2) = synth.MXFP4_PREFILL["shapes"]
+    ch = synth.NVFP4_CHAIN
+    samples = [
+        (gemm_stages[0], gemm_rate(M1, N1, K1, orc.MXFP4, 1024, 4096, 1)),
+        (gemm_stages[1], gemm_rate(M2, N2, K2, orc.MXFP4, 1024, 2048, 2)),
+        (gemm_stages[2], gemm_rate(2048, ch["N1"], ch["H"], orc.NVFP4, 256, 4096, 3, gelu_fp4=True)),
+        (gemm_stages[3], gemm_rate(2048, ch["H"], ch["N1"], orc.NVFP4, 256, 2048, 4)),
+    ]
+    for st, mac_rate in samples:
+        t_step += (st.work / 2) / mac_rate
+    value = 100.0 * step_ideal_s / t_step
     return {"value": value, "unit": "% of 1-GPU roofline", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(parts) + f"; extrapolated step time {t_total:.1f} s"}
+            "sample": "; ".join(parts) + f"; extrapolated step time {t_step:.1f} s"}
+
+
+def source_digest():
+    """sha256 over the kernel sources: counters taken on other sources do not apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_fp4_add_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage_name):
+    """HBM bytes per launch of a stage from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or
+    None when there is none for this stage or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(stage_name)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -221,6 +278,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed region, run a 1 GiB read + 1 GiB write elementwise kernel "
+                         "three times: the known-size kernel that calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -246,6 +306,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
+    if args.copy_probe:
+        # an elementwise kernel that reads and writes COPY_PROBE_BYTES each
+        # (torch.add: a plain streaming kernel; copy_ would go to the runtime's
+        # blit path); 1 GiB so that what the fill leaves in L2 is negligible
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     ideal = sum(s.ideal_s() for s in stages)
     value = 100.0 * ideal / (wall / args.steps)
     kernels = {}
@@ -257,16 +327,21 @@ def main():
                            ("GB/s" if s.unit_work == "B" else "TFLOP/s"):
                                round(rate / (1e9 if s.unit_work == "B" else 1e12), 1),
                            "roofline_frac": round(frac, 4)}
+        if s.own_peak != s.roof:
+            kernels[s.name][f"{s.own_dtype}_mfma_frac"] = round(s.work / t / s.own_peak, 4)
         log(f"[bench] {s.name}: {t * 1e6:.1f} us, "
             f"{rate / (1e9 if s.unit_work == 'B' else 1e12):.1f} {'GB/s' if s.unit_work == 'B' else 'TFLOP/s'}, "
             f"{100 * frac:.1f}% of roofline")
     # dominant kernel: the one with the largest share of the step
     dom = max(stages, key=lambda s: s.mean_s())
     t = dom.mean_s()
-    roof = {"bound": dom.bound, "achieved": round(dom.work / t / (1e9 if dom.bound == "hbm" else 1e12), 2),
-            "peak": (HBM_PEAK / 1e9) if dom.bound == "hbm" else (FP4_PEAK / 1e12),
-            "unit": "GB/s" if dom.bound == "hbm" else "TFLOP/s",
-            "frac": round(dom.ideal_s() / t, 4), "traffic": None, "kernel": dom.name}
+    scale = 1e9 if dom.bound == "hbm" else 1e12
+    roof = {"bound": dom.bound, "achieved": round(dom.work / t / scale, 2),
+            "peak": dom.own_peak / scale, "unit": "GB/s" if dom.bound == "hbm" else "TFLOP/s",
+            "frac": round(dom.work / t / dom.own_peak, 4), "traffic": measured_traffic(dom.name),
+            "kernel": dom.name}
+    if dom.own_dtype:
+        roof["peak_dtype"] = dom.own_dtype
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -1,0 +1,152 @@
+"""The C ABI on the host, no GPU needed: liblowbit.so loads, exports every
+entry point include/lowbit.h declares, and its host-side logic (scale buffer
+sizes, schedule choice, argument checks in the documented order) behaves as
+the header states.  No call here reaches a kernel launch: every argument set
+is rejected before the device check, or, where it passes every check and
+no GPU is visible, the device check itself answers."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch
+
+import block_scaled_fp4_add_amd as lb
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "lowbit.h")
+OK, EINVAL, EALIGN, ESHAPE, EDEVICE, EHIP = 0, 1, 2, 3, 4, 5
+# argument sets that pass every check reach the device check; they are only
+# made where no GPU is visible (host pointers must never reach a kernel)
+NO_DEVICE = torch.cuda.device_count() == 0
+
+
+def declared():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(lowbit_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared() == sorted(lb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(lb.LIB_PATH)
+    for name in declared():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings():
+    L = lb.lib()
+    for s, text in ((OK, b"ok"), (EINVAL, b"invalid argument"), (EALIGN, b"misaligned pointer"),
+                    (ESHAPE, b"unsupported shape"), (EDEVICE, b"device is not gfx950")):
+        assert L.lowbit_status_str(s) == text
+
+
+def test_sf_bytes_matches_the_oracle(orc):
+    L = lb.lib()
+    for rows, K in ((1, 64), (41, 1536), (33, 5120), (8192, 14336), (7, 96)):
+        for fmt in (0, 1):
+            if K % (16 if fmt == 0 else 32):
+                continue
+            for layout in (0, 1):
+                assert L.lowbit_sf_bytes(rows, K, fmt, layout) == orc.sf_bytes(rows, K, fmt, layout)
+
+
+def test_pick_variant():
+    L = lb.lib()
+    assert L.lowbit_gemm_pick_variant(41, 4608, 1536, 1, -1) == 0      # small M: decode schedule
+    assert L.lowbit_gemm_pick_variant(128, 4608, 1536, 1, -1) == 0
+    assert L.lowbit_gemm_pick_variant(129, 4608, 1536, 1, -1) == 1     # prefill schedule
+    assert L.lowbit_gemm_pick_variant(8192, 4096, 14336, 0, -1) == 1
+    assert L.lowbit_gemm_pick_variant(8192, 4096, 14336, 1, 0) < 0     # decode needs M <= 128
+    assert L.lowbit_gemm_pick_variant(1, 17408, 5120, 1, 1) == 1       # prefill accepts any M
+
+
+class Buf:
+    """An aligned host buffer: stands in for operand pointers in calls that
+    are rejected before any memory is touched."""
+
+    def __init__(self, n=1 << 16):
+        self.raw = ctypes.create_string_buffer(n + 512)
+        self.base = (ctypes.addressof(self.raw) + 255) & ~255
+
+    def at(self, off=0):
+        return ctypes.c_void_p(self.base + off)
+
+
+@pytest.fixture
+def buf():
+    return Buf()
+
+
+def quant(L, buf, rows, K, fmt=1, layout=0, gs=None, x=0, p=0, s=0):
+    return L.lowbit_quantize(buf.at(x), rows, K, fmt, layout, gs, buf.at(p), buf.at(s), None)
+
+
+def test_quantize_argument_order(buf):
+    L = lb.lib()
+    assert quant(L, buf, 4, 64, fmt=2) == EINVAL                           # format
+    assert quant(L, buf, 4, 64, layout=5) == EINVAL                        # layout
+    assert quant(L, buf, 4, 64, fmt=1, gs=buf.at()) == EINVAL              # MXFP4 has no global scale
+    assert L.lowbit_quantize(None, 4, 64, 1, 0, None, buf.at(), buf.at(), None) == EINVAL
+    assert quant(L, buf, -1, 64) == ESHAPE
+    assert quant(L, buf, 4, 48) == ESHAPE                                  # K % 32
+    assert quant(L, buf, 4, 8, fmt=0) == ESHAPE                            # K below one block
+    assert quant(L, buf, 4, 64, x=2) == EALIGN                             # input not 16-byte aligned
+    assert quant(L, buf, 4, 64, layout=1, s=1) == EALIGN                   # tiled scales need 4 bytes
+    assert quant(L, buf, 0, 64) == OK                                      # empty: nothing to do
+    if NO_DEVICE:
+        assert quant(L, buf, 4, 64) == EDEVICE                             # all checks pass: no device
+
+
+def test_producer_argument_order(buf):
+    L = lb.lib()
+
+    def call(M, H, fmt=1, layout=0, gs=None, eps=1e-6, x=0):
+        return L.lowbit_add_rmsnorm_quant(buf.at(x), buf.at(), buf.at(), M, H, eps, fmt, layout, gs,
+                                          buf.at(), buf.at(), None)
+
+    assert call(4, 256, fmt=7) == EINVAL
+    assert call(4, 256, fmt=1, gs=buf.at()) == EINVAL
+    assert call(4, 48) == ESHAPE                     # H < 64
+    assert call(4, 100) == ESHAPE                    # H % block
+    assert call(4, 65536) == ESHAPE                  # longer rows than the kernel's limit
+    assert call(4, 256, x=8) == EALIGN
+    assert call(0, 256) == OK
+    if NO_DEVICE:
+        assert call(4, 256) == EDEVICE
+
+
+def test_gemm_argument_order(buf):
+    L = lb.lib()
+    a, b, sa, sb, out = buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288), buf.at(16384)
+
+    def call(M, N, K, fmt=1, la=0, lb_=0, variant=-1, o=out, a_=a):
+        return L.lowbit_gemm_bf16(a_, b, sa, sb, M, N, K, fmt, la, lb_, 1.0, o, variant, None)
+
+    assert call(8, 128, 256, fmt=3) == EINVAL
+    assert call(8, 128, 256, variant=2) == EINVAL
+    assert call(8, 128, 256, o=None) == EINVAL
+    assert call(-1, 128, 256) == ESHAPE
+    assert call(8, 128, 48) == ESHAPE                        # K % 32
+    assert call(200, 128, 256, variant=0) == ESHAPE          # decode schedule needs M <= 128
+    assert call(8, 128, 256, a_=buf.at(4)) == EALIGN
+    assert call(0, 128, 256) == OK
+    if NO_DEVICE:
+        assert call(8, 128, 256) == EDEVICE
+    # epilogues that need an operand reject its absence
+    assert L.lowbit_gemm_bias_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1, None) == EINVAL
+    assert L.lowbit_gemm_residual_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1,
+                                       None) == EINVAL
+    # FP4 out: N must be a multiple of the NVFP4 block
+    assert L.lowbit_gemm_bias_gelu_fp4(a, b, sa, sb, 8, 120, 256, 1, 0, 0, 1.0, buf.at(20480), None,
+                                       buf.at(24576), buf.at(28672), 0, -1, None) == ESHAPE
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(lb, "LIB_PATH", "/nonexistent/liblowbit.so")
+    monkeypatch.setattr(lb, "_lib", None)
+    with pytest.raises(RuntimeError):
+        lb.lib()
