@@ -93,16 +93,21 @@ __device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
 
 // ---------------------------------------------------------------------------
 // Scale layouts.  LINEAR: row * nblk + kb.  TILED: 32-row x 8-block groups of
-// 256 bytes; with j = kb % 8, word ((j/2)%2)*32 + row%32, byte (j%2) + 2(j/4):
-// word h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of row r, the four blocks
-// one MFMA lane half consumes over 256 elements (see gemm.hip).
+// 256 bytes, row-group major; inside a group one 32-bit word per (lane half,
+// row) holds the four blocks that lane half of a GEMM wave reads (gemm.hip),
+// with j = kb % 8:
+//   MXFP4: word ((j/2)%2)*32 + row%32, byte (j%2) + 2(j/4)  -- blocks
+//          {2h, 2h+1, 2h+4, 2h+5}, one per quarter of a 256-element superstep;
+//   NVFP4: word (j/4)*32 + row%32, byte j%4  -- blocks 4c..4c+3, the lane
+//          half's blocks of a 128-element stage.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t sf_offset(int layout, int64_t row, int64_t kb, int64_t nblk) {
+__device__ __forceinline__ int64_t sf_offset(int fmt, int layout, int64_t row, int64_t kb, int64_t nblk) {
   if (layout == kLinear) return row * nblk + kb;
   int64_t ktiles = (nblk + 7) >> 3;
   int64_t j = kb & 7;
-  return (((row >> 5) * ktiles + (kb >> 3)) << 8) + (((((j >> 1) & 1) << 5) + (row & 31)) << 2) + (j & 1) +
-         ((j >> 2) << 1);
+  int64_t base = ((row >> 5) * ktiles + (kb >> 3)) << 8;
+  if (fmt == kNVFP4) return base + ((((j >> 2) << 5) + (row & 31)) << 2) + (j & 3);
+  return base + (((((j >> 1) & 1) << 5) + (row & 31)) << 2) + (j & 1) + ((j >> 2) << 1);
 }
 __host__ __device__ inline int64_t sf_bytes_of(int layout, int64_t rows, int64_t nblk) {
   if (layout == kLinear) return rows * nblk;

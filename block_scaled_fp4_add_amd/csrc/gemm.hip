@@ -60,7 +60,8 @@ struct Frag {
 
 // A lane's scale bytes for one superstep: MXFP4 4 bytes (blocks 2c, 2c+1,
 // 2c+4, 2c+5 of the superstep's 8, byte Q for quarter Q); NVFP4 8 bytes
-// (blocks 4c..4c+3 then 8+4c..8+4c+3 of its 16, byte 2Q + t'/2).
+// (blocks 4c..4c+3 then 8+4c..8+4c+3 of its 16, byte 2Q + t'/2).  In the
+// TILED layout each of these words is one aligned word of the scale buffer.
 template <int FMT> struct SfWord;
 template <> struct SfWord<kMXFP4> { uint32_t w; };
 template <> struct SfWord<kNVFP4> { uint32_t w[2]; };
@@ -87,12 +88,9 @@ __device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int64_t tile = 2 * ss + h;
-          if (tile < ktiles) {
-            const uint8_t* p = sf + (((row >> 5) * ktiles + tile) << 8) + ((row & 31) << 2);
-            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(p);
-            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(p + 128);
-            w[h] = __builtin_amdgcn_perm(w1, w0, pair_sel(c));
-          }
+          if (tile < ktiles)
+            w[h] = *reinterpret_cast<const uint32_t*>(sf + (((row >> 5) * ktiles + tile) << 8) +
+                                                      ((c * 32 + (row & 31)) << 2));
         }
       }
     } else {
@@ -142,26 +140,30 @@ __device__ __forceinline__ v16f mfma_mx(u32x4 a, u32x4 b, v16f acc, uint32_t sa,
                                                          (int)sb);
 }
 
-// Eight E2M1 codes (one dword, element i in nibble i) times an fp16 block
-// scale -> eight fp16.  The E2M1 magnitudes are fp16 values whose low byte is
-// zero, so a v_perm byte lookup builds their high bytes; the sign bit is moved
-// in, and one packed fp16 multiply per pair applies the scale (exact).
-__device__ __forceinline__ v8h dq8(uint32_t w, v2h s2) {
-  constexpr uint32_t kLutLo = 0x3E3C3800u;  // 0, 0.5, 1, 1.5
-  constexpr uint32_t kLutHi = 0x46444240u;  // 2, 3, 4, 6
-  const uint32_t ev = __builtin_amdgcn_perm(kLutHi, kLutLo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
-  const uint32_t od = __builtin_amdgcn_perm(kLutHi, kLutLo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
-  const v2h p0 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x040C000Cu)) * s2;
-  const v2h p1 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x050C010Cu)) * s2;
-  const v2h p2 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x060C020Cu)) * s2;
-  const v2h p3 = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(od, ev, 0x070C030Cu)) * s2;
-  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+// NVFP4 dequantization to fp16, exact.  An E2M1 value (2 significant bits)
+// times an E4M3 scale (4 significant bits) has at most 6 significant bits and
+// lies in [2^-10, 2688], so it is an fp16 normal number.  The E4M3 byte is
+// decoded by the FP8 conversion and split into its power of two p (what the
+// scaled FP4->fp16 conversion applies: that conversion uses only the exponent
+// of its fp32 scale) and its sign-carrying mantissa m = +-1.mmm (applied by
+// one packed fp16 multiply, exact).  A zero scale gives p = 0 and zeros.
+struct NvPart {
+  float p;   // 2^e of the block scale (0 for a zero scale)
+  v2h m;     // sign * 1.mmm, in both halves
+};
+__device__ __forceinline__ NvPart nv_part(const SfWord<kNVFP4>& sw, int blk) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)(sw.w[blk >> 2] >> (8 * (blk & 3))), 0);
+  const uint32_t u = __float_as_uint(s);
+  const _Float16 h = (_Float16)__uint_as_float((u & 0x807FFFFFu) | 0x3F800000u);
+  return NvPart{__uint_as_float(u & 0x7F800000u), v2h{h, h}};
 }
-
-__device__ __forceinline__ v2h nv_scale2(const SfWord<kNVFP4>& sw, int blk) {
-  const uint32_t b = (sw.w[blk >> 2] >> (8 * (blk & 3))) & 0xFF;
-  const _Float16 h = (_Float16)e4m3_to_f32(b);
-  return v2h{h, h};
+// Eight E2M1 codes (one dword, element i in nibble i) times the block scale.
+__device__ __forceinline__ v8h dq8(uint32_t w, NvPart sc) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p, 0) * sc.m;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p, 1) * sc.m;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p, 2) * sc.m;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p, 3) * sc.m;
+  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 __device__ __forceinline__ uint32_t frag_dword(const Frag& f, int t) {
@@ -190,9 +192,9 @@ __device__ __forceinline__ void superstep_mma(v16f (&acc)[TI][TJ], const Frag (&
     for (int t = 0; t < 16; t++) {
       v8h va[TI], vb[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; i++) va[i] = dq8(frag_dword(fa[i], t), nv_scale2(sa[i], t >> 1));
+      for (int i = 0; i < TI; i++) va[i] = dq8(frag_dword(fa[i], t), nv_part(sa[i], t >> 1));
 #pragma unroll
-      for (int j = 0; j < TJ; j++) vb[j] = dq8(frag_dword(fb[j], t), nv_scale2(sb[j], t >> 1));
+      for (int j = 0; j < TJ; j++) vb[j] = dq8(frag_dword(fb[j], t), nv_part(sb[j], t >> 1));
 #pragma unroll
       for (int i = 0; i < TI; i++)
 #pragma unroll
@@ -218,15 +220,51 @@ __device__ __forceinline__ void quarter_mma(v16f (&acc)[TI][TJ], const u32x4 (&q
     for (int t = 0; t < 4; t++) {
       v8h va[TI], vb[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][t], nv_scale2(sa[i], 2 * S + (t >> 1)));
+      for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][t], nv_part(sa[i], 2 * S + (t >> 1)));
 #pragma unroll
-      for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][t], nv_scale2(sb[j], 2 * S + (t >> 1)));
+      for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][t], nv_part(sb[j], 2 * S + (t >> 1)));
 #pragma unroll
       for (int i = 0; i < TI; i++)
 #pragma unroll
         for (int j = 0; j < TJ; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
     }
+  }
+}
+
+// NVFP4 quarter S, software-pipelined: on entry va / vb hold step 0 of this
+// quarter already dequantized; each step t issues its 16 MFMAs while the
+// dequantization of step t + 1 (for t = 3: step 0 of the next quarter, from
+// its fragments xa / xb and scales xsa / xsb, block 2 SN) runs beside them.
+template <int S, int SN, int TI, int TJ>
+__device__ __forceinline__ void quarter_nv(v16f (&acc)[TI][TJ], const u32x4 (&qa)[TI], const u32x4 (&qb)[TJ],
+                                           const SfWord<kNVFP4> (&sa)[TI], const SfWord<kNVFP4> (&sb)[TJ],
+                                           v8h (&va)[TI], v8h (&vb)[TJ], const u32x4 (&xa)[TI],
+                                           const u32x4 (&xb)[TJ], const SfWord<kNVFP4> (&xsa)[TI],
+                                           const SfWord<kNVFP4> (&xsb)[TJ]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    v8h na[TI], nb[TJ];
+    if (t < 3) {
+#pragma unroll
+      for (int i = 0; i < TI; i++) na[i] = dq8(qa[i][t + 1], nv_part(sa[i], 2 * S + ((t + 1) >> 1)));
+#pragma unroll
+      for (int j = 0; j < TJ; j++) nb[j] = dq8(qb[j][t + 1], nv_part(sb[j], 2 * S + ((t + 1) >> 1)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; i++) na[i] = dq8(xa[i][0], nv_part(xsa[i], 2 * SN));
+#pragma unroll
+      for (int j = 0; j < TJ; j++) nb[j] = dq8(xb[j][0], nv_part(xsb[j], 2 * SN));
+    }
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TI; i++) va[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < TJ; j++) vb[j] = nb[j];
   }
 }
 
@@ -257,7 +295,7 @@ __device__ __forceinline__ void epi_run16(const float* t, int64_t m, int64_t n, 
     p.x = e2m1x8(y);
     p.y = e2m1x8(y + 8);
     *reinterpret_cast<uint2*>(g.out_packed + m * (g.N / 2) + n / 2) = p;
-    g.out_sf[sf_offset(g.out_layout, m, n / 16, g.N / 16)] = (uint8_t)sb;
+    g.out_sf[sf_offset(kNVFP4, g.out_layout, m, n / 16, g.N / 16)] = (uint8_t)sb;
   } else {
     const bool vec = (g.N % 8) == 0;
 #pragma unroll
@@ -291,7 +329,9 @@ __device__ __forceinline__ void epi_run16(const float* t, int64_t m, int64_t n, 
         o.w = pack_bf16x2(z[6], z[7]);
         *reinterpret_cast<uint4*>(g.out + m * g.N + nn) = o;
       } else {
-        for (int k = 0; k < 8 && nn + k < g.N; k++) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          if (nn + k >= g.N) continue;   // unrolled with a predicate: z stays in registers
           float v = z[k];
           if constexpr (EPI == kEpiBias || EPI == kEpiBiasResidual || EPI == kEpiBiasGelu)
             v += bf16_to_f32(g.bias[nn + k]);
@@ -321,13 +361,13 @@ __device__ __forceinline__ void fp4_out_padding(const GemmArgs& g, int64_t r0, i
   if (rs < re && b0 < be) {
     const int64_t cnt = (re - rs) * (be - b0);
     for (int64_t i = tid; i < cnt; i += nthreads)
-      g.out_sf[sf_offset(kTiled, rs + i / (be - b0), b0 + i % (be - b0), nblk)] = 0;
+      g.out_sf[sf_offset(kNVFP4, kTiled, rs + i / (be - b0), b0 + i % (be - b0), nblk)] = 0;
   }
   if (last_col_tile && nblk_pad > nblk && r0 < re) {
     const int64_t w = nblk_pad - nblk;
     const int64_t cnt = (re - r0) * w;
     for (int64_t i = tid; i < cnt; i += nthreads)
-      g.out_sf[sf_offset(kTiled, r0 + i / w, nblk + i % w, nblk)] = 0;
+      g.out_sf[sf_offset(kNVFP4, kTiled, r0 + i / w, nblk + i % w, nblk)] = 0;
   }
 }
 
@@ -767,11 +807,9 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
         } else {
 #pragma unroll
           for (int h = 0; h < 2; h++) {
-            const int a0 = tiled ? h * 2048 + grp * 256 + r * 4 : row * 16 + 8 * h + 4 * c;
-            const int a1 = tiled ? a0 + 128 : a0;
-            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(area + a0);
-            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(area + a1);
-            uint32_t w = __builtin_amdgcn_perm(w1, w0, tiled ? pair_sel(c) : 0x03020100u);
+            // one aligned word in both layouts: no byte shuffling
+            const int a0 = tiled ? h * 2048 + grp * 256 + (c * 32 + r) * 4 : row * 16 + 8 * h + 4 * c;
+            uint32_t w = *reinterpret_cast<const uint32_t*>(area + a0);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
               const bool absent = MASK && 8 * h + 4 * c + j >= left;
@@ -796,19 +834,40 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
     for (int i = 1; i < TI; i++)
       qa[i] = *reinterpret_cast<const u32x4*>(base + v3_off(wm * TI * 32 + i * 32 + r, 2 * c + s));
   };
-  // MXFP4: after each of the first MFMAs of a quarter one next-quarter LDS
-  // read (DSR per slot) and one DMA (while VM are left), then the rest of the MFMAs
+  // MXFP4: after each of the first TI + TJ MFMAs of a quarter DSR next-quarter
+  // LDS reads, then after each of the following MFMAs DMAs until VM are
+  // issued.  The reads come first: the compiler cannot tell the DMA's LDS
+  // writes (another ring slot) from the reads, so it keeps them in that order.
   auto interleave = [&](auto dsr, auto vm) {
     constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
     if constexpr (FMT == kMXFP4) {
-      constexpr int SLOTS = (VM > TI + TJ ? VM : TI + TJ) < TI * TJ ? (VM > TI + TJ ? VM : TI + TJ) : TI * TJ;
+      constexpr int NR = TI + TJ;                              // MFMAs carrying reads
+      constexpr int NV = TI * TJ - NR;                         // MFMAs that can carry DMAs
+      constexpr int PER = (VM + NV - 1) / (NV > 0 ? NV : 1);   // DMAs per such MFMA
 #pragma unroll
-      for (int k = 0; k < SLOTS; k++) {
+      for (int k = 0; k < TI * TJ; k++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        if (k < TI + TJ) __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);   // LDS reads
-        if (k < VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one DMA
+        if (k < NR) {
+          __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);   // LDS reads
+        } else if (VM > 0 && (k - NR) * PER < VM) {
+          __builtin_amdgcn_sched_group_barrier(0x010, PER, 0);   // DMAs
+        }
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - SLOTS, 0);
+    }
+  };
+  // NVFP4: one MFMA, then a share of the dequantization VALU work, and one
+  // LDS read per MFMA until DSR are issued, then one DMA per MFMA until VM
+  // are (reads before DMAs, as above)
+  auto interleave_nv = [&](auto dsr, auto vm) {
+    constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
+    if constexpr (FMT == kNVFP4) {
+#pragma unroll
+      for (int k = 0; k < 4 * TI * TJ; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        if (k < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
+        else if (k < DSR + VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one DMA
+      }
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -816,6 +875,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
   using I2 = std::integral_constant<int, 2>;
   using IL = std::integral_constant<int, kV3Loads>;
   using ILS = std::integral_constant<int, kV3Loads + SFL>;
+  using IF = std::integral_constant<int, TI + TJ>;           // fragment reads of a quarter
+  using IFS = std::integral_constant<int, 4 * (TI + TJ)>;    // fragment + scale reads
   auto stage_barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm_le_lgkm0<kInFlight2>();
@@ -831,34 +892,58 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
   stage_barrier();          // stage 0 and the scales of superstep 0 have landed
   read_sf(0, sa, sb, std::true_type{});
   frags(0, 0, qa, qb);
+  v8h va[TI], vb[TJ];   // NVFP4: the next MFMA step's dequantized operands
+  if constexpr (FMT == kNVFP4) {
+#pragma unroll
+    for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][0], nv_part(sa[i], 0));
+#pragma unroll
+    for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][0], nv_part(sb[j], 0));
+  }
   // superstep ss: quarters 0, 1 from stage 2ss, quarters 2, 3 from stage 2ss + 1;
   // it issues stages 2ss + 3 and 2ss + 4 (with the scales of superstep ss + 2)
   auto superstep = [&](int ss, auto fast) {
     constexpr bool F = decltype(fast)::value;
     const int k0 = 2 * ss, k1 = 2 * ss + 1;
     if constexpr (F) {
+      frags(k0, 1, na, nb);
       issue_fast(k0 + 3, kNoSf{});
     } else {
       issue(k0 + 3, kNoSf{});
       __builtin_amdgcn_sched_barrier(0);
+      frags(k0, 1, na, nb);
     }
-    frags(k0, 1, na, nb);
-    quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
-    if constexpr (F) interleave(I1{}, IL{}); else interleave(I1{}, I0{});
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<0, 1>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
+      if constexpr (F) interleave_nv(IF{}, IL{}); else interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
+      if constexpr (F) interleave(I1{}, IL{}); else interleave(I1{}, I0{});
+    }
     stage_barrier();        // stage k1 has landed; every wave is done with stage k0 - 1
     frags(k1, 0, qa, qb);
-    quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
-    interleave(I1{}, I0{});
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<1, 2>(acc, na, nb, sa, sb, va, vb, qa, qb, sa, sb);
+      interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
+      interleave(I1{}, I0{});
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (F) {
+      frags(k1, 1, na, nb);
       issue_fast(k1 + 3, kWithSf{});
     } else {
       issue(k1 + 3, kWithSf{});
       __builtin_amdgcn_sched_barrier(0);
+      frags(k1, 1, na, nb);
     }
-    frags(k1, 1, na, nb);
-    quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
-    if constexpr (F) interleave(I1{}, ILS{}); else interleave(I1{}, I0{});
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<2, 3>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
+      if constexpr (F) interleave_nv(IF{}, ILS{}); else interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
+      if constexpr (F) interleave(I1{}, ILS{}); else interleave(I1{}, I0{});
+    }
     stage_barrier();        // stage k1 + 1 (and the scales of superstep ss + 1) have landed
     if constexpr (F) {
       read_sf(ss + 1, sa_n, sb_n, std::false_type{});
@@ -867,8 +952,13 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
       __builtin_amdgcn_sched_barrier(0);
     }
     frags(k1 + 1, 0, qa, qb);
-    quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
-    if constexpr (F) interleave(I2{}, I0{}); else interleave(I1{}, I0{});
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<3, 0>(acc, na, nb, sa, sb, va, vb, qa, qb, sa_n, sb_n);
+      if constexpr (F) interleave_nv(IFS{}, I0{}); else interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
+      if constexpr (F) interleave(I2{}, I0{}); else interleave(I1{}, I0{});
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TI; i++) sa[i] = sa_n[i];

@@ -71,7 +71,7 @@ __device__ __forceinline__ void quant_store_block(const float* y, float gs, int6
     p.w = e2m1x8(v + 24);
     *reinterpret_cast<uint4*>(dst) = p;
   }
-  a.out_sf[sf_offset(a.layout, row, kb, nblk)] = (uint8_t)sb;
+  a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = (uint8_t)sb;
 }
 
 // FUSED: add + RMSNorm + quant.  Otherwise: quantize x as it is.
@@ -196,10 +196,10 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
     const int64_t nblk_pad = ((nblk + 7) >> 3) << 3;
     if (live) {
       const int64_t pad = nblk_pad - nblk;
-      if (wave_in_row == 0 && lane < pad) a.out_sf[sf_offset(kTiled, row, nblk + lane, nblk)] = 0;
+      if (wave_in_row == 0 && lane < pad) a.out_sf[sf_offset(FMT, kTiled, row, nblk + lane, nblk)] = 0;
     } else {
       for (int64_t kb = kb0 + lane; kb < ((wave_in_row == WPR - 1) ? nblk_pad : kb_end); kb += kWave)
-        a.out_sf[sf_offset(kTiled, row, kb, nblk)] = 0;
+        a.out_sf[sf_offset(FMT, kTiled, row, kb, nblk)] = 0;
     }
   }
 }
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= rows * nblk) return;
   const int64_t row = t / nblk, kb = t % nblk;
-  const uint32_t sb = sf[sf_offset(layout, row, kb, nblk)];
+  const uint32_t sb = sf[sf_offset(FMT, layout, row, kb, nblk)];
   const float scale = (FMT == kNVFP4) ? e4m3_to_f32(sb) : ue8m0_to_f32(sb);
   const float gs = (FMT == kNVFP4 && gsp != nullptr) ? *gsp : 1.0f;
   const uint8_t* src = packed + row * (K / 2) + kb * (B / 2);

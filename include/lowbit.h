@@ -29,13 +29,18 @@
  *   - Scale layouts (per operand, `rows` x `K/B` scale bytes):
  *       LOWBIT_SF_LINEAR: row-major bytes, offset = row*(K/B) + kb.
  *       LOWBIT_SF_TILED : rows grouped by 32, blocks by 8; each group is 256
- *         bytes = 64 little-endian words; with j = kb % 8, block kb of a row
- *         is byte (j%2) + 2*(j/4) of word ((j/2)%2)*32 + row%32, so word
- *         h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of row r; groups
- *         ordered row-group major; size ceil(rows/32)*ceil((K/B)/8)*256;
- *         padding bytes are written as zero by every producer and must be
- *         zero in any TILED input.  One word per MFMA lane feeds four
- *         scaled-MFMA K-steps through the byte select.
+ *         bytes = 64 little-endian words; groups ordered row-group major;
+ *         size ceil(rows/32)*ceil((K/B)/8)*256.  With j = kb % 8, block kb
+ *         of a row is
+ *           MXFP4: byte (j%2) + 2*(j/4) of word ((j/2)%2)*32 + row%32, so
+ *                  word h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of
+ *                  row r (one word per MFMA lane feeds the four scaled-MFMA
+ *                  K-steps of a 256-element superstep through the byte select);
+ *           NVFP4: byte j%4 of word (j/4)*32 + row%32, so word c*32 + r
+ *                  holds blocks 4c..4c+3 of row r (the four 16-blocks a lane
+ *                  half dequantizes in a 128-element stage).
+ *         Padding bytes are written as zero by every producer and must be
+ *         zero in any TILED input.
  *   - Alignment: packed/bf16 tensor pointers 16 bytes; scale pointers 4 bytes
  *     (TILED) or 1 byte (LINEAR); global scales 4 bytes.
  *   - Errors are returned, never raised; on any error nothing is launched and

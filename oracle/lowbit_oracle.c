@@ -138,11 +138,14 @@ double orc_ue8m0_value(uint8_t b) {
  * LINEAR: row-major (rows, K/B) bytes, the FlashInfer page's unswizzled
  *         layout mS[row, sf_idx].
  * TILED:  rows are grouped by 32 and scale blocks by 8.  Each 32 x 8 group is
- *         256 contiguous bytes laid out as 64 little-endian 32-bit words.
- *         With j = kb % 8, block kb of a row sits in word
- *         ((j / 2) % 2) * 32 + row % 32, byte (j % 2) + 2 * (j / 4): word
- *         h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of row r.
- *         Groups are ordered row-group major.  Padding bytes are zero.
+ *         256 contiguous bytes laid out as 64 little-endian 32-bit words;
+ *         groups are ordered row-group major; padding bytes are zero.  Which
+ *         word and byte block kb of a row takes (j = kb % 8) depends on the
+ *         format, so that one word holds the four blocks one GEMM lane reads:
+ *           MXFP4: word ((j / 2) % 2) * 32 + row % 32, byte (j % 2) + 2 * (j / 4)
+ *                  (word h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of row r);
+ *           NVFP4: word (j / 4) * 32 + row % 32, byte j % 4
+ *                  (word c*32 + r holds blocks 4c .. 4c+3 of row r).
  */
 static int64_t block_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
 
@@ -152,11 +155,12 @@ int64_t orc_sf_bytes(int64_t rows, int64_t k, int fmt, int layout) {
     return ((rows + 31) / 32) * ((nblk + 7) / 8) * 256;
 }
 
-int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int layout) {
+int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int fmt, int layout) {
     if (layout == ORC_SF_LINEAR) return row * nblk + kb;
     int64_t ktiles = (nblk + 7) / 8;
     int64_t tile = (row / 32) * ktiles + kb / 8;
     int64_t j = kb % 8;
+    if (fmt == ORC_NVFP4) return tile * 256 + ((j / 4) * 32 + row % 32) * 4 + j % 4;
     return tile * 256 + (((j / 2) % 2) * 32 + row % 32) * 4 + (j % 2) + 2 * (j / 4);
 }
 
@@ -272,7 +276,7 @@ static void quant_row(const float* y, int64_t row, int64_t n, int fmt, float gs,
         quant_block(y + b * B, B, fmt, gs, codes_tmp + b * B, &sb,
                     amax_row ? amax_row + b : NULL, spre_row ? spre_row + b : NULL,
                     v_row ? v_row + b * B : NULL);
-        sf[orc_sf_offset(row, b, nblk, layout)] = sb;
+        sf[orc_sf_offset(row, b, nblk, fmt, layout)] = sb;
     }
     pack_row(codes_tmp, n, packed_row);
 }
@@ -403,7 +407,7 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
         for (int64_t i = 0; i < K; i++) {
             uint8_t byte = packed[m * (K / 2) + i / 2];
             uint8_t code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
-            uint8_t sb = sf[orc_sf_offset(m, i / B, nblk, layout)];
+            uint8_t sb = sf[orc_sf_offset(m, i / B, nblk, fmt, layout)];
             /* q * scale is exact in binary64 (and in binary32) */
             double v = orc_e2m1_value(code) *
                        ((fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb));
@@ -435,7 +439,7 @@ static double dq(const uint8_t* packed, const uint8_t* sf, int64_t row, int64_t 
     int64_t B = block_of(fmt), nblk = K / B;
     uint8_t byte = packed[row * (K / 2) + k / 2];
     uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
-    uint8_t sb = sf[orc_sf_offset(row, k / B, nblk, layout)];
+    uint8_t sb = sf[orc_sf_offset(row, k / B, nblk, fmt, layout)];
     double s = (fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb);
     return orc_e2m1_value(code) * s;
 }

@@ -61,7 +61,7 @@ def lib():
     L.orc_sf_bytes.restype = _i64
     L.orc_sf_bytes.argtypes = [_i64, _i64, _int, _int]
     L.orc_sf_offset.restype = _i64
-    L.orc_sf_offset.argtypes = [_i64, _i64, _i64, _int]
+    L.orc_sf_offset.argtypes = [_i64, _i64, _i64, _int, _int]
     L.orc_encode_with_scale.restype = None
     L.orc_encode_with_scale.argtypes = [_f32p, _int, _int, ctypes.c_float, ctypes.c_uint8, _u8p, _vp]
     L.orc_add_rmsnorm_quant.restype = _int
@@ -129,8 +129,8 @@ def sf_bytes(rows: int, k: int, fmt: int, layout: int) -> int:
     return lib().orc_sf_bytes(rows, k, fmt, layout)
 
 
-def sf_offset(row: int, kb: int, nblk: int, layout: int) -> int:
-    return lib().orc_sf_offset(row, kb, nblk, layout)
+def sf_offset(row: int, kb: int, nblk: int, fmt: int, layout: int) -> int:
+    return lib().orc_sf_offset(row, kb, nblk, fmt, layout)
 
 
 def encode_with_scale(y, fmt: int, gs: float, sbyte: int, with_v: bool = False):

@@ -29,7 +29,17 @@ def unpack_codes(packed):
     return c
 
 
-def gather_scales(orc, sf, rows, nblk, layout):
+def tiled_in_group(fmt, r, j):
+    """Byte of block j (0..7) of row r inside its 256-byte TILED group: one
+    word per (lane half, row) holding the four blocks that lane half reads
+    (MXFP4: blocks {2h, 2h+1, 2h+4, 2h+5} in word h*32 + r; NVFP4: blocks
+    4c..4c+3 in word c*32 + r)."""
+    if fmt == 0:
+        return ((j // 4) * 32 + r % 32) * 4 + j % 4
+    return (((j // 2) % 2) * 32 + r % 32) * 4 + (j % 2) + 2 * (j // 4)
+
+
+def gather_scales(orc, sf, rows, nblk, fmt, layout):
     """(rows, nblk) scale bytes from a buffer in either layout."""
     sf = np.asarray(sf, dtype=np.uint8)
     if layout == orc.LINEAR:
@@ -38,18 +48,18 @@ def gather_scales(orc, sf, rows, nblk, layout):
     kb = np.arange(nblk)[None, :]
     ktiles = (nblk + 7) // 8
     j = kb % 8
-    off = ((r // 32) * ktiles + kb // 8) * 256 + (((j // 2) % 2) * 32 + r % 32) * 4 + (j % 2) + 2 * (j // 4)
+    off = ((r // 32) * ktiles + kb // 8) * 256 + tiled_in_group(fmt, r, j)
     return sf[off]
 
 
-def tiled_padding_is_zero(orc, sf, rows, nblk):
+def tiled_padding_is_zero(orc, sf, rows, nblk, fmt):
     sf = np.asarray(sf, dtype=np.uint8)
     used = np.zeros(sf.size, bool)
     r = np.arange(rows)[:, None]
     kb = np.arange(nblk)[None, :]
     ktiles = (nblk + 7) // 8
     j = kb % 8
-    off = ((r // 32) * ktiles + kb // 8) * 256 + (((j // 2) % 2) * 32 + r % 32) * 4 + (j % 2) + 2 * (j // 4)
+    off = ((r // 32) * ktiles + kb // 8) * 256 + tiled_in_group(fmt, r, j)
     used[off.ravel()] = True
     return not np.any(sf[~used])
 
@@ -96,8 +106,8 @@ def compare_quantized(orc, fmt, gs, gpu_packed, gpu_sf, orc_packed, orc_sf, y, v
     optional absolute window widening (arrays broadcastable to v / spre)."""
     B = 16 if fmt == orc.NVFP4 else 32
     nblk = K // B
-    gs_ = gather_scales(orc, gpu_sf, rows, nblk, layout)
-    os_ = gather_scales(orc, orc_sf, rows, nblk, layout)
+    gs_ = gather_scales(orc, gpu_sf, rows, nblk, fmt, layout)
+    os_ = gather_scales(orc, orc_sf, rows, nblk, fmt, layout)
     gc = unpack_codes(np.asarray(gpu_packed).reshape(rows, K // 2))
     oc = unpack_codes(np.asarray(orc_packed).reshape(rows, K // 2))
     rep = Report(blocks=rows * nblk, scale_diff_in_window=0, code_diff_in_window=0, hard_failures=0,

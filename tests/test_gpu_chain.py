@@ -19,7 +19,7 @@ EPS = 1e-6
 def linear_rows(orc, packed, sf, rows_idx, K, fmt, layout):
     """Sub-operand made of the listed rows, scales re-laid out LINEAR (test plumbing)."""
     B = 16 if fmt == 0 else 32
-    full = checkers.gather_scales(orc, sf, packed.shape[0], K // B, layout)
+    full = checkers.gather_scales(orc, sf, packed.shape[0], K // B, fmt, layout)
     return np.ascontiguousarray(packed[rows_idx]), np.ascontiguousarray(full[rows_idx]).ravel()
 
 

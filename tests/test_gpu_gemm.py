@@ -169,7 +169,7 @@ def run_gelu_fp4(orc, M, N, K, fmt, variant, out_layout, seed, gs_out=1.0):
     banner(f"  report {dict(rep)}")
     assert rep.ok(), rep
     if out_layout == 1:
-        assert checkers.tiled_padding_is_zero(orc, host_u8(s), M, N // 16)
+        assert checkers.tiled_padding_is_zero(orc, host_u8(s), M, N // 16, 0)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 256), (33, 272, 512), (130, 176, 320)])

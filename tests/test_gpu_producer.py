@@ -47,7 +47,7 @@ def run_producer(orc, M, H, fmt, layout, seed, outliers=False, use_gs=False):
     banner(f"  report {dict(rep)}")
     assert rep.ok(), rep
     if layout == orc.TILED:
-        assert checkers.tiled_padding_is_zero(orc, host_u8(sf), M, H // (16 if fmt == 0 else 32))
+        assert checkers.tiled_padding_is_zero(orc, host_u8(sf), M, H // (16 if fmt == 0 else 32), fmt)
     return rep
 
 

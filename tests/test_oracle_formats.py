@@ -154,43 +154,67 @@ def test_bf16_rounding_against_torch(orc):
 
 # --- scale layouts ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("rows,nblk", [(1, 8), (32, 8), (41, 48), (64, 160), (33, 13), (7, 3)])
-def test_tiled_layout_is_a_bijection(orc, rows, nblk):
-    size = orc.sf_bytes(rows, nblk * 32, 1, 1)
+def test_tiled_layout_is_a_bijection(orc, fmt, rows, nblk):
+    B = 16 if fmt == 0 else 32
+    size = orc.sf_bytes(rows, nblk * B, fmt, 1)
     assert size == ((rows + 31) // 32) * ((nblk + 7) // 8) * 256
     seen = set()
     for r in range(rows):
         for kb in range(nblk):
-            off = orc.sf_offset(r, kb, nblk, 1)
+            off = orc.sf_offset(r, kb, nblk, fmt, 1)
             assert 0 <= off < size
             assert off not in seen
             seen.add(off)
 
 
-def test_tiled_layout_word_holds_the_blocks_of_one_lane(orc):
-    """Word h*32 + r of a group holds blocks 2h, 2h+1, 2h+4, 2h+5 of row r in
-    bytes 0..3 (the four blocks one MFMA lane consumes over 256 elements)."""
+def test_tiled_layout_mxfp4_word_holds_the_blocks_of_one_lane(orc):
+    """MXFP4: word h*32 + r of a group holds blocks 2h, 2h+1, 2h+4, 2h+5 of
+    row r in bytes 0..3 (the four 32-blocks one MFMA lane half consumes over
+    256 elements)."""
     nblk = 24
     for r in (0, 5, 31, 32, 63):
         for t in range(nblk // 8):
             for h in (0, 1):
                 blocks = [8 * t + 2 * h, 8 * t + 2 * h + 1, 8 * t + 2 * h + 4, 8 * t + 2 * h + 5]
-                offs = [orc.sf_offset(r, kb, nblk, 1) for kb in blocks]
+                offs = [orc.sf_offset(r, kb, nblk, 1, 1) for kb in blocks]
                 assert offs[0] % 4 == 0 and offs == [offs[0] + j for j in range(4)]
                 assert (offs[0] % 256) // 4 == h * 32 + r % 32
     # a 32-row x 8-block tile is 256 contiguous bytes, rows adjacent per word
-    assert orc.sf_offset(0, 0, 8, 1) == 0
-    assert orc.sf_offset(1, 0, 8, 1) == 4
-    assert orc.sf_offset(0, 2, 8, 1) == 128
-    assert orc.sf_offset(0, 4, 8, 1) == 2
-    assert orc.sf_offset(31, 7, 8, 1) == 255
-    assert orc.sf_offset(32, 0, 8, 1) == 256
-    assert orc.sf_offset(0, 8, 16, 1) == 256
+    assert orc.sf_offset(0, 0, 8, 1, 1) == 0
+    assert orc.sf_offset(1, 0, 8, 1, 1) == 4
+    assert orc.sf_offset(0, 2, 8, 1, 1) == 128
+    assert orc.sf_offset(0, 4, 8, 1, 1) == 2
+    assert orc.sf_offset(31, 7, 8, 1, 1) == 255
+    assert orc.sf_offset(32, 0, 8, 1, 1) == 256
+    assert orc.sf_offset(0, 8, 16, 1, 1) == 256
+
+
+def test_tiled_layout_nvfp4_word_holds_the_blocks_of_one_lane(orc):
+    """NVFP4: word c*32 + r of a group holds blocks 4c .. 4c+3 of row r in
+    bytes 0..3 (the four 16-blocks one lane half reads in a 128-element
+    stage)."""
+    nblk = 24
+    for r in (0, 5, 31, 32, 63):
+        for t in range(nblk // 8):
+            for c in (0, 1):
+                offs = [orc.sf_offset(r, 8 * t + 4 * c + j, nblk, 0, 1) for j in range(4)]
+                assert offs[0] % 4 == 0 and offs == [offs[0] + j for j in range(4)]
+                assert (offs[0] % 256) // 4 == c * 32 + r % 32
+    assert orc.sf_offset(0, 0, 8, 0, 1) == 0
+    assert orc.sf_offset(0, 3, 8, 0, 1) == 3
+    assert orc.sf_offset(0, 4, 8, 0, 1) == 128
+    assert orc.sf_offset(1, 0, 8, 0, 1) == 4
+    assert orc.sf_offset(31, 7, 8, 0, 1) == 255
+    assert orc.sf_offset(32, 0, 8, 0, 1) == 256
+    assert orc.sf_offset(0, 8, 16, 0, 1) == 256
 
 
 def test_linear_layout(orc):
     assert orc.sf_bytes(5, 64, 0, 0) == 20
-    assert orc.sf_offset(3, 2, 4, 0) == 14
+    assert orc.sf_offset(3, 2, 4, 1, 0) == 14
+    assert orc.sf_offset(3, 2, 4, 0, 0) == 14
 
 
 # --- hand-worked blocks ------------------------------------------------------------------------
@@ -209,7 +233,7 @@ def test_hand_worked_blocks(orc, blk):
     bits = xb.view(torch.int16).numpy().view(np.uint16).reshape(1, -1)
     for layout in (orc.LINEAR, orc.TILED):
         packed, sf = orc.quantize(bits, fmt, layout, gs=blk["gs"])
-        assert sf[orc.sf_offset(0, 0, 1, layout)] == blk["scale_byte"]
+        assert sf[orc.sf_offset(0, 0, 1, fmt, layout)] == blk["scale_byte"]
         codes = np.empty(bits.shape[1], np.uint8)
         codes[0::2] = packed[0] & 15
         codes[1::2] = packed[0] >> 4

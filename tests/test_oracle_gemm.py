@@ -33,7 +33,7 @@ def dequant_exact(packed, sf, rows, K, fmt, layout, orc):
         for k in range(K):
             byte = int(packed[r, k // 2])
             code = byte & 15 if k % 2 == 0 else byte >> 4
-            sb = int(sf[orc.sf_offset(r, k // B, K // B, layout)])
+            sb = int(sf[orc.sf_offset(r, k // B, K // B, fmt, layout)])
             row.append(e2m1_exact(code) * scale_exact(fmt, sb))
         out.append(row)
     return out
@@ -47,7 +47,7 @@ def random_operand(rng, rows, K, fmt, orc, layout):
     for r in range(rows):
         for kb in range(K // B):
             sb = rng.integers(118, 136) if fmt == 1 else rng.integers(0x08, 0x70)
-            sf[orc.sf_offset(r, kb, K // B, layout)] = sb
+            sf[orc.sf_offset(r, kb, K // B, fmt, layout)] = sb
     return packed, sf
 
 
@@ -105,7 +105,7 @@ def test_gemm_scale_plus_one_doubles_block(orc):
     A = dequant_exact(a, sfa, M, K, fmt, 0, orc)
     Bm = dequant_exact(b, sfb, N, K, fmt, 0, orc)
     sfa2 = sfa.copy()
-    sfa2[orc.sf_offset(1, 2, K // 32, 0)] += 1  # row 1, block 2 (k 64..95)
+    sfa2[orc.sf_offset(1, 2, K // 32, fmt, 0)] += 1  # row 1, block 2 (k 64..95)
     ref1, _ = orc.gemm(a, b, sfa2, sfb, M, N, K, fmt, 0, 0)
     assert np.array_equal(ref1[0], ref0[0])
     for n in range(N):
@@ -184,7 +184,7 @@ def test_gelu_fp4_output_is_nvfp4_of_the_gelu(orc):
     codes[:, 1::2] = out["packed"] >> 4
     for m in range(M):
         for kb in range(N // 16):
-            sb = int(out["sf"][orc.sf_offset(m, kb, N // 16, orc.TILED)])
+            sb = int(out["sf"][orc.sf_offset(m, kb, N // 16, orc.NVFP4, orc.TILED)])
             y = out["y"][m, kb * 16:(kb + 1) * 16]
             assert np.array_equal(orc.encode_with_scale(y, 0, 1.0, sb), codes[m, kb * 16:(kb + 1) * 16])
             assert sb == orc.e4m3_encode(min(np.float32(np.abs(y).max()) / np.float32(6), 448.0))

@@ -88,7 +88,7 @@ def test_constant_row_closed_form(orc, row, fmt):
         want = row["nv"] if fmt == 0 else row["mx"]
         nblk = H // (16 if fmt == 0 else 32)
         for kb in range(nblk):
-            assert out["sf"][orc.sf_offset(0, kb, nblk, layout)] == want["scale_byte"]
+            assert out["sf"][orc.sf_offset(0, kb, nblk, fmt, layout)] == want["scale_byte"]
         assert (codes_of(out["packed"]) == want["code"]).all()
 
 
