@@ -62,6 +62,21 @@ def test_producer_small(orc, M, H, fmt, layout):
     run_producer(orc, M, H, fmt, layout, seed=M * 7 + H, outliers=True, use_gs=(fmt == 0))
 
 
+# Many rows: the pipelined form (persistent waves, chunks of 512 elements in
+# flight).  Chunk counts 1..12, odd and prime ones included; M beyond the
+# resident waves so that waves carry several rows; M % 32 != 0 for the TILED
+# padding rows.
+PIPED = [(256, 64), (300, 1536), (257, 2560), (2100, 3584), (520, 5632), (4200, 6144), (2049, 512),
+         (4500, 4096)]
+
+
+@pytest.mark.parametrize("M,H", PIPED)
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_producer_many_rows(orc, M, H, fmt, layout):
+    run_producer(orc, M, H, fmt, layout, seed=M + 3 * H, outliers=True, use_gs=(fmt == 0))
+
+
 def test_producer_tiny_mxfp4_workload(orc):
     """8 rows x 256, MXFP4, linear scales (the tiny end-to-end workload)."""
     c = synth.TINY_MXFP4
