@@ -371,6 +371,105 @@ __device__ __forceinline__ void fp4_out_padding(const GemmArgs& g, int64_t r0, i
   }
 }
 
+// Epilogue of one wave's TI x TJ grid of 32x32 accumulator tiles, staged
+// through the wave's LDS area (32 rows x kEpiRowPitch floats).
+//  * bf16 outputs with N % 8 == 0: a whole row block (32 rows x 32*TJ
+//    columns) is written to LDS, then lane l takes 8 consecutive columns
+//    (l % 16) * 8 of rows 4q + l / 16, q = 0..7, so every residual load and
+//    every output store instruction covers four full 2*32*TJ-byte row
+//    segments.  The bias is loaded once (it depends on the column only); the
+//    next row block's residual is loaded while this one is combined.  The
+//    pitch 32*TJ + 8 puts the two lane halves of an accumulator write on
+//    disjoint banks.
+//  * otherwise (FP4 out, ragged N) tile by tile through epi_run16, a lane
+//    holding 16 consecutive columns of one row.
+constexpr int kEpiRowPitch = 4 * 32 + 8;
+template <int EPI, int TI, int TJ>
+__device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, int64_t mb, int64_t nb,
+                                         const GemmArgs& g, int lane) {
+  static_assert(TJ * 32 + 8 <= kEpiRowPitch, "row block wider than the staging pitch");
+  const int r = lane & 31, c = lane >> 5;
+  auto fence = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  constexpr bool kRes = EPI == kEpiResidual || EPI == kEpiBiasResidual;
+  constexpr bool kBias = EPI == kEpiBias || EPI == kEpiBiasResidual || EPI == kEpiBiasGelu;
+  if (EPI == kEpiBiasGeluFp4 || (g.N % 8) != 0) {
+    const int er = lane & 31, ec = (lane >> 5) * 16;
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+      for (int j = 0; j < TJ; j++) {
+#pragma unroll
+        for (int k = 0; k < 16; k++) et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiPitch + r] = acc[i][j][k];
+        fence();
+        epi_run16<EPI>(et + er * kEpiPitch + ec, mb + i * 32 + er, nb + j * 32 + ec, g);
+        fence();
+      }
+    return;
+  }
+  if constexpr (EPI != kEpiBiasGeluFp4) {
+    constexpr int kQ = 32 / 4;   // row groups of 4 per row block
+    const int cl = (lane & 15) * 8, rl = lane >> 4;
+    const int64_t n = nb + cl;
+    const bool col_ok = n < g.N;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const u32x4 bw = (kBias && col_ok) ? *reinterpret_cast<const u32x4*>(g.bias + n) : z4;
+    u32x4 rv[2][kQ];
+    auto load_res = [&](int i, int buf) {
+#pragma unroll
+      for (int q = 0; q < kQ; q++) {
+        const int64_t m = mb + i * 32 + q * 4 + rl;
+        rv[buf][q] = (kRes && col_ok && m < g.M) ? *reinterpret_cast<const u32x4*>(g.residual + m * g.N + n) : z4;
+      }
+    };
+    if constexpr (kRes) load_res(0, 0);
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+      if constexpr (kRes)
+        if (i + 1 < TI) load_res(i + 1, (i + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+#pragma unroll
+        for (int k = 0; k < 16; k++)
+          et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiRowPitch + j * 32 + r] = acc[i][j][k];
+      fence();
+#pragma unroll
+      for (int q = 0; q < kQ; q++) {
+        const int row = q * 4 + rl;
+        const int64_t m = mb + i * 32 + row;
+        const float4 t0 = *reinterpret_cast<const float4*>(et + row * kEpiRowPitch + cl);
+        const float4 t1 = *reinterpret_cast<const float4*>(et + row * kEpiRowPitch + cl + 4);
+        float z[8] = {g.alpha * t0.x, g.alpha * t0.y, g.alpha * t0.z, g.alpha * t0.w,
+                      g.alpha * t1.x, g.alpha * t1.y, g.alpha * t1.z, g.alpha * t1.w};
+        if constexpr (kBias) {
+#pragma unroll
+          for (int k = 0; k < 4; k++) { z[2 * k] += bf16_lo(bw[k]); z[2 * k + 1] += bf16_hi(bw[k]); }
+        }
+        if constexpr (kRes) {
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            z[2 * k] += bf16_lo(rv[i & 1][q][k]);
+            z[2 * k + 1] += bf16_hi(rv[i & 1][q][k]);
+          }
+        }
+        if constexpr (EPI == kEpiBiasGelu) {
+#pragma unroll
+          for (int k = 0; k < 8; k++) z[k] = gelu_erf(z[k]);
+        }
+        if (col_ok && m < g.M) {
+          const u32x4 o = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]), pack_bf16x2(z[4], z[5]),
+                           pack_bf16x2(z[6], z[7])};
+          *reinterpret_cast<u32x4*>(g.out + m * g.N + n) = o;
+        }
+      }
+      fence();
+    }
+  }
+}
+
 // ===========================================================================
 // Prefill schedule
 // ===========================================================================
@@ -383,6 +482,9 @@ __device__ __forceinline__ void fp4_out_padding(const GemmArgs& g, int64_t r0, i
 // At 128 x 128 per wave the fragment reads need 64 B/clk/CU of LDS bandwidth
 // at the full MFMA rate, plus 32 B/clk for the stage writes: within the
 // 128 B/clk the CU delivers.
+#ifndef PREFILL_KERNEL
+#define PREFILL_KERNEL gemm_prefill_w_kernel
+#endif
 constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 2;
 constexpr int kPThreads = kPWM * kPWN * 64;
 constexpr int kPStage = (kPBM + kPBN) * kSSBytes;         // 64 KiB per LDS buffer
@@ -997,6 +1099,409 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
     fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill schedule with 128-byte stages.  A stage is one 256-element
+// superstep: 128 bytes of each of the 256 A and 256 B rows (64 KiB), in a
+// ring of two, so every DMA instruction moves 8 whole 128-byte row segments
+// (the L2 streams those at about twice the rate of 64-byte segments).  In LDS
+// a row's eight 16-byte chunks are XOR-ed with (row / 2) % 8: the 16 lanes of
+// one ds_read_b128 phase (rows r..r+15, one chunk each) then hit 16 distinct
+// 16-byte bank groups.  One barrier per superstep, before its last quarter:
+// after it the slot just consumed is refilled with superstep ss + 2 while the
+// last quarter runs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int w_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int w_off(int row, int chunk) { return row * kSSBytes + ((chunk ^ w_swz(row)) << 4); }
+
+template <int FMT, int EPI, bool LA_TILED, bool LB_TILED>
+__global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g) {
+  constexpr int TI = kPBM / kPWM / 32, TJ = kPBN / kPWN / 32;
+  constexpr int SFB = V3Sf<FMT>::kBytes;
+  constexpr int SFL = V3Sf<FMT>::kLoads;
+  // outstanding DMA instructions of one stage with its scales
+  constexpr int kInFlight1 = kPLoads + SFL;
+  // the ring, the scale slots, and 256 bytes where the L2 prefetch lands
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPStage + 2 * SFB + 256];
+  uint8_t* const sf_lds = smem + 2 * kPStage;
+  uint8_t* const pf_lds = sf_lds + 2 * SFB;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
+  const int r = lane & 31, c = lane >> 5;
+  const int wm = wave / kPWN, wn = wave % kPWN;
+
+  const int64_t tiles_m = (g.M + kPBM - 1) / kPBM, tiles_n = (g.N + kPBN - 1) / kPBN;
+  const int64_t T = tiles_m * tiles_n;
+  int64_t t = blockIdx.x;
+  if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
+  const int64_t group = 8 * tiles_n;
+  const int64_t first_m = (t / group) * 8;
+  const int64_t gsz = (tiles_m - first_m) < 8 ? (tiles_m - first_m) : 8;
+  const int64_t tm = first_m + (t % group) % gsz;
+  const int64_t tn = (t % group) / gsz;
+  const int m0 = (int)(tm * kPBM), n0 = (int)(tn * kPBN);
+
+  const int kbytes = (int)(g.K / 2);
+  const int nblk = (int)(g.K / (FMT == kMXFP4 ? 32 : 16));
+  const int ktiles = (nblk + 7) >> 3;
+  const int nss = (int)((g.K + 255) / 256);
+  const int M = (int)g.M, N = (int)g.N;
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, M * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, N * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rssa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.sfa, (short)0, (int)sf_bytes_of(g.la, g.M, nblk), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rssb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.sfb, (short)0, (int)sf_bytes_of(g.lb, g.N, nblk), 0x00020000);
+  constexpr int kAbsent = 0x40000000;  // beyond every operand buffer (checked by the host)
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; i++)
+#pragma unroll
+    for (int j = 0; j < TJ; j++) acc[i][j] = v16f{};
+
+  // per-thread DMA geometry of a stage (one superstep, 128 bytes per row):
+  // unit u = i*256 + tid is position u%8 of row u/8 and fetches global chunk
+  // (u%8) ^ f(row), so the 8 lanes of a row move its 128 bytes in one request
+  int base_off[kPLoads], chunk_off[kPLoads];
+#pragma unroll
+  for (int i = 0; i < kPLoads; i++) {
+    const int u = i * kPThreads + tid;
+    const int row = u >> 3;
+    chunk_off[i] = ((u & 7) ^ w_swz(row)) * 16;
+    const int gr = (i < kPLoads / 2) ? m0 + row : n0 + row - kPBM;
+    const int R = (i < kPLoads / 2) ? M : N;
+    base_off[i] = (gr < R) ? gr * kbytes + chunk_off[i] : kAbsent;
+  }
+  // L2 prefetch of a later superstep: lane l of wave w touches the 128-byte
+  // segment of A row m0 + 64w + l and of B row n0 + 64w + l (one dword each,
+  // written to a throwaway LDS word, so no register waits for it)
+  constexpr int kPf = 2;   // prefetch instructions per wave per superstep
+  const int pf_a = (m0 + wave * 64 + lane < M) ? (m0 + wave * 64 + lane) * kbytes : kAbsent;
+  const int pf_b = (n0 + wave * 64 + lane < N) ? (n0 + wave * 64 + lane) * kbytes : kAbsent;
+  auto prefetch = [&](int k) {
+    const int so = k * kSSBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)pf_lds, 4, pf_a, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)pf_lds, 4, pf_b, so, 0, 0);
+  };
+
+  // stage k -> slot k%4 (and, when WITH_SF -- k even -- the scales of
+  // superstep k/2 -> sf slot (k/2)%2).  Branch-free, so that the whole loop
+  // body is one basic block the scheduler keeps in the written order.
+  constexpr bool la_t = LA_TILED, lb_t = LB_TILED;
+  auto issue = [&](int k, auto with_sf) {
+    const int so = k * kSSBytes;
+    uint8_t* slot = smem + (k & 1) * kPStage;
+#pragma unroll
+    for (int i = 0; i < kPLoads; i++) {
+      const int voff = (so + chunk_off[i] + 16 <= kbytes) ? base_off[i] + so : kAbsent;
+      lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
+      if (i < kPLoads / 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, voff, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, voff, 0, 0, 0);
+    }
+    if constexpr (decltype(with_sf)::value) {
+      const int ss = k;
+      uint8_t* sfs = sf_lds + (ss & 1) * SFB;
+#pragma unroll
+      for (int q = 0; q < SFL; q++) {
+        constexpr int half = SFL / 2;
+        const bool is_a = q < half;              // first half of the dwords: A (uniform)
+        const int dd = (q % half) * kPThreads + tid;
+        const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
+        const bool tiled = is_a ? la_t : lb_t;   // compile-time per q
+        int vt, vl;
+        bool okt, okl;
+        if constexpr (FMT == kMXFP4) {
+          const int grp = (row0 >> 5) + (dd >> 6);
+          okt = ss < nss && grp * 32 < R;
+          vt = ((grp * ktiles + ss) << 8) + ((dd & 63) << 2);
+          const int gr = row0 + (dd >> 1);
+          okl = ss < nss && gr < R;
+          vl = gr * nblk + 8 * ss + 4 * (dd & 1);
+        } else {
+          const int tile = 2 * ss + (dd >> 9);
+          const int grp = (row0 >> 5) + ((dd >> 6) & 7);
+          okt = tile < ktiles && grp * 32 < R;
+          vt = ((grp * ktiles + tile) << 8) + ((dd & 63) << 2);
+          const int gr = row0 + (dd >> 2);
+          okl = ss < nss && gr < R;
+          vl = gr * nblk + 16 * ss + 4 * (dd & 3);
+        }
+        const int voff = tiled ? (okt ? vt : kAbsent) : (okl ? vl : kAbsent);
+        lds_ptr_t dst = (lds_ptr_t)(sfs + (q * kPThreads + wave * 64) * 4);
+        if (is_a)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, dst, 4, voff, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, dst, 4, voff, 0, 0, 0);
+      }
+    }
+  };
+  using kWithSf = std::integral_constant<bool, true>;
+  using kNoSf = std::integral_constant<bool, false>;
+
+  // Steady state: when stage k and the scales of superstep k/2 lie wholly
+  // inside K, a lane's DMA offsets do not depend on k; the per-stage advance
+  // goes into the scalar offset and the LDS targets are scalar, so a DMA is
+  // one s_mov to m0 and one buffer_load (rows past M / N keep kAbsent).
+  int sf_voff[SFL];
+#pragma unroll
+  for (int q = 0; q < SFL; q++) {
+    constexpr int half = SFL / 2;
+    const bool is_a = q < half;
+    const int dd = (q % half) * kPThreads + tid;
+    const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
+    const bool tiled = is_a ? la_t : lb_t;
+    if constexpr (FMT == kMXFP4) {
+      const int grp = (row0 >> 5) + (dd >> 6);
+      const int gr = row0 + (dd >> 1);
+      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles) << 8) + ((dd & 63) << 2) : kAbsent)
+                         : (gr < R ? gr * nblk + 4 * (dd & 1) : kAbsent);
+    } else {
+      const int grp = (row0 >> 5) + ((dd >> 6) & 7);
+      const int gr = row0 + (dd >> 2);
+      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles + (dd >> 9)) << 8) + ((dd & 63) << 2) : kAbsent)
+                         : (gr < R ? gr * nblk + 4 * (dd & 3) : kAbsent);
+    }
+  }
+  auto issue_fast = [&](int k, auto with_sf) {
+    const int so = k * kSSBytes;
+    uint8_t* slot = smem + (k & 1) * kPStage;
+#pragma unroll
+    for (int i = 0; i < kPLoads; i++) {
+      lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
+      if (i < kPLoads / 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, base_off[i], so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, base_off[i], so, 0, 0);
+    }
+    if constexpr (decltype(with_sf)::value) {
+      const int ss = k;
+      uint8_t* sfs = sf_lds + (ss & 1) * SFB;
+      // scalar advance per superstep: one 256-byte group column (MXFP4) or two
+      // (NVFP4) in the tiled layout, 8 or 16 bytes of a row in the linear one
+      const int adv_t = (FMT == kMXFP4) ? (ss << 8) : (ss << 9);
+      const int adv_l = (FMT == kMXFP4) ? (ss << 3) : (ss << 4);
+      const int soa = la_t ? adv_t : adv_l, sob = lb_t ? adv_t : adv_l;
+#pragma unroll
+      for (int q = 0; q < SFL; q++) {
+        lds_ptr_t dst = (lds_ptr_t)(sfs + (q * kPThreads + wave * 64) * 4);
+        if (q < SFL / 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, dst, 4, sf_voff[q], soa, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, dst, 4, sf_voff[q], sob, 0, 0);
+      }
+    }
+  };
+
+  // the lane's scale words of superstep ss from its LDS area, branch-free:
+  // two dwords are read and v_perm picks the lane's four bytes
+  auto read_sf = [&](int ss, SfWord<FMT> (&xa)[TI], SfWord<FMT> (&xb)[TJ], auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    const uint8_t* sfs = sf_lds + (ss & 1) * SFB;
+    const int blk_per_ss = (FMT == kMXFP4) ? 8 : 16;
+    const int left = nblk - ss * blk_per_ss;   // blocks of this superstep that exist
+#pragma unroll
+    for (int side = 0; side < 2; side++) {
+      const bool tiled = side ? lb_t : la_t;
+      const uint8_t* area = sfs + side * (SFB / 2);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int grp = (side ? wn : wm) * 4 + i;     // 32-row group inside the tile
+        const int row = grp * 32 + r;
+        SfWord<FMT>& o = side ? xb[i] : xa[i];
+        if constexpr (FMT == kMXFP4) {
+          const int a0 = tiled ? grp * 256 + (c * 32 + r) * 4 : row * 8;
+          const uint32_t lo = *reinterpret_cast<const uint32_t*>(area + a0);
+          uint32_t w = lo;    // tiled: the word is the lane's four blocks
+          if (!tiled) w = __builtin_amdgcn_perm(*reinterpret_cast<const uint32_t*>(area + a0 + 4), lo, pair_sel(c));
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const bool absent = MASK && 2 * c + (j & 1) + 4 * (j >> 1) >= left;
+            w = absent ? (w & ~(0xFFu << (8 * j))) | (0x7Fu << (8 * j)) : w;
+          }
+          o.w = w;
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            // one aligned word in both layouts: no byte shuffling
+            const int a0 = tiled ? h * 2048 + grp * 256 + (c * 32 + r) * 4 : row * 16 + 8 * h + 4 * c;
+            uint32_t w = *reinterpret_cast<const uint32_t*>(area + a0);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const bool absent = MASK && 8 * h + 4 * c + j >= left;
+              w = absent ? (w & ~(0xFFu << (8 * j))) : w;
+            }
+            o.w[h] = w;
+          }
+        }
+      }
+    }
+  };
+
+  // quarter Q of superstep k: the lane's 16 bytes at 64(Q/2) + 32c + 16(Q%2)
+  // of each 128-byte row
+  auto frags = [&](int k, int s, u32x4 (&qa)[TI], u32x4 (&qb)[TJ]) {
+    const uint8_t* base = smem + (k & 1) * kPStage;
+    const int ch = 4 * (s >> 1) + 2 * c + (s & 1);
+    // order of first use by quarter_mma (i outer, j inner): a0, b0..b3, a1..a3
+    qa[0] = *reinterpret_cast<const u32x4*>(base + w_off(wm * TI * 32 + r, ch));
+#pragma unroll
+    for (int j = 0; j < TJ; j++)
+      qb[j] = *reinterpret_cast<const u32x4*>(base + w_off(kPBM + wn * TJ * 32 + j * 32 + r, ch));
+#pragma unroll
+    for (int i = 1; i < TI; i++)
+      qa[i] = *reinterpret_cast<const u32x4*>(base + w_off(wm * TI * 32 + i * 32 + r, ch));
+  };
+  // MXFP4: after each of the first TI + TJ MFMAs of a quarter DSR next-quarter
+  // LDS reads, then after each of the following MFMAs DMAs until VM are
+  // issued.  The reads come first: the compiler cannot tell the DMA's LDS
+  // writes (another ring slot) from the reads, so it keeps them in that order.
+  auto interleave = [&](auto dsr, auto vm) {
+    constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
+    if constexpr (FMT == kMXFP4) {
+      constexpr int NR = TI + TJ;                              // MFMAs carrying reads
+      constexpr int NV = TI * TJ - NR;                         // MFMAs that can carry DMAs
+      constexpr int PER = (VM + NV - 1) / (NV > 0 ? NV : 1);   // DMAs per such MFMA
+#pragma unroll
+      for (int k = 0; k < TI * TJ; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        if (k < NR) {
+          __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);   // LDS reads
+        } else if (VM > 0 && (k - NR) * PER < VM) {
+          __builtin_amdgcn_sched_group_barrier(0x010, PER, 0);   // DMAs
+        }
+      }
+    }
+  };
+  // NVFP4: one MFMA, then a share of the dequantization VALU work, and one
+  // LDS read per MFMA until DSR are issued, then one DMA per MFMA until VM
+  // are (reads before DMAs, as above)
+  auto interleave_nv = [&](auto dsr, auto vm) {
+    constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
+    if constexpr (FMT == kNVFP4) {
+#pragma unroll
+      for (int k = 0; k < 4 * TI * TJ; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        if (k < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
+        else if (k < DSR + VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one DMA
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using ILS = std::integral_constant<int, kPLoads + SFL>;
+  using ILSP = std::integral_constant<int, kPLoads + SFL + kPf>;
+  using IF = std::integral_constant<int, TI + TJ>;           // fragment reads of a quarter
+  using IFS = std::integral_constant<int, 4 * (TI + TJ)>;    // fragment + scale reads
+  // VM: DMA instructions issued after the stage being waited for (the prefetch)
+  auto stage_barrier = [&](auto vm) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_le_lgkm0<decltype(vm)::value>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  SfWord<FMT> sa[TI], sb[TJ], sa_n[TI], sb_n[TJ];
+  u32x4 qa[TI], qb[TJ], na[TI], nb[TJ];
+  issue(0, kWithSf{});
+  issue(1, kWithSf{});
+  prefetch(2);   // every stage is followed by kPf prefetch instructions
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_le_lgkm0<kInFlight1 + kPf>();   // superstep 0 has landed (1 may be in flight)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_sf(0, sa, sb, std::true_type{});
+  frags(0, 0, qa, qb);
+  v8h va[TI], vb[TJ];   // NVFP4: the next MFMA step's dequantized operands
+  if constexpr (FMT == kNVFP4) {
+#pragma unroll
+    for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][0], nv_part(sa[i], 0));
+#pragma unroll
+    for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][0], nv_part(sb[j], 0));
+  }
+  // supersteps whose refill (superstep ss + 2, scales included) lies wholly
+  // inside K: (ss + 3) * 256 <= K
+  const int nfast = max(0, min(nss, (int)(g.K / 256) - 2));
+  // superstep ss from slot ss % 2: quarters 0-2, then one barrier (superstep
+  // ss + 1 has landed; every wave is done with slot ss % 2, whose last
+  // quarter is already in registers), then quarter 3 reads superstep ss + 1
+  // and refills slot ss % 2 with superstep ss + 2
+  auto superstep = [&](int ss, auto fast) {
+    constexpr bool F = decltype(fast)::value;
+    frags(ss, 1, na, nb);
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<0, 1>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
+      interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
+      interleave(I1{}, I0{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    frags(ss, 2, qa, qb);
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<1, 2>(acc, na, nb, sa, sb, va, vb, qa, qb, sa, sb);
+      interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
+      interleave(I1{}, I0{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    frags(ss, 3, na, nb);
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<2, 3>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
+      interleave_nv(IF{}, I0{});
+    } else {
+      quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
+      interleave(I1{}, I0{});
+    }
+    // superstep ss + 1 was issued by the previous superstep (or the prologue)
+    // and followed by kPf prefetch instructions when that one was a
+    // steady-state superstep (the prologue always prefetches)
+    if (F || ss == nfast) stage_barrier(std::integral_constant<int, kPf>{});
+    else stage_barrier(std::integral_constant<int, 0>{});
+    if constexpr (F) {
+      read_sf(ss + 1, sa_n, sb_n, std::false_type{});
+      frags(ss + 1, 0, qa, qb);
+      issue_fast(ss + 2, kWithSf{});
+      prefetch(ss + 3);
+    } else {
+      issue(ss + 2, kWithSf{});
+      __builtin_amdgcn_sched_barrier(0);
+      read_sf(ss + 1, sa_n, sb_n, std::true_type{});
+      frags(ss + 1, 0, qa, qb);
+    }
+    if constexpr (FMT == kNVFP4) {
+      quarter_nv<3, 0>(acc, na, nb, sa, sb, va, vb, qa, qb, sa_n, sb_n);
+      if constexpr (F) interleave_nv(IFS{}, ILSP{}); else interleave_nv(IFS{}, I0{});
+    } else {
+      quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
+      if constexpr (F) interleave(I2{}, ILSP{}); else interleave(I2{}, I0{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
+#pragma unroll
+    for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
+  };
+  int ss = 0;
+  for (; ss < nfast; ss++) superstep(ss, std::true_type{});
+  for (; ss < nss; ss++) superstep(ss, std::false_type{});
+  // the DMA issued past the end (zeros) lands before the epilogue reuses LDS
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+
+  epi_wave<EPI, TI, TJ>(acc, reinterpret_cast<float*>(smem) + wave * 32 * kEpiRowPitch, m0 + wm * TI * 32,
+                        n0 + wn * TJ * 32, g, lane);
+  if constexpr (EPI == kEpiBiasGeluFp4)
+    fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
+}
+
 // ===========================================================================
 // Decode schedule (weights as the MFMA row operand, K split across waves)
 // ===========================================================================
@@ -1077,13 +1582,13 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
     const dim3 grid((unsigned)T), block(kPThreads);
     if (g.la == kTiled && g.lb == kTiled)
-      hipLaunchKernelGGL((gemm_prefill_kernel<FMT, EPI, true, true>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, true, true>), grid, block, 0, s, g);
     else if (g.la == kTiled)
-      hipLaunchKernelGGL((gemm_prefill_kernel<FMT, EPI, true, false>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, true, false>), grid, block, 0, s, g);
     else if (g.lb == kTiled)
-      hipLaunchKernelGGL((gemm_prefill_kernel<FMT, EPI, false, true>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, false, true>), grid, block, 0, s, g);
     else
-      hipLaunchKernelGGL((gemm_prefill_kernel<FMT, EPI, false, false>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, false, false>), grid, block, 0, s, g);
   } else
     hipLaunchKernelGGL((gemm_prefill_v2_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
   return hipGetLastError();
