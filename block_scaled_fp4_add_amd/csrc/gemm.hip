@@ -414,7 +414,7 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
     constexpr int kQ = 32 / 4;   // row groups of 4 per row block
     const int cl = (lane & 15) * 8, rl = lane >> 4;
     const int64_t n = nb + cl;
-    const bool col_ok = n < g.N;
+    const bool col_ok = cl < TJ * 32 && n < g.N;   // TJ < 4: the last lanes have no column
     const u32x4 z4 = {0u, 0u, 0u, 0u};
     const u32x4 bw = (kBias && col_ok) ? *reinterpret_cast<const u32x4*>(g.bias + n) : z4;
     u32x4 rv[2][kQ];
@@ -482,9 +482,6 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
 // At 128 x 128 per wave the fragment reads need 64 B/clk/CU of LDS bandwidth
 // at the full MFMA rate, plus 32 B/clk for the stage writes: within the
 // 128 B/clk the CU delivers.
-#ifndef PREFILL_KERNEL
-#define PREFILL_KERNEL gemm_prefill_w_kernel
-#endif
 constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 2;
 constexpr int kPThreads = kPWM * kPWN * 64;
 constexpr int kPStage = (kPBM + kPBN) * kSSBytes;         // 64 KiB per LDS buffer
@@ -1111,18 +1108,32 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) 
 // last quarter runs.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int w_swz(int row) { return (row >> 1) & 7; }
+// tile columns: NVFP4 192 (spreads the NVFP4 chain's shapes more evenly over
+// the CUs; NVFP4 is bound by its fp16 MFMAs and dequantization, not by L2
+// traffic), MXFP4 256
+template <int FMT> struct PrefillTileN {
+  static constexpr int kCols = (FMT == kNVFP4) ? 192 : 256;
+  static_assert(kCols % 64 == 0 && kCols <= 256, "tile width");
+};
 __device__ __forceinline__ int w_off(int row, int chunk) { return row * kSSBytes + ((chunk ^ w_swz(row)) << 4); }
 
 template <int FMT, int EPI, bool LA_TILED, bool LB_TILED>
 __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g) {
-  constexpr int TI = kPBM / kPWM / 32, TJ = kPBN / kPWN / 32;
-  constexpr int SFB = V3Sf<FMT>::kBytes;
-  constexpr int SFL = V3Sf<FMT>::kLoads;
+  constexpr int BN = PrefillTileN<FMT>::kCols;
+  constexpr int TI = kPBM / kPWM / 32, TJ = BN / kPWN / 32;
+  constexpr int kStage = (kPBM + BN) * kSSBytes;            // bytes of one superstep in LDS
+  constexpr int kLoadsA = kPBM * kSSBytes / 16 / kPThreads;  // 16-byte DMAs per thread: A rows
+  constexpr int kLoadsAB = kStage / 16 / kPThreads;            // ... A and B rows
+  // scale bytes of a superstep: one 256-byte group per 32 rows and 8 blocks
+  constexpr int kSfGrp = (FMT == kMXFP4) ? 1 : 2;            // 8-block groups per superstep
+  constexpr int SFA = kPBM / 32 * 256 * kSfGrp, SFB = SFA + BN / 32 * 256 * kSfGrp;
+  constexpr int SFLA = SFA / 4 / kPThreads, SFL = SFB / 4 / kPThreads;   // dword DMAs per thread
+  static_assert(SFB % (4 * kPThreads) == 0 && kStage % (16 * kPThreads) == 0 && kLoadsAB <= kPLoads, "DMA split");
   // outstanding DMA instructions of one stage with its scales
-  constexpr int kInFlight1 = kPLoads + SFL;
+  constexpr int kInFlight1 = kLoadsAB + SFL;
   // the ring, the scale slots, and 256 bytes where the L2 prefetch lands
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPStage + 2 * SFB + 256];
-  uint8_t* const sf_lds = smem + 2 * kPStage;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage + 2 * SFB + 256];
+  uint8_t* const sf_lds = smem + 2 * kStage;
   uint8_t* const pf_lds = sf_lds + 2 * SFB;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1130,7 +1141,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   const int r = lane & 31, c = lane >> 5;
   const int wm = wave / kPWN, wn = wave % kPWN;
 
-  const int64_t tiles_m = (g.M + kPBM - 1) / kPBM, tiles_n = (g.N + kPBN - 1) / kPBN;
+  const int64_t tiles_m = (g.M + kPBM - 1) / kPBM, tiles_n = (g.N + BN - 1) / BN;
   const int64_t T = tiles_m * tiles_n;
   int64_t t = blockIdx.x;
   if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
@@ -1139,7 +1150,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   const int64_t gsz = (tiles_m - first_m) < 8 ? (tiles_m - first_m) : 8;
   const int64_t tm = first_m + (t % group) % gsz;
   const int64_t tn = (t % group) / gsz;
-  const int m0 = (int)(tm * kPBM), n0 = (int)(tn * kPBN);
+  const int m0 = (int)(tm * kPBM), n0 = (int)(tn * BN);
 
   const int kbytes = (int)(g.K / 2);
   const int nblk = (int)(g.K / (FMT == kMXFP4 ? 32 : 16));
@@ -1165,14 +1176,17 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   // per-thread DMA geometry of a stage (one superstep, 128 bytes per row):
   // unit u = i*256 + tid is position u%8 of row u/8 and fetches global chunk
   // (u%8) ^ f(row), so the 8 lanes of a row move its 128 bytes in one request
+  // sized for the widest tile (kPLoads >= kLoadsAB): an array whose bound is
+  // the width-dependent constant, captured by the lambdas below, drops the
+  // kernel's host-side instantiation
   int base_off[kPLoads], chunk_off[kPLoads];
 #pragma unroll
-  for (int i = 0; i < kPLoads; i++) {
+  for (int i = 0; i < kLoadsAB; i++) {
     const int u = i * kPThreads + tid;
     const int row = u >> 3;
     chunk_off[i] = ((u & 7) ^ w_swz(row)) * 16;
-    const int gr = (i < kPLoads / 2) ? m0 + row : n0 + row - kPBM;
-    const int R = (i < kPLoads / 2) ? M : N;
+    const int gr = (i < kLoadsA) ? m0 + row : n0 + row - kPBM;
+    const int R = (i < kLoadsA) ? M : N;
     base_off[i] = (gr < R) ? gr * kbytes + chunk_off[i] : kAbsent;
   }
   // L2 prefetch of a later superstep: lane l of wave w touches the 128-byte
@@ -1180,7 +1194,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   // written to a throwaway LDS word, so no register waits for it)
   constexpr int kPf = 2;   // prefetch instructions per wave per superstep
   const int pf_a = (m0 + wave * 64 + lane < M) ? (m0 + wave * 64 + lane) * kbytes : kAbsent;
-  const int pf_b = (n0 + wave * 64 + lane < N) ? (n0 + wave * 64 + lane) * kbytes : kAbsent;
+  const int pf_b = (wave * 64 + lane < BN && n0 + wave * 64 + lane < N) ? (n0 + wave * 64 + lane) * kbytes : kAbsent;
   auto prefetch = [&](int k) {
     const int so = k * kSSBytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)pf_lds, 4, pf_a, so, 0, 0);
@@ -1193,12 +1207,12 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   constexpr bool la_t = LA_TILED, lb_t = LB_TILED;
   auto issue = [&](int k, auto with_sf) {
     const int so = k * kSSBytes;
-    uint8_t* slot = smem + (k & 1) * kPStage;
+    uint8_t* slot = smem + (k & 1) * kStage;
 #pragma unroll
-    for (int i = 0; i < kPLoads; i++) {
+    for (int i = 0; i < kLoadsAB; i++) {
       const int voff = (so + chunk_off[i] + 16 <= kbytes) ? base_off[i] + so : kAbsent;
       lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
-      if (i < kPLoads / 2)
+      if (i < kLoadsA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, voff, 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, voff, 0, 0, 0);
@@ -1208,10 +1222,10 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       uint8_t* sfs = sf_lds + (ss & 1) * SFB;
 #pragma unroll
       for (int q = 0; q < SFL; q++) {
-        constexpr int half = SFL / 2;
-        const bool is_a = q < half;              // first half of the dwords: A (uniform)
-        const int dd = (q % half) * kPThreads + tid;
+        const bool is_a = q < SFLA;              // the first SFLA dwords: A (uniform)
+        const int dd = (is_a ? q : q - SFLA) * kPThreads + tid;
         const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
+        const int G = is_a ? kPBM / 32 : BN / 32;   // 32-row groups of this side
         const bool tiled = is_a ? la_t : lb_t;   // compile-time per q
         int vt, vl;
         bool okt, okl;
@@ -1223,8 +1237,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
           okl = ss < nss && gr < R;
           vl = gr * nblk + 8 * ss + 4 * (dd & 1);
         } else {
-          const int tile = 2 * ss + (dd >> 9);
-          const int grp = (row0 >> 5) + ((dd >> 6) & 7);
+          const int tile = 2 * ss + dd / (G * 64);
+          const int grp = (row0 >> 5) + (dd % (G * 64)) / 64;
           okt = tile < ktiles && grp * 32 < R;
           vt = ((grp * ktiles + tile) << 8) + ((dd & 63) << 2);
           const int gr = row0 + (dd >> 2);
@@ -1250,9 +1264,9 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   int sf_voff[SFL];
 #pragma unroll
   for (int q = 0; q < SFL; q++) {
-    constexpr int half = SFL / 2;
-    const bool is_a = q < half;
-    const int dd = (q % half) * kPThreads + tid;
+    const bool is_a = q < SFLA;
+    const int dd = (is_a ? q : q - SFLA) * kPThreads + tid;
+    const int G = is_a ? kPBM / 32 : BN / 32;
     const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
     const bool tiled = is_a ? la_t : lb_t;
     if constexpr (FMT == kMXFP4) {
@@ -1261,19 +1275,19 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles) << 8) + ((dd & 63) << 2) : kAbsent)
                          : (gr < R ? gr * nblk + 4 * (dd & 1) : kAbsent);
     } else {
-      const int grp = (row0 >> 5) + ((dd >> 6) & 7);
+      const int grp = (row0 >> 5) + (dd % (G * 64)) / 64;
       const int gr = row0 + (dd >> 2);
-      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles + (dd >> 9)) << 8) + ((dd & 63) << 2) : kAbsent)
+      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles + dd / (G * 64)) << 8) + ((dd & 63) << 2) : kAbsent)
                          : (gr < R ? gr * nblk + 4 * (dd & 3) : kAbsent);
     }
   }
   auto issue_fast = [&](int k, auto with_sf) {
     const int so = k * kSSBytes;
-    uint8_t* slot = smem + (k & 1) * kPStage;
+    uint8_t* slot = smem + (k & 1) * kStage;
 #pragma unroll
-    for (int i = 0; i < kPLoads; i++) {
+    for (int i = 0; i < kLoadsAB; i++) {
       lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
-      if (i < kPLoads / 2)
+      if (i < kLoadsA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, base_off[i], so, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, base_off[i], so, 0, 0);
@@ -1289,7 +1303,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 #pragma unroll
       for (int q = 0; q < SFL; q++) {
         lds_ptr_t dst = (lds_ptr_t)(sfs + (q * kPThreads + wave * 64) * 4);
-        if (q < SFL / 2)
+        if (q < SFLA)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, dst, 4, sf_voff[q], soa, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, dst, 4, sf_voff[q], sob, 0, 0);
@@ -1307,10 +1321,11 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 #pragma unroll
     for (int side = 0; side < 2; side++) {
       const bool tiled = side ? lb_t : la_t;
-      const uint8_t* area = sfs + side * (SFB / 2);
+      const uint8_t* area = sfs + side * SFA;
+      const int G = side ? BN / 32 : kPBM / 32;       // 32-row groups of this side
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int grp = (side ? wn : wm) * 4 + i;     // 32-row group inside the tile
+      for (int i = 0; i < (side ? TJ : TI); i++) {
+        const int grp = (side ? wn * TJ : wm * TI) + i;     // 32-row group inside the tile
         const int row = grp * 32 + r;
         SfWord<FMT>& o = side ? xb[i] : xa[i];
         if constexpr (FMT == kMXFP4) {
@@ -1328,7 +1343,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 #pragma unroll
           for (int h = 0; h < 2; h++) {
             // one aligned word in both layouts: no byte shuffling
-            const int a0 = tiled ? h * 2048 + grp * 256 + (c * 32 + r) * 4 : row * 16 + 8 * h + 4 * c;
+            const int a0 = tiled ? h * (G * 256) + grp * 256 + (c * 32 + r) * 4 : row * 16 + 8 * h + 4 * c;
             uint32_t w = *reinterpret_cast<const uint32_t*>(area + a0);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -1345,7 +1360,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   // quarter Q of superstep k: the lane's 16 bytes at 64(Q/2) + 32c + 16(Q%2)
   // of each 128-byte row
   auto frags = [&](int k, int s, u32x4 (&qa)[TI], u32x4 (&qb)[TJ]) {
-    const uint8_t* base = smem + (k & 1) * kPStage;
+    const uint8_t* base = smem + (k & 1) * kStage;
     const int ch = 4 * (s >> 1) + 2 * c + (s & 1);
     // order of first use by quarter_mma (i outer, j inner): a0, b0..b3, a1..a3
     qa[0] = *reinterpret_cast<const u32x4*>(base + w_off(wm * TI * 32 + r, ch));
@@ -1395,8 +1410,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using ILS = std::integral_constant<int, kPLoads + SFL>;
-  using ILSP = std::integral_constant<int, kPLoads + SFL + kPf>;
+  using ILS = std::integral_constant<int, kLoadsAB + SFL>;
+  using ILSP = std::integral_constant<int, kLoadsAB + SFL + kPf>;
   using IF = std::integral_constant<int, TI + TJ>;           // fragment reads of a quarter
   using IFS = std::integral_constant<int, 4 * (TI + TJ)>;    // fragment + scale reads
   // VM: DMA instructions issued after the stage being waited for (the prefetch)
@@ -1499,7 +1514,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   epi_wave<EPI, TI, TJ>(acc, reinterpret_cast<float*>(smem) + wave * 32 * kEpiRowPitch, m0 + wm * TI * 32,
                         n0 + wn * TJ * 32, g, lane);
   if constexpr (EPI == kEpiBiasGeluFp4)
-    fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
+    fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + BN) / 16, n0 + BN >= g.N, tid, kPThreads);
 }
 
 // ===========================================================================
@@ -1559,6 +1574,20 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
 }
 
 template <int FMT, int EPI>
+void launch_w(const GemmArgs& g, dim3 block, hipStream_t s) {
+  constexpr int BN = PrefillTileN<FMT>::kCols;
+  const dim3 grid((unsigned)(((g.M + kPBM - 1) / kPBM) * ((g.N + BN - 1) / BN)));
+  if (g.la == kTiled && g.lb == kTiled)
+    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, true, true>), grid, block, 0, s, g);
+  else if (g.la == kTiled)
+    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, true, false>), grid, block, 0, s, g);
+  else if (g.lb == kTiled)
+    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, false, true>), grid, block, 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, false, false>), grid, block, 0, s, g);
+}
+
+template <int FMT, int EPI>
 hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   if (variant == 0) {
     const unsigned grid = (unsigned)((g.N + 31) / 32);
@@ -1581,14 +1610,7 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   };
   if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
     const dim3 grid((unsigned)T), block(kPThreads);
-    if (g.la == kTiled && g.lb == kTiled)
-      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, true, true>), grid, block, 0, s, g);
-    else if (g.la == kTiled)
-      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, true, false>), grid, block, 0, s, g);
-    else if (g.lb == kTiled)
-      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, false, true>), grid, block, 0, s, g);
-    else
-      hipLaunchKernelGGL((PREFILL_KERNEL<FMT, EPI, false, false>), grid, block, 0, s, g);
+    launch_w<FMT, EPI>(g, block, s);
   } else
     hipLaunchKernelGGL((gemm_prefill_v2_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
   return hipGetLastError();
