@@ -670,430 +670,11 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_v2_kernel(GemmArgs 
     fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
 }
 
-// ===========================================================================
-// Prefill schedule, pipelined over 128-element stages
-// ===========================================================================
-// Same 256 x 256 macro tile and 4 waves of 128 x 128 as above, but K advances
-// in 128-element stages (64 bytes per row, 32 KiB per stage) through a ring
-// of four LDS slots, with each stage's DMA issued three stages ahead: a
-// stage's global data has three stages of MFMA work (~3000 cycles at the full
-// rate) to arrive, enough to cover an L2 miss to the Infinity Cache or HBM.
-// The block scales of each superstep travel the same way (dword DMA into a
-// small LDS area) so that the only vector-memory traffic in the loop is DMA
-// and a fixed count per stage lets one `s_waitcnt vmcnt` (never 0) confirm
-// exactly the stage about to be read.  One workgroup barrier per stage.
-constexpr int kV3RowBytes = 64;                                 // per row per stage
-constexpr int kV3Stage = (kPBM + kPBN) * kV3RowBytes;           // 32 KiB
-constexpr int kV3Slots = 4;
-constexpr int kV3Loads = kV3Stage / 16 / kPThreads;             // 8 DMA per thread per stage
-template <int FMT> struct V3Sf {
-  static constexpr int kBytes = (FMT == kMXFP4) ? 4096 : 8192;  // A half then B half
-  static constexpr int kLoads = kBytes / 4 / kPThreads;         // dword DMA per thread per superstep
-};
-
-// row function of the stage layout: 4 chunks of 16 bytes per 64-byte row,
-// XOR-ed with (row / 4) % 4 -- measured free of bank conflicts for the
-// 32-row fragment reads (ds_read_b128 serves 16 lanes over 64 banks per cycle)
-__device__ __forceinline__ int v3_swz(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int v3_off(int row, int chunk) {
-  return row * kV3RowBytes + ((chunk ^ v3_swz(row)) << 4);
-}
-
 // s_waitcnt: vmcnt <= N (N < 64), lgkmcnt 0
 template <int N>
 __device__ __forceinline__ void wait_vm_le_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-template <int FMT, int EPI, bool LA_TILED, bool LB_TILED>
-__global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_kernel(GemmArgs g) {
-  constexpr int TI = kPBM / kPWM / 32, TJ = kPBN / kPWN / 32;
-  constexpr int SFB = V3Sf<FMT>::kBytes;
-  constexpr int SFL = V3Sf<FMT>::kLoads;
-  // outstanding DMA instructions of two consecutive stages (one carries scales)
-  constexpr int kInFlight2 = 2 * kV3Loads + SFL;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kV3Slots * kV3Stage + 2 * SFB];
-  uint8_t* const sf_lds = smem + kV3Slots * kV3Stage;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
-  const int r = lane & 31, c = lane >> 5;
-  const int wm = wave / kPWN, wn = wave % kPWN;
-
-  const int64_t tiles_m = (g.M + kPBM - 1) / kPBM, tiles_n = (g.N + kPBN - 1) / kPBN;
-  const int64_t T = tiles_m * tiles_n;
-  int64_t t = blockIdx.x;
-  if (T % 8 == 0) t = (t % 8) * (T / 8) + t / 8;
-  const int64_t group = 8 * tiles_n;
-  const int64_t first_m = (t / group) * 8;
-  const int64_t gsz = (tiles_m - first_m) < 8 ? (tiles_m - first_m) : 8;
-  const int64_t tm = first_m + (t % group) % gsz;
-  const int64_t tn = (t % group) / gsz;
-  const int m0 = (int)(tm * kPBM), n0 = (int)(tn * kPBN);
-
-  const int kbytes = (int)(g.K / 2);
-  const int nblk = (int)(g.K / (FMT == kMXFP4 ? 32 : 16));
-  const int ktiles = (nblk + 7) >> 3;
-  const int nss = (int)((g.K + 255) / 256);
-  const int M = (int)g.M, N = (int)g.N;
-  const __amdgpu_buffer_rsrc_t rsa =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, M * kbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, N * kbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rssa = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.sfa, (short)0, (int)sf_bytes_of(g.la, g.M, nblk), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rssb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.sfb, (short)0, (int)sf_bytes_of(g.lb, g.N, nblk), 0x00020000);
-  constexpr int kAbsent = 0x40000000;  // beyond every operand buffer (checked by the host)
-
-  v16f acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; i++)
-#pragma unroll
-    for (int j = 0; j < TJ; j++) acc[i][j] = v16f{};
-
-  // per-thread DMA geometry of a stage: unit u = i*256 + tid is position u%4
-  // of row u/4 and fetches global chunk (u%4) ^ f(row)
-  int base_off[kV3Loads], chunk_off[kV3Loads];
-#pragma unroll
-  for (int i = 0; i < kV3Loads; i++) {
-    const int u = i * kPThreads + tid;
-    const int row = u >> 2;
-    chunk_off[i] = ((u & 3) ^ v3_swz(row)) * 16;
-    const int gr = (i < kV3Loads / 2) ? m0 + row : n0 + row - kPBM;
-    const int R = (i < kV3Loads / 2) ? M : N;
-    base_off[i] = (gr < R) ? gr * kbytes + chunk_off[i] : kAbsent;
-  }
-
-  // stage k -> slot k%4 (and, when WITH_SF -- k even -- the scales of
-  // superstep k/2 -> sf slot (k/2)%2).  Branch-free, so that the whole loop
-  // body is one basic block the scheduler keeps in the written order.
-  constexpr bool la_t = LA_TILED, lb_t = LB_TILED;
-  auto issue = [&](int k, auto with_sf) {
-    const int so = k * kV3RowBytes;
-    uint8_t* slot = smem + (k & (kV3Slots - 1)) * kV3Stage;
-#pragma unroll
-    for (int i = 0; i < kV3Loads; i++) {
-      const int voff = (so + chunk_off[i] + 16 <= kbytes) ? base_off[i] + so : kAbsent;
-      lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
-      if (i < kV3Loads / 2)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, voff, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, voff, 0, 0, 0);
-    }
-    if constexpr (decltype(with_sf)::value) {
-      const int ss = k >> 1;
-      uint8_t* sfs = sf_lds + (ss & 1) * SFB;
-#pragma unroll
-      for (int q = 0; q < SFL; q++) {
-        constexpr int half = SFL / 2;
-        const bool is_a = q < half;              // first half of the dwords: A (uniform)
-        const int dd = (q % half) * kPThreads + tid;
-        const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
-        const bool tiled = is_a ? la_t : lb_t;   // compile-time per q
-        int vt, vl;
-        bool okt, okl;
-        if constexpr (FMT == kMXFP4) {
-          const int grp = (row0 >> 5) + (dd >> 6);
-          okt = ss < nss && grp * 32 < R;
-          vt = ((grp * ktiles + ss) << 8) + ((dd & 63) << 2);
-          const int gr = row0 + (dd >> 1);
-          okl = ss < nss && gr < R;
-          vl = gr * nblk + 8 * ss + 4 * (dd & 1);
-        } else {
-          const int tile = 2 * ss + (dd >> 9);
-          const int grp = (row0 >> 5) + ((dd >> 6) & 7);
-          okt = tile < ktiles && grp * 32 < R;
-          vt = ((grp * ktiles + tile) << 8) + ((dd & 63) << 2);
-          const int gr = row0 + (dd >> 2);
-          okl = ss < nss && gr < R;
-          vl = gr * nblk + 16 * ss + 4 * (dd & 3);
-        }
-        const int voff = tiled ? (okt ? vt : kAbsent) : (okl ? vl : kAbsent);
-        lds_ptr_t dst = (lds_ptr_t)(sfs + (q * kPThreads + wave * 64) * 4);
-        if (is_a)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, dst, 4, voff, 0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, dst, 4, voff, 0, 0, 0);
-      }
-    }
-  };
-  using kWithSf = std::integral_constant<bool, true>;
-  using kNoSf = std::integral_constant<bool, false>;
-
-  // Steady state: when stage k and the scales of superstep k/2 lie wholly
-  // inside K, a lane's DMA offsets do not depend on k; the per-stage advance
-  // goes into the scalar offset and the LDS targets are scalar, so a DMA is
-  // one s_mov to m0 and one buffer_load (rows past M / N keep kAbsent).
-  int sf_voff[SFL];
-#pragma unroll
-  for (int q = 0; q < SFL; q++) {
-    constexpr int half = SFL / 2;
-    const bool is_a = q < half;
-    const int dd = (q % half) * kPThreads + tid;
-    const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
-    const bool tiled = is_a ? la_t : lb_t;
-    if constexpr (FMT == kMXFP4) {
-      const int grp = (row0 >> 5) + (dd >> 6);
-      const int gr = row0 + (dd >> 1);
-      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles) << 8) + ((dd & 63) << 2) : kAbsent)
-                         : (gr < R ? gr * nblk + 4 * (dd & 1) : kAbsent);
-    } else {
-      const int grp = (row0 >> 5) + ((dd >> 6) & 7);
-      const int gr = row0 + (dd >> 2);
-      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles + (dd >> 9)) << 8) + ((dd & 63) << 2) : kAbsent)
-                         : (gr < R ? gr * nblk + 4 * (dd & 3) : kAbsent);
-    }
-  }
-  auto issue_fast = [&](int k, auto with_sf) {
-    const int so = k * kV3RowBytes;
-    uint8_t* slot = smem + (k & (kV3Slots - 1)) * kV3Stage;
-#pragma unroll
-    for (int i = 0; i < kV3Loads; i++) {
-      lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
-      if (i < kV3Loads / 2)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, base_off[i], so, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, dst, 16, base_off[i], so, 0, 0);
-    }
-    if constexpr (decltype(with_sf)::value) {
-      const int ss = k >> 1;
-      uint8_t* sfs = sf_lds + (ss & 1) * SFB;
-      // scalar advance per superstep: one 256-byte group column (MXFP4) or two
-      // (NVFP4) in the tiled layout, 8 or 16 bytes of a row in the linear one
-      const int adv_t = (FMT == kMXFP4) ? (ss << 8) : (ss << 9);
-      const int adv_l = (FMT == kMXFP4) ? (ss << 3) : (ss << 4);
-      const int soa = la_t ? adv_t : adv_l, sob = lb_t ? adv_t : adv_l;
-#pragma unroll
-      for (int q = 0; q < SFL; q++) {
-        lds_ptr_t dst = (lds_ptr_t)(sfs + (q * kPThreads + wave * 64) * 4);
-        if (q < SFL / 2)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, dst, 4, sf_voff[q], soa, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, dst, 4, sf_voff[q], sob, 0, 0);
-      }
-    }
-  };
-
-  // the lane's scale words of superstep ss from its LDS area, branch-free:
-  // two dwords are read and v_perm picks the lane's four bytes
-  auto read_sf = [&](int ss, SfWord<FMT> (&xa)[TI], SfWord<FMT> (&xb)[TJ], auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    const uint8_t* sfs = sf_lds + (ss & 1) * SFB;
-    const int blk_per_ss = (FMT == kMXFP4) ? 8 : 16;
-    const int left = nblk - ss * blk_per_ss;   // blocks of this superstep that exist
-#pragma unroll
-    for (int side = 0; side < 2; side++) {
-      const bool tiled = side ? lb_t : la_t;
-      const uint8_t* area = sfs + side * (SFB / 2);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int grp = (side ? wn : wm) * 4 + i;     // 32-row group inside the tile
-        const int row = grp * 32 + r;
-        SfWord<FMT>& o = side ? xb[i] : xa[i];
-        if constexpr (FMT == kMXFP4) {
-          const int a0 = tiled ? grp * 256 + (c * 32 + r) * 4 : row * 8;
-          const uint32_t lo = *reinterpret_cast<const uint32_t*>(area + a0);
-          uint32_t w = lo;    // tiled: the word is the lane's four blocks
-          if (!tiled) w = __builtin_amdgcn_perm(*reinterpret_cast<const uint32_t*>(area + a0 + 4), lo, pair_sel(c));
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const bool absent = MASK && 2 * c + (j & 1) + 4 * (j >> 1) >= left;
-            w = absent ? (w & ~(0xFFu << (8 * j))) | (0x7Fu << (8 * j)) : w;
-          }
-          o.w = w;
-        } else {
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            // one aligned word in both layouts: no byte shuffling
-            const int a0 = tiled ? h * 2048 + grp * 256 + (c * 32 + r) * 4 : row * 16 + 8 * h + 4 * c;
-            uint32_t w = *reinterpret_cast<const uint32_t*>(area + a0);
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-              const bool absent = MASK && 8 * h + 4 * c + j >= left;
-              w = absent ? (w & ~(0xFFu << (8 * j))) : w;
-            }
-            o.w[h] = w;
-          }
-        }
-      }
-    }
-  };
-
-  // slice s of stage k (the lane's 16 bytes at 32c + 16s of each 64-byte row)
-  auto frags = [&](int k, int s, u32x4 (&qa)[TI], u32x4 (&qb)[TJ]) {
-    const uint8_t* base = smem + (k & (kV3Slots - 1)) * kV3Stage;
-    // order of first use by quarter_mma (i outer, j inner): a0, b0..b3, a1..a3
-    qa[0] = *reinterpret_cast<const u32x4*>(base + v3_off(wm * TI * 32 + r, 2 * c + s));
-#pragma unroll
-    for (int j = 0; j < TJ; j++)
-      qb[j] = *reinterpret_cast<const u32x4*>(base + v3_off(kPBM + wn * TJ * 32 + j * 32 + r, 2 * c + s));
-#pragma unroll
-    for (int i = 1; i < TI; i++)
-      qa[i] = *reinterpret_cast<const u32x4*>(base + v3_off(wm * TI * 32 + i * 32 + r, 2 * c + s));
-  };
-  // MXFP4: after each of the first TI + TJ MFMAs of a quarter DSR next-quarter
-  // LDS reads, then after each of the following MFMAs DMAs until VM are
-  // issued.  The reads come first: the compiler cannot tell the DMA's LDS
-  // writes (another ring slot) from the reads, so it keeps them in that order.
-  auto interleave = [&](auto dsr, auto vm) {
-    constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
-    if constexpr (FMT == kMXFP4) {
-      constexpr int NR = TI + TJ;                              // MFMAs carrying reads
-      constexpr int NV = TI * TJ - NR;                         // MFMAs that can carry DMAs
-      constexpr int PER = (VM + NV - 1) / (NV > 0 ? NV : 1);   // DMAs per such MFMA
-#pragma unroll
-      for (int k = 0; k < TI * TJ; k++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        if (k < NR) {
-          __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);   // LDS reads
-        } else if (VM > 0 && (k - NR) * PER < VM) {
-          __builtin_amdgcn_sched_group_barrier(0x010, PER, 0);   // DMAs
-        }
-      }
-    }
-  };
-  // NVFP4: one MFMA, then a share of the dequantization VALU work, and one
-  // LDS read per MFMA until DSR are issued, then one DMA per MFMA until VM
-  // are (reads before DMAs, as above)
-  auto interleave_nv = [&](auto dsr, auto vm) {
-    constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
-    if constexpr (FMT == kNVFP4) {
-#pragma unroll
-      for (int k = 0; k < 4 * TI * TJ; k++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
-        if (k < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
-        else if (k < DSR + VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one DMA
-      }
-    }
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using IL = std::integral_constant<int, kV3Loads>;
-  using ILS = std::integral_constant<int, kV3Loads + SFL>;
-  using IF = std::integral_constant<int, TI + TJ>;           // fragment reads of a quarter
-  using IFS = std::integral_constant<int, 4 * (TI + TJ)>;    // fragment + scale reads
-  auto stage_barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_le_lgkm0<kInFlight2>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  SfWord<FMT> sa[TI], sb[TJ], sa_n[TI], sb_n[TJ];
-  u32x4 qa[TI], qb[TJ], na[TI], nb[TJ];
-  issue(0, kWithSf{});
-  issue(1, kNoSf{});
-  issue(2, kWithSf{});
-  stage_barrier();          // stage 0 and the scales of superstep 0 have landed
-  read_sf(0, sa, sb, std::true_type{});
-  frags(0, 0, qa, qb);
-  v8h va[TI], vb[TJ];   // NVFP4: the next MFMA step's dequantized operands
-  if constexpr (FMT == kNVFP4) {
-#pragma unroll
-    for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][0], nv_part(sa[i], 0));
-#pragma unroll
-    for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][0], nv_part(sb[j], 0));
-  }
-  // superstep ss: quarters 0, 1 from stage 2ss, quarters 2, 3 from stage 2ss + 1;
-  // it issues stages 2ss + 3 and 2ss + 4 (with the scales of superstep ss + 2)
-  auto superstep = [&](int ss, auto fast) {
-    constexpr bool F = decltype(fast)::value;
-    const int k0 = 2 * ss, k1 = 2 * ss + 1;
-    if constexpr (F) {
-      frags(k0, 1, na, nb);
-      issue_fast(k0 + 3, kNoSf{});
-    } else {
-      issue(k0 + 3, kNoSf{});
-      __builtin_amdgcn_sched_barrier(0);
-      frags(k0, 1, na, nb);
-    }
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<0, 1>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
-      if constexpr (F) interleave_nv(IF{}, IL{}); else interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
-      if constexpr (F) interleave(I1{}, IL{}); else interleave(I1{}, I0{});
-    }
-    stage_barrier();        // stage k1 has landed; every wave is done with stage k0 - 1
-    frags(k1, 0, qa, qb);
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<1, 2>(acc, na, nb, sa, sb, va, vb, qa, qb, sa, sb);
-      interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
-      interleave(I1{}, I0{});
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (F) {
-      frags(k1, 1, na, nb);
-      issue_fast(k1 + 3, kWithSf{});
-    } else {
-      issue(k1 + 3, kWithSf{});
-      __builtin_amdgcn_sched_barrier(0);
-      frags(k1, 1, na, nb);
-    }
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<2, 3>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
-      if constexpr (F) interleave_nv(IF{}, ILS{}); else interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
-      if constexpr (F) interleave(I1{}, ILS{}); else interleave(I1{}, I0{});
-    }
-    stage_barrier();        // stage k1 + 1 (and the scales of superstep ss + 1) have landed
-    if constexpr (F) {
-      read_sf(ss + 1, sa_n, sb_n, std::false_type{});
-    } else {
-      read_sf(ss + 1, sa_n, sb_n, std::true_type{});
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    frags(k1 + 1, 0, qa, qb);
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<3, 0>(acc, na, nb, sa, sb, va, vb, qa, qb, sa_n, sb_n);
-      if constexpr (F) interleave_nv(IFS{}, I0{}); else interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
-      if constexpr (F) interleave(I2{}, I0{}); else interleave(I1{}, I0{});
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
-#pragma unroll
-    for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
-  };
-  // supersteps whose issued stages and scale groups all lie inside K: the
-  // stages up to 2ss + 4 and superstep ss + 2 complete, (ss + 3) * 256 <= K
-  const int nfast = max(0, min(nss, (int)(g.K / 256) - 2));
-  int ss = 0;
-  for (; ss < nfast; ss++) superstep(ss, std::true_type{});
-  for (; ss < nss; ss++) superstep(ss, std::false_type{});
-  // the DMA issued past the end (zeros) lands before the epilogue reuses LDS
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  __syncthreads();
-
-  float* et = reinterpret_cast<float*>(smem) + wave * 32 * kEpiPitch;
-  const int er = lane & 31, ec = (lane >> 5) * 16;
-#pragma unroll
-  for (int i = 0; i < TI; i++) {
-#pragma unroll
-    for (int j = 0; j < TJ; j++) {
-#pragma unroll
-      for (int k = 0; k < 16; k++) et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiPitch + r] = acc[i][j][k];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      epi_run16<EPI>(et + er * kEpiPitch + ec, m0 + wm * TI * 32 + i * 32 + er,
-                     n0 + wn * TJ * 32 + j * 32 + ec, g);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-  if constexpr (EPI == kEpiBiasGeluFp4)
-    fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
 }
 
 // ---------------------------------------------------------------------------
@@ -1392,7 +973,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       }
     }
   };
-  // NVFP4: one MFMA, then a share of the dequantization VALU work, and one
+  // NVFP4: one MFMA, then a share of the dequantization VALU work (about 6.5
+  // VALU ops per MFMA in the steady state: groups of 7 measured best), and one
   // LDS read per MFMA until DSR are issued, then one DMA per MFMA until VM
   // are (reads before DMAs, as above)
   auto interleave_nv = [&](auto dsr, auto vm) {
@@ -1401,7 +983,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 #pragma unroll
       for (int k = 0; k < 4 * TI * TJ; k++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
         if (k < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
         else if (k < DSR + VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one DMA
       }

@@ -249,12 +249,6 @@ __global__ __launch_bounds__(kThreads, kPipeWgsPerCu) void row_pipe_kernel(RowAr
   const int64_t H = a.H, nblk = H / B;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  if constexpr (FUSED) {
-    for (int64_t i = threadIdx.x; i < H / 8; i += kThreads) wl[i] = reinterpret_cast<const u32x4*>(a.w)[i];
-    __syncthreads();
-  }
-  const float gs = (FMT == kNVFP4 && a.gs != nullptr) ? *a.gs : 1.0f;
-
   // chunk v of `row` into buffer slot (zeros past the row's end or past M)
   u32x4 bx[P], br[P];
   // only the last chunk of a row can be partial (lanes past H are idle)
@@ -274,6 +268,12 @@ __global__ __launch_bounds__(kThreads, kPipeWgsPerCu) void row_pipe_kernel(RowAr
   int64_t row = wid;
 #pragma unroll
   for (int p = 0; p < P; p++) fetch(row, p, p, lane);
+  // the weight row goes to LDS while the first chunks are in flight
+  if constexpr (FUSED) {
+    for (int64_t i = threadIdx.x; i < H / 8; i += kThreads) wl[i] = reinterpret_cast<const u32x4*>(a.w)[i];
+    __syncthreads();
+  }
+  const float gs = (FMT == kNVFP4 && a.gs != nullptr) ? *a.gs : 1.0f;
   for (; row < a.M; row += nw) {
     // the lane index, re-defined opaquely per row: per-chunk lane offsets are
     // recomputed in the loop instead of being hoisted and held for all chunks
