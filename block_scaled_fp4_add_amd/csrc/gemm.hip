@@ -269,6 +269,31 @@ __device__ __forceinline__ void quarter_nv(v16f (&acc)[TI][TJ], const u32x4 (&qa
 }
 
 // ---------------------------------------------------------------------------
+// FP4-out epilogue of one 16-element NVFP4 block of output row m (columns
+// n .. n+15, n a multiple of 16): GELU of the pre-activations z, the block
+// scale with the output global scale gs, codes and scale byte stored.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void gelu_fp4_block(const float (&z)[16], int64_t m, int64_t n, const GemmArgs& g,
+                                               float gs) {
+  float y[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    y[k] = gelu_erf(z[k]);
+    amax = fmaxf(amax, fabsf(y[k]));
+  }
+  float inv;
+  const uint32_t sb = nv_block_scale(amax, gs, &inv);
+#pragma unroll
+  for (int k = 0; k < 16; k++) y[k] = __fmul_rn(y[k], inv);
+  uint2 p;
+  p.x = e2m1x8(y);
+  p.y = e2m1x8(y + 8);
+  *reinterpret_cast<uint2*>(g.out_packed + m * (g.N / 2) + n / 2) = p;
+  g.out_sf[sf_offset(kNVFP4, g.out_layout, m, n / 16, g.N / 16)] = (uint8_t)sb;
+}
+
+// ---------------------------------------------------------------------------
 // Epilogue on one 16-element run of output row m (columns n .. n+15), values
 // from LDS.  n is a multiple of 16.
 // ---------------------------------------------------------------------------
@@ -278,24 +303,10 @@ __device__ __forceinline__ void epi_run16(const float* t, int64_t m, int64_t n, 
   const float alpha = g.alpha;
   if constexpr (EPI == kEpiBiasGeluFp4) {
     // N % 16 == 0, so the whole block is in range
-    float y[16];
-    float amax = 0.0f;
+    float z[16];
 #pragma unroll
-    for (int k = 0; k < 16; k++) {
-      const float z = alpha * t[k] + bf16_to_f32(g.bias[n + k]);
-      y[k] = gelu_erf(z);
-      amax = fmaxf(amax, fabsf(y[k]));
-    }
-    float inv;
-    const float gs = g.gs_out ? *g.gs_out : 1.0f;
-    const uint32_t sb = nv_block_scale(amax, gs, &inv);
-#pragma unroll
-    for (int k = 0; k < 16; k++) y[k] = __fmul_rn(y[k], inv);
-    uint2 p;
-    p.x = e2m1x8(y);
-    p.y = e2m1x8(y + 8);
-    *reinterpret_cast<uint2*>(g.out_packed + m * (g.N / 2) + n / 2) = p;
-    g.out_sf[sf_offset(kNVFP4, g.out_layout, m, n / 16, g.N / 16)] = (uint8_t)sb;
+    for (int k = 0; k < 16; k++) z[k] = alpha * t[k] + bf16_to_f32(g.bias[n + k]);
+    gelu_fp4_block(z, m, n, g, g.gs_out ? *g.gs_out : 1.0f);
   } else {
     const bool vec = (g.N % 8) == 0;
 #pragma unroll
@@ -381,8 +392,10 @@ __device__ __forceinline__ void fp4_out_padding(const GemmArgs& g, int64_t r0, i
 //    next row block's residual is loaded while this one is combined.  The
 //    pitch 32*TJ + 8 puts the two lane halves of an accumulator write on
 //    disjoint banks.
-//  * otherwise (FP4 out, ragged N) tile by tile through epi_run16, a lane
-//    holding 16 consecutive columns of one row.
+//  * FP4 out: the same row-block staging; a lane takes 16-column NVFP4
+//    blocks of one row.
+//  * otherwise (ragged N) tile by tile through epi_run16, a lane holding 16
+//    consecutive columns of one row.
 constexpr int kEpiRowPitch = 4 * 32 + 8;
 template <int EPI, int TI, int TJ>
 __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, int64_t mb, int64_t nb,
@@ -396,7 +409,53 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
   };
   constexpr bool kRes = EPI == kEpiResidual || EPI == kEpiBiasResidual;
   constexpr bool kBias = EPI == kEpiBias || EPI == kEpiBiasResidual || EPI == kEpiBiasGelu;
-  if (EPI == kEpiBiasGeluFp4 || (g.N % 8) != 0) {
+  if constexpr (EPI == kEpiBiasGeluFp4) {
+    // a whole row block (32 rows x 32*TJ columns) in LDS; lane l takes row
+    // l % 32 and the 16-column blocks 2q + l / 32, q < TJ, whose bias it
+    // loads once as two 16-byte vectors (N % 16 == 0: a block is all in or
+    // all out of range)
+    const int half = lane >> 5;
+    const float alpha = g.alpha, gs = g.gs_out ? *g.gs_out : 1.0f;
+    u32x4 bz[TJ][2];
+#pragma unroll
+    for (int q = 0; q < TJ; q++) {
+      const int64_t n = nb + (2 * q + half) * 16;
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+      bz[q][0] = n < g.N ? *reinterpret_cast<const u32x4*>(g.bias + n) : z4;
+      bz[q][1] = n < g.N ? *reinterpret_cast<const u32x4*>(g.bias + n + 8) : z4;
+    }
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+#pragma unroll
+        for (int k = 0; k < 16; k++)
+          et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiRowPitch + j * 32 + r] = acc[i][j][k];
+      fence();
+      const int64_t m = mb + i * 32 + r;
+#pragma unroll
+      for (int q = 0; q < TJ; q++) {
+        const int col = (2 * q + half) * 16;
+        const int64_t n = nb + col;
+        if (m < g.M && n < g.N) {
+          float z[16];
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const float4 tv = *reinterpret_cast<const float4*>(et + r * kEpiRowPitch + col + 4 * v);
+            const uint32_t b0 = bz[q][v >> 1][2 * (v & 1)], b1 = bz[q][v >> 1][2 * (v & 1) + 1];
+            z[4 * v + 0] = alpha * tv.x + bf16_lo(b0);
+            z[4 * v + 1] = alpha * tv.y + bf16_hi(b0);
+            z[4 * v + 2] = alpha * tv.z + bf16_lo(b1);
+            z[4 * v + 3] = alpha * tv.w + bf16_hi(b1);
+          }
+          gelu_fp4_block(z, m, n, g, gs);
+        }
+      }
+      fence();
+    }
+    return;
+  }
+  if ((g.N % 8) != 0) {
     const int er = lane & 31, ec = (lane >> 5) * 16;
 #pragma unroll
     for (int i = 0; i < TI; i++)
