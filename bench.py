@@ -189,7 +189,8 @@ def cpu_baseline(stages, step_ideal_s):
     of the step and extrapolate each stage by its share of the work (bytes
     for the producers, multiply-accumulates for the GEMMs).  The sample is
     the full 4096 x 4096 producer plus a block of rows x columns (full K) of
-    each GEMM, about 60 GMAC in all.  A reported baseline, not a target."""
+    each GEMM, about 300 GMAC in all (10-30 s on the GPU host's cores).  A
+    reported baseline, not a target."""
     from oracle import oracle as orc
 
     orc.lib()
@@ -234,10 +235,10 @@ def cpu_baseline(stages, step_ideal_s):
     (M1, N1, K1), (M2, N2, K2) = synth.MXFP4_PREFILL["shapes"]
     ch = synth.NVFP4_CHAIN
     samples = [
-        (gemm_stages[0], gemm_rate(M1, N1, K1, orc.MXFP4, 1024, 4096, 1)),
-        (gemm_stages[1], gemm_rate(M2, N2, K2, orc.MXFP4, 1024, 2048, 2)),
-        (gemm_stages[2], gemm_rate(2048, ch["N1"], ch["H"], orc.NVFP4, 256, 4096, 3, gelu_fp4=True)),
-        (gemm_stages[3], gemm_rate(2048, ch["H"], ch["N1"], orc.NVFP4, 256, 2048, 4)),
+        (gemm_stages[0], gemm_rate(M1, N1, K1, orc.MXFP4, 2048, 8192, 1)),
+        (gemm_stages[1], gemm_rate(M2, N2, K2, orc.MXFP4, 2048, 4096, 2)),
+        (gemm_stages[2], gemm_rate(2048, ch["N1"], ch["H"], orc.NVFP4, 1024, 8192, 3, gelu_fp4=True)),
+        (gemm_stages[3], gemm_rate(2048, ch["H"], ch["N1"], orc.NVFP4, 1024, 4096, 4)),
     ]
     for st, mac_rate in samples:
         t_step += (st.work / 2) / mac_rate
