@@ -184,6 +184,95 @@ def build_stages():
     return stages
 
 
+def build_decode_stages():
+    """The decode-shaped workloads, timed beside the step and reported apart
+    from `value`: the four MXFP4 decode GEMMs and the NVFP4 chain at 1 and 128
+    tokens (producer, GEMM1 with GELU -> FP4, GEMM2).  These are HBM-bound
+    (the weights dominate); each rotates over enough weight copies that the
+    256 MiB last-level cache cannot hold them, as a decode step sees them."""
+    dev = "cuda"
+    stages = []
+    lay = lb.TILED
+
+    def rotating(N, K, fmt, seed, copies=8):
+        # one quantized weight, copied to `copies` distinct buffers: every
+        # decode stage rotates its own copies, and together they cycle well over
+        # a gigabyte through the last-level cache
+        W = synth.weight(N, K, seed).to(dev)
+        b, sfb = lb.lowbit_quantize(W, fmt, lay)
+        del W
+        return [(b.clone(), sfb.clone()) for _ in range(copies)]
+
+    c = synth.MXFP4_DECODE
+    for (M, N, K) in c["shapes"]:
+        A = synth.activation(M, K, c["seed"]).to(dev)
+        a, sfa = lb.lowbit_quantize(A, lb.MXFP4, lay)
+        ws = rotating(N, K, lb.MXFP4, c["seed"])
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        it = {"i": 0}
+
+        def gemm(a=a, sfa=sfa, ws=ws, out=out, it=it):
+            b, sfb = ws[it["i"] % len(ws)]
+            it["i"] += 1
+            lb.lowbit_gemm_bf16(a, b, sfa, sfb, fmt=lb.MXFP4, sfa_layout=lay, sfb_layout=lay, out=out)
+
+        stages.append(Stage(f"mxfp4_decode_gemm_{M}x{N}x{K}", gemm, "hbm", gemm_bytes(M, N, K, 32), "B",
+                            HBM_PEAK))
+    c = synth.NVFP4_CHAIN
+    H, N1 = c["H"], c["N1"]
+    gs1 = torch.tensor([1.0], dtype=torch.float32, device=dev)
+    w1 = rotating(N1, H, lb.NVFP4, c["seed"] + 50)
+    w2 = rotating(H, N1, lb.NVFP4, c["seed"] + 70)
+    bias1 = synth.bias(N1, c["seed"], index=12).to(dev)
+    for M in (1, 128):
+        x, r, w = (t.to(dev) for t in synth.producer_inputs(M, H, c["seed"] + M, outliers=True))
+        a1 = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+        sa1 = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lay), dtype=torch.uint8, device=dev)
+        a2 = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
+        sa2 = torch.empty(lb.lowbit_sf_bytes(M, N1, lb.NVFP4, lay), dtype=torch.uint8, device=dev)
+        out2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        it = {"i": 0}
+
+        def prod(x=x, r=r, w=w, a1=a1, sa1=sa1):
+            lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.NVFP4, lay, global_scale=gs1, out_packed=a1, out_sf=sa1)
+
+        def g1(a1=a1, sa1=sa1, a2=a2, sa2=sa2, it=it):
+            b, sfb = w1[it["i"] % len(w1)]
+            lb.lowbit_gemm_bias_gelu_fp4(a1, b, sa1, sfb, bias1, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay,
+                                         out_packed=a2, out_sf=sa2, out_layout=lay)
+
+        def g2(a2=a2, sa2=sa2, out2=out2, it=it):
+            b, sfb = w2[it["i"] % len(w2)]
+            it["i"] += 1
+            lb.lowbit_gemm_bf16(a2, b, sa2, sfb, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay, out=out2)
+
+        stages.append(Stage(f"chain_m{M}_add_rmsnorm_nvfp4_{M}x{H}", prod, "hbm", producer_bytes(M, H, 16), "B",
+                            HBM_PEAK))
+        stages.append(Stage(f"chain_m{M}_nvfp4_gemm_gelu_fp4_{M}x{N1}x{H}", g1, "hbm",
+                            gemm_bytes(M, N1, H, 16, epi_bias=True, out_fp4=True), "B", HBM_PEAK))
+        stages.append(Stage(f"chain_m{M}_nvfp4_gemm_{M}x{H}x{N1}", g2, "hbm", gemm_bytes(M, H, N1, 16), "B",
+                            HBM_PEAK))
+    return stages
+
+
+def report(stages):
+    kernels = {}
+    for s in stages:
+        t = s.mean_s()
+        rate = s.work / t
+        frac = s.ideal_s() / t
+        kernels[s.name] = {"us": round(t * 1e6, 2),
+                           ("GB/s" if s.unit_work == "B" else "TFLOP/s"):
+                               round(rate / (1e9 if s.unit_work == "B" else 1e12), 1),
+                           "roofline_frac": round(frac, 4)}
+        if s.own_peak != s.roof:
+            kernels[s.name][f"{s.own_dtype}_mfma_frac"] = round(s.work / t / s.own_peak, 4)
+        log(f"[bench] {s.name}: {t * 1e6:.1f} us, "
+            f"{rate / (1e9 if s.unit_work == 'B' else 1e12):.1f} {'GB/s' if s.unit_work == 'B' else 'TFLOP/s'}, "
+            f"{100 * frac:.1f}% of roofline")
+    return kernels
+
+
 def cpu_baseline(stages, step_ideal_s):
     """Time the CPU oracle, as it stands, on a bounded sample of every stage
     of the step and extrapolate each stage by its share of the work (bytes
@@ -279,6 +368,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-shaped workloads reported beside the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed region, run a 1 GiB read + 1 GiB write elementwise kernel "
                          "three times: the known-size kernel that calibrates the HBM byte counters")
@@ -319,20 +410,20 @@ def main():
         del src, dst
     ideal = sum(s.ideal_s() for s in stages)
     value = 100.0 * ideal / (wall / args.steps)
-    kernels = {}
-    for s in stages:
-        t = s.mean_s()
-        rate = s.work / t
-        frac = s.ideal_s() / t
-        kernels[s.name] = {"us": round(t * 1e6, 2),
-                           ("GB/s" if s.unit_work == "B" else "TFLOP/s"):
-                               round(rate / (1e9 if s.unit_work == "B" else 1e12), 1),
-                           "roofline_frac": round(frac, 4)}
-        if s.own_peak != s.roof:
-            kernels[s.name][f"{s.own_dtype}_mfma_frac"] = round(s.work / t / s.own_peak, 4)
-        log(f"[bench] {s.name}: {t * 1e6:.1f} us, "
-            f"{rate / (1e9 if s.unit_work == 'B' else 1e12):.1f} {'GB/s' if s.unit_work == 'B' else 'TFLOP/s'}, "
-            f"{100 * frac:.1f}% of roofline")
+    kernels = report(stages)
+    decode = None
+    if not args.no_decode:
+        # decode-shaped workloads: timed after the step, reported apart from `value`
+        log("[bench] decode workloads")
+        dstages = build_decode_stages()
+        for _ in range(3):
+            for s in dstages:
+                s(False)
+        for _ in range(args.steps):
+            for s in dstages:
+                s(True)
+        torch.cuda.synchronize()
+        decode = report(dstages)
     # dominant kernel: the one with the largest share of the step
     dom = max(stages, key=lambda s: s.mean_s())
     t = dom.mean_s()
@@ -355,7 +446,7 @@ def main():
                                    "mxfp4_prefill_gemm_bias_residual (8192,14336,4096),(8192,4096,14336) + "
                                    "nvfp4_chain_m2048_h5120_n17408",
                        "parallelism": "none (1 GPU)"},
-            "roofline": roof, "cpu_baseline": cpu, "kernels": kernels}
+            "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode}
     print(json.dumps(line), flush=True)
 
 

@@ -117,13 +117,17 @@ __device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int
 __device__ __forceinline__ int quarter_off(int Q, int c) { return 64 * (Q >> 1) + 32 * c + 16 * (Q & 1); }
 
 // the 64 packed bytes lane half c owns of `row` in superstep ss; zero outside.
+// STREAM: nontemporal (an operand read once, the weights); otherwise cached
+// (the activations, which every workgroup reads).
+template <bool STREAM>
 __device__ __forceinline__ void load_frag_global(Frag& f, const uint8_t* base, int64_t row, int64_t R,
                                                  int64_t kbytes, int64_t ss, int c) {
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     const int64_t o = ss * kSSBytes + quarter_off(s, c);
+    const u32x4* p = reinterpret_cast<const u32x4*>(base + row * kbytes + o);
     if (row < R && o + 16 <= kbytes)
-      f.q[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + row * kbytes + o));
+      f.q[s] = STREAM ? __builtin_nontemporal_load(p) : *p;
     else
       f.q[s] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -1177,17 +1181,35 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < MT; i++) acc[0][i] = v16f{};
 
-  for (int64_t ss = wave; ss < nss; ss += W) {
-    Frag fw[1], fx[MT];
-    SfWord<FMT> sw[1], sx[MT];
-    load_frag_global(fw[0], g.b, n0 + r, g.N, kbytes, ss, c);
-    load_sf<FMT>(sw[0], g.sfb, g.lb, n0 + r, g.N, nblk, ss, c);
+  // two supersteps in flight per wave: the loads of superstep ss + W are
+  // issued before the MFMAs of ss (buffers 0 / 1 alternate, unrolled by two
+  // so that every register index stays static)
+  Frag fw[2][1], fx[2][MT];
+  SfWord<FMT> sw[2][1], sx[2][MT];
+  auto load = [&](auto bufc, int64_t ss) {
+    constexpr int buf = decltype(bufc)::value;
+    Frag(&w)[1] = fw[buf];
+    Frag(&x)[MT] = fx[buf];
+    SfWord<FMT>(&ws)[1] = sw[buf];
+    SfWord<FMT>(&xs)[MT] = sx[buf];
+    load_frag_global<true>(w[0], g.b, n0 + r, g.N, kbytes, ss, c);
+    load_sf<FMT>(ws[0], g.sfb, g.lb, n0 + r, g.N, nblk, ss, c);
 #pragma unroll
     for (int i = 0; i < MT; i++) {
-      load_frag_global(fx[i], g.a, 32 * i + r, g.M, kbytes, ss, c);
-      load_sf<FMT>(sx[i], g.sfa, g.la, 32 * i + r, g.M, nblk, ss, c);
+      load_frag_global<false>(x[i], g.a, 32 * i + r, g.M, kbytes, ss, c);
+      load_sf<FMT>(xs[i], g.sfa, g.la, 32 * i + r, g.M, nblk, ss, c);
     }
-    superstep_mma<FMT, 1, MT>(acc, fw, fx, sw, sx);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int64_t ss = wave;
+  if (ss < nss) load(B0{}, ss);
+  for (; ss < nss; ss += 2 * W) {
+    if (ss + W < nss) load(B1{}, ss + W);
+    superstep_mma<FMT, 1, MT>(acc, fw[0], fx[0], sw[0], sx[0]);
+    if (ss + W >= nss) break;
+    if (ss + 2 * W < nss) load(B0{}, ss + 2 * W);
+    superstep_mma<FMT, 1, MT>(acc, fw[1], fx[1], sw[1], sx[1]);
   }
 
   // cross-wave sum of the partial C^T tiles

@@ -55,7 +55,7 @@ def run_gemm(orc, M, N, K, fmt, la, lb_, epi, variant, seed, alpha=1.0, sample=N
 
 
 # small shapes, compared in full; they span several tiles and ragged tails
-SHAPES = [(8, 128, 256), (1, 32, 32), (5, 40, 96), (33, 70, 320), (128, 256, 512), (130, 200, 768),
+SHAPES = [(8, 128, 256), (1, 32, 32), (1, 200, 1056), (1, 17, 4096), (5, 40, 96), (33, 70, 320), (128, 256, 512), (130, 200, 768),
           (41, 4608, 1536), (200, 96, 1056)]
 
 
