@@ -845,9 +845,9 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)pf_lds, 4, pf_b, so, 0, 0);
   };
 
-  // stage k -> slot k%4 (and, when WITH_SF -- k even -- the scales of
-  // superstep k/2 -> sf slot (k/2)%2).  Branch-free, so that the whole loop
-  // body is one basic block the scheduler keeps in the written order.
+  // superstep k -> ring slot k % 2 (and, with_sf, its scales -> scale slot
+  // k % 2), masked at the K tail and past M / N.  Branch-free, so that the
+  // whole loop body is one basic block the scheduler keeps in the written order.
   constexpr bool la_t = LA_TILED, lb_t = LB_TILED;
   auto issue = [&](int k, auto with_sf) {
     const int so = k * kSSBytes;
