@@ -71,22 +71,30 @@ class Stage:
         self.own_dtype = own_dtype
         self.times = []
 
-    def __call__(self, timed):
-        if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            self.fn()
-            e1.record()
-            self.times.append((e0, e1))
-        else:
-            self.fn()
-
     def mean_s(self):
         return float(np.mean([a.elapsed_time(b) for a, b in self.times])) * 1e-3
 
     def ideal_s(self):
         return self.work / self.roof
+
+
+def run_pass(stages, timed):
+    """One pass over the stages.  Timed: one HIP event on the launch stream
+    before the first stage and one after each stage, so that a stage's time
+    runs from the event that ends the previous stage to its own (consecutive
+    stages share an event, one event's overhead per stage)."""
+    if not timed:
+        for s in stages:
+            s.fn()
+        return
+    prev = torch.cuda.Event(enable_timing=True)
+    prev.record()
+    for s in stages:
+        s.fn()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        s.times.append((prev, e))
+        prev = e
 
 
 def build_stages():
@@ -387,14 +395,12 @@ def main():
     torch.cuda.synchronize()
     log("[bench] warmup")
     for _ in range(args.warmup):
-        for s in stages:
-            s(False)
+        run_pass(stages, False)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for s in stages:
-            s(True)
+        run_pass(stages, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -417,11 +423,9 @@ def main():
         log("[bench] decode workloads")
         dstages = build_decode_stages()
         for _ in range(3):
-            for s in dstages:
-                s(False)
+            run_pass(dstages, False)
         for _ in range(args.steps):
-            for s in dstages:
-                s(True)
+            run_pass(dstages, True)
         torch.cuda.synchronize()
         decode = report(dstages)
     # dominant kernel: the one with the largest share of the step

@@ -4,9 +4,9 @@
 //   * plain FP4 quantization of a bf16 tensor and its dequantization (FlashRT
 //     fp4-gemm README, quantize_fp4_sfa_* / dequantize_fp4_sfa_*).
 //
-// Two forms.  Many rows (M >= 256) of up to 6144 elements take the pipelined
-// form (row_pipe_kernel, below).  Otherwise a row is owned by WPR wavefronts
-// (1, 2 or 4) of a 256-thread workgroup; inside a wave, lane l owns
+// Two forms.  Many rows (M >= 256) of up to 16384 elements take one
+// workgroup per row (row_wg_kernel, below).  Otherwise a row is owned by WPR
+// wavefronts (1, 2 or 4) of a 256-thread workgroup; inside a wave, lane l owns
 // quantization blocks l, l+64, ... (NBL of them) of the wave's stretch of the
 // row.  In both, the whole row stays in registers as bf16 between the
 // reduction and the quantization, so HBM sees exactly: x and r read once, r
@@ -205,173 +205,136 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined form for many rows of at most 12 * 512 elements.  Waves are
-// persistent over rows (row = wave id, + waves, ...) and stream each row in
-// chunks of 512 elements with PIPE chunks of x and r in flight: the residual
-// of a chunk is written as soon as its loads land, and the last chunks of a
-// row already fetch the first chunks of the wave's next row, so that HBM sees
-// a steady mix of reads and writes instead of a read phase and a write phase.
-// The row's bf16 h stays in registers (4 VGPRs per chunk) for the second
-// pass, which quantizes and stores the codes once the row's sum of squares
-// is known.  In chunk v lane l holds the 8 elements at v*512 + 8l, so every
-// load and store instruction covers one contiguous span (16 B per lane of
-// bf16, 4 B per lane of codes).  A block is B/8 adjacent lanes (2 for NVFP4,
-// 4 for MXFP4): its amax is exchanged with one or two lane shuffles and its
-// first lane writes the scale byte.  The RMSNorm weight row is staged once
-// per workgroup in LDS.
+// Row-per-workgroup form for many rows of at most 16384 elements.  A row is
+// H/8 vectors of 8 bf16 (16 B); the workgroup has T = 64 * NW threads, NW =
+// ceil(H / 1024), and thread t owns vectors t and t + T, so that every load
+// and store instruction of a wave covers one contiguous 1 KiB span (256 B of
+// codes) and each thread keeps four 16-byte loads of x and r in flight.
+// Resident workgroups (up to eight 4-wave ones per CU) are what keeps enough
+// bytes in flight to stream HBM: measured 20.5 us on 4096 x 4096 NVFP4 against
+// 25.3 us for a form with persistent waves carrying several rows, and 18 us for
+// a plain stream of the same x and r reads and residual writes without the
+// codes.  The row's sum of squares is reduced with a wave butterfly and
+// across the NW waves through LDS, in wave order.  A quantization block is B/8
+// adjacent lanes (2 for NVFP4, 4 for MXFP4): its amax is exchanged with one or
+// two lane shuffles and its first lane writes the scale byte.  Workgroups of
+// the TILED padding rows (M .. rows_grid - 1) only zero their scale bytes.
 // ---------------------------------------------------------------------------
-constexpr int kPipeChunk = 512;          // elements per wave-wide chunk
-constexpr int kPipeMaxChunks = 12;       // H <= 6144
-constexpr int kPipeMinRows = 256;        // fewer rows: the row-split form has more parallelism
-// Measured on the 4096 x 4096 and 2048 x 5120 NVFP4 producers: two waves
-// per SIMD (registers for the row's bf16 h, 4 per chunk, and the loads in
-// flight) with three to four chunks in flight beat deeper prefetch and more
-// waves.  The depth divides the row's chunk count: chunk c of every row then
-// lives in buffer slot c % depth, also when the last chunks of a row fetch
-// the first chunks of the next.
-constexpr int pipe_depth(int ch) {
-  return ch % 4 == 0 ? 4 : ch % 3 == 0 ? 3 : ch == 10 ? 5 : ch % 2 == 0 ? 2 : ch <= 7 ? ch : 1;
-}
-constexpr int kPipeWgsPerCu = 2;     // 4-wave workgroups per CU = waves per SIMD
-constexpr int kCUs = 256;
+constexpr int kWgMinRows = 256;     // fewer rows: the row-split form has more parallelism
+constexpr int kWgMaxWaves = 16;     // H <= 16384
+constexpr int kWgVecs = 2;          // 16-byte vectors per thread and tensor
 
-template <int FMT, int CH, bool FUSED>
-__global__ __launch_bounds__(kThreads, kPipeWgsPerCu) void row_pipe_kernel(RowArgs a) {
+template <int FMT, int NW, bool FUSED>
+__global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   constexpr int B = FmtTraits<FMT>::B;
   constexpr int LPB = B / 8;   // lanes per block
-  constexpr int P = pipe_depth(CH);
-  static_assert(CH % P == 0, "the depth must divide the chunk count");
-  __shared__ u32x4 wl[FUSED ? CH * kPipeChunk / 8 : 1];
-  const int lane = threadIdx.x % kWave;
-  // wave-uniform row indices: row base addresses stay scalar, one per-lane offset serves every chunk
-  const int64_t wid = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave));
-  const int64_t nw = (int64_t)gridDim.x * (kThreads / kWave);
-  const int64_t H = a.H, nblk = H / B;
+  constexpr int T = NW * kWave;
+  constexpr int V = kWgVecs;
+  __shared__ double part[NW];
+  const int t = threadIdx.x, lane = t % kWave;
+  const int64_t row = blockIdx.x;
+  const int64_t H = a.H, nblk = H / B, nvec = H / 8;
+  const int64_t nblk_pad = ((nblk + 7) >> 3) << 3;
+  if (row >= a.M) {
+    // TILED padding row: every scale byte zero
+    for (int64_t kb = t; kb < nblk_pad; kb += T) a.out_sf[sf_offset(FMT, kTiled, row, kb, nblk)] = 0;
+    return;
+  }
   const u32x4 zero = {0u, 0u, 0u, 0u};
-
-  // chunk v of `row` into buffer slot (zeros past the row's end or past M)
-  u32x4 bx[P], br[P];
-  // only the last chunk of a row can be partial (lanes past H are idle)
-  auto in_row = [&](int v, int ln) { return v < CH - 1 || v * kPipeChunk + ln * 8 < H; };
-  auto fetch = [&](int64_t row, int v, int slot, int ln) {
-    bx[slot] = zero;
-    if constexpr (FUSED) br[slot] = zero;
-    if (row < a.M && in_row(v, ln)) {
+  const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + row * H);
+  u32x4* rr = reinterpret_cast<u32x4*>(a.residual + row * H);
+  u32x4 xv[V], rv[V], wv[V];
+#pragma unroll
+  for (int j = 0; j < V; j++) {
+    const int q = j * T + t;
+    xv[j] = zero;
+    rv[j] = zero;
+    wv[j] = zero;
+    if (q < nvec) {
       // nontemporal: x and r are read once (measured faster than cached loads
       // when the inputs are not in the last-level cache)
-      bx[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + row * H) + v * (kPipeChunk / 8) + ln);
-      if constexpr (FUSED)
-        br[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.residual + row * H) + v * (kPipeChunk / 8) + ln);
+      xv[j] = __builtin_nontemporal_load(xr + q);
+      if constexpr (FUSED) {
+        rv[j] = __builtin_nontemporal_load(rr + q);
+        wv[j] = reinterpret_cast<const u32x4*>(a.w)[q];   // shared by every row: cached
+      }
     }
-  };
-
-  int64_t row = wid;
-#pragma unroll
-  for (int p = 0; p < P; p++) fetch(row, p, p, lane);
-  // the weight row goes to LDS while the first chunks are in flight
-  if constexpr (FUSED) {
-    for (int64_t i = threadIdx.x; i < H / 8; i += kThreads) wl[i] = reinterpret_cast<const u32x4*>(a.w)[i];
-    __syncthreads();
   }
   const float gs = (FMT == kNVFP4 && a.gs != nullptr) ? *a.gs : 1.0f;
-  for (; row < a.M; row += nw) {
-    // the lane index, re-defined opaquely per row: per-chunk lane offsets are
-    // recomputed in the loop instead of being hoisted and held for all chunks
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    u32x4 hb[CH];
+  float rstd = 1.0f;
+  if constexpr (FUSED) {
     double ss = 0.0;
-    u32x4* const res_row = reinterpret_cast<u32x4*>(a.residual + row * H);
-    uint32_t* const code_row = reinterpret_cast<uint32_t*>(a.out_packed + row * (H / 2));
-    // the row's scale bytes: a scalar base and a 32-bit per-block offset
-    uint8_t* const sf_row = (a.layout == kLinear)
-                                ? a.out_sf + row * nblk
-                                : a.out_sf + (((row >> 5) * ((nblk + 7) >> 3)) << 8) + ((row & 31) << 2);
 #pragma unroll
-    for (int v = 0; v < CH; v++) {
-      const u32x4 xv = bx[v % P], rv = br[v % P];
-      // refill the slot: chunk v + P of this row, or the next row's first chunks
-      if (v + P < CH) fetch(row, v + P, v % P, ln); else fetch(row + nw, v + P - CH, v % P, ln);
-      if constexpr (FUSED) {
-        u32x4 hw;
+    for (int j = 0; j < V; j++) {
+      u32x4 hw;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float h0 = __fadd_rn(bf16_lo(xv[j]), bf16_lo(rv[j]));
-          const float h1 = __fadd_rn(bf16_hi(xv[j]), bf16_hi(rv[j]));
-          ss = __fma_rn((double)h0, (double)h0, ss);
-          ss = __fma_rn((double)h1, (double)h1, ss);
-          hw[j] = pack_bf16x2(h0, h1);
-        }
-        hb[v] = hw;
-        if (in_row(v, ln)) __builtin_nontemporal_store(hw, res_row + v * (kPipeChunk / 8) + ln);
-      } else {
-        hb[v] = xv;
+      for (int k = 0; k < 4; k++) {
+        const float h0 = __fadd_rn(bf16_lo(xv[j][k]), bf16_lo(rv[j][k]));
+        const float h1 = __fadd_rn(bf16_hi(xv[j][k]), bf16_hi(rv[j][k]));
+        ss = __fma_rn((double)h0, (double)h0, ss);
+        ss = __fma_rn((double)h1, (double)h1, ss);
+        hw[k] = pack_bf16x2(h0, h1);
       }
-      __builtin_amdgcn_sched_barrier(0);   // loads stay where they are issued: PIPE chunks in flight
+      xv[j] = hw;   // the row's bf16 h, kept for the second pass
+      if (j * T + t < nvec) __builtin_nontemporal_store(hw, rr + j * T + t);
     }
-    float rstd = 1.0f;
-    if constexpr (FUSED) {
-      ss = wave_sum_f64(ss);
-      rstd = (float)(1.0 / sqrt(ss / (double)H + (double)a.eps));
+    ss = wave_sum_f64(ss);
+    if constexpr (NW > 1) {
+      if (lane == 0) part[t / kWave] = ss;
+      __syncthreads();
+      ss = part[0];
+#pragma unroll
+      for (int i = 1; i < NW; i++) ss += part[i];
     }
-#pragma unroll
-    for (int v = 0; v < CH; v++) {
-      const int e = v * kPipeChunk + ln * 8;
-      float y[8];
-      if constexpr (FUSED) {
-        const u32x4 wv = wl[v * (kPipeChunk / 8) + ln];   // past H: stale LDS, the lane stores nothing
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          y[2 * j] = __fmul_rn(__fmul_rn(bf16_lo(hb[v][j]), rstd), bf16_lo(wv[j]));
-          y[2 * j + 1] = __fmul_rn(__fmul_rn(bf16_hi(hb[v][j]), rstd), bf16_hi(wv[j]));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          y[2 * j] = bf16_lo(hb[v][j]);
-          y[2 * j + 1] = bf16_hi(hb[v][j]);
-        }
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(y[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-      if constexpr (LPB == 4) amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-      float inv;
-      const uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv) : mx_block_scale(amax, &inv);
-#pragma unroll
-      for (int i = 0; i < 8; i++) y[i] = __fmul_rn(y[i], inv);
-      const uint32_t code = e2m1x8(y);
-      if (in_row(v, ln)) {
-        code_row[v * (kPipeChunk / 8) + ln] = code;
-        if (ln % LPB == 0) {
-          const int kb = e / B, j = kb & 7;
-          const int in_grp = (FMT == kNVFP4) ? ((j >> 2) << 7) + (j & 3)
-                                             : (((j >> 1) & 1) << 7) + (j & 1) + ((j >> 2) << 1);
-          sf_row[(a.layout == kLinear) ? kb : ((kb >> 3) << 8) + in_grp] = (uint8_t)sb;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);   // one chunk at a time: keeps the wave's registers few
-    }
-    if (a.layout == kTiled)
-      for (int64_t kb = nblk + ln; kb < (((nblk + 7) >> 3) << 3); kb += kWave)
-        a.out_sf[sf_offset(FMT, kTiled, row, kb, nblk)] = 0;
+    rstd = (float)(1.0 / sqrt(ss / (double)H + (double)a.eps));
   }
-  // TILED: every scale byte of the padding rows M .. rows_grid - 1 is zero
-  if (a.layout == kTiled) {
-    const int64_t nblk_pad = ((nblk + 7) >> 3) << 3;
-    for (int64_t r = a.M + wid; r < a.rows_grid; r += nw)
-      for (int64_t kb = lane; kb < nblk_pad; kb += kWave) a.out_sf[sf_offset(FMT, kTiled, r, kb, nblk)] = 0;
+  uint32_t* const code_row = reinterpret_cast<uint32_t*>(a.out_packed + row * (H / 2));
+  uint8_t* const sf_row = (a.layout == kLinear)
+                              ? a.out_sf + row * nblk
+                              : a.out_sf + (((row >> 5) * (nblk_pad >> 3)) << 8) + ((row & 31) << 2);
+#pragma unroll
+  for (int j = 0; j < V; j++) {
+    const int q = j * T + t;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      if constexpr (FUSED) {
+        y[2 * k] = __fmul_rn(__fmul_rn(bf16_lo(xv[j][k]), rstd), bf16_lo(wv[j][k]));
+        y[2 * k + 1] = __fmul_rn(__fmul_rn(bf16_hi(xv[j][k]), rstd), bf16_hi(wv[j][k]));
+      } else {
+        y[2 * k] = bf16_lo(xv[j][k]);
+        y[2 * k + 1] = bf16_hi(xv[j][k]);
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(y[i]));
+    // the block's lanes are all inside the row or all past it (H % B == 0, T % 64 == 0)
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    if constexpr (LPB == 4) amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    float inv;
+    const uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv) : mx_block_scale(amax, &inv);
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] = __fmul_rn(y[i], inv);
+    const uint32_t code = e2m1x8(y);
+    if (q < nvec) {
+      code_row[q] = code;
+      if (q % LPB == 0) {
+        const int kb = q / LPB, jj = kb & 7;
+        const int in_grp = (FMT == kNVFP4) ? ((jj >> 2) << 7) + (jj & 3)
+                                           : (((jj >> 1) & 1) << 7) + (jj & 1) + ((jj >> 2) << 1);
+        sf_row[(a.layout == kLinear) ? kb : ((kb >> 3) << 8) + in_grp] = (uint8_t)sb;
+      }
+    }
   }
+  // TILED: the row's padding blocks nblk .. nblk_pad - 1 are zero
+  if (a.layout == kTiled && t < nblk_pad - nblk) a.out_sf[sf_offset(FMT, kTiled, row, nblk + t, nblk)] = 0;
 }
 
-template <int FMT, int CH, bool FUSED>
-hipError_t launch_pipe(const RowArgs& a, hipStream_t s) {
-  constexpr int kWavesPerWg = kThreads / kWave;
-  int64_t grid = (a.rows_grid + kWavesPerWg - 1) / kWavesPerWg;
-  if (grid > (int64_t)kCUs * kPipeWgsPerCu) grid = (int64_t)kCUs * kPipeWgsPerCu;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((row_pipe_kernel<FMT, CH, FUSED>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+template <int FMT, int NW, bool FUSED>
+hipError_t launch_wg(const RowArgs& a, hipStream_t s) {
+  if (a.rows_grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((row_wg_kernel<FMT, NW, FUSED>), dim3((unsigned)a.rows_grid), dim3(NW * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -385,28 +348,32 @@ hipError_t launch_row(const RowArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Many rows of at most 6144 elements: the pipelined form.  Otherwise pick
+// Many rows of at most 16384 elements: a workgroup per row.  Otherwise pick
 // (WPR, NBL) of the row-split form for a row of nblk blocks: one wave per row
 // when there are many rows, a row spread over up to 4 waves when there are few.
 template <int FMT, bool FUSED>
 hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
   constexpr int MAXNBL = (FMT == kNVFP4) ? 8 : 4;
   const int64_t nblk = a.H / FmtTraits<FMT>::B;
-  const int64_t nch = (a.H + kPipeChunk - 1) / kPipeChunk;
-  if (a.M >= kPipeMinRows && nch <= kPipeMaxChunks) {
-    switch (nch) {
-      case 1: return launch_pipe<FMT, 1, FUSED>(a, s);
-      case 2: return launch_pipe<FMT, 2, FUSED>(a, s);
-      case 3: return launch_pipe<FMT, 3, FUSED>(a, s);
-      case 4: return launch_pipe<FMT, 4, FUSED>(a, s);
-      case 5: return launch_pipe<FMT, 5, FUSED>(a, s);
-      case 6: return launch_pipe<FMT, 6, FUSED>(a, s);
-      case 7: return launch_pipe<FMT, 7, FUSED>(a, s);
-      case 8: return launch_pipe<FMT, 8, FUSED>(a, s);
-      case 9: return launch_pipe<FMT, 9, FUSED>(a, s);
-      case 10: return launch_pipe<FMT, 10, FUSED>(a, s);
-      case 11: return launch_pipe<FMT, 11, FUSED>(a, s);
-      default: return launch_pipe<FMT, 12, FUSED>(a, s);
+  const int64_t nw = (a.H + kWgVecs * 8 * kWave - 1) / (kWgVecs * 8 * kWave);
+  if (a.M >= kWgMinRows && nw <= kWgMaxWaves && a.rows_grid <= 0x7FFFFFFF) {
+    switch (nw) {
+      case 1: return launch_wg<FMT, 1, FUSED>(a, s);
+      case 2: return launch_wg<FMT, 2, FUSED>(a, s);
+      case 3: return launch_wg<FMT, 3, FUSED>(a, s);
+      case 4: return launch_wg<FMT, 4, FUSED>(a, s);
+      case 5: return launch_wg<FMT, 5, FUSED>(a, s);
+      case 6: return launch_wg<FMT, 6, FUSED>(a, s);
+      case 7: return launch_wg<FMT, 7, FUSED>(a, s);
+      case 8: return launch_wg<FMT, 8, FUSED>(a, s);
+      case 9: return launch_wg<FMT, 9, FUSED>(a, s);
+      case 10: return launch_wg<FMT, 10, FUSED>(a, s);
+      case 11: return launch_wg<FMT, 11, FUSED>(a, s);
+      case 12: return launch_wg<FMT, 12, FUSED>(a, s);
+      case 13: return launch_wg<FMT, 13, FUSED>(a, s);
+      case 14: return launch_wg<FMT, 14, FUSED>(a, s);
+      case 15: return launch_wg<FMT, 15, FUSED>(a, s);
+      default: return launch_wg<FMT, 16, FUSED>(a, s);
     }
   }
   int wpr = (a.M >= 1024) ? 1 : 4;

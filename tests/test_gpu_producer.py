@@ -62,15 +62,15 @@ def test_producer_small(orc, M, H, fmt, layout):
     run_producer(orc, M, H, fmt, layout, seed=M * 7 + H, outliers=True, use_gs=(fmt == 0))
 
 
-# Many rows: the pipelined form (persistent waves, chunks of 512 elements in
-# flight).  Chunk counts 1..12, odd and prime ones included; M beyond the
-# resident waves so that waves carry several rows; M % 32 != 0 for the TILED
-# padding rows.
-PIPED = [(256, 64), (300, 1536), (257, 2560), (2100, 3584), (520, 5632), (4200, 6144), (2049, 512),
-         (4500, 4096)]
+# Many rows: one workgroup per row (NW = ceil(H/1024) waves, two 16-byte
+# vectors per thread).  Rows of 1..6 waves, with H % 1024 != 0 so that the
+# second vector of some threads lies past the row's end; M % 32 != 0 for the
+# TILED padding rows.
+MANY_ROWS = [(256, 64), (300, 1536), (257, 2560), (2100, 3584), (520, 5632), (4200, 6144), (2049, 512),
+         (4500, 4096), (256, 16384), (300, 11264)]
 
 
-@pytest.mark.parametrize("M,H", PIPED)
+@pytest.mark.parametrize("M,H", MANY_ROWS)
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_producer_many_rows(orc, M, H, fmt, layout):
