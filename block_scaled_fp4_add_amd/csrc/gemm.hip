@@ -117,9 +117,9 @@ __device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int
 __device__ __forceinline__ int quarter_off(int Q, int c) { return 64 * (Q >> 1) + 32 * c + 16 * (Q & 1); }
 
 // the 64 packed bytes lane half c owns of `row` in superstep ss; zero outside.
-// STREAM: nontemporal (an operand read once, the weights); otherwise cached
-// (the activations, which every workgroup reads).
-template <bool STREAM>
+// Plain cached loads for both operands: a lane's four 16-byte loads share
+// 128-byte lines with the other lane half, and nontemporal loads of the
+// weights were measured 15-30% slower on every decode shape (same HBM bytes).
 __device__ __forceinline__ void load_frag_global(Frag& f, const uint8_t* base, int64_t row, int64_t R,
                                                  int64_t kbytes, int64_t ss, int c) {
 #pragma unroll
@@ -127,7 +127,7 @@ __device__ __forceinline__ void load_frag_global(Frag& f, const uint8_t* base, i
     const int64_t o = ss * kSSBytes + quarter_off(s, c);
     const u32x4* p = reinterpret_cast<const u32x4*>(base + row * kbytes + o);
     if (row < R && o + 16 <= kbytes)
-      f.q[s] = STREAM ? __builtin_nontemporal_load(p) : *p;
+      f.q[s] = *p;
     else
       f.q[s] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -1192,11 +1192,11 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
     Frag(&x)[MT] = fx[buf];
     SfWord<FMT>(&ws)[1] = sw[buf];
     SfWord<FMT>(&xs)[MT] = sx[buf];
-    load_frag_global<true>(w[0], g.b, n0 + r, g.N, kbytes, ss, c);
+    load_frag_global(w[0], g.b, n0 + r, g.N, kbytes, ss, c);
     load_sf<FMT>(ws[0], g.sfb, g.lb, n0 + r, g.N, nblk, ss, c);
 #pragma unroll
     for (int i = 0; i < MT; i++) {
-      load_frag_global<false>(x[i], g.a, 32 * i + r, g.M, kbytes, ss, c);
+      load_frag_global(x[i], g.a, 32 * i + r, g.M, kbytes, ss, c);
       load_sf<FMT>(xs[i], g.sfa, g.la, 32 * i + r, g.M, nblk, ss, c);
     }
   };
@@ -1259,6 +1259,14 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
     if (mt == MT) {                                                                            \
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, MT, W, EPI>), dim3(grid), dim3(W * 64), 0, s, g); \
       return hipGetLastError();                                                                \
+    }
+    // NVFP4 with one M-tile: its 8-wave workgroups (145 VGPRs) fit once per
+    // CU, so past 256 workgroups 4-wave ones (three per CU) finish sooner:
+    // measured 25.7 against 28.1 us at N = 17408, K = 5120, and 31.0 against
+    // 26.0 us the other way round at N = 5120 (160 workgroups)
+    if (FMT == kNVFP4 && mt == 1 && grid > 256) {
+      hipLaunchKernelGGL((gemm_decode_kernel<FMT, 1, 4, EPI>), dim3(grid), dim3(4 * 64), 0, s, g);
+      return hipGetLastError();
     }
     LB_DEC(1, 8) LB_DEC(2, 8) LB_DEC(3, 4) LB_DEC(4, 4)
 #undef LB_DEC

@@ -56,9 +56,12 @@ def run_gemm(orc, M, N, K, fmt, la, lb_, epi, variant, seed, alpha=1.0, sample=N
 
 # small shapes, compared in full; they span several tiles and ragged tails,
 # and (the last three) give the decode schedule's waves odd superstep counts
-# (K / 256 = 9, 17, 18 over 8, 8 and 4 waves)
+# (K / 256 = 9, 17, 18 over 8, 8 and 4 waves); the two with N > 8192 put
+# more than 256 workgroups on the decode schedule, which NVFP4 runs with
+# 4-wave workgroups
 SHAPES = [(8, 128, 256), (1, 32, 32), (1, 200, 1056), (1, 17, 4096), (5, 40, 96), (33, 70, 320), (128, 256, 512), (130, 200, 768),
-          (41, 4608, 1536), (200, 96, 1056), (3, 96, 2304), (40, 64, 4352), (100, 48, 4608)]
+          (41, 4608, 1536), (200, 96, 1056), (3, 96, 2304), (40, 64, 4352), (100, 48, 4608),
+          (1, 8224, 544), (2, 9000, 1056)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -174,7 +177,7 @@ def run_gelu_fp4(orc, M, N, K, fmt, variant, out_layout, seed, gs_out=1.0):
         assert checkers.tiled_padding_is_zero(orc, host_u8(s), M, N // 16, 0)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (33, 272, 512), (130, 176, 320)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (33, 272, 512), (130, 176, 320), (1, 8256, 256)])
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("out_layout", [0, 1])
 def test_gemm_gelu_fp4(orc, M, N, K, fmt, out_layout):
