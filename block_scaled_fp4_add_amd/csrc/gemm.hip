@@ -479,13 +479,23 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
     const int64_t n = nb + cl;
     const bool col_ok = cl < TJ * 32 && n < g.N;   // TJ < 4: the last lanes have no column
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    const u32x4 bw = (kBias && col_ok) ? *reinterpret_cast<const u32x4*>(g.bias + n) : z4;
+    float bf[8];   // the lane's 8 bias values (zero without bias)
+    {
+      const u32x4 bw = (kBias && col_ok) ? *reinterpret_cast<const u32x4*>(g.bias + n) : z4;
+#pragma unroll
+      for (int k = 0; k < 4; k++) { bf[2 * k] = bf16_lo(bw[k]); bf[2 * k + 1] = bf16_hi(bw[k]); }
+    }
+    // element (mb + 32i + 4q + rl, nb + cl): a wave-uniform row-group base
+    // plus the lane's 32-bit offset rl * N + cl (the row block is < 2^31 elements)
+    const uint32_t loff = (uint32_t)(rl * g.N + cl);
+    const float alpha = g.alpha;
     u32x4 rv[2][kQ];
     auto load_res = [&](int i, int buf) {
 #pragma unroll
       for (int q = 0; q < kQ; q++) {
         const int64_t m = mb + i * 32 + q * 4 + rl;
-        rv[buf][q] = (kRes && col_ok && m < g.M) ? *reinterpret_cast<const u32x4*>(g.residual + m * g.N + n) : z4;
+        const uint16_t* base = g.residual + (mb + i * 32 + q * 4) * g.N + nb;
+        rv[buf][q] = (kRes && col_ok && m < g.M) ? *reinterpret_cast<const u32x4*>(base + loff) : z4;
       }
     };
     if constexpr (kRes) load_res(0, 0);
@@ -505,12 +515,10 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
         const int64_t m = mb + i * 32 + row;
         const float4 t0 = *reinterpret_cast<const float4*>(et + row * kEpiRowPitch + cl);
         const float4 t1 = *reinterpret_cast<const float4*>(et + row * kEpiRowPitch + cl + 4);
-        float z[8] = {g.alpha * t0.x, g.alpha * t0.y, g.alpha * t0.z, g.alpha * t0.w,
-                      g.alpha * t1.x, g.alpha * t1.y, g.alpha * t1.z, g.alpha * t1.w};
-        if constexpr (kBias) {
+        const float t[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        float z[8];
 #pragma unroll
-          for (int k = 0; k < 4; k++) { z[2 * k] += bf16_lo(bw[k]); z[2 * k + 1] += bf16_hi(bw[k]); }
-        }
+        for (int k = 0; k < 8; k++) z[k] = kBias ? __fmaf_rn(alpha, t[k], bf[k]) : alpha * t[k];
         if constexpr (kRes) {
 #pragma unroll
           for (int k = 0; k < 4; k++) {
@@ -525,7 +533,8 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
         if (col_ok && m < g.M) {
           const u32x4 o = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]), pack_bf16x2(z[4], z[5]),
                            pack_bf16x2(z[6], z[7])};
-          *reinterpret_cast<u32x4*>(g.out + m * g.N + n) = o;
+          uint16_t* base = g.out + (mb + i * 32 + q * 4) * g.N + nb;
+          *reinterpret_cast<u32x4*>(base + loff) = o;
         }
       }
       fence();
