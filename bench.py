@@ -241,6 +241,35 @@ def build_stages():
     return stages
 
 
+def build_variant_stages():
+    """Format variants of the step's kernels, timed beside the step and
+    reported apart from `value`: the fused producer on fp16 tensors at the
+    4096 x 4096 NVFP4 workload (same draws, rounded to fp16), rotated over 4
+    input sets like the bf16 stage."""
+    dev = "cuda"
+    c = synth.NVFP4_PRODUCER
+    M, H = c["M"], c["H"]
+    sets = []
+    for i in range(4):
+        x, r, w = synth.producer_inputs(M, H, c["seed"] + 100 * i, outliers=True, dtype=torch.float16)
+        sets.append((x.to(dev), r.to(dev), w.to(dev)))
+    x0, r0, w0 = synth.producer_inputs(M, H, c["seed"], outliers=True, dtype=torch.float16)
+    p, s = lb.lowbit_add_rmsnorm_quant(x0.to(dev), r0.to(dev), w0.to(dev), EPS, lb.NVFP4, lb.LINEAR)
+    amax = lb.lowbit_dequantize(p, s, lb.NVFP4, lb.LINEAR).float().abs().max().item()
+    gs = torch.tensor([2688.0 / amax], dtype=torch.float32, device=dev)
+    pk = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lb.LINEAR), dtype=torch.uint8, device=dev)
+    it = {"i": 0}
+
+    def producer():
+        x, r, w = sets[it["i"] % 4]
+        it["i"] += 1
+        lb.lowbit_add_rmsnorm_quant_fp16(x, r, w, EPS, lb.NVFP4, lb.LINEAR, global_scale=gs, out_packed=pk,
+                                         out_sf=sf)
+
+    return [Stage(f"add_rmsnorm_nvfp4_fp16_{M}x{H}", producer, "hbm", producer_bytes(M, H, 16), "B", HBM_PEAK)]
+
+
 def build_decode_stages():
     """The decode-shaped workloads, timed beside the step and reported apart
     from `value`: the four MXFP4 decode GEMMs and the NVFP4 chain at 1 and 128
@@ -480,6 +509,15 @@ def main():
             run_pass(dstages, True)
         torch.cuda.synchronize()
         decode = report(dstages)
+    # format variants (fp16 producer), also apart from `value`
+    log("[bench] variants")
+    vstages = build_variant_stages()
+    for _ in range(3):
+        run_pass(vstages, False)
+    for _ in range(args.steps):
+        run_pass(vstages, True)
+    torch.cuda.synchronize()
+    variants = report(vstages)
     # dominant kernel: the one with the largest share of the step
     dom = max(stages, key=lambda s: s.mean_s())
     t = dom.mean_s()
@@ -502,7 +540,8 @@ def main():
                                    "mxfp4_prefill_gemm_bias_residual (8192,14336,4096),(8192,4096,14336) + "
                                    "nvfp4_chain_m2048_h5120_n17408",
                        "parallelism": "none (1 GPU)"},
-            "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode}
+            "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode,
+            "variants": variants}
     print(json.dumps(line), flush=True)
 
 

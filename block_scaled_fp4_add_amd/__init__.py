@@ -24,6 +24,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "misaligned pointer", 3: "unsuppor
 # exported symbols (the entry points of include/lowbit.h)
 EXPORTS = (
     "lowbit_status_str", "lowbit_sf_bytes", "lowbit_add_rmsnorm_quant", "lowbit_quantize",
+    "lowbit_add_rmsnorm_quant_fp16", "lowbit_quantize_fp16",
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
     "lowbit_gemm_pick_variant",
@@ -55,6 +56,10 @@ def lib():
         L.lowbit_add_rmsnorm_quant.argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _vp, _vp, _vp]
         L.lowbit_quantize.restype = _int
         L.lowbit_quantize.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]
+        L.lowbit_add_rmsnorm_quant_fp16.restype = _int
+        L.lowbit_add_rmsnorm_quant_fp16.argtypes = L.lowbit_add_rmsnorm_quant.argtypes
+        L.lowbit_quantize_fp16.restype = _int
+        L.lowbit_quantize_fp16.argtypes = L.lowbit_quantize.argtypes
         L.lowbit_dequantize.restype = _int
         L.lowbit_dequantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
         head = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f32]
@@ -113,34 +118,62 @@ def _alloc_q(rows, k, fmt, layout, device, out_packed, out_sf):
     return out_packed, out_sf
 
 
+def _in_dtype(t, name):
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+    return t.dtype
+
+
 def lowbit_add_rmsnorm_quant(input, residual, weight, eps=1e-6, fmt=NVFP4, layout=LINEAR,
                              global_scale=None, out_packed=None, out_sf=None, stream=None):
     """residual += input (in place); y = RMSNorm(residual) * weight; y -> FP4.
+    bf16 tensors call lowbit_add_rmsnorm_quant, fp16 ones
+    lowbit_add_rmsnorm_quant_fp16 (input, residual and weight share the dtype).
     Returns (packed (M, H/2) uint8, scales uint8)."""
-    _need(input, torch.bfloat16, "input")
-    _need(residual, torch.bfloat16, "residual")
-    _need(weight, torch.bfloat16, "weight")
+    dt = _in_dtype(input, "input")
+    _need(input, dt, "input")
+    _need(residual, dt, "residual")
+    _need(weight, dt, "weight")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
     M, H = input.shape
     out_packed, out_sf = _alloc_q(M, H, fmt, layout, input.device, out_packed, out_sf)
-    _check("lowbit_add_rmsnorm_quant", lib().lowbit_add_rmsnorm_quant(
+    name = "lowbit_add_rmsnorm_quant" if dt == torch.bfloat16 else "lowbit_add_rmsnorm_quant_fp16"
+    _check(name, getattr(lib(), name)(
         _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, layout, _ptr(global_scale),
         _ptr(out_packed), _ptr(out_sf), _stream(stream)))
     return out_packed, out_sf
 
 
+def lowbit_add_rmsnorm_quant_fp16(input, residual, weight, eps=1e-6, fmt=NVFP4, layout=LINEAR,
+                                  global_scale=None, out_packed=None, out_sf=None, stream=None):
+    """The fp16 producer by name (lowbit_add_rmsnorm_quant dispatches on dtype)."""
+    _need(input, torch.float16, "input")
+    return lowbit_add_rmsnorm_quant(input, residual, weight, eps, fmt, layout, global_scale, out_packed,
+                                    out_sf, stream)
+
+
 def lowbit_quantize(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=None, out_sf=None,
                     stream=None):
-    _need(x, torch.bfloat16, "x")
+    """x (rows, K) bf16 or fp16 -> (packed (rows, K/2) uint8, scales uint8)."""
+    dt = _in_dtype(x, "x")
+    _need(x, dt, "x")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
     rows, K = x.shape
     out_packed, out_sf = _alloc_q(rows, K, fmt, layout, x.device, out_packed, out_sf)
-    _check("lowbit_quantize", lib().lowbit_quantize(
+    name = "lowbit_quantize" if dt == torch.bfloat16 else "lowbit_quantize_fp16"
+    _check(name, getattr(lib(), name)(
         _ptr(x), rows, K, fmt, layout, _ptr(global_scale), _ptr(out_packed), _ptr(out_sf),
         _stream(stream)))
     return out_packed, out_sf
+
+
+def lowbit_quantize_fp16(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=None, out_sf=None,
+                         stream=None):
+    """The fp16 quantizer by name (lowbit_quantize dispatches on dtype)."""
+    _need(x, torch.float16, "x")
+    return lowbit_quantize(x, fmt, layout, global_scale, out_packed, out_sf, stream)
 
 
 def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):

@@ -128,6 +128,41 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   return from_hip(lowbit::launch_gemm(g, v, stream));
 }
 
+static lowbit_status producer(const void* input, void* residual, const void* weight, int64_t M, int64_t H,
+                              float eps, lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
+                              uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
+  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (M < 0) return LOWBIT_ESHAPE;
+  if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
+  if (H < 64 || H % block_of(fmt) != 0 || H > kMaxRowElems) return LOWBIT_ESHAPE;
+  if (M == 0) return LOWBIT_OK;
+  if (!aligned(input, 16) || !aligned(residual, 16) || !aligned(weight, 16) || !aligned(out_packed, 16))
+    return LOWBIT_EALIGN;
+  if (check_sf_ptr(out_sf, layout) || (global_scale && !aligned(global_scale, 4))) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_add_rmsnorm_quant(
+      static_cast<const uint16_t*>(input), static_cast<uint16_t*>(residual),
+      static_cast<const uint16_t*>(weight), M, H, eps, fmt, layout, global_scale, out_packed, out_sf,
+      in_f16, stream));
+}
+
+static lowbit_status quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt, lowbit_sf_layout layout,
+                              const float* global_scale, uint8_t* out_packed, uint8_t* out_sf, int in_f16,
+                              hipStream_t stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
+  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (rows < 0) return LOWBIT_ESHAPE;
+  if (rows > 0 && (!x || !out_packed || !out_sf)) return LOWBIT_EINVAL;
+  if (K < block_of(fmt) || K % block_of(fmt) != 0 || K > kMaxRowElems) return LOWBIT_ESHAPE;
+  if (rows == 0) return LOWBIT_OK;
+  if (!aligned(x, 16) || !aligned(out_packed, 16)) return LOWBIT_EALIGN;
+  if (check_sf_ptr(out_sf, layout) || (global_scale && !aligned(global_scale, 4))) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_quantize(static_cast<const uint16_t*>(x), rows, K, fmt, layout,
+                                          global_scale, out_packed, out_sf, in_f16, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,36 +188,26 @@ lowbit_status lowbit_add_rmsnorm_quant(const void* input, void* residual, const 
                                        int64_t H, float eps, lowbit_format fmt, lowbit_sf_layout layout,
                                        const float* global_scale, uint8_t* out_packed, uint8_t* out_sf,
                                        hipStream_t stream) {
-  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
-  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
-  if (M < 0) return LOWBIT_ESHAPE;
-  if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
-  if (H < 64 || H % block_of(fmt) != 0 || H > kMaxRowElems) return LOWBIT_ESHAPE;
-  if (M == 0) return LOWBIT_OK;
-  if (!aligned(input, 16) || !aligned(residual, 16) || !aligned(weight, 16) || !aligned(out_packed, 16))
-    return LOWBIT_EALIGN;
-  if (check_sf_ptr(out_sf, layout) || (global_scale && !aligned(global_scale, 4))) return LOWBIT_EALIGN;
-  if (lowbit_status d = device_check()) return d;
-  return from_hip(lowbit::launch_add_rmsnorm_quant(
-      static_cast<const uint16_t*>(input), static_cast<uint16_t*>(residual),
-      static_cast<const uint16_t*>(weight), M, H, eps, fmt, layout, global_scale, out_packed, out_sf,
-      stream));
+  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf, 0, stream);
+}
+
+lowbit_status lowbit_add_rmsnorm_quant_fp16(const void* input, void* residual, const void* weight, int64_t M,
+                                            int64_t H, float eps, lowbit_format fmt, lowbit_sf_layout layout,
+                                            const float* global_scale, uint8_t* out_packed, uint8_t* out_sf,
+                                            hipStream_t stream) {
+  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf, 1, stream);
 }
 
 lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
                               lowbit_sf_layout layout, const float* global_scale, uint8_t* out_packed,
                               uint8_t* out_sf, hipStream_t stream) {
-  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
-  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
-  if (rows < 0) return LOWBIT_ESHAPE;
-  if (rows > 0 && (!x || !out_packed || !out_sf)) return LOWBIT_EINVAL;
-  if (K < block_of(fmt) || K % block_of(fmt) != 0 || K > kMaxRowElems) return LOWBIT_ESHAPE;
-  if (rows == 0) return LOWBIT_OK;
-  if (!aligned(x, 16) || !aligned(out_packed, 16)) return LOWBIT_EALIGN;
-  if (check_sf_ptr(out_sf, layout) || (global_scale && !aligned(global_scale, 4))) return LOWBIT_EALIGN;
-  if (lowbit_status d = device_check()) return d;
-  return from_hip(lowbit::launch_quantize(static_cast<const uint16_t*>(x), rows, K, fmt, layout,
-                                          global_scale, out_packed, out_sf, stream));
+  return quantize(x, rows, K, fmt, layout, global_scale, out_packed, out_sf, 0, stream);
+}
+
+lowbit_status lowbit_quantize_fp16(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
+                                   lowbit_sf_layout layout, const float* global_scale, uint8_t* out_packed,
+                                   uint8_t* out_sf, hipStream_t stream) {
+  return quantize(x, rows, K, fmt, layout, global_scale, out_packed, out_sf, 1, stream);
 }
 
 lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,

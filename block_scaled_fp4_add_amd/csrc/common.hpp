@@ -43,6 +43,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// IEEE binary16 (fp16), the producer's other input format: widening is exact
+// (v_cvt_f32_f16); narrowing rounds to nearest-even (v_cvt_pk_f16_f32).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+// The two 16-bit halves of a word of the input format (F16: fp16, else bf16).
+template <bool F16> __device__ __forceinline__ float in_lo(uint32_t w) { return F16 ? f16_lo(w) : bf16_lo(w); }
+template <bool F16> __device__ __forceinline__ float in_hi(uint32_t w) { return F16 ? f16_hi(w) : bf16_hi(w); }
+template <bool F16> __device__ __forceinline__ uint32_t pack_in2(float lo, float hi) {
+  return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
 // ---------------------------------------------------------------------------
 // FP4 E2M1: two fp32 -> one byte (first value in the low nibble).  The gfx950
 // conversion rounds to nearest-even, saturates at +-6 and keeps the sign of a

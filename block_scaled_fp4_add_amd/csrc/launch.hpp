@@ -7,12 +7,13 @@
 
 namespace lowbit {
 
+// in_f16: the 16-bit input tensors (x, residual, weight) are fp16, else bf16
 hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w, int64_t M,
                                     int64_t H, float eps, int fmt, int layout, const float* gs,
-                                    uint8_t* out_packed, uint8_t* out_sf, hipStream_t s);
+                                    uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s);
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
-                           const float* gs, uint8_t* out_packed, uint8_t* out_sf, hipStream_t s);
+                           const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s);
 
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
                              int layout, const float* gs, uint16_t* out, hipStream_t s);

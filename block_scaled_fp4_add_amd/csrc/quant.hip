@@ -74,8 +74,9 @@ __device__ __forceinline__ void quant_store_block(const float* y, float gs, int6
   a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = (uint8_t)sb;
 }
 
-// FUSED: add + RMSNorm + quant.  Otherwise: quantize x as it is.
-template <int FMT, int NBL, int WPR, bool FUSED>
+// FUSED: add + RMSNorm + quant.  Otherwise: quantize x as it is.  F16: the
+// 16-bit tensors (x, residual, weight) are fp16, else bf16.
+template <int FMT, int NBL, int WPR, bool FUSED, bool F16>
 __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
   constexpr int B = FmtTraits<FMT>::B;
   constexpr int VECS = BlockVec<B>::kVecs;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
   const int64_t kb_end = (kb0 + per_wave < nblk) ? kb0 + per_wave : nblk;
   const bool live = row < a.M;
 
-  // bf16 h (or x) of the lane's blocks, two values per word
+  // h (or x) of the lane's blocks in the input format, two values per word
   uint32_t hb[NBL][B / 2];
   double ss = 0.0;
 
@@ -117,11 +118,11 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
             const uint32_t* rw = reinterpret_cast<const uint32_t*>(&rv[v]);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-              float h0 = __fadd_rn(bf16_lo(xw[j]), bf16_lo(rw[j]));
-              float h1 = __fadd_rn(bf16_hi(xw[j]), bf16_hi(rw[j]));
+              float h0 = __fadd_rn(in_lo<F16>(xw[j]), in_lo<F16>(rw[j]));
+              float h1 = __fadd_rn(in_hi<F16>(xw[j]), in_hi<F16>(rw[j]));
               ss = __fma_rn((double)h0, (double)h0, ss);
               ss = __fma_rn((double)h1, (double)h1, ss);
-              hb[i][v * 4 + j] = pack_bf16x2(h0, h1);
+              hb[i][v * 4 + j] = pack_in2<F16>(h0, h1);
             }
           }
           // residual <- bf16(h), same positions
@@ -174,15 +175,15 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; j++) {
               const uint32_t h2 = hb[i][v * 4 + j];
-              y[v * 8 + 2 * j] = __fmul_rn(__fmul_rn(bf16_lo(h2), rstd), bf16_lo(ww[j]));
-              y[v * 8 + 2 * j + 1] = __fmul_rn(__fmul_rn(bf16_hi(h2), rstd), bf16_hi(ww[j]));
+              y[v * 8 + 2 * j] = __fmul_rn(__fmul_rn(in_lo<F16>(h2), rstd), in_lo<F16>(ww[j]));
+              y[v * 8 + 2 * j + 1] = __fmul_rn(__fmul_rn(in_hi<F16>(h2), rstd), in_hi<F16>(ww[j]));
             }
           }
         } else {
 #pragma unroll
           for (int j = 0; j < B / 2; j++) {
-            y[2 * j] = bf16_lo(hb[i][j]);
-            y[2 * j + 1] = bf16_hi(hb[i][j]);
+            y[2 * j] = in_lo<F16>(hb[i][j]);
+            y[2 * j + 1] = in_hi<F16>(hb[i][j]);
           }
         }
         quant_store_block<FMT>(y, gs, row, kb, nblk, a);
@@ -224,7 +225,7 @@ constexpr int kWgMinRows = 256;     // fewer rows: the row-split form has more p
 constexpr int kWgMaxWaves = 16;     // H <= 16384
 constexpr int kWgVecs = 2;          // 16-byte vectors per thread and tensor
 
-template <int FMT, int NW, bool FUSED>
+template <int FMT, int NW, bool FUSED, bool F16>
 __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   constexpr int B = FmtTraits<FMT>::B;
   constexpr int LPB = B / 8;   // lanes per block
@@ -269,13 +270,13 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
       u32x4 hw;
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        const float h0 = __fadd_rn(bf16_lo(xv[j][k]), bf16_lo(rv[j][k]));
-        const float h1 = __fadd_rn(bf16_hi(xv[j][k]), bf16_hi(rv[j][k]));
+        const float h0 = __fadd_rn(in_lo<F16>(xv[j][k]), in_lo<F16>(rv[j][k]));
+        const float h1 = __fadd_rn(in_hi<F16>(xv[j][k]), in_hi<F16>(rv[j][k]));
         ss = __fma_rn((double)h0, (double)h0, ss);
         ss = __fma_rn((double)h1, (double)h1, ss);
-        hw[k] = pack_bf16x2(h0, h1);
+        hw[k] = pack_in2<F16>(h0, h1);
       }
-      xv[j] = hw;   // the row's bf16 h, kept for the second pass
+      xv[j] = hw;   // the row's h in the input format, kept for the second pass
       if (j * T + t < nvec) __builtin_nontemporal_store(hw, rr + j * T + t);
     }
     ss = wave_sum_f64(ss);
@@ -299,11 +300,11 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       if constexpr (FUSED) {
-        y[2 * k] = __fmul_rn(__fmul_rn(bf16_lo(xv[j][k]), rstd), bf16_lo(wv[j][k]));
-        y[2 * k + 1] = __fmul_rn(__fmul_rn(bf16_hi(xv[j][k]), rstd), bf16_hi(wv[j][k]));
+        y[2 * k] = __fmul_rn(__fmul_rn(in_lo<F16>(xv[j][k]), rstd), in_lo<F16>(wv[j][k]));
+        y[2 * k + 1] = __fmul_rn(__fmul_rn(in_hi<F16>(xv[j][k]), rstd), in_hi<F16>(wv[j][k]));
       } else {
-        y[2 * k] = bf16_lo(xv[j][k]);
-        y[2 * k + 1] = bf16_hi(xv[j][k]);
+        y[2 * k] = in_lo<F16>(xv[j][k]);
+        y[2 * k + 1] = in_hi<F16>(xv[j][k]);
       }
     }
     float amax = 0.0f;
@@ -331,19 +332,19 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   if (a.layout == kTiled && t < nblk_pad - nblk) a.out_sf[sf_offset(FMT, kTiled, row, nblk + t, nblk)] = 0;
 }
 
-template <int FMT, int NW, bool FUSED>
+template <int FMT, int NW, bool FUSED, bool F16>
 hipError_t launch_wg(const RowArgs& a, hipStream_t s) {
   if (a.rows_grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((row_wg_kernel<FMT, NW, FUSED>), dim3((unsigned)a.rows_grid), dim3(NW * kWave), 0, s, a);
+  hipLaunchKernelGGL((row_wg_kernel<FMT, NW, FUSED, F16>), dim3((unsigned)a.rows_grid), dim3(NW * kWave), 0, s, a);
   return hipGetLastError();
 }
 
-template <int FMT, int NBL, int WPR, bool FUSED>
+template <int FMT, int NBL, int WPR, bool FUSED, bool F16>
 hipError_t launch_row(const RowArgs& a, hipStream_t s) {
   constexpr int ROWS_PER_WG = (kThreads / kWave) / WPR;
   int64_t grid = (a.rows_grid + ROWS_PER_WG - 1) / ROWS_PER_WG;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((row_quant_kernel<FMT, NBL, WPR, FUSED>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((row_quant_kernel<FMT, NBL, WPR, FUSED, F16>), dim3((unsigned)grid), dim3(kThreads), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -351,29 +352,29 @@ hipError_t launch_row(const RowArgs& a, hipStream_t s) {
 // Many rows of at most 16384 elements: a workgroup per row.  Otherwise pick
 // (WPR, NBL) of the row-split form for a row of nblk blocks: one wave per row
 // when there are many rows, a row spread over up to 4 waves when there are few.
-template <int FMT, bool FUSED>
+template <int FMT, bool FUSED, bool F16>
 hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
   constexpr int MAXNBL = (FMT == kNVFP4) ? 8 : 4;
   const int64_t nblk = a.H / FmtTraits<FMT>::B;
   const int64_t nw = (a.H + kWgVecs * 8 * kWave - 1) / (kWgVecs * 8 * kWave);
   if (a.M >= kWgMinRows && nw <= kWgMaxWaves && a.rows_grid <= 0x7FFFFFFF) {
     switch (nw) {
-      case 1: return launch_wg<FMT, 1, FUSED>(a, s);
-      case 2: return launch_wg<FMT, 2, FUSED>(a, s);
-      case 3: return launch_wg<FMT, 3, FUSED>(a, s);
-      case 4: return launch_wg<FMT, 4, FUSED>(a, s);
-      case 5: return launch_wg<FMT, 5, FUSED>(a, s);
-      case 6: return launch_wg<FMT, 6, FUSED>(a, s);
-      case 7: return launch_wg<FMT, 7, FUSED>(a, s);
-      case 8: return launch_wg<FMT, 8, FUSED>(a, s);
-      case 9: return launch_wg<FMT, 9, FUSED>(a, s);
-      case 10: return launch_wg<FMT, 10, FUSED>(a, s);
-      case 11: return launch_wg<FMT, 11, FUSED>(a, s);
-      case 12: return launch_wg<FMT, 12, FUSED>(a, s);
-      case 13: return launch_wg<FMT, 13, FUSED>(a, s);
-      case 14: return launch_wg<FMT, 14, FUSED>(a, s);
-      case 15: return launch_wg<FMT, 15, FUSED>(a, s);
-      default: return launch_wg<FMT, 16, FUSED>(a, s);
+      case 1: return launch_wg<FMT, 1, FUSED, F16>(a, s);
+      case 2: return launch_wg<FMT, 2, FUSED, F16>(a, s);
+      case 3: return launch_wg<FMT, 3, FUSED, F16>(a, s);
+      case 4: return launch_wg<FMT, 4, FUSED, F16>(a, s);
+      case 5: return launch_wg<FMT, 5, FUSED, F16>(a, s);
+      case 6: return launch_wg<FMT, 6, FUSED, F16>(a, s);
+      case 7: return launch_wg<FMT, 7, FUSED, F16>(a, s);
+      case 8: return launch_wg<FMT, 8, FUSED, F16>(a, s);
+      case 9: return launch_wg<FMT, 9, FUSED, F16>(a, s);
+      case 10: return launch_wg<FMT, 10, FUSED, F16>(a, s);
+      case 11: return launch_wg<FMT, 11, FUSED, F16>(a, s);
+      case 12: return launch_wg<FMT, 12, FUSED, F16>(a, s);
+      case 13: return launch_wg<FMT, 13, FUSED, F16>(a, s);
+      case 14: return launch_wg<FMT, 14, FUSED, F16>(a, s);
+      case 15: return launch_wg<FMT, 15, FUSED, F16>(a, s);
+      default: return launch_wg<FMT, 16, FUSED, F16>(a, s);
     }
   }
   int wpr = (a.M >= 1024) ? 1 : 4;
@@ -382,7 +383,7 @@ hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
   int64_t nbl = (nblk + 64 * wpr - 1) / (64 * wpr);
   if (nbl > MAXNBL) return hipErrorInvalidValue;
 #define LB_CASE(W, N)                                                            \
-  if (wpr == W && nbl == N) return launch_row<FMT, N, W, FUSED>(a, s);
+  if (wpr == W && nbl == N) return launch_row<FMT, N, W, FUSED, F16>(a, s);
 #define LB_ALL(W) LB_CASE(W, 1) LB_CASE(W, 2) LB_CASE(W, 3) LB_CASE(W, 4)
   LB_ALL(1) LB_ALL(2) LB_ALL(4)
   if constexpr (MAXNBL == 8) {
@@ -434,17 +435,19 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
 
 hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w, int64_t M,
                                     int64_t H, float eps, int fmt, int layout, const float* gs,
-                                    uint8_t* out_packed, uint8_t* out_sf, hipStream_t s) {
+                                    uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
   RowArgs a{x, residual, w, M, H, M, eps, layout, gs, out_packed, out_sf};
   if (layout == kTiled) a.rows_grid = (M + 31) / 32 * 32;
-  return fmt == kNVFP4 ? dispatch_row<kNVFP4, true>(a, s) : dispatch_row<kMXFP4, true>(a, s);
+  if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, true>(a, s) : dispatch_row<kMXFP4, true, true>(a, s);
+  return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, false>(a, s) : dispatch_row<kMXFP4, true, false>(a, s);
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
-                           const float* gs, uint8_t* out_packed, uint8_t* out_sf, hipStream_t s) {
+                           const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
   RowArgs a{x, nullptr, nullptr, rows, K, rows, 0.0f, layout, gs, out_packed, out_sf};
   if (layout == kTiled) a.rows_grid = (rows + 31) / 32 * 32;
-  return fmt == kNVFP4 ? dispatch_row<kNVFP4, false>(a, s) : dispatch_row<kMXFP4, false>(a, s);
+  if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, true>(a, s) : dispatch_row<kMXFP4, false, true>(a, s);
+  return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, false>(a, s) : dispatch_row<kMXFP4, false, false>(a, s);
 }
 
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,

@@ -39,25 +39,28 @@ def outlier_columns(ncols: int, seed: int, index: int = 99) -> torch.Tensor:
 
 
 def normal_bf16(shape, seed: int, index: int, std: float = 1.0, mean: float = 0.0,
-                outliers: bool = False, outlier_scale: float = 20.0) -> torch.Tensor:
-    """bf16 CPU tensor of mean + std * N(0, 1), optional outlier columns."""
+                outliers: bool = False, outlier_scale: float = 20.0,
+                dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """bf16 (or `dtype`) CPU tensor of mean + std * N(0, 1), optional outlier columns."""
     t = torch.randn(*shape, generator=_gen(seed, index), dtype=torch.float32) * std + mean
     if outliers:
         cols = outlier_columns(shape[-1], seed, 100 + index)
         t[..., cols] *= outlier_scale
-    return t.to(torch.bfloat16)
+    return t.to(dtype)
 
 
-def producer_inputs(M: int, H: int, seed: int, outliers: bool = False):
-    """(input, residual, rmsnorm weight) as bf16 CPU tensors."""
-    x = normal_bf16((M, H), seed, 0, outliers=outliers)
-    r = normal_bf16((M, H), seed, 1)
-    w = normal_bf16((H,), seed, 2, std=0.1, mean=1.0)
+def producer_inputs(M: int, H: int, seed: int, outliers: bool = False, dtype: torch.dtype = torch.bfloat16):
+    """(input, residual, rmsnorm weight) as bf16 (or fp16) CPU tensors: the same
+    fp32 draws either way, rounded to the requested 16-bit format."""
+    x = normal_bf16((M, H), seed, 0, outliers=outliers, dtype=dtype)
+    r = normal_bf16((M, H), seed, 1, dtype=dtype)
+    w = normal_bf16((H,), seed, 2, std=0.1, mean=1.0, dtype=dtype)
     return x, r, w
 
 
-def activation(M: int, K: int, seed: int, index: int = 3, outliers: bool = False) -> torch.Tensor:
-    return normal_bf16((M, K), seed, index, outliers=outliers)
+def activation(M: int, K: int, seed: int, index: int = 3, outliers: bool = False,
+               dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    return normal_bf16((M, K), seed, index, outliers=outliers, dtype=dtype)
 
 
 def weight(N: int, K: int, seed: int, index: int = 4) -> torch.Tensor:
@@ -73,7 +76,7 @@ def residual(M: int, N: int, seed: int, index: int = 6) -> torch.Tensor:
 
 
 def bits(t: torch.Tensor):
-    """uint16 numpy view of a bf16 tensor's bit patterns (host)."""
+    """uint16 numpy view of a bf16 (or fp16) tensor's bit patterns (host)."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")
 
 

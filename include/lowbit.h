@@ -104,12 +104,28 @@ lowbit_status lowbit_add_rmsnorm_quant(const void* input, void* residual, const 
                                        lowbit_sf_layout layout, const float* global_scale,
                                        uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
 
+/* The same with fp16 input, residual and weight ([FI] add_rmsnorm_fp4quant
+ * accepts float16 as well as bfloat16 tensors): every bf16 above reads fp16,
+ * and the residual write-back rounds h to fp16 (nearest-even; |h| >= 65520
+ * becomes an infinity, as an IEEE conversion does).  Same checks, layouts and
+ * outputs. */
+lowbit_status lowbit_add_rmsnorm_quant_fp16(const void* input, void* residual, const void* weight,
+                                            int64_t M, int64_t H, float eps, lowbit_format fmt,
+                                            lowbit_sf_layout layout, const float* global_scale,
+                                            uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
+
 /* Quantize a bf16 (rows, K) tensor: the per-block rule above with y = x
  * ([FRT] quantize_fp4_sfa_bf16; used for activations and prepacked weights).
  * Requires K % B == 0, rows >= 0. */
 lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
                               lowbit_sf_layout layout, const float* global_scale,
                               uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
+
+/* Quantize an fp16 (rows, K) tensor: y = f32(x) (exact), then the same rule
+ * ([FRT] quantize_fp4_sfa_fp16).  Same checks and outputs as lowbit_quantize. */
+lowbit_status lowbit_quantize_fp16(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
+                                   lowbit_sf_layout layout, const float* global_scale,
+                                   uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
 
 /* Dequantize to bf16: x = bf16(fl32(E2M1 * scale / gs)) (NVFP4, gs from
  * global_scale or 1.0) or bf16(E2M1 * 2^(b-127)) (MXFP4; global_scale NULL)

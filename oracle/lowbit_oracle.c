@@ -63,6 +63,52 @@ uint16_t orc_f32_to_bf16(float f) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* fp16 (IEEE binary16) <-> fp32                                              */
+/* ------------------------------------------------------------------------- */
+
+/* binary16: a sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent
+ * field 0 holds the subnormals f * 2^-24, field 31 infinities and NaNs.
+ * Widening is exact. */
+float orc_f16_to_f32(uint16_t b) {
+    int sgn = b >> 15, e = (b >> 10) & 31, f = b & 1023;
+    double v;
+    if (e == 31) v = f ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)f, -24);
+    else v = ldexp((double)(1024 + f), e - 25);   /* (1 + f/1024) * 2^(e-15) */
+    return (float)(sgn ? -v : v);
+}
+
+/* Round a binary32 to binary16, nearest-even: count the value in steps of the
+ * binary16 grid of its binade (2^(E-10) for a normal value in [2^E, 2^(E+1)),
+ * 2^-24 below 2^-14) and round the count to the nearest integer, ties to even
+ * (rint in the default rounding mode).  A count that reaches the next binade
+ * carries into the exponent.  Magnitudes from 65520, the midpoint between the
+ * largest finite value 65504 and 2^16, become infinity. */
+uint16_t orc_f32_to_f16(float f) {
+    uint16_t sign = (f32_bits(f) >> 31) ? 0x8000u : 0u;
+    if (isnan(f)) return (uint16_t)(sign | 0x7E00u);
+    double a = fabs((double)f);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    int e2;
+    frexp(a, &e2);               /* a = m * 2^e2, m in [0.5, 1) */
+    int E = e2 - 1;              /* floor(log2 a) */
+    if (a == 0.0 || E < -14) {
+        double q = rint(a * 0x1p24);   /* exact scaling; q <= 1024 (1024 = 2^-14) */
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    double q = rint(ldexp(a, 10 - E));  /* in [1024, 2048] */
+    if (q == 2048.0) { q = 1024.0; E += 1; }
+    return (uint16_t)(sign | (uint16_t)(((E + 15) << 10) | ((int)q - 1024)));
+}
+
+/* The 16-bit input formats of the producer and the quantizer. */
+enum { ORC_IN_BF16 = 0, ORC_IN_F16 = 1 };
+typedef float (*orc_widen_fn)(uint16_t);
+typedef uint16_t (*orc_narrow_fn)(float);
+static orc_widen_fn widen_of(int dtype) { return dtype == ORC_IN_F16 ? orc_f16_to_f32 : orc_bf16_to_f32; }
+static orc_narrow_fn narrow_of(int dtype) { return dtype == ORC_IN_F16 ? orc_f32_to_f16 : orc_f32_to_bf16; }
+
+/* ------------------------------------------------------------------------- */
 /* FP4 E2M1                                                                   */
 /* ------------------------------------------------------------------------- */
 
@@ -293,7 +339,8 @@ static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
 /* Fused producer (FlashInfer page, AddRMSNormFP4QuantKernel)                  */
 /* ------------------------------------------------------------------------- */
 /*
- * For each row m (H elements; x, r, w are bf16 bit patterns):
+ * For each row m (H elements; x, r, w are bf16 bit patterns, or fp16 with dtype
+ * ORC_IN_F16, where every bf16 conversion below is the fp16 one):
  *  1. h_i = fl32(x_i + r_i); residual_i <- bf16(h_i)     (Phase 2, in place)
  *  2. S = sum_i h_i^2 over the fp32 h (the page squares the unrounded h),
  *     accumulated in binary64 (each h_i^2 is exact there);
@@ -306,12 +353,15 @@ static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
  * Optional diagnostics (NULL to skip): y (M*H fp32), v (M*H fp32),
  * amax and s_pre (M*H/B fp32 each), rstd (M fp32).
  */
-int orc_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w,
-                          int64_t M, int64_t H, float eps, int fmt, int layout, float gs,
-                          uint8_t* out_packed, uint8_t* out_sf,
-                          float* diag_y, float* diag_v, float* diag_amax, float* diag_spre,
-                          float* diag_rstd) {
+int orc_add_rmsnorm_quant_dt(const uint16_t* x, uint16_t* residual, const uint16_t* w,
+                             int64_t M, int64_t H, float eps, int fmt, int layout, float gs,
+                             uint8_t* out_packed, uint8_t* out_sf,
+                             float* diag_y, float* diag_v, float* diag_amax, float* diag_spre,
+                             float* diag_rstd, int dtype) {
     if (check_common(M, H, fmt, layout)) return 1;
+    if (dtype != ORC_IN_BF16 && dtype != ORC_IN_F16) return 1;
+    const orc_widen_fn wid = widen_of(dtype);
+    const orc_narrow_fn nar = narrow_of(dtype);
     int64_t B = block_of(fmt), nblk = H / B;
     memset(out_sf, 0, (size_t)orc_sf_bytes(M, H, fmt, layout)); /* padding is zero */
     int err = 0;
@@ -330,7 +380,7 @@ int orc_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t*
                 uint16_t* rr = residual + m * H;
                 /* step 1 */
                 for (int64_t i = 0; i < H; i++) {
-                    volatile float s = orc_bf16_to_f32(xr[i]) + orc_bf16_to_f32(rr[i]);
+                    volatile float s = wid(xr[i]) + wid(rr[i]);
                     h[i] = s;
                 }
                 /* step 2 */
@@ -339,12 +389,12 @@ int orc_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t*
                 double denom = sqrt(S / (double)H + (double)eps);
                 float rstd = (float)(1.0 / denom);
                 if (diag_rstd) diag_rstd[m] = rstd;
-                /* residual write-back, then step 3 from the bf16 copy */
+                /* residual write-back, then step 3 from the rounded copy */
                 for (int64_t i = 0; i < H; i++) {
-                    uint16_t hb = orc_f32_to_bf16(h[i]);
+                    uint16_t hb = nar(h[i]);
                     rr[i] = hb;
-                    volatile float t = orc_bf16_to_f32(hb) * rstd;
-                    volatile float yi = t * orc_bf16_to_f32(w[i]);
+                    volatile float t = wid(hb) * rstd;
+                    volatile float yi = t * wid(w[i]);
                     y[i] = yi;
                 }
                 if (diag_y) memcpy(diag_y + m * H, y, sizeof(float) * H);
@@ -360,14 +410,27 @@ int orc_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t*
     return err;
 }
 
+/* bf16 tensors (the page's default dtype). */
+int orc_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w,
+                          int64_t M, int64_t H, float eps, int fmt, int layout, float gs,
+                          uint8_t* out_packed, uint8_t* out_sf,
+                          float* diag_y, float* diag_v, float* diag_amax, float* diag_spre,
+                          float* diag_rstd) {
+    return orc_add_rmsnorm_quant_dt(x, residual, w, M, H, eps, fmt, layout, gs, out_packed, out_sf,
+                                    diag_y, diag_v, diag_amax, diag_spre, diag_rstd, ORC_IN_BF16);
+}
+
 /* ------------------------------------------------------------------------- */
 /* Quantize (FlashRT README: quantize_fp4_sfa_bf16)                            */
 /* ------------------------------------------------------------------------- */
-/* y_i = f32(x_i) (exact), then the per-block rule above.  This makes every
- * GEMM operand: activations and the prepacked weights alike. */
-int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout, float gs,
-                 uint8_t* out_packed, uint8_t* out_sf, float* diag_spre) {
+/* y_i = f32(x_i) (exact; x is bf16, or fp16 with dtype ORC_IN_F16 as in the
+ * README's quantize_fp4_sfa_fp16), then the per-block rule above.  This makes
+ * every GEMM operand: activations and the prepacked weights alike. */
+int orc_quantize_dt(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout, float gs,
+                    uint8_t* out_packed, uint8_t* out_sf, float* diag_spre, int dtype) {
     if (check_common(rows, K, fmt, layout)) return 1;
+    if (dtype != ORC_IN_BF16 && dtype != ORC_IN_F16) return 1;
+    const orc_widen_fn wid = widen_of(dtype);
     int64_t nblk = K / block_of(fmt);
     memset(out_sf, 0, (size_t)orc_sf_bytes(rows, K, fmt, layout));
     int err = 0;
@@ -381,7 +444,7 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout
         } else {
 #pragma omp for schedule(static)
             for (int64_t m = 0; m < rows; m++) {
-                for (int64_t i = 0; i < K; i++) y[i] = orc_bf16_to_f32(x[m * K + i]);
+                for (int64_t i = 0; i < K; i++) y[i] = wid(x[m * K + i]);
                 quant_row(y, m, K, fmt, gs, layout, out_packed + m * (K / 2), out_sf, codes, NULL,
                           diag_spre ? diag_spre + m * nblk : NULL, NULL);
             }
@@ -389,6 +452,11 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout
         free(y); free(codes);
     }
     return err;
+}
+
+int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout, float gs,
+                 uint8_t* out_packed, uint8_t* out_sf, float* diag_spre) {
+    return orc_quantize_dt(x, rows, K, fmt, layout, gs, out_packed, out_sf, diag_spre, ORC_IN_BF16);
 }
 
 /* ------------------------------------------------------------------------- */

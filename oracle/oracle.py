@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  Imported by tests/, by the smoke check and by the
 benchmark's CPU-baseline leg; never by the product package.  All arrays are
-numpy host arrays; bf16 tensors travel as their uint16 bit patterns.
+numpy host arrays; bf16 and fp16 tensors travel as their uint16 bit patterns
+(dtype BF16 = 0 or F16 = 1 says which).
 
 Enum values: fmt NVFP4 = 0 (16-blocks, E4M3 scales), MXFP4 = 1 (32-blocks,
 UE8M0 scales); layout LINEAR = 0, TILED = 1; epilogue NONE = 0, BIAS = 1,
@@ -18,6 +19,7 @@ from . import build as _build
 NVFP4, MXFP4 = 0, 1
 LINEAR, TILED = 0, 1
 EPI_NONE, EPI_BIAS, EPI_RESIDUAL, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3, 4
+BF16, F16 = 0, 1
 
 _lib = None
 
@@ -65,6 +67,15 @@ def lib():
     L.orc_encode_with_scale.restype = None
     L.orc_encode_with_scale.argtypes = [_f32p, _int, _int, ctypes.c_float, ctypes.c_uint8, _u8p, _vp]
     L.orc_add_rmsnorm_quant.restype = _int
+    L.orc_f16_to_f32.restype = ctypes.c_float
+    L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    L.orc_f32_to_f16.restype = ctypes.c_uint16
+    L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    L.orc_add_rmsnorm_quant_dt.restype = _int
+    L.orc_add_rmsnorm_quant_dt.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, ctypes.c_float, _int, _int,
+                                           ctypes.c_float, _u8p, _u8p, _vp, _vp, _vp, _vp, _vp, _int]
+    L.orc_quantize_dt.restype = _int
+    L.orc_quantize_dt.argtypes = [_u16p, _i64, _i64, _int, _int, ctypes.c_float, _u8p, _u8p, _vp, _int]
     L.orc_add_rmsnorm_quant.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, ctypes.c_float, _int, _int,
                                         ctypes.c_float, _u8p, _u8p, _vp, _vp, _vp, _vp, _vp]
     L.orc_quantize.restype = _int
@@ -125,6 +136,14 @@ def bf16_to_f32(b: int) -> float:
     return lib().orc_bf16_to_f32(b)
 
 
+def f32_to_f16(v: float) -> int:
+    return lib().orc_f32_to_f16(v)
+
+
+def f16_to_f32(b: int) -> float:
+    return lib().orc_f16_to_f32(b)
+
+
 def sf_bytes(rows: int, k: int, fmt: int, layout: int) -> int:
     return lib().orc_sf_bytes(rows, k, fmt, layout)
 
@@ -144,8 +163,9 @@ def encode_with_scale(y, fmt: int, gs: float, sbyte: int, with_v: bool = False):
 
 # --- tensor entry points --------------------------------------------------------------------
 
-def add_rmsnorm_quant(x, residual, weight, eps, fmt, layout, gs=1.0, diag=False):
-    """Fused producer.  x, residual: uint16 (M, H) bf16 bits; weight uint16 (H,).
+def add_rmsnorm_quant(x, residual, weight, eps, fmt, layout, gs=1.0, diag=False, dtype=BF16):
+    """Fused producer.  x, residual: uint16 (M, H) bf16 bits (fp16 bits with
+    dtype F16); weight uint16 (H,).
     Returns a dict with the updated residual, packed codes, scales and, when
     diag is set, y / v / amax / s_pre / rstd."""
     x = _c(x, np.uint16)
@@ -160,10 +180,10 @@ def add_rmsnorm_quant(x, residual, weight, eps, fmt, layout, gs=1.0, diag=False)
         d = dict(y=np.zeros((M, H), np.float32), v=np.zeros((M, H), np.float32),
                  amax=np.zeros((M, H // B), np.float32), spre=np.zeros((M, H // B), np.float32),
                  rstd=np.zeros(M, np.float32))
-    rc = lib().orc_add_rmsnorm_quant(
+    rc = lib().orc_add_rmsnorm_quant_dt(
         x, res, w, M, H, eps, fmt, layout, gs, packed, sf,
         _ptr(d.get("y")), _ptr(d.get("v")), _ptr(d.get("amax")), _ptr(d.get("spre")),
-        _ptr(d.get("rstd")))
+        _ptr(d.get("rstd")), dtype)
     if rc:
         raise ValueError(f"oracle add_rmsnorm_quant rejected its arguments (rc={rc})")
     out = dict(residual=res, packed=packed, sf=sf)
@@ -171,13 +191,14 @@ def add_rmsnorm_quant(x, residual, weight, eps, fmt, layout, gs=1.0, diag=False)
     return out
 
 
-def quantize(x, fmt, layout, gs=1.0, diag=False):
+def quantize(x, fmt, layout, gs=1.0, diag=False, dtype=BF16):
+    """Quantizer.  x: uint16 (rows, K) bf16 bits (fp16 bits with dtype F16)."""
     x = _c(x, np.uint16)
     rows, K = x.shape
     packed = np.zeros((rows, K // 2), dtype=np.uint8)
     sf = np.zeros(sf_bytes(rows, K, fmt, layout), dtype=np.uint8)
     spre = np.zeros((rows, K // block_size(fmt)), np.float32) if diag else None
-    rc = lib().orc_quantize(x, rows, K, fmt, layout, gs, packed, sf, _ptr(spre))
+    rc = lib().orc_quantize_dt(x, rows, K, fmt, layout, gs, packed, sf, _ptr(spre), dtype)
     if rc:
         raise ValueError(f"oracle quantize rejected its arguments (rc={rc})")
     return (packed, sf, spre) if diag else (packed, sf)

@@ -19,19 +19,23 @@ EPS = 1e-6
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _gs_for(orc, x, r, w, M, H):
+def _odt(orc, dtype):
+    return orc.F16 if dtype == torch.float16 else orc.BF16
+
+
+def _gs_for(orc, x, r, w, M, H, dtype=torch.bfloat16):
     """NVFP4 global scale 6*448/amax(y), amax from the oracle's own y."""
     d = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4, orc.LINEAR,
-                              diag=True)
+                              diag=True, dtype=_odt(orc, dtype))
     return float(np.float32(2688.0 / np.abs(d["y"]).max()))
 
 
-def run_producer(orc, M, H, fmt, layout, seed, outliers=False, use_gs=False):
-    banner(f"producer M={M} H={H} fmt={fmt} layout={layout} seed={seed} gs={use_gs}")
-    x, r, w = synth.producer_inputs(M, H, seed, outliers=outliers)
-    gs = _gs_for(orc, x, r, w, M, H) if (use_gs and fmt == orc.NVFP4) else 1.0
+def run_producer(orc, M, H, fmt, layout, seed, outliers=False, use_gs=False, dtype=torch.bfloat16):
+    banner(f"producer M={M} H={H} fmt={fmt} layout={layout} seed={seed} gs={use_gs} dtype={dtype}")
+    x, r, w = synth.producer_inputs(M, H, seed, outliers=outliers, dtype=dtype)
+    gs = _gs_for(orc, x, r, w, M, H, dtype) if (use_gs and fmt == orc.NVFP4) else 1.0
     ref = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, fmt, layout,
-                                gs=gs, diag=True)
+                                gs=gs, diag=True, dtype=_odt(orc, dtype))
     xd, rd, wd = dev_bf16(x), dev_bf16(r), dev_bf16(w)
     sf_n = lb.lowbit_sf_bytes(M, H, fmt, layout)
     packed = torch.full((M, H // 2), 0xAA, dtype=torch.uint8, device="cuda")
@@ -40,7 +44,7 @@ def run_producer(orc, M, H, fmt, layout, seed, outliers=False, use_gs=False):
                                 global_scale=dev_f32(gs) if (use_gs and fmt == lb.NVFP4) else None,
                                 out_packed=packed, out_sf=sf)
     torch.cuda.synchronize()
-    assert np.array_equal(host_bits(rd), ref["residual"]), "residual must be bf16(x + r) bit-exact"
+    assert np.array_equal(host_bits(rd), ref["residual"]), "residual must be the rounded x + r bit-exact"
     spre = ref["spre"] if fmt == orc.NVFP4 else ref["amax"]
     rep = checkers.compare_quantized(orc, fmt, gs, host_u8(packed), host_u8(sf), ref["packed"], ref["sf"],
                                      ref["y"], ref["v"], spre, M, H, layout)
@@ -75,6 +79,19 @@ MANY_ROWS = [(256, 64), (300, 1536), (257, 2560), (2100, 3584), (520, 5632), (42
 @pytest.mark.parametrize("layout", [0, 1])
 def test_producer_many_rows(orc, M, H, fmt, layout):
     run_producer(orc, M, H, fmt, layout, seed=M + 3 * H, outliers=True, use_gs=(fmt == 0))
+
+
+# fp16 tensors (lowbit_add_rmsnorm_quant_fp16): both kernel forms, both
+# formats and layouts, ragged rows of the workgroup form included
+FP16_SHAPES = [(8, 256), (1, 5120), (33, 1024), (300, 1536), (2049, 512), (520, 5632), (4500, 4096)]
+
+
+@pytest.mark.parametrize("M,H", FP16_SHAPES)
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_producer_fp16(orc, M, H, fmt, layout):
+    run_producer(orc, M, H, fmt, layout, seed=M + 5 * H, outliers=True, use_gs=(fmt == 0),
+                 dtype=torch.float16)
 
 
 def test_producer_tiny_mxfp4_workload(orc):
@@ -138,6 +155,22 @@ def test_quantize_bit_exact(orc, rows, K, fmt, layout):
     gs = 3.25 if fmt == 0 else 1.0
     ref_p, ref_s = orc.quantize(synth.bits(x), fmt, layout, gs=gs)
     p, s = lb.lowbit_quantize(dev_bf16(x), fmt, layout, global_scale=dev_f32(gs) if fmt == 0 else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(p), ref_p)
+    assert np.array_equal(host_u8(s), ref_s)
+
+
+@pytest.mark.parametrize("rows,K", QSHAPES + [(300, 2560), (1000, 5120)])
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_quantize_fp16_bit_exact(orc, rows, K, fmt, layout):
+    if K % (16 if fmt == 0 else 32):
+        pytest.skip("K not a multiple of the block")
+    banner(f"quantize fp16 rows={rows} K={K} fmt={fmt} layout={layout}")
+    x = synth.activation(rows, K, seed=rows + 3 * K, outliers=True, dtype=torch.float16)
+    gs = 3.25 if fmt == 0 else 1.0
+    ref_p, ref_s = orc.quantize(synth.bits(x), fmt, layout, gs=gs, dtype=orc.F16)
+    p, s = lb.lowbit_quantize_fp16(dev_bf16(x), fmt, layout, global_scale=dev_f32(gs) if fmt == 0 else None)
     torch.cuda.synchronize()
     assert np.array_equal(host_u8(p), ref_p)
     assert np.array_equal(host_u8(s), ref_s)

@@ -243,3 +243,37 @@ def test_hand_worked_blocks(orc, blk):
         if layout == orc.TILED:
             nz = np.flatnonzero(sf)
             assert set(nz.tolist()) <= {0}, "tiled padding must be zero"
+
+
+# --- fp16 (the producer's and quantizer's other input format) -------------------------------
+
+def test_f16_widening_exhaustive_against_numpy(orc):
+    """Every binary16 bit pattern widens exactly as numpy's float16 does."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float32)
+    got = np.array([orc.f16_to_f32(int(b)) for b in pats], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_rounding_against_numpy(orc):
+    """fp32 -> fp16 nearest-even against numpy's conversion: every finite fp16
+    value, the midpoints between neighbours (exact ties, both parities), one
+    fp32 ulp either side of them, the overflow boundary and random values
+    from the subnormal range to beyond 65504."""
+    fin = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    mids = ((fin[:-1].astype(np.float64) + fin[1:].astype(np.float64)) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (fin[:-1].astype(np.float64) + fin[1:]) / 2)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    rng = np.random.default_rng(11)
+    rnd = np.ldexp(rng.uniform(1, 2, 20000), rng.integers(-26, 18, 20000)).astype(np.float32)
+    edge = np.array([65504.0, 65519.996, 65520.0, 65536.0, 1e6, np.inf, 2.0 ** -24, 2.0 ** -25,
+                     3 * 2.0 ** -26, 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25], dtype=np.float32)
+    vals = np.concatenate([fin, mids, up, dn, rnd, edge])
+    vals = np.concatenate([vals, -vals])
+    with np.errstate(over="ignore"):   # the overflow cases are meant to become infinities
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)

@@ -172,3 +172,48 @@ def test_nvfp4_dequantize_divides_by_global_scale(orc):
     want = (x1 / 3.0).astype(np.float32)
     assert np.array_equal(x3.astype(np.float32), want)
     assert np.array_equal(bits, synth.bits(torch.from_numpy(want).to(torch.bfloat16)))
+
+
+# --- fp16 tensors ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_residual_is_fp16_sum(orc, fmt):
+    """With fp16 tensors the residual is numpy's fp16 rounding of the fp32 sum."""
+    x, r, w = synth.producer_inputs(16, 512, seed=15, outliers=True, dtype=torch.float16)
+    out = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, fmt, orc.LINEAR,
+                                dtype=orc.F16)
+    ref = (x.numpy().astype(np.float32) + r.numpy().astype(np.float32)).astype(np.float16)
+    assert np.array_equal(out["residual"], ref.view(np.uint16))
+
+
+def test_fp16_y_definition(orc):
+    """y = fl32(fl32(fp16(h) * rstd) * w) with fp16 h and w, in numpy fp32."""
+    x, r, w = synth.producer_inputs(8, 256, seed=14, outliers=True, dtype=torch.float16)
+    out = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, 0, orc.LINEAR,
+                                diag=True, dtype=orc.F16)
+    hb = (x.numpy().astype(np.float32) + r.numpy().astype(np.float32)).astype(np.float16).astype(np.float32)
+    y = (hb * out["rstd"][:, None]) * w.numpy().astype(np.float32)
+    assert np.array_equal(out["y"], y.astype(np.float32))
+
+
+def test_fp16_and_bf16_agree_on_common_values(orc):
+    """Values exact in both formats (small integers times powers of two within
+    range) give identical codes and scales through the fp16 and bf16 paths of
+    the quantizer and the producer."""
+    rng = np.random.default_rng(21)
+    v = (rng.integers(-64, 65, (12, 256)) * np.ldexp(1.0, rng.integers(-6, 4, (12, 1)))).astype(np.float32)
+    xb = torch.from_numpy(v).to(torch.bfloat16)
+    xh = torch.from_numpy(v).to(torch.float16)
+    assert torch.equal(xb.float(), xh.float())
+    for fmt in (0, 1):
+        pb, sb = orc.quantize(synth.bits(xb), fmt, orc.TILED)
+        ph, sh = orc.quantize(synth.bits(xh), fmt, orc.TILED, dtype=orc.F16)
+        assert np.array_equal(pb, ph) and np.array_equal(sb, sh)
+    zb, zh = torch.zeros_like(xb), torch.zeros_like(xh)
+    wb = torch.ones(256, dtype=torch.bfloat16)
+    wh = torch.ones(256, dtype=torch.float16)
+    for fmt in (0, 1):
+        ob = orc.add_rmsnorm_quant(synth.bits(xb), synth.bits(zb), synth.bits(wb), EPS, fmt, orc.LINEAR)
+        oh = orc.add_rmsnorm_quant(synth.bits(xh), synth.bits(zh), synth.bits(wh), EPS, fmt, orc.LINEAR,
+                                   dtype=orc.F16)
+        assert np.array_equal(ob["packed"], oh["packed"]) and np.array_equal(ob["sf"], oh["sf"])
