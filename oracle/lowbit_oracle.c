@@ -36,7 +36,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1 };
+enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1, ORC_MXFP8 = 2 };
 enum { ORC_SF_LINEAR = 0, ORC_SF_TILED = 1 };
 enum { ORC_EPI_NONE = 0, ORC_EPI_BIAS = 1, ORC_EPI_RESIDUAL = 2, ORC_EPI_BIAS_RESIDUAL = 3,
        ORC_EPI_BIAS_GELU = 4 };
@@ -225,6 +225,11 @@ int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int fmt, int layout
  * MXFP4 (B = 32, UE8M0 scale, OCP MX rule, gs unused):
  *     e = clamp(floor(log2 amax) - 2, -127, 127)  (amax == 0 gives -127)
  *     sbyte = e + 127;  v_i = y_i * 2^-e (exact);  code_i = E2M1(v_i)
+ * MXFP8 (B = 32, UE8M0 scale, E4M3 elements, the same OCP MX rule with the
+ * element format's largest exponent, 8 for E4M3):
+ *     e = clamp(floor(log2 amax) - 8, -127, 127);  sbyte = e + 127
+ *     v_i = y_i * 2^-e;  code_i = E4M3(v_i) (nearest-even, saturating at 448,
+ *     sign kept), one byte per element
  */
 static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes, uint8_t* sbyte,
                         float* amax_out, float* spre_out, float* v_out) {
@@ -256,13 +261,14 @@ static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes
             codes[i] = orc_e2m1_encode(v);
         }
     } else {
+        const int emax = (fmt == ORC_MXFP8) ? 8 : 2;   /* largest exponent of E4M3 / E2M1 */
         int e;
         if (amax == 0.0f) {
             e = -127;
         } else {
             int E;
             (void)frexp((double)amax, &E);       /* amax = f * 2^E, f in [0.5, 1) */
-            e = (E - 1) - 2;                     /* floor(log2 amax) - emax(E2M1) */
+            e = (E - 1) - emax;                  /* floor(log2 amax) - emax */
             if (e < -127) e = -127;
             if (e > 127) e = 127;
         }
@@ -271,7 +277,7 @@ static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes
         for (int i = 0; i < B; i++) {
             float v = ldexpf(y[i], -e);          /* exact unless it underflows */
             if (v_out) v_out[i] = v;
-            codes[i] = orc_e2m1_encode(v);
+            codes[i] = (fmt == ORC_MXFP8) ? orc_e4m3_encode(v) : orc_e2m1_encode(v);
         }
     }
 }
@@ -300,16 +306,24 @@ void orc_encode_with_scale(const float* y, int B, int fmt, float gs, uint8_t sby
         for (int i = 0; i < B; i++) {
             float v = ldexpf(y[i], -e);
             if (v_out) v_out[i] = v;
-            codes[i] = orc_e2m1_encode(v);
+            codes[i] = (fmt == ORC_MXFP8) ? orc_e4m3_encode(v) : orc_e2m1_encode(v);
         }
     }
 }
 
-/* Pack codes two per byte: element 2j in the low nibble, 2j+1 in the high. */
-static void pack_row(const uint8_t* codes, int64_t n, uint8_t* out) {
+/* FP4: codes two per byte, element 2j in the low nibble, 2j+1 in the high.
+ * MXFP8: one byte per element. */
+static void pack_row(const uint8_t* codes, int64_t n, int fmt, uint8_t* out) {
+    if (fmt == ORC_MXFP8) {
+        memcpy(out, codes, (size_t)n);
+        return;
+    }
     for (int64_t j = 0; j < n / 2; j++)
         out[j] = (uint8_t)((codes[2 * j] & 15) | ((codes[2 * j + 1] & 15) << 4));
 }
+
+/* Bytes of one packed row of n elements. */
+static int64_t row_bytes(int fmt, int64_t n) { return fmt == ORC_MXFP8 ? n : n / 2; }
 
 /* Quantize one row of n fp32 values and write codes + scales in the layout. */
 static void quant_row(const float* y, int64_t row, int64_t n, int fmt, float gs, int layout,
@@ -324,13 +338,14 @@ static void quant_row(const float* y, int64_t row, int64_t n, int fmt, float gs,
                     v_row ? v_row + b * B : NULL);
         sf[orc_sf_offset(row, b, nblk, fmt, layout)] = sb;
     }
-    pack_row(codes_tmp, n, packed_row);
+    pack_row(codes_tmp, n, fmt, packed_row);
 }
 
 static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
     if (rows < 0 || k <= 0) return 1;
-    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return 1;
+    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4 && fmt != ORC_MXFP8) return 1;
     if (layout != ORC_SF_LINEAR && layout != ORC_SF_TILED) return 1;
+    if (fmt == ORC_MXFP8 && layout != ORC_SF_LINEAR) return 1;   /* MXFP8 scales: LINEAR only */
     if (k % block_of(fmt) != 0) return 1;
     return 0;
 }
@@ -399,7 +414,7 @@ int orc_add_rmsnorm_quant_dt(const uint16_t* x, uint16_t* residual, const uint16
                 }
                 if (diag_y) memcpy(diag_y + m * H, y, sizeof(float) * H);
                 /* step 4 */
-                quant_row(y, m, H, fmt, gs, layout, out_packed + m * (H / 2), out_sf, codes,
+                quant_row(y, m, H, fmt, gs, layout, out_packed + m * row_bytes(fmt, H), out_sf, codes,
                           diag_amax ? diag_amax + m * nblk : NULL,
                           diag_spre ? diag_spre + m * nblk : NULL,
                           diag_v ? diag_v + m * H : NULL);
@@ -445,7 +460,7 @@ int orc_quantize_dt(const uint16_t* x, int64_t rows, int64_t K, int fmt, int lay
 #pragma omp for schedule(static)
             for (int64_t m = 0; m < rows; m++) {
                 for (int64_t i = 0; i < K; i++) y[i] = wid(x[m * K + i]);
-                quant_row(y, m, K, fmt, gs, layout, out_packed + m * (K / 2), out_sf, codes, NULL,
+                quant_row(y, m, K, fmt, gs, layout, out_packed + m * row_bytes(fmt, K), out_sf, codes, NULL,
                           diag_spre ? diag_spre + m * nblk : NULL, NULL);
             }
         }
@@ -463,7 +478,8 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout
 /* Dequantize (FlashRT README: dequantize_fp4_sfa_fp16, here to bf16)          */
 /* ------------------------------------------------------------------------- */
 /* x_hat = fl32(E2M1(code) * scale / gs) for NVFP4 (gs divides: it was folded
- * into the block scale on the way in), E2M1(code) * 2^(b-127) for MXFP4, then
+ * into the block scale on the way in), E2M1(code) * 2^(b-127) for MXFP4,
+ * E4M3(byte) * 2^(b-127) for MXFP8, then
  * stored as bf16 (nearest-even).  Also returns the binary64 values when
  * out_f64 is non-NULL. */
 int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
@@ -473,12 +489,16 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < rows; m++) {
         for (int64_t i = 0; i < K; i++) {
-            uint8_t byte = packed[m * (K / 2) + i / 2];
-            uint8_t code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
             uint8_t sb = sf[orc_sf_offset(m, i / B, nblk, fmt, layout)];
+            double q;
+            if (fmt == ORC_MXFP8) {
+                q = orc_e4m3_value(packed[m * K + i]);
+            } else {
+                uint8_t byte = packed[m * (K / 2) + i / 2];
+                q = orc_e2m1_value((i % 2 == 0) ? (byte & 15) : (byte >> 4));
+            }
             /* q * scale is exact in binary64 (and in binary32) */
-            double v = orc_e2m1_value(code) *
-                       ((fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb));
+            double v = q * ((fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb));
             /* NVFP4: one division by gs; the binary64 quotient rounded to
              * binary32 equals the correctly rounded binary32 quotient */
             if (fmt == ORC_NVFP4) v = v / (double)gs;
@@ -531,6 +551,7 @@ int orc_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8
              int epi, const uint16_t* bias, const uint16_t* residual,
              double* out_ref, double* out_l1) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only */
     double* A = (double*)malloc(sizeof(double) * (size_t)(M * K));
     double* Bm = (double*)malloc(sizeof(double) * (size_t)(N * K));
     if (!A || !Bm) { free(A); free(Bm); return 2; }
@@ -565,6 +586,7 @@ int orc_gemm_entries(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, con
                      int64_t count, const int64_t* idx_m, const int64_t* idx_n,
                      double* out_ref, double* out_l1) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only */
     for (int64_t t = 0; t < count; t++)
         if (idx_m[t] < 0 || idx_m[t] >= M || idx_n[t] < 0 || idx_n[t] >= N) return 1;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -598,6 +620,7 @@ int orc_gemm_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, co
                       float* diag_y, float* diag_v, double* diag_l1, float* diag_spre,
                       float* diag_amax) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only */
     if (N % 16 != 0) return 1;
     double* ref = (double*)malloc(sizeof(double) * (size_t)(M * N));
     double* l1 = (double*)malloc(sizeof(double) * (size_t)(M * N));

@@ -6,7 +6,8 @@ numpy host arrays; bf16 and fp16 tensors travel as their uint16 bit patterns
 (dtype BF16 = 0 or F16 = 1 says which).
 
 Enum values: fmt NVFP4 = 0 (16-blocks, E4M3 scales), MXFP4 = 1 (32-blocks,
-UE8M0 scales); layout LINEAR = 0, TILED = 1; epilogue NONE = 0, BIAS = 1,
+UE8M0 scales), MXFP8 = 2 (32-blocks, UE8M0 scales, E4M3 elements, one byte
+each; LINEAR scales only, no GEMM); layout LINEAR = 0, TILED = 1; epilogue NONE = 0, BIAS = 1,
 RESIDUAL = 2, BIAS_RESIDUAL = 3, BIAS_GELU = 4.
 """
 import ctypes
@@ -16,7 +17,7 @@ import numpy as np
 
 from . import build as _build
 
-NVFP4, MXFP4 = 0, 1
+NVFP4, MXFP4, MXFP8 = 0, 1, 2
 LINEAR, TILED = 0, 1
 EPI_NONE, EPI_BIAS, EPI_RESIDUAL, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3, 4
 BF16, F16 = 0, 1
@@ -35,6 +36,11 @@ _int = ctypes.c_int
 
 def block_size(fmt: int) -> int:
     return 16 if fmt == NVFP4 else 32
+
+
+def row_bytes(fmt: int, n: int) -> int:
+    """Bytes of a packed row of n elements: two FP4 codes per byte, one MXFP8 byte each."""
+    return n if fmt == MXFP8 else n // 2
 
 
 def lib():
@@ -173,7 +179,7 @@ def add_rmsnorm_quant(x, residual, weight, eps, fmt, layout, gs=1.0, diag=False,
     w = _c(weight, np.uint16)
     M, H = x.shape
     B = block_size(fmt)
-    packed = np.zeros((M, H // 2), dtype=np.uint8)
+    packed = np.zeros((M, row_bytes(fmt, H)), dtype=np.uint8)
     sf = np.zeros(sf_bytes(M, H, fmt, layout), dtype=np.uint8)
     d = {}
     if diag:
@@ -195,7 +201,7 @@ def quantize(x, fmt, layout, gs=1.0, diag=False, dtype=BF16):
     """Quantizer.  x: uint16 (rows, K) bf16 bits (fp16 bits with dtype F16)."""
     x = _c(x, np.uint16)
     rows, K = x.shape
-    packed = np.zeros((rows, K // 2), dtype=np.uint8)
+    packed = np.zeros((rows, row_bytes(fmt, K)), dtype=np.uint8)
     sf = np.zeros(sf_bytes(rows, K, fmt, layout), dtype=np.uint8)
     spre = np.zeros((rows, K // block_size(fmt)), np.float32) if diag else None
     rc = lib().orc_quantize_dt(x, rows, K, fmt, layout, gs, packed, sf, _ptr(spre), dtype)

@@ -217,3 +217,88 @@ def test_fp16_and_bf16_agree_on_common_values(orc):
         oh = orc.add_rmsnorm_quant(synth.bits(xh), synth.bits(zh), synth.bits(wh), EPS, fmt, orc.LINEAR,
                                    dtype=orc.F16)
         assert np.array_equal(ob["packed"], oh["packed"]) and np.array_equal(ob["sf"], oh["sf"])
+
+
+# --- MXFP8 (E4M3 elements, UE8M0 32-blocks) ------------------------------------------------
+
+def _e4m3_bits(v):
+    """E4M3 byte of a value exactly on the grid (torch's own conversion)."""
+    return int(torch.tensor([v], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+
+
+def test_mxfp8_hand_worked_blocks(orc):
+    """Blocks worked out by hand from the OCP MX rule (e = floor(log2 amax) - 8,
+    E4M3 elements nearest-even, saturating at 448, sign kept)."""
+    rows = []
+    want_sf, want_codes = [], []
+    # all zero: scale byte 0, every element 0
+    rows.append([0.0] * 32)
+    want_sf.append(0)
+    want_codes.append([0] * 32)
+    # one outlier 1000 and 31 x 0.01 (bf16 0.010009765625): floor(log2 1000) = 9,
+    # e = 1 (X = 2); 1000 / 2 = 500 saturates to 448 (0x7E); 0.01000977 / 2 =
+    # 0.00500488 = 2.5625 steps of the subnormal step 2^-9 -> 3 steps (0x03)
+    rows.append([1000.0] + [0.01] * 31)
+    want_sf.append(128)
+    want_codes.append([0x7E] + [0x03] * 31)
+    # exact grid: amax 448 gives e = 0 (X = 1); grid values keep their codes, a
+    # negative value its sign, and -0.001 (0.512 of the subnormal step) rounds
+    # to 1 step with its sign (0x81)
+    grid = [448.0, -448.0, 1.0, -1.125, 0.015625, 240.0, -0.001953125, 3.5]
+    vals = grid + [-0.001] + [0.0] * 23
+    rows.append(vals)
+    want_sf.append(127)
+    want_codes.append([_e4m3_bits(v) for v in grid] + [0x81] + [0] * 23)
+    # amax 512 moves to the next binade: e = 1 (X = 2), elements 256 and 8
+    rows.append([512.0, 16.0] + [0.0] * 30)
+    want_sf.append(128)
+    want_codes.append([_e4m3_bits(256.0), _e4m3_bits(8.0)] + [0] * 30)
+    x = torch.tensor(rows, dtype=torch.float32).to(torch.bfloat16)
+    p, s = orc.quantize(synth.bits(x), orc.MXFP8, orc.LINEAR)
+    assert s.tolist() == want_sf
+    assert p.tolist() == want_codes
+
+
+@pytest.mark.parametrize("K", [64, 256, 5120])
+def test_mxfp8_quantize_dequantize_idempotent(orc, K):
+    """Dequantized MXFP8 values (at most 4 significant bits: exact in bf16)
+    quantize back to the same values."""
+    x = synth.activation(6, K, seed=23, outliers=True)
+    p, s = orc.quantize(synth.bits(x), orc.MXFP8, orc.LINEAR)
+    xq, f1 = orc.dequantize(p, s, 6, K, orc.MXFP8, orc.LINEAR)
+    assert np.array_equal(synth.from_bits(xq).double().numpy(), f1)   # bf16-exact
+    p2, s2 = orc.quantize(xq, orc.MXFP8, orc.LINEAR)
+    _, f2 = orc.dequantize(p2, s2, 6, K, orc.MXFP8, orc.LINEAR)
+    assert np.array_equal(f1, f2)
+
+
+def test_mxfp8_dequantize_error_bound(orc):
+    """|x - dq(q(x))| <= half an E4M3 step at the element's binade (relative
+    2^-4 for normal elements), or 448 * X saturation, from the definitions."""
+    x = synth.activation(16, 1024, seed=24, outliers=True)
+    p, s = orc.quantize(synth.bits(x), orc.MXFP8, orc.LINEAR)
+    _, f = orc.dequantize(p, s, 16, 1024, orc.MXFP8, orc.LINEAR)
+    xv = x.double().numpy()
+    X = np.repeat(np.ldexp(1.0, (s.reshape(16, -1).astype(np.int32) - 127)), 32, axis=1)
+    v = np.abs(xv) / X
+    step = np.ldexp(1.0, (np.maximum(np.floor(np.log2(np.maximum(v, 1e-300))), -6) - 3).astype(np.int32))
+    bound = np.where(v > 448, v - 448, step / 2) * X
+    assert np.all(np.abs(xv - f) <= bound * (1 + 1e-12))
+
+
+def test_mxfp8_producer_equals_quantize_of_its_y(orc):
+    """The fused producer's MXFP8 codes are the quantizer's codes of its own y."""
+    x, r, w = synth.producer_inputs(8, 512, seed=25, outliers=True)
+    out = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.MXFP8, orc.LINEAR,
+                                diag=True)
+    assert out["packed"].shape == (8, 512)
+    y = out["y"].reshape(-1, 32)
+    for i in range(y.shape[0]):
+        codes, _ = orc.encode_with_scale(y[i], orc.MXFP8, 1.0, int(out["sf"][i]), with_v=True)
+        assert np.array_equal(codes, out["packed"].reshape(-1, 32)[i])
+
+
+def test_mxfp8_rejects_tiled_scales(orc):
+    x = synth.activation(2, 64, seed=1)
+    with pytest.raises(ValueError):
+        orc.quantize(synth.bits(x), orc.MXFP8, orc.TILED)
