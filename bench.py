@@ -45,10 +45,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def producer_bytes(M, H, B):
-    # x read, r read, r written (bf16) + FP4 codes + one scale byte per block
-    # + the weight row and the global scale once per launch
-    return M * H * 6 + M * H // 2 + M * H // B + 2 * H + 4
+def producer_bytes(M, H, B, elem_bytes=0.5):
+    # x read, r read, r written (bf16) + the codes (half a byte per FP4
+    # element, one per MXFP8 element) + one scale byte per block + the weight
+    # row and the global scale once per launch
+    return M * H * 6 + int(M * H * elem_bytes) + M * H // B + 2 * H + 4
 
 
 def gemm_bytes(M, N, K, B, epi_bias=False, epi_res=False, out_fp4=False):
@@ -243,9 +244,9 @@ def build_stages():
 
 def build_variant_stages():
     """Format variants of the step's kernels, timed beside the step and
-    reported apart from `value`: the fused producer on fp16 tensors at the
-    4096 x 4096 NVFP4 workload (same draws, rounded to fp16), rotated over 4
-    input sets like the bf16 stage."""
+    reported apart from `value`, at the 4096 x 4096 producer workload with 4
+    rotating input sets like the bf16 stage: the NVFP4 producer on fp16
+    tensors (same draws, rounded to fp16) and the producer with MXFP8 output."""
     dev = "cuda"
     c = synth.NVFP4_PRODUCER
     M, H = c["M"], c["H"]
@@ -267,7 +268,25 @@ def build_variant_stages():
         lb.lowbit_add_rmsnorm_quant_fp16(x, r, w, EPS, lb.NVFP4, lb.LINEAR, global_scale=gs, out_packed=pk,
                                          out_sf=sf)
 
-    return [Stage(f"add_rmsnorm_nvfp4_fp16_{M}x{H}", producer, "hbm", producer_bytes(M, H, 16), "B", HBM_PEAK)]
+    stages = [Stage(f"add_rmsnorm_nvfp4_fp16_{M}x{H}", producer, "hbm", producer_bytes(M, H, 16), "B", HBM_PEAK)]
+
+    # the same bf16 workload quantized to MXFP8 (E4M3 elements, one byte each)
+    bsets = []
+    for i in range(4):
+        x, r, w = synth.producer_inputs(M, H, c["seed"] + 100 * i, outliers=True)
+        bsets.append((x.to(dev), r.to(dev), w.to(dev)))
+    pk8 = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    sf8 = torch.empty(lb.lowbit_sf_bytes(M, H, lb.MXFP8, lb.LINEAR), dtype=torch.uint8, device=dev)
+    it8 = {"i": 0}
+
+    def producer8():
+        x, r, w = bsets[it8["i"] % 4]
+        it8["i"] += 1
+        lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.MXFP8, lb.LINEAR, out_packed=pk8, out_sf=sf8)
+
+    stages.append(Stage(f"add_rmsnorm_mxfp8_{M}x{H}", producer8, "hbm", producer_bytes(M, H, 32, 1.0), "B",
+                        HBM_PEAK))
+    return stages
 
 
 def build_decode_stages():

@@ -12,7 +12,7 @@ import os
 
 import torch
 
-NVFP4, MXFP4 = 0, 1
+NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: producer / quantizer / dequantizer, LINEAR scales
 LINEAR, TILED = 0, 1
 VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = -1, 0, 1
 
@@ -112,7 +112,7 @@ def lowbit_sf_bytes(rows, k, fmt, layout):
 
 def _alloc_q(rows, k, fmt, layout, device, out_packed, out_sf):
     if out_packed is None:
-        out_packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=device)
+        out_packed = torch.empty((rows, k if fmt == MXFP8 else k // 2), dtype=torch.uint8, device=device)
     if out_sf is None:
         out_sf = torch.empty(lowbit_sf_bytes(rows, k, fmt, layout), dtype=torch.uint8, device=device)
     return out_packed, out_sf
@@ -179,7 +179,7 @@ def lowbit_quantize_fp16(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_pac
 def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):
     _need(packed, torch.uint8, "packed")
     _need(sf, torch.uint8, "sf")
-    rows, K = packed.shape[0], packed.shape[1] * 2
+    rows, K = packed.shape[0], packed.shape[1] * (1 if fmt == MXFP8 else 2)
     if out is None:
         out = torch.empty((rows, K), dtype=torch.bfloat16, device=packed.device)
     _check("lowbit_dequantize", lib().lowbit_dequantize(

@@ -24,8 +24,14 @@ using lowbit::GemmArgs;
 
 constexpr int64_t kMaxRowElems = 32768;  // 4 waves x 64 lanes x 128 elements per lane
 
-bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }
+bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }   // GEMM operands
 bool layout_ok(int l) { return l == LOWBIT_SF_LINEAR || l == LOWBIT_SF_TILED; }
+// producer / quantizer / dequantizer formats: MXFP8 as well, with LINEAR scales only
+bool qfmt_layout_ok(int f, int l) {
+  if (f == LOWBIT_MXFP8) return l == LOWBIT_SF_LINEAR;
+  return fmt_ok(f) && layout_ok(l);
+}
+
 int64_t block_of(int f) { return f == LOWBIT_NVFP4 ? 16 : 32; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -131,8 +137,8 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
 static lowbit_status producer(const void* input, void* residual, const void* weight, int64_t M, int64_t H,
                               float eps, lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
                               uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t stream) {
-  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
-  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
+  if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
   if (M < 0) return LOWBIT_ESHAPE;
   if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
   if (H < 64 || H % block_of(fmt) != 0 || H > kMaxRowElems) return LOWBIT_ESHAPE;
@@ -150,8 +156,8 @@ static lowbit_status producer(const void* input, void* residual, const void* wei
 static lowbit_status quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt, lowbit_sf_layout layout,
                               const float* global_scale, uint8_t* out_packed, uint8_t* out_sf, int in_f16,
                               hipStream_t stream) {
-  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
-  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
+  if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
   if (rows < 0) return LOWBIT_ESHAPE;
   if (rows > 0 && (!x || !out_packed || !out_sf)) return LOWBIT_EINVAL;
   if (K < block_of(fmt) || K % block_of(fmt) != 0 || K > kMaxRowElems) return LOWBIT_ESHAPE;
@@ -180,7 +186,7 @@ const char* lowbit_status_str(lowbit_status s) {
 }
 
 size_t lowbit_sf_bytes(int64_t rows, int64_t k, lowbit_format fmt, lowbit_sf_layout layout) {
-  if (!fmt_ok(fmt) || !layout_ok(layout) || rows < 0 || k < 0 || k % block_of(fmt) != 0) return 0;
+  if (!qfmt_layout_ok(fmt, layout) || rows < 0 || k < 0 || k % block_of(fmt) != 0) return 0;
   return (size_t)lowbit::sf_bytes_of(layout, rows, k / block_of(fmt));
 }
 
@@ -213,8 +219,8 @@ lowbit_status lowbit_quantize_fp16(const void* x, int64_t rows, int64_t K, lowbi
 lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
                                 lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
                                 void* out, hipStream_t stream) {
-  if (!fmt_ok(fmt) || !layout_ok(layout)) return LOWBIT_EINVAL;
-  if (fmt == LOWBIT_MXFP4 && global_scale) return LOWBIT_EINVAL;
+  if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
+  if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
   if (rows < 0) return LOWBIT_ESHAPE;
   if (rows > 0 && (!packed || !sf || !out)) return LOWBIT_EINVAL;
   if (K < block_of(fmt) || K % block_of(fmt) != 0) return LOWBIT_ESHAPE;

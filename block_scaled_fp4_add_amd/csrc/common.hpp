@@ -12,7 +12,7 @@ namespace lowbit {
 
 constexpr int kWave = 64;
 
-enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1 };
+enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2 };   // MXFP8: quantization only, no GEMM
 enum Layout : int { kLinear = 0, kTiled = 1 };
 enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual = 3, kEpiBiasGelu = 4,
                  kEpiBiasGeluFp4 = 5 };
@@ -20,6 +20,7 @@ enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual 
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<kNVFP4> { static constexpr int B = 16; };
 template <> struct FmtTraits<kMXFP4> { static constexpr int B = 32; };
+template <> struct FmtTraits<kMXFP8> { static constexpr int B = 32; };
 
 // ---------------------------------------------------------------------------
 // bf16
@@ -103,6 +104,20 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float x) {
   int code = (e + 7) * 8 + (int)q - 8;
   return code > 0x7E ? 0x7Eu : (uint32_t)code;
 }
+// E4M3 element (MXFP8): nearest-even, saturating at 448, the sign bit copied
+// from v (so a negative value that rounds to zero gives 0x80).
+__device__ __forceinline__ uint32_t e4m3_encode_signed(float v) {
+  return ((__float_as_uint(v) >> 24) & 0x80u) | e4m3_encode_nonneg(fabsf(v));
+}
+// Eight fp32 -> eight E4M3 bytes (element i in byte i).
+__device__ __forceinline__ uint2 e4m3x8(const float* v) {
+  uint2 r;
+  r.x = e4m3_encode_signed(v[0]) | (e4m3_encode_signed(v[1]) << 8) | (e4m3_encode_signed(v[2]) << 16) |
+        (e4m3_encode_signed(v[3]) << 24);
+  r.y = e4m3_encode_signed(v[4]) | (e4m3_encode_signed(v[5]) << 8) | (e4m3_encode_signed(v[6]) << 16) |
+        (e4m3_encode_signed(v[7]) << 24);
+  return r;
+}
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   uint32_t e = (b >> 3) & 15, m = b & 7;
   float v = (e == 0) ? (float)m * 0x1p-9f : (float)(8 + m) * __uint_as_float((e + 117u) << 23);
@@ -185,14 +200,17 @@ __device__ __forceinline__ uint32_t nv_block_scale(float amax, float gs, float* 
   *inv = (sdec == 0.0f) ? 0.0f : __fmul_rn(__fdiv_rn(1.0f, sdec), gs);
   return sb;
 }
-// MXFP4 block scale (OCP MX): e = clamp(floor(log2 amax) - 2, -127, 127);
+// MX block scale (OCP MX): e = clamp(floor(log2 amax) - EMAX, -127, 127) with
+// EMAX the element format's largest exponent (2 for E2M1, 8 for E4M3);
 // returns the byte e + 127 and the exact power of two 2^-e.
-__device__ __forceinline__ uint32_t mx_block_scale(float amax, float* inv) {
+template <int EMAX>
+__device__ __forceinline__ uint32_t mx_block_scale_e(float amax, float* inv) {
   int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);  // amax >= 0, finite
-  int sb = eb - 2;
+  int sb = eb - EMAX;
   if (sb < 0) sb = 0;                                     // e = -127 (also amax == 0 / subnormal)
   *inv = __uint_as_float((uint32_t)(254 - sb) << 23);     // 2^(127 - sb) = 2^-e
   return (uint32_t)sb;
 }
+__device__ __forceinline__ uint32_t mx_block_scale(float amax, float* inv) { return mx_block_scale_e<2>(amax, inv); }
 
 }  // namespace lowbit

@@ -2,7 +2,9 @@
 //   * fused add + RMSNorm + FP4 quantization (FlashInfer page,
 //     cute_dsl/add_rmsnorm_fp4quant.py, AddRMSNormFP4QuantKernel phases 1-3);
 //   * plain FP4 quantization of a bf16 tensor and its dequantization (FlashRT
-//     fp4-gemm README, quantize_fp4_sfa_* / dequantize_fp4_sfa_*).
+//     fp4-gemm README, quantize_fp4_sfa_* / dequantize_fp4_sfa_*);
+//   * the same three for MXFP8 (E4M3 elements, one byte each, UE8M0 32-blocks;
+//     the vLLM page's FusedWoAKernel quantizes to this format).
 //
 // Two forms.  Many rows (M >= 256) of up to 16384 elements take one
 // workgroup per row (row_wg_kernel, below).  Otherwise a row is owned by WPR
@@ -53,10 +55,20 @@ __device__ __forceinline__ void quant_store_block(const float* y, float gs, int6
 #pragma unroll
   for (int i = 0; i < B; i++) amax = fmaxf(amax, fabsf(y[i]));
   float inv;
-  uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv) : mx_block_scale(amax, &inv);
+  uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv)
+                : (FMT == kMXFP8) ? mx_block_scale_e<8>(amax, &inv) : mx_block_scale(amax, &inv);
   float v[B];
 #pragma unroll
   for (int i = 0; i < B; i++) v[i] = __fmul_rn(y[i], inv);
+  if constexpr (FMT == kMXFP8) {
+    // one E4M3 byte per element: the block's 32 bytes as two 16-byte stores
+    uint8_t* dst = a.out_packed + row * a.H + kb * B;
+    const uint2 c0 = e4m3x8(v), c1 = e4m3x8(v + 8), c2 = e4m3x8(v + 16), c3 = e4m3x8(v + 24);
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
+    a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = (uint8_t)sb;
+    return;
+  }
   uint8_t* dst = a.out_packed + row * (a.H / 2) + kb * (B / 2);
   if constexpr (B == 16) {
     uint2 p;
@@ -314,12 +326,15 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
     amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
     if constexpr (LPB == 4) amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
     float inv;
-    const uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv) : mx_block_scale(amax, &inv);
+    const uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv)
+                        : (FMT == kMXFP8) ? mx_block_scale_e<8>(amax, &inv) : mx_block_scale(amax, &inv);
 #pragma unroll
     for (int i = 0; i < 8; i++) y[i] = __fmul_rn(y[i], inv);
-    const uint32_t code = e2m1x8(y);
     if (q < nvec) {
-      code_row[q] = code;
+      if constexpr (FMT == kMXFP8)   // one E4M3 byte per element: 8 bytes per vector
+        reinterpret_cast<uint2*>(a.out_packed + row * H)[q] = e4m3x8(y);
+      else
+        code_row[q] = e2m1x8(y);
       if (q % LPB == 0) {
         const int kb = q / LPB, jj = kb & 7;
         const int in_grp = (FMT == kNVFP4) ? ((jj >> 2) << 7) + (jj & 3)
@@ -354,7 +369,7 @@ hipError_t launch_row(const RowArgs& a, hipStream_t s) {
 // when there are many rows, a row spread over up to 4 waves when there are few.
 template <int FMT, bool FUSED, bool F16>
 hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
-  constexpr int MAXNBL = (FMT == kNVFP4) ? 8 : 4;
+  constexpr int MAXNBL = (FMT == kNVFP4) ? 8 : 4;   // MXFP4, MXFP8: 32-blocks
   const int64_t nblk = a.H / FmtTraits<FMT>::B;
   const int64_t nw = (a.H + kWgVecs * 8 * kWave - 1) / (kWgVecs * 8 * kWave);
   if (a.M >= kWgMinRows && nw <= kWgMaxWaves && a.rows_grid <= 0x7FFFFFFF) {
@@ -411,8 +426,28 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
   const uint32_t sb = sf[sf_offset(FMT, layout, row, kb, nblk)];
   const float scale = (FMT == kNVFP4) ? e4m3_to_f32(sb) : ue8m0_to_f32(sb);
   const float gs = (FMT == kNVFP4 && gsp != nullptr) ? *gsp : 1.0f;
-  const uint8_t* src = packed + row * (K / 2) + kb * (B / 2);
   uint16_t* dst = out + row * K + kb * B;
+  if constexpr (FMT == kMXFP8) {
+    // 32 E4M3 bytes; value * 2^e is exact in fp32 and has 4 significant bits
+    const uint4* src8 = reinterpret_cast<const uint4*>(packed + row * K + kb * B);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint4 p = src8[h];
+      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint32_t wd = w4[j >> 1], sh = 16 * (j & 1);
+        o[j] = pack_bf16x2(__fmul_rn(e4m3_to_f32((wd >> sh) & 0xFF), scale),
+                           __fmul_rn(e4m3_to_f32((wd >> (sh + 8)) & 0xFF), scale));
+      }
+      uint4* d4 = reinterpret_cast<uint4*>(dst + h * 16);
+      d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+    return;
+  }
+  const uint8_t* src = packed + row * (K / 2) + kb * (B / 2);
 #pragma unroll
   for (int q = 0; q < B / 16; q++) {
     uint2 p = *reinterpret_cast<const uint2*>(src + q * 8);
@@ -438,6 +473,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const
                                     uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
   RowArgs a{x, residual, w, M, H, M, eps, layout, gs, out_packed, out_sf};
   if (layout == kTiled) a.rows_grid = (M + 31) / 32 * 32;
+  if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, true, true>(a, s) : dispatch_row<kMXFP8, true, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, true>(a, s) : dispatch_row<kMXFP4, true, true>(a, s);
   return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, false>(a, s) : dispatch_row<kMXFP4, true, false>(a, s);
 }
@@ -446,6 +482,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, 
                            const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
   RowArgs a{x, nullptr, nullptr, rows, K, rows, 0.0f, layout, gs, out_packed, out_sf};
   if (layout == kTiled) a.rows_grid = (rows + 31) / 32 * 32;
+  if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, false, true>(a, s) : dispatch_row<kMXFP8, false, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, true>(a, s) : dispatch_row<kMXFP4, false, true>(a, s);
   return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, false>(a, s) : dispatch_row<kMXFP4, false, false>(a, s);
 }
@@ -458,6 +495,9 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t r
   const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
   if (fmt == kNVFP4)
     hipLaunchKernelGGL(dequant_kernel<kNVFP4>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
+                       gs, out);
+  else if (fmt == kMXFP8)
+    hipLaunchKernelGGL(dequant_kernel<kMXFP8>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
                        gs, out);
   else
     hipLaunchKernelGGL(dequant_kernel<kMXFP4>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,

@@ -68,7 +68,15 @@ typedef enum {
   LOWBIT_EHIP = 5,        /* a HIP runtime call or launch failed */
 } lowbit_status;
 
-typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1 } lowbit_format;
+/* NVFP4: 16-element blocks, E4M3 scales, optional fp32 global scale.
+ * MXFP4: 32-element blocks, UE8M0 scales.  Both pack two E2M1 codes per byte:
+ *        packed (rows, K/2), element 2j in the low nibble of byte j.
+ * MXFP8: 32-element blocks, UE8M0 scales, E4M3 elements, one byte each:
+ *        packed (rows, K).  Scale rule e = clamp(floor(log2 amax) - 8, -127,
+ *        127) (OCP MX, emax 8 for E4M3); elements nearest-even, saturating at
+ *        448, sign kept.  Producer, quantizer and dequantizer only, LINEAR
+ *        scales only; the GEMMs return LOWBIT_EINVAL for it. */
+typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2 } lowbit_format;
 typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1 } lowbit_sf_layout;
 
 /* GEMM schedule: -1 picks by shape; 0 = decode (weights as the MFMA row

@@ -52,6 +52,9 @@ def test_sf_bytes_matches_the_oracle(orc):
                 continue
             for layout in (0, 1):
                 assert L.lowbit_sf_bytes(rows, K, fmt, layout) == orc.sf_bytes(rows, K, fmt, layout)
+    # MXFP8: 32-blocks, LINEAR only
+    assert L.lowbit_sf_bytes(33, 5120, 2, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 2, 0)
+    assert L.lowbit_sf_bytes(33, 5120, 2, 1) == 0
 
 
 def test_pick_variant():
@@ -87,7 +90,10 @@ def quant(L, buf, rows, K, fmt=1, layout=0, gs=None, x=0, p=0, s=0):
 
 def test_quantize_argument_order(buf):
     L = lb.lib()
-    assert quant(L, buf, 4, 64, fmt=2) == EINVAL                           # format
+    assert quant(L, buf, 4, 64, fmt=3) == EINVAL                           # format
+    assert quant(L, buf, 4, 64, fmt=2, layout=1) == EINVAL                 # MXFP8: LINEAR scales only
+    assert quant(L, buf, 4, 64, fmt=2, gs=buf.at()) == EINVAL              # MXFP8 has no global scale
+    assert quant(L, buf, 4, 48, fmt=2) == ESHAPE                           # MXFP8: K % 32
     assert quant(L, buf, 4, 64, layout=5) == EINVAL                        # layout
     assert quant(L, buf, 4, 64, fmt=1, gs=buf.at()) == EINVAL              # MXFP4 has no global scale
     assert L.lowbit_quantize(None, 4, 64, 1, 0, None, buf.at(), buf.at(), None) == EINVAL
@@ -127,6 +133,7 @@ def test_gemm_argument_order(buf):
         return L.lowbit_gemm_bf16(a_, b, sa, sb, M, N, K, fmt, la, lb_, 1.0, o, variant, None)
 
     assert call(8, 128, 256, fmt=3) == EINVAL
+    assert call(8, 128, 256, fmt=2) == EINVAL                # MXFP8: no GEMM
     assert call(8, 128, 256, variant=2) == EINVAL
     assert call(8, 128, 256, o=None) == EINVAL
     assert call(-1, 128, 256) == ESHAPE

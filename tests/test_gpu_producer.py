@@ -229,3 +229,73 @@ def test_argument_errors_on_device():
     with pytest.raises(lb.LowbitError) as e:
         lb.lowbit_add_rmsnorm_quant(x, x.clone(), w, EPS, 1, 0, global_scale=dev_f32(1.0))
     assert e.value.status == 1
+
+
+# --- MXFP8 (E4M3 elements, UE8M0 32-blocks, LINEAR scales) ----------------------------------
+
+def _mxfp8_compare(orc, got_p, got_s, ref_p, ref_s, y):
+    """Scales bit-exact except where amax lies within 2^-20 of a power of two;
+    elements bit-exact except where the pre-rounding value lies within 2^-20
+    relative of an E4M3 midpoint (re-derived from the device's scale byte)."""
+    assert got_p.shape == ref_p.shape and got_s.shape == ref_s.shape
+    bad = np.nonzero((got_s != ref_s))[0]
+    for b in bad:   # scale differs: only allowed at a binade boundary, then re-encode
+        blk = y.reshape(-1, 32)[b]
+        amax = float(np.abs(blk).max())
+        assert amax > 0 and abs(amax / 2.0 ** np.round(np.log2(amax)) - 1) <= 2.0 ** -20, b
+        codes = orc.encode_with_scale(blk, orc.MXFP8, 1.0, int(got_s[b]))
+        assert np.array_equal(codes, got_p.reshape(-1, 32)[b])
+    ok = np.ones(ref_s.size, bool)
+    ok[bad] = False
+    gp, rp = got_p.reshape(-1, 32)[ok], ref_p.reshape(-1, 32)[ok]
+    diff = np.nonzero(gp != rp)
+    if diff[0].size:
+        yb = y.reshape(-1, 32)[ok]
+        X = np.ldexp(1.0, ref_s[ok].astype(np.int32) - 127)[:, None]
+        v = (yb / X)[diff]
+        # the two candidate codes must be neighbours and v within 2^-20 of their midpoint
+        lo = np.array([orc.e4m3_value(int(c)) for c in rp[diff]])
+        hi = np.array([orc.e4m3_value(int(c)) for c in gp[diff]])
+        assert np.all(np.abs(v - (lo + hi) / 2) <= 2.0 ** -20 * np.abs(v)), (v, lo, hi)
+    return diff[0].size + bad.size
+
+
+MXFP8_SHAPES = [(8, 256), (1, 5120), (33, 1024), (300, 1536), (2049, 512), (4500, 4096), (5, 17408)]
+
+
+@pytest.mark.parametrize("M,H", MXFP8_SHAPES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_producer_mxfp8(orc, M, H, dtype):
+    banner(f"producer mxfp8 M={M} H={H} dtype={dtype}")
+    x, r, w = synth.producer_inputs(M, H, M + 7 * H, outliers=True, dtype=dtype)
+    ref = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.MXFP8, orc.LINEAR,
+                                diag=True, dtype=_odt(orc, dtype))
+    rd = dev_bf16(r)
+    p, s = lb.lowbit_add_rmsnorm_quant(dev_bf16(x), rd, dev_bf16(w), EPS, lb.MXFP8, lb.LINEAR)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(rd), ref["residual"])
+    n = _mxfp8_compare(orc, host_u8(p), host_u8(s), ref["packed"], ref["sf"], ref["y"])
+    assert n <= 0.001 * ref["sf"].size
+
+
+@pytest.mark.parametrize("rows,K", [(1, 64), (7, 160), (41, 1536), (128, 5120), (300, 2560), (5, 17408)])
+def test_quantize_mxfp8_bit_exact(orc, rows, K):
+    banner(f"quantize mxfp8 rows={rows} K={K}")
+    x = synth.activation(rows, K, seed=rows + 11 * K, outliers=True)
+    ref_p, ref_s = orc.quantize(synth.bits(x), orc.MXFP8, orc.LINEAR)
+    p, s = lb.lowbit_quantize(dev_bf16(x), lb.MXFP8, lb.LINEAR)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(p), ref_p)
+    assert np.array_equal(host_u8(s), ref_s)
+
+
+def test_dequantize_mxfp8_bit_exact(orc):
+    rows, K = 37, 512
+    rng = np.random.default_rng(8)
+    packed = rng.integers(0, 256, (rows, K), dtype=np.uint8)
+    packed[(packed & 0x7F) == 0x7F] = 0x7E          # no NaN codes
+    sf = rng.integers(100, 150, orc.sf_bytes(rows, K, orc.MXFP8, orc.LINEAR), dtype=np.uint8)
+    want, _ = orc.dequantize(packed, sf, rows, K, orc.MXFP8, orc.LINEAR)
+    out = lb.lowbit_dequantize(dev_u8(packed), dev_u8(sf), lb.MXFP8, lb.LINEAR)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), want)
