@@ -10,6 +10,7 @@ If the native library is missing, every call raises: there is no fallback.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: producer / quantizer / dequantizer, LINEAR scales
@@ -110,9 +111,12 @@ def lowbit_sf_bytes(rows, k, fmt, layout):
     return int(lib().lowbit_sf_bytes(rows, k, fmt, layout))
 
 
-def _alloc_q(rows, k, fmt, layout, device, out_packed, out_sf):
+def _alloc_q(rows, k, fmt, layout, device, out_packed, out_sf, lead=None):
+    """Outputs the caller did not pass: packed codes shaped like the input's
+    leading dims (rows when none are given) and the flat scale buffer."""
     if out_packed is None:
-        out_packed = torch.empty((rows, k if fmt == MXFP8 else k // 2), dtype=torch.uint8, device=device)
+        shape = (tuple(lead) if lead is not None else (rows,)) + (k if fmt == MXFP8 else k // 2,)
+        out_packed = torch.empty(shape, dtype=torch.uint8, device=device)
     if out_sf is None:
         out_sf = torch.empty(lowbit_sf_bytes(rows, k, fmt, layout), dtype=torch.uint8, device=device)
     return out_packed, out_sf
@@ -136,8 +140,11 @@ def lowbit_add_rmsnorm_quant(input, residual, weight, eps=1e-6, fmt=NVFP4, layou
     _need(weight, dt, "weight")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
-    M, H = input.shape
-    out_packed, out_sf = _alloc_q(M, H, fmt, layout, input.device, out_packed, out_sf)
+    if residual.shape != input.shape:
+        raise ValueError(f"residual shape {tuple(residual.shape)} differs from input {tuple(input.shape)}")
+    lead, H = tuple(input.shape[:-1]), input.shape[-1]   # leading dims are rows
+    M = int(np.prod(lead)) if lead else 1
+    out_packed, out_sf = _alloc_q(M, H, fmt, layout, input.device, out_packed, out_sf, lead)
     name = "lowbit_add_rmsnorm_quant" if dt == torch.bfloat16 else "lowbit_add_rmsnorm_quant_fp16"
     _check(name, getattr(lib(), name)(
         _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, layout, _ptr(global_scale),
@@ -160,8 +167,9 @@ def lowbit_quantize(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=N
     _need(x, dt, "x")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
-    rows, K = x.shape
-    out_packed, out_sf = _alloc_q(rows, K, fmt, layout, x.device, out_packed, out_sf)
+    lead, K = tuple(x.shape[:-1]), x.shape[-1]           # leading dims are rows
+    rows = int(np.prod(lead)) if lead else 1
+    out_packed, out_sf = _alloc_q(rows, K, fmt, layout, x.device, out_packed, out_sf, lead)
     name = "lowbit_quantize" if dt == torch.bfloat16 else "lowbit_quantize_fp16"
     _check(name, getattr(lib(), name)(
         _ptr(x), rows, K, fmt, layout, _ptr(global_scale), _ptr(out_packed), _ptr(out_sf),

@@ -299,3 +299,43 @@ def test_dequantize_mxfp8_bit_exact(orc):
     out = lb.lowbit_dequantize(dev_u8(packed), dev_u8(sf), lb.MXFP8, lb.LINEAR)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), want)
+
+
+def test_mxfp8_element_encoding_exhaustive(orc):
+    """Every bf16 value with |v| <= 448 (and -0), as elements of blocks that
+    start with 448 (so e = 0 and v is encoded as it is): the device's E4M3
+    codes equal the oracle's nearest-even encoder's."""
+    pos = np.arange(0, 0x43E0 + 1, dtype=np.uint16)            # bf16 bit patterns 0 .. 448
+    vals = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
+    per = 31
+    nblk = ((vals.size + per - 1) // per + 15) // 16 * 16        # rows of 16 blocks (512 elements)
+    blocks = np.zeros((nblk, 32), np.uint16)
+    blocks[:, 0] = 0x43E0                                        # 448
+    flat = np.concatenate([vals, np.zeros(nblk * per - vals.size, np.uint16)])
+    blocks[:, 1:] = flat.reshape(nblk, per)
+    rows = blocks.reshape(-1, 32 * 16)
+    x = synth.from_bits(rows)
+    ref_p, ref_s = orc.quantize(synth.bits(x), orc.MXFP8, orc.LINEAR)
+    p, s = lb.lowbit_quantize(dev_bf16(x), lb.MXFP8, lb.LINEAR)
+    torch.cuda.synchronize()
+    assert (ref_s == 127).all()
+    assert np.array_equal(host_u8(s), ref_s)
+    assert np.array_equal(host_u8(p), ref_p)
+
+
+def test_producer_accepts_leading_dims(orc):
+    """(batch, tokens, H) tensors are rows of H: the same bytes as the 2-D call."""
+    x, r, w = synth.producer_inputs(24, 512, 77, outliers=True)
+    r3 = dev_bf16(r).reshape(2, 12, 512).clone()
+    p3, s3 = lb.lowbit_add_rmsnorm_quant(dev_bf16(x).reshape(2, 12, 512), r3, dev_bf16(w), EPS, lb.NVFP4,
+                                         lb.LINEAR)
+    r2 = dev_bf16(r)
+    p2, s2 = lb.lowbit_add_rmsnorm_quant(dev_bf16(x), r2, dev_bf16(w), EPS, lb.NVFP4, lb.LINEAR)
+    torch.cuda.synchronize()
+    assert p3.shape == (2, 12, 256)
+    assert torch.equal(p3.reshape(24, 256), p2) and torch.equal(s3, s2)
+    assert torch.equal(r3.reshape(24, 512), r2)
+    q3, t3 = lb.lowbit_quantize(dev_bf16(x).reshape(4, 6, 512), lb.MXFP4, lb.TILED)
+    q2, t2 = lb.lowbit_quantize(dev_bf16(x), lb.MXFP4, lb.TILED)
+    torch.cuda.synchronize()
+    assert q3.shape == (4, 6, 256) and torch.equal(q3.reshape(24, 256), q2) and torch.equal(t3, t2)
