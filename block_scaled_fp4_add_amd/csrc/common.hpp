@@ -109,13 +109,24 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float x) {
 __device__ __forceinline__ uint32_t e4m3_encode_signed(float v) {
   return ((__float_as_uint(v) >> 24) & 0x80u) | e4m3_encode_nonneg(fabsf(v));
 }
-// Eight fp32 -> eight E4M3 bytes (element i in byte i).
+// Eight fp32 -> eight E4M3 bytes (element i in byte i): each value clamped to
+// [-448, 448] (v_med3, keeps the sign of zero), then gfx950's packed FP8
+// conversion at unit scale, which rounds to nearest-even and keeps the sign
+// of a value that rounds to zero (checked on the device against the
+// nearest-even encoder above for every bf16 value up to 510 in magnitude).
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  s16x2_t r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                               __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f),
+                                               __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
 __device__ __forceinline__ uint2 e4m3x8(const float* v) {
   uint2 r;
-  r.x = e4m3_encode_signed(v[0]) | (e4m3_encode_signed(v[1]) << 8) | (e4m3_encode_signed(v[2]) << 16) |
-        (e4m3_encode_signed(v[3]) << 24);
-  r.y = e4m3_encode_signed(v[4]) | (e4m3_encode_signed(v[5]) << 8) | (e4m3_encode_signed(v[6]) << 16) |
-        (e4m3_encode_signed(v[7]) << 24);
+  r.x = e4m3x4(v[0], v[1], v[2], v[3]);
+  r.y = e4m3x4(v[4], v[5], v[6], v[7]);
   return r;
 }
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {

@@ -302,10 +302,11 @@ def test_dequantize_mxfp8_bit_exact(orc):
 
 
 def test_mxfp8_element_encoding_exhaustive(orc):
-    """Every bf16 value with |v| <= 448 (and -0), as elements of blocks that
-    start with 448 (so e = 0 and v is encoded as it is): the device's E4M3
-    codes equal the oracle's nearest-even encoder's."""
-    pos = np.arange(0, 0x43E0 + 1, dtype=np.uint16)            # bf16 bit patterns 0 .. 448
+    """Every bf16 value with |v| <= 510 (and -0), as elements of blocks that
+    start with 448 (so e = 0 and v is encoded as it is; values above 448
+    saturate): the device's E4M3 codes equal the oracle's nearest-even,
+    saturating encoder's."""
+    pos = np.arange(0, 0x43FF + 1, dtype=np.uint16)            # bf16 bit patterns 0 .. 510
     vals = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
     per = 31
     nblk = ((vals.size + per - 1) // per + 15) // 16 * 16        # rows of 16 blocks (512 elements)
