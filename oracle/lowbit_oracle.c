@@ -514,6 +514,7 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
 /* ------------------------------------------------------------------------- */
 /*
  * D[m,n] = alpha * sum_k Ahat[m,k] * Bhat[n,k], Ahat/Bhat dequantized exactly
+ * (NVFP4, MXFP4, or MXFP8 with one E4M3 byte per element)
  * (no global scale: the caller folds 1/(gsA*gsB) into alpha), then
  *   bias:          + bias[n]
  *   residual:      + residual[m,n]
@@ -525,10 +526,11 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
 static double dq(const uint8_t* packed, const uint8_t* sf, int64_t row, int64_t k, int64_t K,
                  int fmt, int layout) {
     int64_t B = block_of(fmt), nblk = K / B;
-    uint8_t byte = packed[row * (K / 2) + k / 2];
-    uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
     uint8_t sb = sf[orc_sf_offset(row, k / B, nblk, fmt, layout)];
     double s = (fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb);
+    if (fmt == ORC_MXFP8) return orc_e4m3_value(packed[row * K + k]) * s;   /* one byte per element */
+    uint8_t byte = packed[row * (K / 2) + k / 2];
+    uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
     return orc_e2m1_value(code) * s;
 }
 
@@ -551,7 +553,6 @@ int orc_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8
              int epi, const uint16_t* bias, const uint16_t* residual,
              double* out_ref, double* out_l1) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
-    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only */
     double* A = (double*)malloc(sizeof(double) * (size_t)(M * K));
     double* Bm = (double*)malloc(sizeof(double) * (size_t)(N * K));
     if (!A || !Bm) { free(A); free(Bm); return 2; }
@@ -586,7 +587,6 @@ int orc_gemm_entries(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, con
                      int64_t count, const int64_t* idx_m, const int64_t* idx_n,
                      double* out_ref, double* out_l1) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
-    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only */
     for (int64_t t = 0; t < count; t++)
         if (idx_m[t] < 0 || idx_m[t] >= M || idx_n[t] < 0 || idx_n[t] >= N) return 1;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -620,7 +620,7 @@ int orc_gemm_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, co
                       float* diag_y, float* diag_v, double* diag_l1, float* diag_spre,
                       float* diag_amax) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
-    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only */
+    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only: the output is NVFP4 for the next FP4 GEMM */
     if (N % 16 != 0) return 1;
     double* ref = (double*)malloc(sizeof(double) * (size_t)(M * N));
     double* l1 = (double*)malloc(sizeof(double) * (size_t)(M * N));

@@ -188,3 +188,53 @@ def test_gelu_fp4_output_is_nvfp4_of_the_gelu(orc):
             y = out["y"][m, kb * 16:(kb + 1) * 16]
             assert np.array_equal(orc.encode_with_scale(y, 0, 1.0, sb), codes[m, kb * 16:(kb + 1) * 16])
             assert sb == orc.e4m3_encode(min(np.float32(np.abs(y).max()) / np.float32(6), 448.0))
+
+
+# --- MXFP8 operands (E4M3 elements, UE8M0 32-blocks, LINEAR scales) -------------------------
+
+def e4m3_exact(b):
+    s, e, m = (b >> 7) & 1, (b >> 3) & 15, b & 7
+    v = Fraction(m, 8) * Fraction(1, 64) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def random_mxfp8(rng, rows, K):
+    packed = rng.integers(0, 256, (rows, K), dtype=np.uint8)
+    packed[(packed & 0x7F) == 0x7F] = 0x7E                      # no NaN codes
+    sf = rng.integers(118, 136, rows * (K // 32), dtype=np.uint8)
+    return packed, sf
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 2, 64), (2, 4, 160)])
+def test_gemm_mxfp8_brute_force_exact(orc, M, N, K):
+    """MXFP8 GEMM against exact rationals decoded from the bit fields here."""
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    a, sfa = random_mxfp8(rng, M, K)
+    b, sfb = random_mxfp8(rng, N, K)
+    A = [[e4m3_exact(int(a[m, k])) * Fraction(2) ** (int(sfa[m * (K // 32) + k // 32]) - 127) for k in range(K)]
+         for m in range(M)]
+    Bm = [[e4m3_exact(int(b[n, k])) * Fraction(2) ** (int(sfb[n * (K // 32) + k // 32]) - 127) for k in range(K)]
+          for n in range(N)]
+    alpha = 1.25
+    ref, l1 = orc.gemm(a, b, sfa, sfb, M, N, K, orc.MXFP8, orc.LINEAR, orc.LINEAR, alpha=alpha)
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(alpha) * sum(A[m][k] * Bm[n][k] for k in range(K))
+            absum = Fraction(alpha) * sum(abs(A[m][k] * Bm[n][k]) for k in range(K))
+            assert abs(Fraction(ref[m, n]) - exact) <= absum * Fraction(1, 2 ** 50)
+            assert abs(Fraction(l1[m, n]) - absum) <= absum * Fraction(1, 2 ** 50)
+
+
+def test_gemm_mxfp8_closed_forms(orc):
+    """All elements 1.0 (0x38) at unit scale give alpha * K; raising one row's
+    first scale byte by one adds exactly that block's contribution again."""
+    M, N, K = 2, 3, 96
+    a = np.full((M, K), 0x38, np.uint8)
+    b = np.full((N, K), 0x38, np.uint8)
+    sfa = np.full(M * 3, 127, np.uint8)
+    sfb = np.full(N * 3, 127, np.uint8)
+    ref, _ = orc.gemm(a, b, sfa, sfb, M, N, K, orc.MXFP8, orc.LINEAR, orc.LINEAR, alpha=0.5)
+    assert np.all(ref == 0.5 * K)
+    sfa[3] = 128                     # row 1, block 0: doubled
+    ref, _ = orc.gemm(a, b, sfa, sfb, M, N, K, orc.MXFP8, orc.LINEAR, orc.LINEAR, alpha=1.0)
+    assert np.all(ref[0] == K) and np.all(ref[1] == K + 32)
