@@ -559,7 +559,6 @@ constexpr int kPThreads = kPWM * kPWN * 64;
 constexpr int kPStage = (kPBM + kPBN) * kSSBytes;         // 64 KiB per LDS buffer
 constexpr int kPUnits = (kPBM + kPBN) * kSSBytes / 16;    // 16-byte units per stage
 constexpr int kPLoads = kPUnits / kPThreads;              // 16 per thread per superstep
-constexpr int kOOB = 0x7FFFFFF0;                          // offset beyond any operand buffer
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -908,7 +907,6 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     }
   };
   using kWithSf = std::integral_constant<bool, true>;
-  using kNoSf = std::integral_constant<bool, false>;
 
   // Steady state: when stage k and the scales of superstep k/2 lie wholly
   // inside K, a lane's DMA offsets do not depend on k; the per-stage advance
@@ -1064,7 +1062,6 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using ILS = std::integral_constant<int, kLoadsAB + SFL>;
   using ILSP = std::integral_constant<int, kLoadsAB + SFL + kPf>;
   using IF = std::integral_constant<int, TI + TJ>;           // fragment reads of a quarter
   using IFS = std::integral_constant<int, 4 * (TI + TJ)>;    // fragment + scale reads
