@@ -562,6 +562,7 @@ def main():
             "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode,
             "variants": variants}
     print(json.dumps(line), flush=True)
+    EVENTS.release()
 
 
 if __name__ == "__main__":
