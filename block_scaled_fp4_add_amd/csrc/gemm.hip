@@ -1171,7 +1171,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 // ===========================================================================
 // Decode schedule (weights as the MFMA row operand, K split across waves)
 // ===========================================================================
-template <int FMT, int MT, int W, int EPI>
+template <int FMT, int MT, int W, int EPI, bool DB = true>
 __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float red[W * MT * 64 * 16];
   __shared__ __attribute__((aligned(16))) float tile[MT * 32 * kEpiPitch];
@@ -1187,9 +1187,10 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < MT; i++) acc[0][i] = v16f{};
 
-  // two supersteps in flight per wave: the loads of superstep ss + W are
+  // DB: two supersteps in flight per wave -- the loads of superstep ss + W are
   // issued before the MFMAs of ss (buffers 0 / 1 alternate, unrolled by two
-  // so that every register index stays static)
+  // so that every register index stays static).  Otherwise one superstep at a
+  // time, which leaves registers for twice the waves (see the launcher).
   Frag fw[2][1], fx[2][MT];
   SfWord<FMT> sw[2][1], sx[2][MT];
   auto load = [&](auto bufc, int64_t ss) {
@@ -1209,13 +1210,20 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   int64_t ss = wave;
-  if (ss < nss) load(B0{}, ss);
-  for (; ss < nss; ss += 2 * W) {
-    if (ss + W < nss) load(B1{}, ss + W);
-    superstep_mma<FMT, 1, MT>(acc, fw[0], fx[0], sw[0], sx[0]);
-    if (ss + W >= nss) break;
-    if (ss + 2 * W < nss) load(B0{}, ss + 2 * W);
-    superstep_mma<FMT, 1, MT>(acc, fw[1], fx[1], sw[1], sx[1]);
+  if constexpr (DB) {
+    if (ss < nss) load(B0{}, ss);
+    for (; ss < nss; ss += 2 * W) {
+      if (ss + W < nss) load(B1{}, ss + W);
+      superstep_mma<FMT, 1, MT>(acc, fw[0], fx[0], sw[0], sx[0]);
+      if (ss + W >= nss) break;
+      if (ss + 2 * W < nss) load(B0{}, ss + 2 * W);
+      superstep_mma<FMT, 1, MT>(acc, fw[1], fx[1], sw[1], sx[1]);
+    }
+  } else {
+    for (; ss < nss; ss += W) {
+      load(B0{}, ss);
+      superstep_mma<FMT, 1, MT>(acc, fw[0], fx[0], sw[0], sx[0]);
+    }
   }
 
   // cross-wave sum of the partial C^T tiles
@@ -1266,13 +1274,20 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
       hipLaunchKernelGGL((gemm_decode_kernel<FMT, MT, W, EPI>), dim3(grid), dim3(W * 64), 0, s, g); \
       return hipGetLastError();                                                                \
     }
-    // NVFP4 with one M-tile: its 8-wave workgroups (145 VGPRs) fit once per
-    // CU, so past 256 workgroups 4-wave ones (three per CU) finish sooner:
-    // measured 25.7 against 28.1 us at N = 17408, K = 5120, and 31.0 against
-    // 26.0 us the other way round at N = 5120 (160 workgroups)
-    if (FMT == kNVFP4 && mt == 1 && grid > 256) {
-      hipLaunchKernelGGL((gemm_decode_kernel<FMT, 1, 4, EPI>), dim3(grid), dim3(4 * 64), 0, s, g);
-      return hipGetLastError();
+    // NVFP4 is bound by its dequantization VALU work: 8 single-buffered waves
+    // (two per SIMD) beat double-buffered ones at 1, 3 and 4 M-tiles, e.g.
+    // (128, 17408, 5120) GELU -> FP4 87.6 -> 66.3 us, (128, 5120, 17408) 86.3
+    // -> 65.8 us, (1, 5120, 17408) 26.0 -> 23.4 us.  MXFP4, bound by load
+    // latency, keeps two supersteps in flight (its single-buffered forms
+    // measured 15-35% slower), as does NVFP4 at 2 M-tiles.
+    if constexpr (FMT == kNVFP4) {
+#define LB_DEC_SB(MT)                                                                                  \
+      if (mt == MT) {                                                                                  \
+        hipLaunchKernelGGL((gemm_decode_kernel<FMT, MT, 8, EPI, false>), dim3(grid), dim3(8 * 64), 0, s, g); \
+        return hipGetLastError();                                                                      \
+      }
+      LB_DEC_SB(1) LB_DEC_SB(3) LB_DEC_SB(4)
+#undef LB_DEC_SB
     }
     LB_DEC(1, 8) LB_DEC(2, 8) LB_DEC(3, 4) LB_DEC(4, 4)
 #undef LB_DEC

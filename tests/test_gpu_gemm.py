@@ -57,8 +57,9 @@ def run_gemm(orc, M, N, K, fmt, la, lb_, epi, variant, seed, alpha=1.0, sample=N
 # small shapes, compared in full; they span several tiles and ragged tails,
 # and (the last three) give the decode schedule's waves odd superstep counts
 # (K / 256 = 9, 17, 18 over 8, 8 and 4 waves); the two with N > 8192 put
-# more than 256 workgroups on the decode schedule, which NVFP4 runs with
-# 4-wave workgroups
+# more than 256 workgroups on the decode schedule.  NVFP4 runs 1, 3 and 4
+# M-tiles with 8 single-buffered waves (M = 1, 3, 65-128 below), 2 M-tiles
+# double-buffered.
 SHAPES = [(8, 128, 256), (1, 32, 32), (1, 200, 1056), (1, 17, 4096), (5, 40, 96), (33, 70, 320), (128, 256, 512), (130, 200, 768),
           (41, 4608, 1536), (200, 96, 1056), (3, 96, 2304), (40, 64, 4352), (100, 48, 4608),
           (1, 8224, 544), (2, 9000, 1056)]
