@@ -62,7 +62,7 @@ def run_gemm(orc, M, N, K, fmt, la, lb_, epi, variant, seed, alpha=1.0, sample=N
 # double-buffered.
 SHAPES = [(8, 128, 256), (1, 32, 32), (1, 200, 1056), (1, 17, 4096), (5, 40, 96), (33, 70, 320), (128, 256, 512), (130, 200, 768),
           (41, 4608, 1536), (200, 96, 1056), (3, 96, 2304), (40, 64, 4352), (100, 48, 4608),
-          (1, 8224, 544), (2, 9000, 1056)]
+          (1, 8224, 544), (2, 9000, 1056), (70, 200, 2560), (96, 136, 1568)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -178,7 +178,8 @@ def run_gelu_fp4(orc, M, N, K, fmt, variant, out_layout, seed, gs_out=1.0):
         assert checkers.tiled_padding_is_zero(orc, host_u8(s), M, N // 16, 0)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (33, 272, 512), (130, 176, 320), (1, 8256, 256)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (33, 272, 512), (130, 176, 320), (1, 8256, 256), (96, 272, 512),
+                                   (128, 160, 1024)])
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("out_layout", [0, 1])
 def test_gemm_gelu_fp4(orc, M, N, K, fmt, out_layout):
