@@ -246,7 +246,8 @@ def build_variant_stages():
     """Format variants of the step's kernels, timed beside the step and
     reported apart from `value`, at the 4096 x 4096 producer workload with 4
     rotating input sets like the bf16 stage: the NVFP4 producer on fp16
-    tensors (same draws, rounded to fp16) and the producer with MXFP8 output."""
+    tensors (same draws, rounded to fp16), the producer with MXFP8 output, and
+    the NVFP4 producer writing both scale layouts in one pass."""
     dev = "cuda"
     c = synth.NVFP4_PRODUCER
     M, H = c["M"], c["H"]
@@ -286,6 +287,22 @@ def build_variant_stages():
 
     stages.append(Stage(f"add_rmsnorm_mxfp8_{M}x{H}", producer8, "hbm", producer_bytes(M, H, 32, 1.0), "B",
                         HBM_PEAK))
+
+    # the bf16 NVFP4 producer writing TILED and LINEAR scales in one pass: one
+    # more scale byte per block (4096 rows and 256 blocks per row: no padding)
+    pkb = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    sft = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lb.TILED), dtype=torch.uint8, device=dev)
+    sfl = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lb.LINEAR), dtype=torch.uint8, device=dev)
+    itb = {"i": 0}
+
+    def producer_both():
+        x, r, w = bsets[itb["i"] % 4]
+        itb["i"] += 1
+        lb.lowbit_add_rmsnorm_quant_both_sf(x, r, w, EPS, lb.NVFP4, global_scale=gs, out_packed=pkb,
+                                            out_sf_tiled=sft, out_sf_linear=sfl)
+
+    stages.append(Stage(f"add_rmsnorm_nvfp4_both_sf_{M}x{H}", producer_both, "hbm",
+                        producer_bytes(M, H, 16) + M * H // 16, "B", HBM_PEAK))
     return stages
 
 
@@ -467,6 +484,38 @@ def measured_traffic(stage_name):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def copy_probe():
+    """An elementwise kernel that reads and writes COPY_PROBE_BYTES each, three
+    times (torch.add: a plain streaming kernel; copy_ would go to the runtime's
+    blit path); 1 GiB so that what the fill leaves in L2 is negligible."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def counter_run(args):
+    """Launches for a counter profiler (rocprofv3 --pmc): every selected stage
+    args.counters times back to back, untimed, then the copy probe."""
+    stages = build_stages()
+    if not args.no_decode:
+        stages += build_decode_stages() + build_variant_stages()
+    sel = [k for k in args.only.split(",") if k]
+    torch.cuda.synchronize()
+    for s in stages:
+        if sel and not any(k in s.name for k in sel):
+            continue
+        for _ in range(args.counters):
+            s.fn()
+        torch.cuda.synchronize()
+        log(f"[bench] ran {s.name} x{args.counters}")
+    if args.copy_probe:
+        copy_probe()
+        log("[bench] ran copy probe")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -478,6 +527,12 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed region, run a 1 GiB read + 1 GiB write elementwise kernel "
                          "three times: the known-size kernel that calibrates the HBM byte counters")
+    ap.add_argument("--counters", type=int, default=0, metavar="REPS",
+                    help="counter-collection run for a profiler: build the stages (the decode and format "
+                         "variants too unless --no-decode), launch each selected stage REPS times with no "
+                         "timing, then the copy probe if asked, and print no JSON line")
+    ap.add_argument("--only", default="",
+                    help="with --counters: comma-separated substrings; run only stages whose name has one")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -490,6 +545,9 @@ def main():
     global EVENTS
     torch.cuda.init()
     EVENTS = HipEvents()
+    if args.counters > 0:
+        counter_run(args)
+        return
     log("[bench] building inputs")
     stages = build_stages()
     torch.cuda.synchronize()
@@ -505,15 +563,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     if args.copy_probe:
-        # an elementwise kernel that reads and writes COPY_PROBE_BYTES each
-        # (torch.add: a plain streaming kernel; copy_ would go to the runtime's
-        # blit path); 1 GiB so that what the fill leaves in L2 is negligible
-        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.add(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe()
     ideal = sum(s.ideal_s() for s in stages)
     value = 100.0 * ideal / (wall / args.steps)
     kernels = report(stages)

@@ -26,6 +26,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "misaligned pointer", 3: "unsuppor
 EXPORTS = (
     "lowbit_status_str", "lowbit_sf_bytes", "lowbit_add_rmsnorm_quant", "lowbit_quantize",
     "lowbit_add_rmsnorm_quant_fp16", "lowbit_quantize_fp16",
+    "lowbit_add_rmsnorm_quant_both_sf", "lowbit_add_rmsnorm_quant_both_sf_fp16",
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
     "lowbit_gemm_pick_variant",
@@ -59,6 +60,9 @@ def lib():
         L.lowbit_quantize.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]
         L.lowbit_add_rmsnorm_quant_fp16.restype = _int
         L.lowbit_add_rmsnorm_quant_fp16.argtypes = L.lowbit_add_rmsnorm_quant.argtypes
+        for name in ("lowbit_add_rmsnorm_quant_both_sf", "lowbit_add_rmsnorm_quant_both_sf_fp16"):
+            getattr(L, name).restype = _int
+            getattr(L, name).argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _int, _vp, _vp, _vp, _vp, _vp]
         L.lowbit_quantize_fp16.restype = _int
         L.lowbit_quantize_fp16.argtypes = L.lowbit_quantize.argtypes
         L.lowbit_dequantize.restype = _int
@@ -158,6 +162,39 @@ def lowbit_add_rmsnorm_quant_fp16(input, residual, weight, eps=1e-6, fmt=NVFP4, 
     _need(input, torch.float16, "input")
     return lowbit_add_rmsnorm_quant(input, residual, weight, eps, fmt, layout, global_scale, out_packed,
                                     out_sf, stream)
+
+
+def lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps=1e-6, fmt=NVFP4, global_scale=None,
+                                     out_packed=None, out_sf_tiled=None, out_sf_linear=None, stream=None):
+    """The producer with its scales in both layouts, one pass: bf16 tensors
+    call lowbit_add_rmsnorm_quant_both_sf, fp16 ones the _fp16 entry point.
+    Returns (packed uint8, TILED scales uint8, LINEAR scales uint8)."""
+    dt = _in_dtype(input, "input")
+    _need(input, dt, "input")
+    _need(residual, dt, "residual")
+    _need(weight, dt, "weight")
+    if global_scale is not None:
+        _need(global_scale, torch.float32, "global_scale")
+    if residual.shape != input.shape:
+        raise ValueError(f"residual shape {tuple(residual.shape)} differs from input {tuple(input.shape)}")
+    lead, H = tuple(input.shape[:-1]), input.shape[-1]
+    M = int(np.prod(lead)) if lead else 1
+    out_packed, out_sf_tiled = _alloc_q(M, H, fmt, TILED, input.device, out_packed, out_sf_tiled, lead)
+    if out_sf_linear is None:
+        out_sf_linear = torch.empty(lowbit_sf_bytes(M, H, fmt, LINEAR), dtype=torch.uint8, device=input.device)
+    name = "lowbit_add_rmsnorm_quant_both_sf" + ("" if dt == torch.bfloat16 else "_fp16")
+    _check(name, getattr(lib(), name)(
+        _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, _ptr(global_scale),
+        _ptr(out_packed), _ptr(out_sf_tiled), _ptr(out_sf_linear), _stream(stream)))
+    return out_packed, out_sf_tiled, out_sf_linear
+
+
+def lowbit_add_rmsnorm_quant_both_sf_fp16(input, residual, weight, eps=1e-6, fmt=NVFP4, global_scale=None,
+                                          out_packed=None, out_sf_tiled=None, out_sf_linear=None, stream=None):
+    """The fp16 form by name (lowbit_add_rmsnorm_quant_both_sf dispatches on dtype)."""
+    _need(input, torch.float16, "input")
+    return lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps, fmt, global_scale, out_packed,
+                                            out_sf_tiled, out_sf_linear, stream)
 
 
 def lowbit_quantize(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=None, out_sf=None,

@@ -136,9 +136,11 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
 
 static lowbit_status producer(const void* input, void* residual, const void* weight, int64_t M, int64_t H,
                               float eps, lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
-                              uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t stream) {
+                              uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_lin, int in_f16,
+                              hipStream_t stream) {
   if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
   if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
+  if (out_sf_lin && layout != LOWBIT_SF_TILED) return LOWBIT_EINVAL;
   if (M < 0) return LOWBIT_ESHAPE;
   if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
   if (H < 64 || H % block_of(fmt) != 0 || H > kMaxRowElems) return LOWBIT_ESHAPE;
@@ -150,7 +152,7 @@ static lowbit_status producer(const void* input, void* residual, const void* wei
   return from_hip(lowbit::launch_add_rmsnorm_quant(
       static_cast<const uint16_t*>(input), static_cast<uint16_t*>(residual),
       static_cast<const uint16_t*>(weight), M, H, eps, fmt, layout, global_scale, out_packed, out_sf,
-      in_f16, stream));
+      out_sf_lin, in_f16, stream));
 }
 
 static lowbit_status quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt, lowbit_sf_layout layout,
@@ -194,14 +196,35 @@ lowbit_status lowbit_add_rmsnorm_quant(const void* input, void* residual, const 
                                        int64_t H, float eps, lowbit_format fmt, lowbit_sf_layout layout,
                                        const float* global_scale, uint8_t* out_packed, uint8_t* out_sf,
                                        hipStream_t stream) {
-  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf, 0, stream);
+  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf, nullptr,
+                  0, stream);
 }
 
 lowbit_status lowbit_add_rmsnorm_quant_fp16(const void* input, void* residual, const void* weight, int64_t M,
                                             int64_t H, float eps, lowbit_format fmt, lowbit_sf_layout layout,
                                             const float* global_scale, uint8_t* out_packed, uint8_t* out_sf,
                                             hipStream_t stream) {
-  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf, 1, stream);
+  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf, nullptr,
+                  1, stream);
+}
+
+lowbit_status lowbit_add_rmsnorm_quant_both_sf(const void* input, void* residual, const void* weight, int64_t M,
+                                               int64_t H, float eps, lowbit_format fmt, const float* global_scale,
+                                               uint8_t* out_packed, uint8_t* out_sf_tiled, uint8_t* out_sf_linear,
+                                               hipStream_t stream) {
+  if (M > 0 && !out_sf_linear) return LOWBIT_EINVAL;
+  return producer(input, residual, weight, M, H, eps, fmt, LOWBIT_SF_TILED, global_scale, out_packed,
+                  out_sf_tiled, out_sf_linear, 0, stream);
+}
+
+lowbit_status lowbit_add_rmsnorm_quant_both_sf_fp16(const void* input, void* residual, const void* weight,
+                                                    int64_t M, int64_t H, float eps, lowbit_format fmt,
+                                                    const float* global_scale, uint8_t* out_packed,
+                                                    uint8_t* out_sf_tiled, uint8_t* out_sf_linear,
+                                                    hipStream_t stream) {
+  if (M > 0 && !out_sf_linear) return LOWBIT_EINVAL;
+  return producer(input, residual, weight, M, H, eps, fmt, LOWBIT_SF_TILED, global_scale, out_packed,
+                  out_sf_tiled, out_sf_linear, 1, stream);
 }
 
 lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt,

@@ -7,10 +7,13 @@
 
 namespace lowbit {
 
-// in_f16: the 16-bit input tensors (x, residual, weight) are fp16, else bf16
+// in_f16: the 16-bit input tensors (x, residual, weight) are fp16, else bf16.
+// out_sf_lin: nullptr, or (with layout TILED) a second scale buffer that gets
+// the same bytes in the LINEAR layout.
 hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w, int64_t M,
                                     int64_t H, float eps, int fmt, int layout, const float* gs,
-                                    uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s);
+                                    uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_lin, int in_f16,
+                                    hipStream_t s);
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
                            const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s);

@@ -44,6 +44,7 @@ struct RowArgs {
   const float* gs;         // NVFP4 global scale or nullptr
   uint8_t* out_packed;
   uint8_t* out_sf;
+  uint8_t* out_sf_lin;     // nullptr, or a LINEAR copy of the scales beside TILED out_sf
 };
 
 // Quantize the NBL blocks a lane owns (values y in registers) and store them.
@@ -67,6 +68,7 @@ __device__ __forceinline__ void quant_store_block(const float* y, float gs, int6
     reinterpret_cast<uint4*>(dst)[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
     reinterpret_cast<uint4*>(dst)[1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
     a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = (uint8_t)sb;
+    if (a.out_sf_lin != nullptr) a.out_sf_lin[row * nblk + kb] = (uint8_t)sb;
     return;
   }
   uint8_t* dst = a.out_packed + row * (a.H / 2) + kb * (B / 2);
@@ -84,6 +86,7 @@ __device__ __forceinline__ void quant_store_block(const float* y, float gs, int6
     *reinterpret_cast<uint4*>(dst) = p;
   }
   a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = (uint8_t)sb;
+  if (a.out_sf_lin != nullptr) a.out_sf_lin[row * nblk + kb] = (uint8_t)sb;
 }
 
 // FUSED: add + RMSNorm + quant.  Otherwise: quantize x as it is.  F16: the
@@ -237,6 +240,18 @@ constexpr int kWgMinRows = 256;     // fewer rows: the row-split form has more p
 constexpr int kWgMaxWaves = 16;     // H <= 16384
 constexpr int kWgVecs = 2;          // 16-byte vectors per thread and tensor
 
+// TILED: the row of workgroup b.  Workgroups start on XCD b % 8; this order
+// puts the 32 rows of each 32-row scale group on one XCD, whose L2 then
+// merges the group's scale bytes into whole lines before writing them back
+// (in launch order, each line was written back partially by up to 8 L2s).
+// A bijection on [0, G): blocks past the last multiple of 256 keep their row.
+__device__ __forceinline__ int64_t tiled_row_of_block(int64_t b, int64_t G) {
+  const int64_t full = G & ~int64_t(255);
+  if (b >= full) return b;
+  const int64_t x = b & 7, i = b >> 3;
+  return ((x + 8 * (i >> 5)) << 5) + (i & 31);
+}
+
 template <int FMT, int NW, bool FUSED, bool F16>
 __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   constexpr int B = FmtTraits<FMT>::B;
@@ -245,7 +260,7 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   constexpr int V = kWgVecs;
   __shared__ double part[NW];
   const int t = threadIdx.x, lane = t % kWave;
-  const int64_t row = blockIdx.x;
+  const int64_t row = (a.layout == kTiled) ? tiled_row_of_block(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t H = a.H, nblk = H / B, nvec = H / 8;
   const int64_t nblk_pad = ((nblk + 7) >> 3) << 3;
   if (row >= a.M) {
@@ -340,6 +355,7 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
         const int in_grp = (FMT == kNVFP4) ? ((jj >> 2) << 7) + (jj & 3)
                                            : (((jj >> 1) & 1) << 7) + (jj & 1) + ((jj >> 2) << 1);
         sf_row[(a.layout == kLinear) ? kb : ((kb >> 3) << 8) + in_grp] = (uint8_t)sb;
+        if (a.out_sf_lin != nullptr) a.out_sf_lin[row * nblk + kb] = (uint8_t)sb;
       }
     }
   }
@@ -470,8 +486,9 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
 
 hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const uint16_t* w, int64_t M,
                                     int64_t H, float eps, int fmt, int layout, const float* gs,
-                                    uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
-  RowArgs a{x, residual, w, M, H, M, eps, layout, gs, out_packed, out_sf};
+                                    uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_lin, int in_f16,
+                                    hipStream_t s) {
+  RowArgs a{x, residual, w, M, H, M, eps, layout, gs, out_packed, out_sf, out_sf_lin};
   if (layout == kTiled) a.rows_grid = (M + 31) / 32 * 32;
   if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, true, true>(a, s) : dispatch_row<kMXFP8, true, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, true>(a, s) : dispatch_row<kMXFP4, true, true>(a, s);
@@ -480,7 +497,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
                            const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
-  RowArgs a{x, nullptr, nullptr, rows, K, rows, 0.0f, layout, gs, out_packed, out_sf};
+  RowArgs a{x, nullptr, nullptr, rows, K, rows, 0.0f, layout, gs, out_packed, out_sf, nullptr};
   if (layout == kTiled) a.rows_grid = (rows + 31) / 32 * 32;
   if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, false, true>(a, s) : dispatch_row<kMXFP8, false, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, true>(a, s) : dispatch_row<kMXFP4, false, true>(a, s);

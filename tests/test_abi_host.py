@@ -125,6 +125,27 @@ def test_producer_argument_order(buf):
         assert call(4, 256) == EDEVICE
 
 
+def test_producer_both_sf_argument_order(buf):
+    L = lb.lib()
+
+    def call(M, H, fmt=1, gs=None, lin=True, x=0, fp16=False):
+        fn = L.lowbit_add_rmsnorm_quant_both_sf_fp16 if fp16 else L.lowbit_add_rmsnorm_quant_both_sf
+        return fn(buf.at(x), buf.at(), buf.at(), M, H, 1e-6, fmt, gs, buf.at(), buf.at(),
+                  buf.at() if lin else None, None)
+
+    for fp16 in (False, True):
+        assert call(4, 256, fmt=2, fp16=fp16) == EINVAL            # MXFP8: no TILED layout
+        assert call(4, 256, fmt=7, fp16=fp16) == EINVAL
+        assert call(4, 256, fmt=1, gs=buf.at(), fp16=fp16) == EINVAL
+        assert call(4, 256, lin=False, fp16=fp16) == EINVAL        # no LINEAR buffer
+        assert call(4, 48, fp16=fp16) == ESHAPE
+        assert call(4, 256, x=8, fp16=fp16) == EALIGN
+        assert call(0, 256, lin=False, fp16=fp16) == OK            # M == 0: nothing is written
+        if NO_DEVICE:
+            assert call(4, 256, fp16=fp16) == EDEVICE
+            assert call(4, 256, fmt=0, gs=buf.at(), fp16=fp16) == EDEVICE
+
+
 def test_gemm_argument_order(buf):
     L = lb.lib()
     a, b, sa, sb, out = buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288), buf.at(16384)
