@@ -52,9 +52,10 @@ def run_both(orc, M, H, fmt, seed, use_gs, dtype=torch.bfloat16):
 
 
 # both producer forms (row-split below 256 rows, a workgroup per row above),
-# M % 32 != 0 for TILED padding rows, nblk % 8 != 0 for padding blocks
+# M % 32 != 0 for TILED padding rows, nblk % 8 != 0 for padding blocks, and the
+# 4096 x 4096 workload the benchmark times
 SHAPES = [(1, 64), (8, 256), (33, 1024), (5, 5120), (70, 4096), (300, 1536), (257, 2560), (520, 5632),
-          (2049, 512), (1000, 5120)]
+          (2049, 512), (1000, 5120), (4096, 4096)]
 
 
 @pytest.mark.parametrize("M,H", SHAPES)
