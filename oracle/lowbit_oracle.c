@@ -36,7 +36,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1, ORC_MXFP8 = 2 };
+enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1, ORC_MXFP8 = 2, ORC_NVFP4_B32 = 3 };
 enum { ORC_SF_LINEAR = 0, ORC_SF_TILED = 1 };
 enum { ORC_EPI_NONE = 0, ORC_EPI_BIAS = 1, ORC_EPI_RESIDUAL = 2, ORC_EPI_BIAS_RESIDUAL = 3,
        ORC_EPI_BIAS_GELU = 4 };
@@ -195,6 +195,10 @@ double orc_ue8m0_value(uint8_t b) {
  */
 static int64_t block_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
 
+/* The formats whose block scale is E4M3 with the global scale folded in:
+ * NVFP4, and the same rule on 32-element blocks. */
+static int e4m3_scaled(int fmt) { return fmt == ORC_NVFP4 || fmt == ORC_NVFP4_B32; }
+
 int64_t orc_sf_bytes(int64_t rows, int64_t k, int fmt, int layout) {
     int64_t nblk = k / block_of(fmt);
     if (layout == ORC_SF_LINEAR) return rows * nblk;
@@ -222,6 +226,8 @@ int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int fmt, int layout
  *     s_pre = min(fl32(fl32(gs * amax) / 6), 448);  sbyte = E4M3(s_pre)
  *     inv   = sdec == 0 ? 0 : fl32(fl32(1 / sdec) * gs)
  *     v_i   = fl32(y_i * inv);  code_i = E2M1(v_i)
+ * NVFP4 with 32-element blocks (the page's producer takes an E4M3 scale
+ * format override at block size 32): the NVFP4 rule above, amax over 32.
  * MXFP4 (B = 32, UE8M0 scale, OCP MX rule, gs unused):
  *     e = clamp(floor(log2 amax) - 2, -127, 127)  (amax == 0 gives -127)
  *     sbyte = e + 127;  v_i = y_i * 2^-e (exact);  code_i = E2M1(v_i)
@@ -239,7 +245,7 @@ static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes
         if (a > amax) amax = a;
     }
     if (amax_out) *amax_out = amax;
-    if (fmt == ORC_NVFP4) {
+    if (e4m3_scaled(fmt)) {
         volatile float t = gs * amax;            /* fl32(gs * amax) */
         volatile float s_pre = t / 6.0f;         /* fl32(. / 6) */
         float sp = s_pre;
@@ -287,7 +293,7 @@ static void quant_block(const float* y, int B, int fmt, float gs, uint8_t* codes
  * (optional) receives the pre-rounding values. */
 void orc_encode_with_scale(const float* y, int B, int fmt, float gs, uint8_t sbyte, uint8_t* codes,
                            float* v_out) {
-    if (fmt == ORC_NVFP4) {
+    if (e4m3_scaled(fmt)) {
         float sdec = (float)orc_e4m3_value(sbyte);
         float inv;
         if (sdec == 0.0f) {
@@ -343,9 +349,10 @@ static void quant_row(const float* y, int64_t row, int64_t n, int fmt, float gs,
 
 static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
     if (rows < 0 || k <= 0) return 1;
-    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4 && fmt != ORC_MXFP8) return 1;
+    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4 && fmt != ORC_MXFP8 && fmt != ORC_NVFP4_B32) return 1;
     if (layout != ORC_SF_LINEAR && layout != ORC_SF_TILED) return 1;
-    if (fmt == ORC_MXFP8 && layout != ORC_SF_LINEAR) return 1;   /* MXFP8 scales: LINEAR only */
+    /* MXFP8 and 32-block NVFP4 scales: LINEAR only */
+    if ((fmt == ORC_MXFP8 || fmt == ORC_NVFP4_B32) && layout != ORC_SF_LINEAR) return 1;
     if (k % block_of(fmt) != 0) return 1;
     return 0;
 }
@@ -364,7 +371,7 @@ static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
  *  3. y_i = fl32(fl32(bf16(h_i) * rstd) * w_i)  (the page reads h back from its
  *     bf16 shared-memory copy and computes h * rstd * w)
  *  4. per block: quant_block above; scales go to out_sf in the layout.
- * gs: the global scale value (NVFP4; ignored for MXFP4).
+ * gs: the global scale value (NVFP4 and its 32-block form; ignored for MXFP4 and MXFP8).
  * Optional diagnostics (NULL to skip): y (M*H fp32), v (M*H fp32),
  * amax and s_pre (M*H/B fp32 each), rstd (M fp32).
  */
@@ -498,10 +505,10 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
                 q = orc_e2m1_value((i % 2 == 0) ? (byte & 15) : (byte >> 4));
             }
             /* q * scale is exact in binary64 (and in binary32) */
-            double v = q * ((fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb));
+            double v = q * (e4m3_scaled(fmt) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb));
             /* NVFP4: one division by gs; the binary64 quotient rounded to
              * binary32 equals the correctly rounded binary32 quotient */
-            if (fmt == ORC_NVFP4) v = v / (double)gs;
+            if (e4m3_scaled(fmt)) v = v / (double)gs;
             if (out_f64) out_f64[m * K + i] = v;
             if (out_bf16) out_bf16[m * K + i] = orc_f32_to_bf16((float)v);
         }
@@ -527,7 +534,7 @@ static double dq(const uint8_t* packed, const uint8_t* sf, int64_t row, int64_t 
                  int fmt, int layout) {
     int64_t B = block_of(fmt), nblk = K / B;
     uint8_t sb = sf[orc_sf_offset(row, k / B, nblk, fmt, layout)];
-    double s = (fmt == ORC_NVFP4) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb);
+    double s = e4m3_scaled(fmt) ? orc_e4m3_value(sb) : orc_ue8m0_value(sb);
     if (fmt == ORC_MXFP8) return orc_e4m3_value(packed[row * K + k]) * s;   /* one byte per element */
     uint8_t byte = packed[row * (K / 2) + k / 2];
     uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
@@ -620,7 +627,8 @@ int orc_gemm_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, co
                       float* diag_y, float* diag_v, double* diag_l1, float* diag_spre,
                       float* diag_amax) {
     if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
-    if (fmt == ORC_MXFP8) return 1;   /* FP4 operands only: the output is NVFP4 for the next FP4 GEMM */
+    /* NVFP4 or MXFP4 operands only: the output is NVFP4 for the next FP4 GEMM */
+    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return 1;
     if (N % 16 != 0) return 1;
     double* ref = (double*)malloc(sizeof(double) * (size_t)(M * N));
     double* l1 = (double*)malloc(sizeof(double) * (size_t)(M * N));

@@ -7,7 +7,9 @@ numpy host arrays; bf16 and fp16 tensors travel as their uint16 bit patterns
 
 Enum values: fmt NVFP4 = 0 (16-blocks, E4M3 scales), MXFP4 = 1 (32-blocks,
 UE8M0 scales), MXFP8 = 2 (32-blocks, UE8M0 scales, E4M3 elements, one byte
-each; LINEAR scales only, no GEMM); layout LINEAR = 0, TILED = 1; epilogue NONE = 0, BIAS = 1,
+each; LINEAR scales only, no GEMM), NVFP4_B32 = 3 (the NVFP4 rule on
+32-blocks: E4M3 scales with the global scale; LINEAR scales only, no GEMM);
+layout LINEAR = 0, TILED = 1; epilogue NONE = 0, BIAS = 1,
 RESIDUAL = 2, BIAS_RESIDUAL = 3, BIAS_GELU = 4.
 """
 import ctypes
@@ -17,7 +19,7 @@ import numpy as np
 
 from . import build as _build
 
-NVFP4, MXFP4, MXFP8 = 0, 1, 2
+NVFP4, MXFP4, MXFP8, NVFP4_B32 = 0, 1, 2, 3
 LINEAR, TILED = 0, 1
 EPI_NONE, EPI_BIAS, EPI_RESIDUAL, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3, 4
 BF16, F16 = 0, 1
