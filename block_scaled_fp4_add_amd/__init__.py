@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: producer / quantizer / dequantizer, LINEAR scales
+NVFP4_B32 = 3                   # the NVFP4 rule on 32-blocks: the same three calls, LINEAR scales
 LINEAR, TILED = 0, 1
 VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = -1, 0, 1
 

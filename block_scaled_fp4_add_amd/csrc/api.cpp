@@ -28,11 +28,13 @@ bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }   // GEMM 
 bool layout_ok(int l) { return l == LOWBIT_SF_LINEAR || l == LOWBIT_SF_TILED; }
 // producer / quantizer / dequantizer formats: MXFP8 as well, with LINEAR scales only
 bool qfmt_layout_ok(int f, int l) {
-  if (f == LOWBIT_MXFP8) return l == LOWBIT_SF_LINEAR;
+  if (f == LOWBIT_MXFP8 || f == LOWBIT_NVFP4_B32) return l == LOWBIT_SF_LINEAR;
   return fmt_ok(f) && layout_ok(l);
 }
 
 int64_t block_of(int f) { return f == LOWBIT_NVFP4 ? 16 : 32; }
+// formats with E4M3 block scales, the only ones that take a global scale
+bool takes_gs(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_NVFP4_B32; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // gfx950 check, cached per device ordinal.
@@ -139,7 +141,7 @@ static lowbit_status producer(const void* input, void* residual, const void* wei
                               uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_lin, int in_f16,
                               hipStream_t stream) {
   if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
-  if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
+  if (!takes_gs(fmt) && global_scale) return LOWBIT_EINVAL;
   if (out_sf_lin && layout != LOWBIT_SF_TILED) return LOWBIT_EINVAL;
   if (M < 0) return LOWBIT_ESHAPE;
   if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
@@ -159,7 +161,7 @@ static lowbit_status quantize(const void* x, int64_t rows, int64_t K, lowbit_for
                               const float* global_scale, uint8_t* out_packed, uint8_t* out_sf, int in_f16,
                               hipStream_t stream) {
   if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
-  if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
+  if (!takes_gs(fmt) && global_scale) return LOWBIT_EINVAL;
   if (rows < 0) return LOWBIT_ESHAPE;
   if (rows > 0 && (!x || !out_packed || !out_sf)) return LOWBIT_EINVAL;
   if (K < block_of(fmt) || K % block_of(fmt) != 0 || K > kMaxRowElems) return LOWBIT_ESHAPE;
@@ -243,7 +245,7 @@ lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_
                                 lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
                                 void* out, hipStream_t stream) {
   if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
-  if (fmt != LOWBIT_NVFP4 && global_scale) return LOWBIT_EINVAL;
+  if (!takes_gs(fmt) && global_scale) return LOWBIT_EINVAL;
   if (rows < 0) return LOWBIT_ESHAPE;
   if (rows > 0 && (!packed || !sf || !out)) return LOWBIT_EINVAL;
   if (K < block_of(fmt) || K % block_of(fmt) != 0) return LOWBIT_ESHAPE;

@@ -12,7 +12,8 @@ namespace lowbit {
 
 constexpr int kWave = 64;
 
-enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2 };   // MXFP8: quantization only, no GEMM
+// MXFP8 and kNV32 (the NVFP4 rule on 32-blocks): quantization only, no GEMM
+enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2, kNV32 = 3 };
 enum Layout : int { kLinear = 0, kTiled = 1 };
 enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual = 3, kEpiBiasGelu = 4,
                  kEpiBiasGeluFp4 = 5 };
@@ -21,6 +22,10 @@ template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<kNVFP4> { static constexpr int B = 16; };
 template <> struct FmtTraits<kMXFP4> { static constexpr int B = 32; };
 template <> struct FmtTraits<kMXFP8> { static constexpr int B = 32; };
+template <> struct FmtTraits<kNV32> { static constexpr int B = 32; };
+
+// block scale E4M3 with the global scale folded in (NVFP4 and its 32-block form)
+constexpr bool e4m3_scaled(int f) { return f == kNVFP4 || f == kNV32; }
 
 // ---------------------------------------------------------------------------
 // bf16

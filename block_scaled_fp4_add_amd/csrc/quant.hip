@@ -56,7 +56,7 @@ __device__ __forceinline__ void quant_store_block(const float* y, float gs, int6
 #pragma unroll
   for (int i = 0; i < B; i++) amax = fmaxf(amax, fabsf(y[i]));
   float inv;
-  uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv)
+  uint32_t sb = e4m3_scaled(FMT) ? nv_block_scale(amax, gs, &inv)
                 : (FMT == kMXFP8) ? mx_block_scale_e<8>(amax, &inv) : mx_block_scale(amax, &inv);
   float v[B];
 #pragma unroll
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
     rstd = (float)(1.0 / sqrt(ss / (double)a.H + (double)a.eps));
   }
 
-  const float gs = (FMT == kNVFP4 && a.gs != nullptr) ? *a.gs : 1.0f;
+  const float gs = (e4m3_scaled(FMT) && a.gs != nullptr) ? *a.gs : 1.0f;
 
   if (live) {
 #pragma unroll
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
       }
     }
   }
-  const float gs = (FMT == kNVFP4 && a.gs != nullptr) ? *a.gs : 1.0f;
+  const float gs = (e4m3_scaled(FMT) && a.gs != nullptr) ? *a.gs : 1.0f;
   float rstd = 1.0f;
   if constexpr (FUSED) {
     double ss = 0.0;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
     amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
     if constexpr (LPB == 4) amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
     float inv;
-    const uint32_t sb = (FMT == kNVFP4) ? nv_block_scale(amax, gs, &inv)
+    const uint32_t sb = e4m3_scaled(FMT) ? nv_block_scale(amax, gs, &inv)
                         : (FMT == kMXFP8) ? mx_block_scale_e<8>(amax, &inv) : mx_block_scale(amax, &inv);
 #pragma unroll
     for (int i = 0; i < 8; i++) y[i] = __fmul_rn(y[i], inv);
@@ -440,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
   if (t >= rows * nblk) return;
   const int64_t row = t / nblk, kb = t % nblk;
   const uint32_t sb = sf[sf_offset(FMT, layout, row, kb, nblk)];
-  const float scale = (FMT == kNVFP4) ? e4m3_to_f32(sb) : ue8m0_to_f32(sb);
-  const float gs = (FMT == kNVFP4 && gsp != nullptr) ? *gsp : 1.0f;
+  const float scale = e4m3_scaled(FMT) ? e4m3_to_f32(sb) : ue8m0_to_f32(sb);
+  const float gs = (e4m3_scaled(FMT) && gsp != nullptr) ? *gsp : 1.0f;
   uint16_t* dst = out + row * K + kb * B;
   if constexpr (FMT == kMXFP8) {
     // 32 E4M3 bytes; value * 2^e is exact in fp32 and has 4 significant bits
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
       uint32_t byte = ((j < 4 ? p.x : p.y) >> (8 * (j & 3))) & 0xFF;
       float v0 = __fmul_rn(e2m1_to_f32(byte & 15), scale);   // exact
       float v1 = __fmul_rn(e2m1_to_f32(byte >> 4), scale);
-      if (FMT == kNVFP4) { v0 = __fdiv_rn(v0, gs); v1 = __fdiv_rn(v1, gs); }
+      if (e4m3_scaled(FMT)) { v0 = __fdiv_rn(v0, gs); v1 = __fdiv_rn(v1, gs); }
       o[j] = pack_bf16x2(v0, v1);
     }
     uint4* d4 = reinterpret_cast<uint4*>(dst + q * 16);
@@ -491,6 +491,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const
   RowArgs a{x, residual, w, M, H, M, eps, layout, gs, out_packed, out_sf, out_sf_lin};
   if (layout == kTiled) a.rows_grid = (M + 31) / 32 * 32;
   if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, true, true>(a, s) : dispatch_row<kMXFP8, true, false>(a, s);
+  if (fmt == kNV32) return in_f16 ? dispatch_row<kNV32, true, true>(a, s) : dispatch_row<kNV32, true, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, true>(a, s) : dispatch_row<kMXFP4, true, true>(a, s);
   return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, false>(a, s) : dispatch_row<kMXFP4, true, false>(a, s);
 }
@@ -500,6 +501,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, 
   RowArgs a{x, nullptr, nullptr, rows, K, rows, 0.0f, layout, gs, out_packed, out_sf, nullptr};
   if (layout == kTiled) a.rows_grid = (rows + 31) / 32 * 32;
   if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, false, true>(a, s) : dispatch_row<kMXFP8, false, false>(a, s);
+  if (fmt == kNV32) return in_f16 ? dispatch_row<kNV32, false, true>(a, s) : dispatch_row<kNV32, false, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, true>(a, s) : dispatch_row<kMXFP4, false, true>(a, s);
   return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, false>(a, s) : dispatch_row<kMXFP4, false, false>(a, s);
 }
@@ -512,6 +514,9 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t r
   const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
   if (fmt == kNVFP4)
     hipLaunchKernelGGL(dequant_kernel<kNVFP4>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
+                       gs, out);
+  else if (fmt == kNV32)
+    hipLaunchKernelGGL(dequant_kernel<kNV32>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
                        gs, out);
   else if (fmt == kMXFP8)
     hipLaunchKernelGGL(dequant_kernel<kMXFP8>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,

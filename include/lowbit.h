@@ -75,8 +75,12 @@ typedef enum {
  *        packed (rows, K).  Scale rule e = clamp(floor(log2 amax) - 8, -127,
  *        127) (OCP MX, emax 8 for E4M3); elements nearest-even, saturating at
  *        448, sign kept.  Producer, quantizer and dequantizer only, LINEAR
- *        scales only; the GEMMs return LOWBIT_EINVAL for it. */
-typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2 } lowbit_format;
+ *        scales only; the GEMMs return LOWBIT_EINVAL for it.
+ * NVFP4_B32: the NVFP4 rule (E4M3 scales, optional global scale, clamp at
+ *        448) on 32-element blocks ([FI] add_rmsnorm_fp4quant's E4M3 scale
+ *        format at block size 32); packed like NVFP4.  Producer, quantizer and
+ *        dequantizer only, LINEAR scales only; the GEMMs return LOWBIT_EINVAL. */
+typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2, LOWBIT_NVFP4_B32 = 3 } lowbit_format;
 typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1 } lowbit_sf_layout;
 
 /* GEMM schedule: -1 picks by shape; 0 = decode (weights as the MFMA row

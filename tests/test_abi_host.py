@@ -55,6 +55,9 @@ def test_sf_bytes_matches_the_oracle(orc):
     # MXFP8: 32-blocks, LINEAR only
     assert L.lowbit_sf_bytes(33, 5120, 2, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 2, 0)
     assert L.lowbit_sf_bytes(33, 5120, 2, 1) == 0
+    # the NVFP4 rule on 32-blocks: LINEAR only
+    assert L.lowbit_sf_bytes(33, 5120, 3, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 3, 0)
+    assert L.lowbit_sf_bytes(33, 5120, 3, 1) == 0
 
 
 def test_pick_variant():
@@ -90,7 +93,9 @@ def quant(L, buf, rows, K, fmt=1, layout=0, gs=None, x=0, p=0, s=0):
 
 def test_quantize_argument_order(buf):
     L = lb.lib()
-    assert quant(L, buf, 4, 64, fmt=3) == EINVAL                           # format
+    assert quant(L, buf, 4, 64, fmt=4) == EINVAL                           # format
+    assert quant(L, buf, 4, 64, fmt=3, layout=1) == EINVAL                 # 32-block NVFP4: LINEAR only
+    assert quant(L, buf, 4, 48, fmt=3) == ESHAPE                           # 32-block NVFP4: K % 32
     assert quant(L, buf, 4, 64, fmt=2, layout=1) == EINVAL                 # MXFP8: LINEAR scales only
     assert quant(L, buf, 4, 64, fmt=2, gs=buf.at()) == EINVAL              # MXFP8 has no global scale
     assert quant(L, buf, 4, 48, fmt=2) == ESHAPE                           # MXFP8: K % 32
@@ -105,6 +110,7 @@ def test_quantize_argument_order(buf):
     assert quant(L, buf, 0, 64) == OK                                      # empty: nothing to do
     if NO_DEVICE:
         assert quant(L, buf, 4, 64) == EDEVICE                             # all checks pass: no device
+        assert quant(L, buf, 4, 64, fmt=3, gs=buf.at()) == EDEVICE         # 32-block NVFP4 takes gs
 
 
 def test_producer_argument_order(buf):
@@ -136,6 +142,7 @@ def test_producer_both_sf_argument_order(buf):
     for fp16 in (False, True):
         assert call(4, 256, fmt=2, fp16=fp16) == EINVAL            # MXFP8: no TILED layout
         assert call(4, 256, fmt=7, fp16=fp16) == EINVAL
+        assert call(4, 256, fmt=3, fp16=fp16) == EINVAL            # 32-block NVFP4: no TILED layout
         assert call(4, 256, fmt=1, gs=buf.at(), fp16=fp16) == EINVAL
         assert call(4, 256, lin=False, fp16=fp16) == EINVAL        # no LINEAR buffer
         assert call(4, 48, fp16=fp16) == ESHAPE
@@ -153,7 +160,8 @@ def test_gemm_argument_order(buf):
     def call(M, N, K, fmt=1, la=0, lb_=0, variant=-1, o=out, a_=a):
         return L.lowbit_gemm_bf16(a_, b, sa, sb, M, N, K, fmt, la, lb_, 1.0, o, variant, None)
 
-    assert call(8, 128, 256, fmt=3) == EINVAL
+    assert call(8, 128, 256, fmt=3) == EINVAL                # 32-block NVFP4: no GEMM
+    assert call(8, 128, 256, fmt=4) == EINVAL
     assert call(8, 128, 256, fmt=2) == EINVAL                # MXFP8: no GEMM
     assert call(8, 128, 256, variant=2) == EINVAL
     assert call(8, 128, 256, o=None) == EINVAL
