@@ -37,7 +37,7 @@
 #endif
 
 enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1, ORC_MXFP8 = 2, ORC_NVFP4_B32 = 3 };
-enum { ORC_SF_LINEAR = 0, ORC_SF_TILED = 1 };
+enum { ORC_SF_LINEAR = 0, ORC_SF_TILED = 1, ORC_SF_SWZ128 = 2 };
 enum { ORC_EPI_NONE = 0, ORC_EPI_BIAS = 1, ORC_EPI_RESIDUAL = 2, ORC_EPI_BIAS_RESIDUAL = 3,
        ORC_EPI_BIAS_GELU = 4 };
 
@@ -192,6 +192,12 @@ double orc_ue8m0_value(uint8_t b) {
  *                  (word h*32 + r holds blocks {2h, 2h+1, 2h+4, 2h+5} of row r);
  *           NVFP4: word (j / 4) * 32 + row % 32, byte j % 4
  *                  (word c*32 + r holds blocks 4c .. 4c+3 of row r).
+ * SWZ128: the FlashInfer page's swizzled layout (its output_swizzled path):
+ *         rows grouped by 128 and blocks by 4, each 128 x 4 tile 512
+ *         contiguous bytes, tiles ordered row-tile major (ceil(nblk/4) tiles
+ *         per row tile).  Inside a tile, row r and block kb sit at byte
+ *         16 * (r % 32) + 4 * ((r % 128) / 32) + kb % 4.  The page allocates
+ *         the buffer uninitialised; here the padding bytes are zero.
  */
 static int64_t block_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
 
@@ -202,11 +208,16 @@ static int e4m3_scaled(int fmt) { return fmt == ORC_NVFP4 || fmt == ORC_NVFP4_B3
 int64_t orc_sf_bytes(int64_t rows, int64_t k, int fmt, int layout) {
     int64_t nblk = k / block_of(fmt);
     if (layout == ORC_SF_LINEAR) return rows * nblk;
+    if (layout == ORC_SF_SWZ128) return ((rows + 127) / 128) * ((nblk + 3) / 4) * 512;
     return ((rows + 31) / 32) * ((nblk + 7) / 8) * 256;
 }
 
 int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int fmt, int layout) {
     if (layout == ORC_SF_LINEAR) return row * nblk + kb;
+    if (layout == ORC_SF_SWZ128) {
+        int64_t tile = (row / 128) * ((nblk + 3) / 4) + kb / 4;
+        return tile * 512 + (row % 32) * 16 + ((row % 128) / 32) * 4 + kb % 4;
+    }
     int64_t ktiles = (nblk + 7) / 8;
     int64_t tile = (row / 32) * ktiles + kb / 8;
     int64_t j = kb % 8;
@@ -350,7 +361,7 @@ static void quant_row(const float* y, int64_t row, int64_t n, int fmt, float gs,
 static int check_common(int64_t rows, int64_t k, int fmt, int layout) {
     if (rows < 0 || k <= 0) return 1;
     if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4 && fmt != ORC_MXFP8 && fmt != ORC_NVFP4_B32) return 1;
-    if (layout != ORC_SF_LINEAR && layout != ORC_SF_TILED) return 1;
+    if (layout != ORC_SF_LINEAR && layout != ORC_SF_TILED && layout != ORC_SF_SWZ128) return 1;
     /* MXFP8 and 32-block NVFP4 scales: LINEAR only */
     if ((fmt == ORC_MXFP8 || fmt == ORC_NVFP4_B32) && layout != ORC_SF_LINEAR) return 1;
     if (k % block_of(fmt) != 0) return 1;

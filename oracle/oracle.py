@@ -9,7 +9,7 @@ Enum values: fmt NVFP4 = 0 (16-blocks, E4M3 scales), MXFP4 = 1 (32-blocks,
 UE8M0 scales), MXFP8 = 2 (32-blocks, UE8M0 scales, E4M3 elements, one byte
 each; LINEAR scales only, no GEMM), NVFP4_B32 = 3 (the NVFP4 rule on
 32-blocks: E4M3 scales with the global scale; LINEAR scales only, no GEMM);
-layout LINEAR = 0, TILED = 1; epilogue NONE = 0, BIAS = 1,
+layout LINEAR = 0, TILED = 1, SWZ128 = 2 (the page's 128 x 4 swizzle); epilogue NONE = 0, BIAS = 1,
 RESIDUAL = 2, BIAS_RESIDUAL = 3, BIAS_GELU = 4.
 """
 import ctypes
@@ -20,7 +20,7 @@ import numpy as np
 from . import build as _build
 
 NVFP4, MXFP4, MXFP8, NVFP4_B32 = 0, 1, 2, 3
-LINEAR, TILED = 0, 1
+LINEAR, TILED, SWZ128 = 0, 1, 2
 EPI_NONE, EPI_BIAS, EPI_RESIDUAL, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3, 4
 BF16, F16 = 0, 1
 
