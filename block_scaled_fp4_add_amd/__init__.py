@@ -15,7 +15,7 @@ import torch
 
 NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: producer / quantizer / dequantizer, LINEAR scales
 NVFP4_B32 = 3                   # the NVFP4 rule on 32-blocks: the same three calls, LINEAR scales
-LINEAR, TILED = 0, 1
+LINEAR, TILED, SWZ128 = 0, 1, 2   # SWZ128: the 128 x 4 swizzle, quantization side only
 VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = -1, 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowbit.so")

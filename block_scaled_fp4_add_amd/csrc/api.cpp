@@ -26,10 +26,11 @@ constexpr int64_t kMaxRowElems = 32768;  // 4 waves x 64 lanes x 128 elements pe
 
 bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }   // GEMM operands
 bool layout_ok(int l) { return l == LOWBIT_SF_LINEAR || l == LOWBIT_SF_TILED; }
-// producer / quantizer / dequantizer formats: MXFP8 as well, with LINEAR scales only
+// producer / quantizer / dequantizer: MXFP8 and 32-block NVFP4 as well, with
+// LINEAR scales only; the FP4 GEMM formats also take the 128 x 4 swizzle
 bool qfmt_layout_ok(int f, int l) {
   if (f == LOWBIT_MXFP8 || f == LOWBIT_NVFP4_B32) return l == LOWBIT_SF_LINEAR;
-  return fmt_ok(f) && layout_ok(l);
+  return fmt_ok(f) && (layout_ok(l) || l == LOWBIT_SF_SWZ128);
 }
 
 int64_t block_of(int f) { return f == LOWBIT_NVFP4 ? 16 : 32; }

@@ -14,7 +14,8 @@ constexpr int kWave = 64;
 
 // MXFP8 and kNV32 (the NVFP4 rule on 32-blocks): quantization only, no GEMM
 enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2, kNV32 = 3 };
-enum Layout : int { kLinear = 0, kTiled = 1 };
+// kSwz128: the producer page's 128 x 4 swizzled layout (quantization side only)
+enum Layout : int { kLinear = 0, kTiled = 1, kSwz128 = 2 };
 enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual = 3, kEpiBiasGelu = 4,
                  kEpiBiasGeluFp4 = 5 };
 
@@ -156,6 +157,12 @@ __device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t sf_offset(int fmt, int layout, int64_t row, int64_t kb, int64_t nblk) {
   if (layout == kLinear) return row * nblk + kb;
+  if (layout == kSwz128) {
+    // 128-row x 4-block tiles of 512 bytes, row-tile major; inside a tile row
+    // r, block kb at 16 (r % 32) + 4 ((r % 128) / 32) + kb % 4
+    const int64_t tile = (row >> 7) * ((nblk + 3) >> 2) + (kb >> 2);
+    return (tile << 9) + ((row & 31) << 4) + (((row >> 5) & 3) << 2) + (kb & 3);
+  }
   int64_t ktiles = (nblk + 7) >> 3;
   int64_t j = kb & 7;
   int64_t base = ((row >> 5) * ktiles + (kb >> 3)) << 8;
@@ -164,7 +171,15 @@ __device__ __forceinline__ int64_t sf_offset(int fmt, int layout, int64_t row, i
 }
 __host__ __device__ inline int64_t sf_bytes_of(int layout, int64_t rows, int64_t nblk) {
   if (layout == kLinear) return rows * nblk;
+  if (layout == kSwz128) return ((rows + 127) / 128) * ((nblk + 3) / 4) * 512;
   return ((rows + 31) / 32) * ((nblk + 7) / 8) * 256;
+}
+// blocks per row and rows the padded layouts cover (padding bytes are zero)
+__host__ __device__ inline int64_t sf_pad_blocks(int layout, int64_t nblk) {
+  return layout == kTiled ? (nblk + 7) / 8 * 8 : layout == kSwz128 ? (nblk + 3) / 4 * 4 : nblk;
+}
+__host__ __device__ inline int64_t sf_pad_rows(int layout, int64_t rows) {
+  return layout == kTiled ? (rows + 31) / 32 * 32 : layout == kSwz128 ? (rows + 127) / 128 * 128 : rows;
 }
 
 // ---------------------------------------------------------------------------

@@ -206,16 +206,16 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
     }
   }
 
-  // TILED padding: zero the scale bytes of blocks nblk..8*ceil(nblk/8)-1 of
-  // every covered row, and all bytes of the rows M..rows_grid-1.
-  if (a.layout == kTiled && row < a.rows_grid) {
-    const int64_t nblk_pad = ((nblk + 7) >> 3) << 3;
+  // TILED / SWZ128 padding: zero the scale bytes of blocks nblk..nblk_pad-1
+  // of every covered row, and all bytes of the rows M..rows_grid-1.
+  if (a.layout != kLinear && row < a.rows_grid) {
+    const int64_t nblk_pad = sf_pad_blocks(a.layout, nblk);
     if (live) {
       const int64_t pad = nblk_pad - nblk;
-      if (wave_in_row == 0 && lane < pad) a.out_sf[sf_offset(FMT, kTiled, row, nblk + lane, nblk)] = 0;
+      if (wave_in_row == 0 && lane < pad) a.out_sf[sf_offset(FMT, a.layout, row, nblk + lane, nblk)] = 0;
     } else {
       for (int64_t kb = kb0 + lane; kb < ((wave_in_row == WPR - 1) ? nblk_pad : kb_end); kb += kWave)
-        a.out_sf[sf_offset(FMT, kTiled, row, kb, nblk)] = 0;
+        a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = 0;
     }
   }
 }
@@ -262,10 +262,10 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   const int t = threadIdx.x, lane = t % kWave;
   const int64_t row = (a.layout == kTiled) ? tiled_row_of_block(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t H = a.H, nblk = H / B, nvec = H / 8;
-  const int64_t nblk_pad = ((nblk + 7) >> 3) << 3;
+  const int64_t nblk_pad = sf_pad_blocks(a.layout, nblk);
   if (row >= a.M) {
-    // TILED padding row: every scale byte zero
-    for (int64_t kb = t; kb < nblk_pad; kb += T) a.out_sf[sf_offset(FMT, kTiled, row, kb, nblk)] = 0;
+    // TILED / SWZ128 padding row: every scale byte zero
+    for (int64_t kb = t; kb < nblk_pad; kb += T) a.out_sf[sf_offset(FMT, a.layout, row, kb, nblk)] = 0;
     return;
   }
   const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -354,13 +354,16 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
         const int kb = q / LPB, jj = kb & 7;
         const int in_grp = (FMT == kNVFP4) ? ((jj >> 2) << 7) + (jj & 3)
                                            : (((jj >> 1) & 1) << 7) + (jj & 1) + ((jj >> 2) << 1);
-        sf_row[(a.layout == kLinear) ? kb : ((kb >> 3) << 8) + in_grp] = (uint8_t)sb;
+        if (a.layout == kSwz128)
+          a.out_sf[sf_offset(FMT, kSwz128, row, kb, nblk)] = (uint8_t)sb;
+        else
+          sf_row[(a.layout == kLinear) ? kb : ((kb >> 3) << 8) + in_grp] = (uint8_t)sb;
         if (a.out_sf_lin != nullptr) a.out_sf_lin[row * nblk + kb] = (uint8_t)sb;
       }
     }
   }
-  // TILED: the row's padding blocks nblk .. nblk_pad - 1 are zero
-  if (a.layout == kTiled && t < nblk_pad - nblk) a.out_sf[sf_offset(FMT, kTiled, row, nblk + t, nblk)] = 0;
+  // TILED / SWZ128: the row's padding blocks nblk .. nblk_pad - 1 are zero
+  if (a.layout != kLinear && t < nblk_pad - nblk) a.out_sf[sf_offset(FMT, a.layout, row, nblk + t, nblk)] = 0;
 }
 
 template <int FMT, int NW, bool FUSED, bool F16>
@@ -489,7 +492,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const
                                     uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_lin, int in_f16,
                                     hipStream_t s) {
   RowArgs a{x, residual, w, M, H, M, eps, layout, gs, out_packed, out_sf, out_sf_lin};
-  if (layout == kTiled) a.rows_grid = (M + 31) / 32 * 32;
+  a.rows_grid = sf_pad_rows(layout, M);
   if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, true, true>(a, s) : dispatch_row<kMXFP8, true, false>(a, s);
   if (fmt == kNV32) return in_f16 ? dispatch_row<kNV32, true, true>(a, s) : dispatch_row<kNV32, true, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, true, true>(a, s) : dispatch_row<kMXFP4, true, true>(a, s);
@@ -499,7 +502,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
                            const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s) {
   RowArgs a{x, nullptr, nullptr, rows, K, rows, 0.0f, layout, gs, out_packed, out_sf, nullptr};
-  if (layout == kTiled) a.rows_grid = (rows + 31) / 32 * 32;
+  a.rows_grid = sf_pad_rows(layout, rows);
   if (fmt == kMXFP8) return in_f16 ? dispatch_row<kMXFP8, false, true>(a, s) : dispatch_row<kMXFP8, false, false>(a, s);
   if (fmt == kNV32) return in_f16 ? dispatch_row<kNV32, false, true>(a, s) : dispatch_row<kNV32, false, false>(a, s);
   if (in_f16) return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, true>(a, s) : dispatch_row<kMXFP4, false, true>(a, s);

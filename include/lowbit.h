@@ -81,7 +81,14 @@ typedef enum {
  *        format at block size 32); packed like NVFP4.  Producer, quantizer and
  *        dequantizer only, LINEAR scales only; the GEMMs return LOWBIT_EINVAL. */
 typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2, LOWBIT_NVFP4_B32 = 3 } lowbit_format;
-typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1 } lowbit_sf_layout;
+/* LOWBIT_SF_SWZ128: the 128 x 4 swizzled scale layout of [FI]'s producer
+ * (its swizzled output): rows grouped by 128 and blocks by 4, each tile 512
+ * contiguous bytes, tiles row-tile major with ceil(K/B/4) tiles per row tile;
+ * inside a tile row r and block kb sit at byte 16*(r%32) + 4*((r%128)/32) +
+ * kb%4.  lowbit_sf_bytes = ceil(rows/128) * ceil(K/B/4) * 512; padding bytes
+ * are written zero.  Producer, quantizer and dequantizer with NVFP4 or MXFP4
+ * only; the GEMMs return LOWBIT_EINVAL for it. */
+typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1, LOWBIT_SF_SWZ128 = 2 } lowbit_sf_layout;
 
 /* GEMM schedule: -1 picks by shape; 0 = decode (weights as the MFMA row
  * operand, K split across the waves of a workgroup, for small M); 1 = prefill

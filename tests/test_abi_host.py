@@ -55,6 +55,10 @@ def test_sf_bytes_matches_the_oracle(orc):
     # MXFP8: 32-blocks, LINEAR only
     assert L.lowbit_sf_bytes(33, 5120, 2, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 2, 0)
     assert L.lowbit_sf_bytes(33, 5120, 2, 1) == 0
+    # the 128 x 4 swizzle: FP4 GEMM formats, quantization side
+    for rows, K, fmt in ((1, 64, 0), (129, 1120, 1), (300, 5120, 0)):
+        assert L.lowbit_sf_bytes(rows, K, fmt, 2) == orc.sf_bytes(rows, K, fmt, 2)
+    assert L.lowbit_sf_bytes(33, 5120, 2, 2) == 0 and L.lowbit_sf_bytes(33, 5120, 3, 2) == 0
     # the NVFP4 rule on 32-blocks: LINEAR only
     assert L.lowbit_sf_bytes(33, 5120, 3, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 3, 0)
     assert L.lowbit_sf_bytes(33, 5120, 3, 1) == 0
@@ -162,6 +166,7 @@ def test_gemm_argument_order(buf):
 
     assert call(8, 128, 256, fmt=3) == EINVAL                # 32-block NVFP4: no GEMM
     assert call(8, 128, 256, fmt=4) == EINVAL
+    assert call(8, 128, 256, la=2) == EINVAL                 # 128 x 4 swizzle: no GEMM
     assert call(8, 128, 256, fmt=2) == EINVAL                # MXFP8: no GEMM
     assert call(8, 128, 256, variant=2) == EINVAL
     assert call(8, 128, 256, o=None) == EINVAL
