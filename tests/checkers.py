@@ -142,7 +142,7 @@ def compare_quantized(orc, fmt, gs, gpu_packed, gpu_sf, orc_packed, orc_sf, y, v
 
 
 def gemm_within_tolerance(gpu, ref, l1):
-    """Elementwise the benchmark spec GEMM rule; returns (ok_mask, worst ratio)."""
+    """Elementwise GEMM tolerance rule; returns (ok_mask, worst ratio)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     tol = 2.0 ** -7 * np.abs(ref) + 1e-6 * l1
     err = np.abs(gpu - ref)
