@@ -41,8 +41,10 @@
  *                  half dequantizes in a 128-element stage).
  *         Padding bytes are written as zero by every producer and must be
  *         zero in any TILED input.
+ *       LOWBIT_SF_SWZ128: [FI]'s 128 x 4 swizzle, quantization side only
+ *         (the definition is at the lowbit_sf_layout enum below).
  *   - Alignment: packed/bf16 tensor pointers 16 bytes; scale pointers 4 bytes
- *     (TILED) or 1 byte (LINEAR); global scales 4 bytes.
+ *     (TILED) or 1 byte (LINEAR, SWZ128); global scales 4 bytes.
  *   - Errors are returned, never raised; on any error nothing is launched and
  *     no output is touched.  Asynchronous launch failures surface as
  *     LOWBIT_EHIP.  The device must be gfx950 (LOWBIT_EDEVICE otherwise).
