@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblowbit.so")
-SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["gemm_inst_nv2.hip", "gemm_inst_nv1.hip", "gemm_inst_nv0.hip", "gemm_inst_mx2.hip",
+           "gemm_inst_mx1.hip", "gemm_inst_mx0.hip", "quant.hip", "gemm.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -22,7 +23,8 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, jobs: int = 3) -> str:
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    jobs = jobs or max(1, min(9, os.cpu_count() or 1))
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
     procs = []

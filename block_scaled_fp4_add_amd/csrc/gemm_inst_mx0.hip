@@ -1,0 +1,10 @@
+// gemm_inst_mx0.hip -- instantiates the GEMM launchers for MXFP4 with the
+// None and Bias epilogues (one compilation unit per pair).
+#include "gemm_kernels.hpp"
+
+namespace lowbit {
+namespace gk {
+template hipError_t launch_fmt_epi<kMXFP4, kEpiNone>(const GemmArgs& g, int variant, hipStream_t s);
+template hipError_t launch_fmt_epi<kMXFP4, kEpiBias>(const GemmArgs& g, int variant, hipStream_t s);
+}  // namespace gk
+}  // namespace lowbit

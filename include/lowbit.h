@@ -187,7 +187,10 @@ lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_
  * bias: bf16 (N); residual: bf16 (M, N) (may alias out).
  * Requires K % B == 0, K >= B, M, N >= 0 (empty is a no-op).
  * variant: LOWBIT_VARIANT_*; an explicit variant that cannot run the shape
- * returns LOWBIT_ESHAPE instead of silently picking another schedule. */
+ * returns LOWBIT_ESHAPE instead of silently picking another schedule.
+ * NVFP4 with K % 32 == 16 (packed rows of 8 mod 16 bytes) runs on the decode
+ * schedule only, at any M (more than 128 rows go as consecutive launches
+ * over 128-row slices); LOWBIT_VARIANT_PREFILL returns LOWBIT_ESHAPE for it. */
 lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                lowbit_format fmt, lowbit_sf_layout sfa_layout,
