@@ -196,16 +196,20 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 
-// GELU with the exact erf form, fp32.
-// GELU, exact (erf) form, written as gelu(z) = z/2 * erfc(-z/sqrt(2)) so
-// that the negative tail keeps its relative precision (1 + erf cancels there).
-// erfc(x) for x >= 0 is t * exp(-x^2 + g(t)) with t = 1 / (1 + x/2) and g a
-// degree-9 polynomial in t, least-squares fitted to ln(erfc(x) * exp(x^2) / t)
-// over t in (0, 1] (relative error of erfc below 1.1e-7 for every x >= 0);
+// GELU, exact (erf) form, fp32, written as gelu(z) = z/2 * erfc(-z/sqrt(2))
+// so that the negative tail keeps its relative precision (1 + erf cancels
+// there).  erfc(x) for x >= 0 takes the published Chebyshev-fitted form of
+// the "erfcc" routine in Press et al., Numerical Recipes (section 6.2):
+// t * exp(-x^2 + g(t)), t = 1 / (1 + x/2), g a degree-9 polynomial in t.  Its
+// coefficients here are our own least-squares refit of ln(erfc(x) e^{x^2} / t)
+// over t in (0, 1] (relative error of that erfc below 1.1e-7 for x >= 0);
 // erfc(-x) = 2 - erfc(x).  -x^2 is formed as fma(-z/2, z, g): z/2 is exact,
-// so the exponent argument is rounded once.  Branch-free; in fp32 the
-// result's relative error stays below 2e-6 for |z| < 6 (checked against a
-// binary64 erfc on the CPU with the same operation sequence).
+// so the exponent argument is rounded once.  Branch-free.  The fp32
+// evaluation is less accurate than the fit: the roundings of the exponent
+// argument (|arg| up to about 40) dominate, and with v_rcp_f32 and
+// v_exp_f32 each allowed one ulp the result's relative error stays below
+// 2.6e-6 for z >= -6 and 4.5e-6 for z >= -9 (operation sequence replayed on
+// the CPU against a binary64 erfc).  Below -9 |gelu(z)| < 1.1e-18.
 constexpr float kGeluErfcPoly[10] = {-1.26551222f, 1.00002284f, 0.37412141f,  0.09641923f, -0.18410964f,
                                      0.27173793f,  -1.12172492f, 1.4738528f, -0.81363612f, 0.1688286f};
 __device__ __forceinline__ float gelu_erf(float z) {

@@ -12,13 +12,28 @@
 * GEMM bf16 outputs: |gpu - ref| <= 2^-7 |ref| + 1e-6 * L1, with ref the
   oracle's unrounded binary64 value and L1 = |alpha| sum_k |a_k b_k|.
 * FP4-output epilogue: as the producer, with the window widened by the GEMM's
-  own accumulation budget: 2^-20 |y| + 1.13e-6 L1 in units of y (1.13 bounds
-  the slope of GELU).
+  own accumulation budget and by the device GELU's error:
+  2^-20 |y| + GELU_REL |y| + 1.13e-6 L1 in units of y (1.13 bounds the slope
+  of GELU; GELU_REL bounds the fp32 evaluation's relative error under a
+  one-ulp model of the hardware reciprocal and power of two, see
+  tests/test_gelu_form.py).
 """
 import numpy as np
 
 E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 WIN = 2.0 ** -20
+GELU_REL = 4.5e-6   # relative error bound of the device GELU for z >= -9
+
+
+def fp4_out_windows(ref, gs_out, rows, N):
+    """Extra window terms of the FP4-output epilogue, from the oracle's
+    diagnostics (y, v, l1): codes in units of v, scales in units of s_pre."""
+    l1 = ref["l1"]
+    inv = np.abs(ref["v"]) / np.maximum(np.abs(ref["y"]), 1e-30)
+    code_extra = 1.13e-6 * l1 * inv + GELU_REL * np.abs(ref["v"])
+    blk_l1 = l1.reshape(rows, N // 16, 16).max(axis=2)
+    scale_extra = 1.13e-6 * blk_l1 * gs_out / 6.0 + GELU_REL * np.abs(ref["spre"])
+    return code_extra, scale_extra
 
 
 def unpack_codes(packed):

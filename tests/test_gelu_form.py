@@ -1,6 +1,13 @@
 """CPU check of the GPU epilogue's GELU: the erfc polynomial constants in
 csrc/common.hpp and the fp32 operation sequence of gelu_erf, replayed in
-numpy, against GELU(z) = z/2 * erfc(-z/sqrt 2) from scipy in binary64."""
+numpy, against GELU(z) = z/2 * erfc(-z/sqrt 2) from scipy in binary64.
+
+The device evaluates the reciprocal and the power of two with v_rcp_f32 and
+v_exp_f32, which the CDNA instruction set documents as accurate to one ulp.
+The hardware model below lets each of those two results sit one ulp either
+side of the correctly rounded value; its worst case over a dense sweep is
+the GELU error bound (checkers.GELU_REL) that the FP4-output comparison
+window carries."""
 import os
 import re
 
@@ -26,16 +33,24 @@ def fma32(a, b, c):
     return (np.asarray(a, np.float64) * np.asarray(b, np.float64) + np.asarray(c, np.float64)).astype(f32)
 
 
-def gelu_gpu_form(z, c):
+def _ulp_step(v, d):
+    """v moved d (-1, 0, +1) ulps (fp32)."""
+    return v if d == 0 else np.nextafter(v, f32(np.inf * d)).astype(f32)
+
+
+def gelu_gpu_form(z, c, d_rcp=0, d_exp=0):
+    """gelu_erf's fp32 sequence; d_rcp / d_exp shift the reciprocal and the
+    power of two by that many ulps (the one-ulp hardware model)."""
     z = np.asarray(z, f32)
     cf = c.astype(f32)
     x = (np.abs(z) * f32(0.70710678118654752440)).astype(f32)
-    t = (f32(1.0) / fma32(f32(0.5), x, f32(1.0))).astype(f32)
+    t = _ulp_step((f32(1.0) / fma32(f32(0.5), x, f32(1.0))).astype(f32), d_rcp)
     g = np.full_like(t, cf[9])
     for k in range(8, -1, -1):
         g = fma32(g, t, cf[k])
     arg = fma32((f32(-0.5) * z).astype(f32), z, g)
-    e = (t * np.exp2((arg * f32(1.44269504088896340736)).astype(f32).astype(np.float64)).astype(f32)).astype(f32)
+    p2 = _ulp_step(np.exp2((arg * f32(1.44269504088896340736)).astype(f32).astype(np.float64)).astype(f32), d_exp)
+    e = (t * p2).astype(f32)
     fac = np.where(z >= 0, (f32(2.0) - e).astype(f32), e)
     return ((f32(0.5) * z).astype(f32) * fac).astype(f32)
 
@@ -74,3 +89,30 @@ def test_gelu_special_values():
     assert g[5] == 0 and np.signbit(g[5])                  # deep negative tail: -0, the sign kept
     assert g[7] == 0 and np.signbit(g[7])
     np.testing.assert_allclose(g[2:4].astype(np.float64), [5e-31, -5e-31], rtol=1e-6)
+
+
+@pytest.mark.parametrize("lo,hi,bound", [(-9.0, -6.0, 4.5e-6), (-6.0, -4.0, 2.6e-6), (-4.0, -2.0, 1.6e-6),
+                                         (-2.0, 2.0, 1.0e-6), (2.0, 16.0, 2e-7)])
+def test_gelu_hardware_model_bound(lo, hi, bound):
+    """With v_rcp_f32 and v_exp_f32 each one ulp off in either direction the
+    relative error stays inside the bound the FP4-output window uses (the
+    whole-range bound is checkers.GELU_REL)."""
+    from .checkers import GELU_REL
+    assert bound <= GELU_REL
+    z = np.linspace(lo, hi, 200001, dtype=np.float64).astype(f32)
+    z = z[z != 0]
+    ref = gelu_ref(z)
+    worst = 0.0
+    for dr in (-1, 0, 1):
+        for de in (-1, 0, 1):
+            got = gelu_gpu_form(z, poly(), dr, de).astype(np.float64)
+            worst = max(worst, float((np.abs(got - ref) / np.abs(ref)).max()))
+    assert worst < bound, (lo, hi, worst)
+
+
+def test_gelu_deep_tail_is_negligible():
+    """Below z = -9 the bound is not needed: |gelu(z)| < 1.1e-18 there, so
+    any value scaled by an FP4 block inverse of at most 2^9 * gs_out stays
+    far below the first E2M1 boundary (0.25) for any gs_out < 4e14."""
+    z = np.linspace(-200.0, -9.0, 100001)
+    assert np.abs(gelu_ref(z)).max() < 1.1e-18

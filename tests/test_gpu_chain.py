@@ -1,7 +1,15 @@
 """The NVFP4 chain -- add + RMSNorm + quant (H = 5120) -> GEMM N = 17408 with a
 bias + GELU epilogue emitting NVFP4 -> GEMM N = 5120, K = 17408 to bf16 -- at
-M = 1, 128, 2048, checked stage by stage (each device stage fed with the
-oracle's bytes of the previous stage) on sampled rows, and end to end."""
+M = 1, 128, 2048, checked stage by stage:
+
+* the producer in full;
+* each GEMM relaunched on sampled rows of the oracle's bytes of the previous
+  stage;
+* each GEMM at the full-M launch the benchmark times (decode with four M-tiles
+  at M = 128, the prefill tiles at M = 2048), on sampled rows and every
+  column, against the oracle fed with the bytes that launch consumed (the
+  device producer's output for GEMM1, the device GEMM1's for GEMM2), under
+  the same rules as everywhere else and with no allowance."""
 import numpy as np
 import pytest
 import torch
@@ -61,7 +69,10 @@ def test_nvfp4_chain(orc, weights, M):
     banner(f"  producer {dict(rep)}")
     assert rep.ok(), rep
 
-    rows = np.arange(M) if M <= 4 else np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, 6)])
+    # sampled rows: the first and last, tile edges, and random ones (every column is checked)
+    edges = [r for r in (31, 32, 127, 128, 255, 256, 1023, 1024) if r < M]
+    rows = np.arange(M) if M <= 4 else np.unique(np.r_[0, M - 1, edges,
+                                                        np.random.default_rng(M).integers(0, M, 8)])
     alpha1 = 1.0 / (gsA * W["gs1"])
     alpha2 = 1.0 / W["gs2"]
     # --- stage 2: GEMM1 + bias + GELU -> NVFP4, device fed with the oracle's producer bytes
@@ -73,11 +84,10 @@ def test_nvfp4_chain(orc, weights, M):
                                           out_layout=lb.TILED)
     torch.cuda.synchronize()
     gp, gsf = linear_rows(orc, host_u8(p1), host_u8(s1), rows, N1, 0, orc.TILED)
-    inv = np.abs(g1["v"]) / np.maximum(np.abs(g1["y"]), 1e-30)
+    ce, se = checkers.fp4_out_windows(g1, 1.0, len(rows), N1)
     rep = checkers.compare_quantized(
         orc, 0, 1.0, gp, gsf, g1["packed"], g1["sf"], g1["y"], g1["v"], g1["spre"], len(rows), N1,
-        orc.LINEAR, code_extra=1.13e-6 * g1["l1"] * inv,
-        scale_extra=1.13e-6 * g1["l1"].reshape(len(rows), -1, 16).max(axis=2) / 6.0)
+        orc.LINEAR, code_extra=ce, scale_extra=se)
     banner(f"  gemm1 fp4 {dict(rep)}")
     assert rep.ok(), rep
     # --- stage 3: GEMM2 -> bf16, device fed with the oracle's GEMM1 bytes (sampled rows)
@@ -89,16 +99,27 @@ def test_nvfp4_chain(orc, weights, M):
     ok, worst = checkers.gemm_within_tolerance(host_f64(out2), ref2, l12)
     banner(f"  gemm2 worst {worst:.3g}")
     assert ok.all()
-    # --- end to end on the device, at the full M and in the benchmark's launch shapes
+    # --- the full-M launches the benchmark times, each against the oracle fed
+    # with the bytes that launch consumed
     p1d, s1d = lb.lowbit_gemm_bias_gelu_fp4(a1, W["d_b1"], sfa1, W["d_sfb1"], W["d_bias1"], fmt=0,
                                             sfa_layout=1, sfb_layout=1, alpha=alpha1, out_layout=lb.TILED)
     out_e2e = lb.lowbit_gemm_bf16(p1d, W["d_b2"], s1d, W["d_sfb2"], fmt=0, sfa_layout=1, sfb_layout=1,
                                   alpha=alpha2)
     torch.cuda.synchronize()
+    a_dev, sfa_dev = linear_rows(orc, host_u8(a1), host_u8(sfa1), rows, H, 0, orc.TILED)
+    g1d = orc.gemm_gelu_fp4(a_dev, W["b1"], sfa_dev, W["sfb1"], len(rows), N1, H, 0, 0, 1, alpha1,
+                            synth.bits(W["bias1"]), 1.0, orc.LINEAR, diag=True)
+    gp, gsf = linear_rows(orc, host_u8(p1d), host_u8(s1d), rows, N1, 0, orc.TILED)
+    ce, se = checkers.fp4_out_windows(g1d, 1.0, len(rows), N1)
+    rep = checkers.compare_quantized(
+        orc, 0, 1.0, gp, gsf, g1d["packed"], g1d["sf"], g1d["y"], g1d["v"], g1d["spre"], len(rows), N1,
+        orc.LINEAR, code_extra=ce, scale_extra=se)
+    banner(f"  gemm1 at the full launch {dict(rep)}")
+    assert rep.ok(), rep
+    assert checkers.tiled_padding_is_zero(orc, host_u8(s1d), M, N1 // 16, 0)
+    ref2d, l12d = orc.gemm(gp, W["b2"], gsf, W["sfb2"], len(rows), H, N1, 0, 0, 1, alpha=alpha2)
     got = host_f64(out_e2e)[rows]
     assert np.all(np.isfinite(got))
-    ok, worst = checkers.gemm_within_tolerance(got, ref2, l12)
-    frac = float((~ok).mean())
-    banner(f"  end-to-end fraction out of tolerance {frac:.2e} (worst {worst:.3g})")
-    # a code flipped inside a window upstream moves a few outputs by one FP4 step
-    assert frac <= 1e-3
+    ok, worst = checkers.gemm_within_tolerance(got, ref2d, l12d)
+    banner(f"  gemm2 at the full launch: worst {worst:.3g}, violations {int((~ok).sum())}")
+    assert ok.all(), f"{int((~ok).sum())} outputs out of tolerance (worst ratio {worst})"
