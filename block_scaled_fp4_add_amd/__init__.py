@@ -112,6 +112,23 @@ def block_size(fmt):
     return 16 if fmt == NVFP4 else 32
 
 
+def _row_bytes(fmt, k):
+    """Packed bytes of a row of k elements: one per MXFP8 element, else two codes a byte."""
+    return k if fmt == MXFP8 else k // 2
+
+
+def _at_least(t, n, name):
+    """Every buffer handed to the library must hold what the contract writes or reads."""
+    if n > 0 and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _rows_of(t):
+    """Leading dimensions of a tensor fold into rows; the last one is the row."""
+    lead = tuple(t.shape[:-1])
+    return lead, (int(np.prod(lead)) if lead else 1), int(t.shape[-1])
+
+
 def lowbit_sf_bytes(rows, k, fmt, layout):
     return int(lib().lowbit_sf_bytes(rows, k, fmt, layout))
 
@@ -125,6 +142,13 @@ def _alloc_q(rows, k, fmt, layout, device, out_packed, out_sf, lead=None):
     if out_sf is None:
         out_sf = torch.empty(lowbit_sf_bytes(rows, k, fmt, layout), dtype=torch.uint8, device=device)
     return out_packed, out_sf
+
+
+def _check_q_out(out_packed, out_sf, rows, k, fmt, layout):
+    _need(out_packed, torch.uint8, "out_packed")
+    _need(out_sf, torch.uint8, "out_sf")
+    _at_least(out_packed, rows * _row_bytes(fmt, k), "out_packed")
+    _at_least(out_sf, lowbit_sf_bytes(rows, k, fmt, layout), "out_sf")
 
 
 def _in_dtype(t, name):
@@ -145,11 +169,14 @@ def lowbit_add_rmsnorm_quant(input, residual, weight, eps=1e-6, fmt=NVFP4, layou
     _need(weight, dt, "weight")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
+        _at_least(global_scale, 1, "global_scale")
     if residual.shape != input.shape:
         raise ValueError(f"residual shape {tuple(residual.shape)} differs from input {tuple(input.shape)}")
-    lead, H = tuple(input.shape[:-1]), input.shape[-1]   # leading dims are rows
-    M = int(np.prod(lead)) if lead else 1
+    lead, M, H = _rows_of(input)   # leading dims are rows
+    if weight.numel() != H:
+        raise ValueError(f"weight has {weight.numel()} elements, the rows have {H}")
     out_packed, out_sf = _alloc_q(M, H, fmt, layout, input.device, out_packed, out_sf, lead)
+    _check_q_out(out_packed, out_sf, M, H, fmt, layout)
     name = "lowbit_add_rmsnorm_quant" if dt == torch.bfloat16 else "lowbit_add_rmsnorm_quant_fp16"
     _check(name, getattr(lib(), name)(
         _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, layout, _ptr(global_scale),
@@ -176,13 +203,18 @@ def lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps=1e-6, fmt=NVFP
     _need(weight, dt, "weight")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
+        _at_least(global_scale, 1, "global_scale")
     if residual.shape != input.shape:
         raise ValueError(f"residual shape {tuple(residual.shape)} differs from input {tuple(input.shape)}")
-    lead, H = tuple(input.shape[:-1]), input.shape[-1]
-    M = int(np.prod(lead)) if lead else 1
+    lead, M, H = _rows_of(input)
+    if weight.numel() != H:
+        raise ValueError(f"weight has {weight.numel()} elements, the rows have {H}")
     out_packed, out_sf_tiled = _alloc_q(M, H, fmt, TILED, input.device, out_packed, out_sf_tiled, lead)
     if out_sf_linear is None:
         out_sf_linear = torch.empty(lowbit_sf_bytes(M, H, fmt, LINEAR), dtype=torch.uint8, device=input.device)
+    _check_q_out(out_packed, out_sf_tiled, M, H, fmt, TILED)
+    _need(out_sf_linear, torch.uint8, "out_sf_linear")
+    _at_least(out_sf_linear, lowbit_sf_bytes(M, H, fmt, LINEAR), "out_sf_linear")
     name = "lowbit_add_rmsnorm_quant_both_sf" + ("" if dt == torch.bfloat16 else "_fp16")
     _check(name, getattr(lib(), name)(
         _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, _ptr(global_scale),
@@ -205,9 +237,10 @@ def lowbit_quantize(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=N
     _need(x, dt, "x")
     if global_scale is not None:
         _need(global_scale, torch.float32, "global_scale")
-    lead, K = tuple(x.shape[:-1]), x.shape[-1]           # leading dims are rows
-    rows = int(np.prod(lead)) if lead else 1
+        _at_least(global_scale, 1, "global_scale")
+    lead, rows, K = _rows_of(x)           # leading dims are rows
     out_packed, out_sf = _alloc_q(rows, K, fmt, layout, x.device, out_packed, out_sf, lead)
+    _check_q_out(out_packed, out_sf, rows, K, fmt, layout)
     name = "lowbit_quantize" if dt == torch.bfloat16 else "lowbit_quantize_fp16"
     _check(name, getattr(lib(), name)(
         _ptr(x), rows, K, fmt, layout, _ptr(global_scale), _ptr(out_packed), _ptr(out_sf),
@@ -223,37 +256,68 @@ def lowbit_quantize_fp16(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_pac
 
 
 def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):
+    """packed (..., K/2) (MXFP8: (..., K)) + scales -> bf16 (..., K)."""
     _need(packed, torch.uint8, "packed")
     _need(sf, torch.uint8, "sf")
-    rows, K = packed.shape[0], packed.shape[1] * (1 if fmt == MXFP8 else 2)
+    lead, rows, kb = _rows_of(packed)
+    K = kb * (1 if fmt == MXFP8 else 2)
+    _at_least(sf, lowbit_sf_bytes(rows, K, fmt, layout), "sf")
+    if global_scale is not None:
+        _need(global_scale, torch.float32, "global_scale")
+        _at_least(global_scale, 1, "global_scale")
     if out is None:
-        out = torch.empty((rows, K), dtype=torch.bfloat16, device=packed.device)
+        out = torch.empty(lead + (K,), dtype=torch.bfloat16, device=packed.device)
+    _need(out, torch.bfloat16, "out")
+    _at_least(out, rows * K, "out")
     _check("lowbit_dequantize", lib().lowbit_dequantize(
         _ptr(packed), _ptr(sf), rows, K, fmt, layout, _ptr(global_scale), _ptr(out), _stream(stream)))
     return out
 
 
 def _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha):
+    """Sizes of a GEMM call: A (..., K/2) with its leading dims as the M rows,
+    B (N, K/2); every buffer checked against the contract's sizes."""
     for t, n in ((a, "a"), (b, "b"), (sfa, "sfa"), (sfb, "sfb")):
         _need(t, torch.uint8, n)
-    M, N, K = a.shape[0], b.shape[0], a.shape[1] * 2
-    if b.shape[1] * 2 != K:
+    _, M, ka = _rows_of(a)
+    _, N, kb = _rows_of(b)
+    K = ka * 2
+    if kb * 2 != K:
         raise ValueError("a and b disagree on K")
+    # sizes are checked for the layouts the GEMM takes; any other layout or
+    # format is the C ABI's to refuse (LOWBIT_EINVAL)
+    if fmt in (NVFP4, MXFP4) and sfa_layout in (LINEAR, TILED) and sfb_layout in (LINEAR, TILED):
+        _at_least(sfa, lowbit_sf_bytes(M, K, fmt, sfa_layout), "sfa")
+        _at_least(sfb, lowbit_sf_bytes(N, K, fmt, sfb_layout), "sfb")
     return M, N, K, [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), M, N, K, fmt, sfa_layout, sfb_layout,
                      float(alpha)]
 
 
-def _out_bf16(out, M, N, dev):
+def _out_bf16(out, a, M, N):
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out = torch.empty(tuple(a.shape[:-1]) + (N,), dtype=torch.bfloat16, device=a.device)
     _need(out, torch.bfloat16, "out")
+    if out.numel() != M * N:
+        raise ValueError(f"out has {out.numel()} elements, the product has {M} x {N}")
     return out
+
+
+def _bias(bias, N):
+    _need(bias, torch.bfloat16, "bias")
+    if bias.numel() != N:
+        raise ValueError(f"bias has {bias.numel()} elements, the product has {N} columns")
+
+
+def _residual(residual, M, N):
+    _need(residual, torch.bfloat16, "residual")
+    if residual.numel() != M * N:
+        raise ValueError(f"residual has {residual.numel()} elements, the product has {M} x {N}")
 
 
 def lowbit_gemm_bf16(a, b, sfa, sfb, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR, alpha=1.0,
                      out=None, variant=VARIANT_AUTO, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
-    out = _out_bf16(out, M, N, a.device)
+    out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bf16", lib().lowbit_gemm_bf16(*head, _ptr(out), variant, _stream(stream)))
     return out
 
@@ -261,8 +325,8 @@ def lowbit_gemm_bf16(a, b, sfa, sfb, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LI
 def lowbit_gemm_bias_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
                           alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
-    _need(bias, torch.bfloat16, "bias")
-    out = _out_bf16(out, M, N, a.device)
+    _bias(bias, N)
+    out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bias_bf16",
            lib().lowbit_gemm_bias_bf16(*head, _ptr(bias), _ptr(out), variant, _stream(stream)))
     return out
@@ -271,8 +335,8 @@ def lowbit_gemm_bias_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sf
 def lowbit_gemm_residual_bf16(a, b, sfa, sfb, residual, fmt=NVFP4, sfa_layout=LINEAR,
                               sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
-    _need(residual, torch.bfloat16, "residual")
-    out = _out_bf16(out, M, N, a.device)
+    _residual(residual, M, N)
+    out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_residual_bf16",
            lib().lowbit_gemm_residual_bf16(*head, _ptr(residual), _ptr(out), variant, _stream(stream)))
     return out
@@ -282,9 +346,9 @@ def lowbit_gemm_bias_residual_bf16(a, b, sfa, sfb, bias, residual, fmt=NVFP4, sf
                                    sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO,
                                    stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
-    _need(bias, torch.bfloat16, "bias")
-    _need(residual, torch.bfloat16, "residual")
-    out = _out_bf16(out, M, N, a.device)
+    _bias(bias, N)
+    _residual(residual, M, N)
+    out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bias_residual_bf16", lib().lowbit_gemm_bias_residual_bf16(
         *head, _ptr(bias), _ptr(residual), _ptr(out), variant, _stream(stream)))
     return out
@@ -293,8 +357,8 @@ def lowbit_gemm_bias_residual_bf16(a, b, sfa, sfb, bias, residual, fmt=NVFP4, sf
 def lowbit_gemm_bias_gelu_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
                                alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
-    _need(bias, torch.bfloat16, "bias")
-    out = _out_bf16(out, M, N, a.device)
+    _bias(bias, N)
+    out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bias_gelu_bf16",
            lib().lowbit_gemm_bias_gelu_bf16(*head, _ptr(bias), _ptr(out), variant, _stream(stream)))
     return out
@@ -305,10 +369,13 @@ def lowbit_gemm_bias_gelu_fp4(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR
                               out_layout=LINEAR, variant=VARIANT_AUTO, stream=None):
     """GELU(alpha * A.B^T + bias) quantized to NVFP4 along N.  Returns (packed, scales)."""
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
-    _need(bias, torch.bfloat16, "bias")
+    _bias(bias, N)
     if out_global_scale is not None:
         _need(out_global_scale, torch.float32, "out_global_scale")
-    out_packed, out_sf = _alloc_q(M, N, NVFP4, out_layout, a.device, out_packed, out_sf)
+        _at_least(out_global_scale, 1, "out_global_scale")
+    out_packed, out_sf = _alloc_q(M, N, NVFP4, out_layout, a.device, out_packed, out_sf,
+                                  tuple(a.shape[:-1]))
+    _check_q_out(out_packed, out_sf, M, N, NVFP4, out_layout)
     _check("lowbit_gemm_bias_gelu_fp4", lib().lowbit_gemm_bias_gelu_fp4(
         *head, _ptr(bias), _ptr(out_global_scale), _ptr(out_packed), _ptr(out_sf), out_layout, variant,
         _stream(stream)))

@@ -340,3 +340,51 @@ def test_producer_accepts_leading_dims(orc):
     q2, t2 = lb.lowbit_quantize(dev_bf16(x), lb.MXFP4, lb.TILED)
     torch.cuda.synchronize()
     assert q3.shape == (4, 6, 256) and torch.equal(q3.reshape(24, 256), q2) and torch.equal(t3, t2)
+
+
+def test_binding_rejects_short_buffers():
+    """Buffers smaller than the contract needs are refused before any launch:
+    a LINEAR-sized scale buffer handed over for the padded layouts, short
+    packed outputs, a weight of the wrong length, short GEMM operands."""
+    x = torch.zeros((40, 512), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(512, dtype=torch.bfloat16, device="cuda")
+    lin = torch.empty(lb.lowbit_sf_bytes(40, 512, lb.NVFP4, lb.LINEAR), dtype=torch.uint8, device="cuda")
+    for layout in (lb.TILED, lb.SWZ128):
+        with pytest.raises(ValueError):
+            lb.lowbit_quantize(x, lb.NVFP4, layout, out_sf=lin)
+        with pytest.raises(ValueError):
+            lb.lowbit_add_rmsnorm_quant(x, x.clone(), w, EPS, lb.NVFP4, layout, out_sf=lin)
+    with pytest.raises(ValueError):
+        lb.lowbit_quantize(x, lb.NVFP4, lb.LINEAR, out_packed=torch.empty((40, 255), dtype=torch.uint8,
+                                                                          device="cuda"))
+    with pytest.raises(ValueError):
+        lb.lowbit_add_rmsnorm_quant(x, x.clone(), w[:256], EPS, lb.NVFP4, lb.LINEAR)
+    a, sa = lb.lowbit_quantize(x, lb.MXFP4, lb.TILED)
+    with pytest.raises(ValueError):
+        lb.lowbit_gemm_bf16(a, a, sa[:100], sa, fmt=lb.MXFP4, sfa_layout=lb.TILED, sfb_layout=lb.TILED)
+    with pytest.raises(ValueError):
+        lb.lowbit_gemm_bias_bf16(a, a, sa, sa, torch.zeros(39, dtype=torch.bfloat16, device="cuda"),
+                                 fmt=lb.MXFP4, sfa_layout=lb.TILED, sfb_layout=lb.TILED)
+    with pytest.raises(ValueError):
+        lb.lowbit_gemm_residual_bf16(a, a, sa, sa, torch.zeros((40, 39), dtype=torch.bfloat16, device="cuda"),
+                                     fmt=lb.MXFP4, sfa_layout=lb.TILED, sfb_layout=lb.TILED)
+    with pytest.raises(ValueError):
+        lb.lowbit_dequantize(a, sa[:10], lb.MXFP4, lb.TILED)
+    torch.cuda.synchronize()
+
+
+def test_dequantize_and_gemm_accept_leading_dims(orc):
+    """A packed (batch, tokens, K/2) tensor is rows x K for the dequantizer
+    and the GEMM (the shape lowbit_quantize returns for 3-D input)."""
+    x = synth.activation(24, 512, 91, outliers=True)
+    W = synth.weight(64, 512, 91)
+    p3, s3 = lb.lowbit_quantize(dev_bf16(x).reshape(2, 12, 512), lb.NVFP4, lb.TILED)
+    p2, s2 = lb.lowbit_quantize(dev_bf16(x), lb.NVFP4, lb.TILED)
+    b, sb = lb.lowbit_quantize(dev_bf16(W), lb.NVFP4, lb.TILED)
+    d3 = lb.lowbit_dequantize(p3, s3, lb.NVFP4, lb.TILED)
+    d2 = lb.lowbit_dequantize(p2, s2, lb.NVFP4, lb.TILED)
+    g3 = lb.lowbit_gemm_bf16(p3, b, s3, sb, fmt=lb.NVFP4, sfa_layout=lb.TILED, sfb_layout=lb.TILED)
+    g2 = lb.lowbit_gemm_bf16(p2, b, s2, sb, fmt=lb.NVFP4, sfa_layout=lb.TILED, sfb_layout=lb.TILED)
+    torch.cuda.synchronize()
+    assert d3.shape == (2, 12, 512) and torch.equal(d3.reshape(24, 512), d2)
+    assert g3.shape == (2, 12, 64) and torch.equal(g3.reshape(24, 64), g2)
