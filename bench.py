@@ -340,14 +340,29 @@ def build_decode_stages():
 
         stages.append(Stage(f"mxfp4_decode_gemm_{M}x{N}x{K}", gemm, "hbm", gemm_bytes(M, N, K, 32), "B",
                             HBM_PEAK))
+    # the NVFP4 chain as the workload defines it: weights quantized with
+    # gs_B = 6*448/amax(B), activations with gs_A = 6*448/amax(y) (calibrated
+    # once with the path itself at gs = 1), alpha = 1/(gs_A gs_B) for GEMM1 and
+    # 1/gs_B for GEMM2 (GEMM1 writes its FP4 output with gs_out = 1)
     c = synth.NVFP4_CHAIN
     H, N1 = c["H"], c["N1"]
-    gs1 = torch.tensor([1.0], dtype=torch.float32, device=dev)
-    w1 = rotating(N1, H, lb.NVFP4, c["seed"] + 50)
-    w2 = rotating(H, N1, lb.NVFP4, c["seed"] + 70)
+
+    def rotating_gs(N, K, seed, index, copies=8):
+        W = synth.weight(N, K, seed, index=index).to(dev)
+        gsb = 2688.0 / W.float().abs().max().item()
+        b, sfb = lb.lowbit_quantize(W, lb.NVFP4, lay, global_scale=torch.tensor([gsb], device=dev))
+        del W
+        return [(b.clone(), sfb.clone()) for _ in range(copies)], gsb
+
+    w1, gsb1 = rotating_gs(N1, H, c["seed"], 10)
+    w2, gsb2 = rotating_gs(H, N1, c["seed"], 11)
     bias1 = synth.bias(N1, c["seed"], index=12).to(dev)
     for M in (1, 128):
         x, r, w = (t.to(dev) for t in synth.producer_inputs(M, H, c["seed"] + M, outliers=True))
+        p, s = lb.lowbit_add_rmsnorm_quant(x, r.clone(), w, EPS, lb.NVFP4, lay)
+        amax = lb.lowbit_dequantize(p, s, lb.NVFP4, lay).float().abs().max().item()
+        gs1 = torch.tensor([2688.0 / amax], dtype=torch.float32, device=dev)
+        alpha1, alpha2 = 1.0 / (gs1.item() * gsb1), 1.0 / gsb2
         a1 = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
         sa1 = torch.empty(lb.lowbit_sf_bytes(M, H, lb.NVFP4, lay), dtype=torch.uint8, device=dev)
         a2 = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
@@ -355,18 +370,19 @@ def build_decode_stages():
         out2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
         it = {"i": 0}
 
-        def prod(x=x, r=r, w=w, a1=a1, sa1=sa1):
+        def prod(x=x, r=r, w=w, a1=a1, sa1=sa1, gs1=gs1):
             lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.NVFP4, lay, global_scale=gs1, out_packed=a1, out_sf=sa1)
 
-        def g1(a1=a1, sa1=sa1, a2=a2, sa2=sa2, it=it):
+        def g1(a1=a1, sa1=sa1, a2=a2, sa2=sa2, it=it, alpha1=alpha1):
             b, sfb = w1[it["i"] % len(w1)]
             lb.lowbit_gemm_bias_gelu_fp4(a1, b, sa1, sfb, bias1, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay,
-                                         out_packed=a2, out_sf=sa2, out_layout=lay)
+                                         alpha=alpha1, out_packed=a2, out_sf=sa2, out_layout=lay)
 
-        def g2(a2=a2, sa2=sa2, out2=out2, it=it):
+        def g2(a2=a2, sa2=sa2, out2=out2, it=it, alpha2=alpha2):
             b, sfb = w2[it["i"] % len(w2)]
             it["i"] += 1
-            lb.lowbit_gemm_bf16(a2, b, sa2, sfb, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay, out=out2)
+            lb.lowbit_gemm_bf16(a2, b, sa2, sfb, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay, alpha=alpha2,
+                                out=out2)
 
         stages.append(Stage(f"chain_m{M}_add_rmsnorm_nvfp4_{M}x{H}", prod, "hbm", producer_bytes(M, H, 16), "B",
                             HBM_PEAK))
@@ -395,17 +411,22 @@ def report(stages):
     return kernels
 
 
-def cpu_baseline(stages, step_ideal_s):
-    """Time the CPU oracle, as it stands, on a bounded sample of every stage
-    of the step and extrapolate each stage by its share of the work (bytes
-    for the producers, multiply-accumulates for the GEMMs).  The sample is
-    the full 4096 x 4096 producer plus a block of rows x columns (full K) of
-    each GEMM, about 300 GMAC in all (10-30 s on the GPU host's cores).  A
-    reported baseline, not a target."""
-    from oracle import oracle as orc
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    orc.lib()
-    threads = orc.num_threads()
+
+def _oracle_step_time(orc, stages, small):
+    """Extrapolated oracle time of one step: the full 4096 x 4096 producer,
+    timed, plus a rows x columns block (full K) of each GEMM, timed and scaled
+    by its share of the GEMM's multiply-accumulates.  small: blocks 16x
+    smaller (the one-core run)."""
     parts = []
     t_step = 0.0
 
@@ -424,11 +445,12 @@ def cpu_baseline(stages, step_ideal_s):
     parts.append(f"producer {c['M']}x{c['H']} nvfp4 full ({dt:.2f} s)")
 
     def gemm_rate(M, N, K, fmt, Msub, Nsub, seed, gelu_fp4=False):
+        if small:
+            Msub, Nsub = Msub // 4, Nsub // 4
         A = synth.activation(Msub, K, seed, outliers=True)
         Wt = synth.weight(Nsub, K, seed)
-        gs = 1.0
-        a, sfa = orc.quantize(synth.bits(A), fmt, orc.TILED, gs=gs)
-        b, sfb = orc.quantize(synth.bits(Wt), fmt, orc.TILED, gs=gs)
+        a, sfa = orc.quantize(synth.bits(A), fmt, orc.TILED)
+        b, sfb = orc.quantize(synth.bits(Wt), fmt, orc.TILED)
         bias = synth.bits(synth.bias(Nsub, seed))
         if gelu_fp4:
             fn = lambda: orc.gemm_gelu_fp4(a, b, sfa, sfb, Msub, Nsub, K, fmt, orc.TILED, orc.TILED, 1.0,
@@ -453,9 +475,93 @@ def cpu_baseline(stages, step_ideal_s):
     ]
     for st, mac_rate in samples:
         t_step += (st.work / 2) / mac_rate
-    value = 100.0 * step_ideal_s / t_step
-    return {"value": value, "unit": "% of 1-GPU roofline", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(parts) + f"; extrapolated step time {t_step:.1f} s"}
+    return t_step, parts
+
+
+def oracle_config_seconds(orc):
+    """Oracle seconds of each workload on all host cores: the tiny MXFP4
+    case, the 4096 x 4096 producer and the four decode GEMMs in full; the
+    prefill GEMMs and the chain's GEMMs from a timed block scaled by its share
+    of the multiply-accumulates (the chain at M = 1 and 128 in full)."""
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    c = synth.TINY_MXFP4
+    x, r, w = synth.producer_inputs(c["M"], c["H"], c["seed"])
+    W = synth.weight(c["N"], c["H"], c["seed"])
+
+    def tiny():
+        d = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.MXFP4, orc.LINEAR)
+        b, sfb = orc.quantize(synth.bits(W), orc.MXFP4, orc.LINEAR)
+        orc.gemm(d["packed"], b, d["sf"], sfb, c["M"], c["N"], c["H"], orc.MXFP4, orc.LINEAR, orc.LINEAR)
+    out["tiny_mxfp4_m8_h256_gemm_8x128x256"] = round(timed(tiny), 5)
+
+    c = synth.NVFP4_PRODUCER
+    x, r, w = synth.producer_inputs(c["M"], c["H"], c["seed"], outliers=True)
+    out["nvfp4_producer_4096x4096"] = round(timed(lambda: orc.add_rmsnorm_quant(
+        synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4, orc.LINEAR, gs=1.0)), 3)
+
+    def gemm_s(M, N, K, fmt, epi=orc.EPI_NONE, rows=None, gelu_fp4=False, seed=9):
+        Ms = M if rows is None else min(M, rows)
+        A = synth.activation(Ms, K, seed)
+        Wt = synth.weight(N, K, seed)
+        a, sfa = orc.quantize(synth.bits(A), fmt, orc.TILED)
+        b, sfb = orc.quantize(synth.bits(Wt), fmt, orc.TILED)
+        bias = synth.bits(synth.bias(N, seed))
+        res = synth.bits(synth.residual(Ms, N, seed))
+        if gelu_fp4:
+            dt = timed(lambda: orc.gemm_gelu_fp4(a, b, sfa, sfb, Ms, N, K, fmt, orc.TILED, orc.TILED, 1.0, bias,
+                                                 1.0, orc.TILED))
+        else:
+            dt = timed(lambda: orc.gemm(a, b, sfa, sfb, Ms, N, K, fmt, orc.TILED, orc.TILED, 1.0, epi, bias, res))
+        return dt * M / Ms
+
+    for (M, N, K) in synth.MXFP4_DECODE["shapes"]:
+        out[f"mxfp4_decode_gemm_{M}x{N}x{K}"] = round(gemm_s(M, N, K, orc.MXFP4), 3)
+    for (M, N, K) in synth.MXFP4_PREFILL["shapes"]:
+        out[f"mxfp4_prefill_gemm_bias_residual_{M}x{N}x{K}_extrapolated"] = round(
+            gemm_s(M, N, K, orc.MXFP4, orc.EPI_BIAS_RESIDUAL, rows=256), 2)
+    ch = synth.NVFP4_CHAIN
+    for M in ch["Ms"]:
+        x, r, w = synth.producer_inputs(M, ch["H"], ch["seed"] + M, outliers=True)
+        tp = timed(lambda: orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4,
+                                                 orc.TILED))
+        rows = None if M <= 128 else 64
+        t1 = gemm_s(M, ch["N1"], ch["H"], orc.NVFP4, rows=rows, gelu_fp4=True)
+        t2 = gemm_s(M, ch["H"], ch["N1"], orc.NVFP4, rows=rows)
+        key = f"nvfp4_chain_m{M}" + ("_extrapolated" if rows else "")
+        out[key] = round(tp + t1 + t2, 3)
+    return out
+
+
+def cpu_baseline(stages, step_ideal_s):
+    """Time the CPU oracle, as it stands, on a bounded sample of every stage
+    of the step and extrapolate each stage by its share of the work (bytes
+    for the producers, multiply-accumulates for the GEMMs): once on all the
+    host's cores and once on one core (smaller GEMM blocks), plus the oracle
+    seconds of each workload.  A reported baseline, not a target."""
+    from oracle import oracle as orc
+
+    orc.lib()
+    threads = orc.num_threads()
+    t_all, parts = _oracle_step_time(orc, stages, small=False)
+    orc.set_num_threads(1)
+    try:
+        t_one, parts1 = _oracle_step_time(orc, stages, small=True)
+    finally:
+        orc.set_num_threads(threads)
+    configs = oracle_config_seconds(orc)
+    return {"value": 100.0 * step_ideal_s / t_all, "unit": "% of 1-GPU roofline", "cores": threads,
+            "kind": "oracle", "step_s": round(t_all, 2),
+            "value_1core": 100.0 * step_ideal_s / t_one, "step_s_1core": round(t_one, 2),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": "; ".join(parts) + f"; extrapolated step time {t_all:.1f} s on {threads} threads",
+            "sample_1core": "; ".join(parts1) + f"; extrapolated step time {t_one:.1f} s on 1 thread",
+            "config_seconds": configs}
 
 
 def source_digest():
@@ -591,12 +697,16 @@ def main():
     dom = max(stages, key=lambda s: s.mean_s())
     t = dom.mean_s()
     scale = 1e9 if dom.bound == "hbm" else 1e12
+    # priced at the step's roof (FP4 for every GEMM, as `value` and `dtype`);
+    # an NVFP4 GEMM's fraction of the fp16 MFMA peak it executes on rides beside
     roof = {"bound": dom.bound, "achieved": round(dom.work / t / scale, 2),
-            "peak": dom.own_peak / scale, "unit": "GB/s" if dom.bound == "hbm" else "TFLOP/s",
-            "frac": round(dom.work / t / dom.own_peak, 4), "traffic": measured_traffic(dom.name),
-            "kernel": dom.name}
-    if dom.own_dtype:
-        roof["peak_dtype"] = dom.own_dtype
+            "peak": dom.roof / scale, "unit": "GB/s" if dom.bound == "hbm" else "TFLOP/s",
+            "frac": round(dom.work / t / dom.roof, 4), "traffic": measured_traffic(dom.name),
+            "kernel": dom.name, "peak_dtype": "fp4" if dom.bound == "mfma" else "hbm"}
+    if dom.own_peak != dom.roof:
+        roof["executed_peak"] = dom.own_peak / scale
+        roof["executed_dtype"] = dom.own_dtype
+        roof["frac_of_executed_peak"] = round(dom.work / t / dom.own_peak, 4)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -681,3 +681,13 @@ int orc_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the following calls use (the timing of the oracle on one core and
+ * on all of them); n < 1 is ignored. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

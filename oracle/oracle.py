@@ -102,6 +102,8 @@ def lib():
                                     _vp, _vp, _vp, _vp, _vp]
     L.orc_num_threads.restype = _int
     L.orc_num_threads.argtypes = []
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads.argtypes = [_int]
     _lib = L
     return L
 
@@ -278,3 +280,8 @@ def gemm_gelu_fp4(a, b, sfa, sfb, M, N, K, fmt, layout_a, layout_b, alpha, bias,
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following oracle calls (OpenMP)."""
+    lib().orc_set_num_threads(int(n))
