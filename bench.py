@@ -115,16 +115,17 @@ class Stage:
     """A kernel launch with its per-launch HIP-event timing on torch's stream
     (the stream every lowbit call is launched on)."""
 
-    def __init__(self, name, fn, bound, work, unit_work, roof, own_peak=None, own_dtype=None):
+    def __init__(self, name, fn, bound, work, unit_work, roof, own_peak=None, own_dtype=None, reps=1):
         self.name, self.fn, self.bound, self.work, self.unit_work, self.roof = name, fn, bound, work, unit_work, roof
         # the peak of the arithmetic the kernel executes (the NVFP4 GEMM runs fp16
         # MFMAs on exactly dequantized operands); the step value prices every GEMM at FP4
         self.own_peak = roof if own_peak is None else own_peak
         self.own_dtype = own_dtype
+        self.reps = reps          # launches per call of fn (a graph replay holds several)
         self.times = []
 
     def mean_s(self):
-        return float(np.mean([EVENTS.elapsed_ms(a, b) for a, b in self.times])) * 1e-3
+        return float(np.mean([EVENTS.elapsed_ms(a, b) for a, b in self.times])) * 1e-3 / self.reps
 
     def ideal_s(self):
         return self.work / self.roof
@@ -306,12 +307,43 @@ def build_variant_stages():
     return stages
 
 
+DECODE_REPS = 8   # launches per graph replay: one per rotating weight copy
+
+
+def graphed(stage):
+    """The stage as a HIP graph of DECODE_REPS launches (captured from torch's
+    stream, onto which every lowbit call launches), replayed by stage.fn.  A
+    decode step is a launch-bound loop: replaying it as a graph measures the
+    kernels back to back, not the host's launch overhead (the library
+    allocates nothing and never synchronizes, so its calls capture as they
+    are).  The stage runs once eagerly first.
+
+    The graph holds raw device pointers of every tensor the captured calls
+    touch, and every later capture starts with torch.cuda.empty_cache(),
+    which returns freed blocks to the driver: the eager function, whose
+    closure owns those tensors, stays referenced by the stage for as long as
+    the graph can be replayed."""
+    log(f"[bench] capturing {stage.name}")
+    stage.fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(DECODE_REPS):
+            stage.fn()
+    torch.cuda.synchronize()
+    stage.eager_fn = stage.fn          # keeps the captured tensors alive
+    stage.fn, stage.reps, stage.graph = g.replay, DECODE_REPS, g
+    return stage
+
+
 def build_decode_stages():
     """The decode-shaped workloads, timed beside the step and reported apart
-    from `value`: the four MXFP4 decode GEMMs and the NVFP4 chain at 1 and 128
-    tokens (producer, GEMM1 with GELU -> FP4, GEMM2).  These are HBM-bound
-    (the weights dominate); each rotates over enough weight copies that the
-    256 MiB last-level cache cannot hold them, as a decode step sees them."""
+    from `value`: the four MXFP4 decode GEMMs (with a split-K workspace
+    offered, and without) and the NVFP4 chain at 1 and 128 tokens (producer,
+    GEMM1 with GELU -> FP4, GEMM2, the GEMMs with the workspace offered).
+    These are HBM-bound (the weights dominate); each rotates over enough
+    weight copies that the 256 MiB last-level cache cannot hold them, as a
+    decode step sees them."""
     dev = "cuda"
     stages = []
     lay = lb.TILED
@@ -325,21 +357,31 @@ def build_decode_stages():
         del W
         return [(b.clone(), sfb.clone()) for _ in range(copies)]
 
+    # one split-K workspace for every decode GEMM (the automatic choice splits
+    # K where the library's plan says so; each stage also runs without it)
     c = synth.MXFP4_DECODE
+    need = [lb.lowbit_gemm_workspace_bytes(M, N, K, f, lb.VARIANT_AUTO) for (M, N, K) in c["shapes"]
+            for f in (lb.NVFP4, lb.MXFP4)]
+    need += [lb.lowbit_gemm_workspace_bytes(M, N, K, lb.NVFP4, lb.VARIANT_AUTO)
+             for M in (1, 128) for (N, K) in ((synth.NVFP4_CHAIN["N1"], synth.NVFP4_CHAIN["H"]),
+                                              (synth.NVFP4_CHAIN["H"], synth.NVFP4_CHAIN["N1"]))]
+    wspace = torch.empty(max(need + [16]), dtype=torch.uint8, device=dev)
     for (M, N, K) in c["shapes"]:
         A = synth.activation(M, K, c["seed"]).to(dev)
         a, sfa = lb.lowbit_quantize(A, lb.MXFP4, lay)
-        ws = rotating(N, K, lb.MXFP4, c["seed"])
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        it = {"i": 0}
+        for use_ws in (True, False):
+            wts = rotating(N, K, lb.MXFP4, c["seed"])   # own copies: the other stage leaves nothing warm
+            it = {"i": 0}
 
-        def gemm(a=a, sfa=sfa, ws=ws, out=out, it=it):
-            b, sfb = ws[it["i"] % len(ws)]
-            it["i"] += 1
-            lb.lowbit_gemm_bf16(a, b, sfa, sfb, fmt=lb.MXFP4, sfa_layout=lay, sfb_layout=lay, out=out)
+            def gemm(a=a, sfa=sfa, wts=wts, out=out, it=it, ws=wspace if use_ws else None):
+                b, sfb = wts[it["i"] % len(wts)]
+                it["i"] += 1
+                lb.lowbit_gemm_bf16(a, b, sfa, sfb, fmt=lb.MXFP4, sfa_layout=lay, sfb_layout=lay, out=out,
+                                    workspace=ws)
 
-        stages.append(Stage(f"mxfp4_decode_gemm_{M}x{N}x{K}", gemm, "hbm", gemm_bytes(M, N, K, 32), "B",
-                            HBM_PEAK))
+            stages.append(graphed(Stage(f"mxfp4_decode_gemm_{M}x{N}x{K}" + ("" if use_ws else "_no_workspace"),
+                                        gemm, "hbm", gemm_bytes(M, N, K, 32), "B", HBM_PEAK)))
     # the NVFP4 chain as the workload defines it: weights quantized with
     # gs_B = 6*448/amax(B), activations with gs_A = 6*448/amax(y) (calibrated
     # once with the path itself at gs = 1), alpha = 1/(gs_A gs_B) for GEMM1 and
@@ -368,28 +410,30 @@ def build_decode_stages():
         a2 = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
         sa2 = torch.empty(lb.lowbit_sf_bytes(M, N1, lb.NVFP4, lay), dtype=torch.uint8, device=dev)
         out2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-        it = {"i": 0}
+        it = {"i": 0, "j": 0}
 
         def prod(x=x, r=r, w=w, a1=a1, sa1=sa1, gs1=gs1):
             lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.NVFP4, lay, global_scale=gs1, out_packed=a1, out_sf=sa1)
 
         def g1(a1=a1, sa1=sa1, a2=a2, sa2=sa2, it=it, alpha1=alpha1):
-            b, sfb = w1[it["i"] % len(w1)]
+            b, sfb = w1[it["j"] % len(w1)]
+            it["j"] += 1
             lb.lowbit_gemm_bias_gelu_fp4(a1, b, sa1, sfb, bias1, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay,
-                                         alpha=alpha1, out_packed=a2, out_sf=sa2, out_layout=lay)
+                                         alpha=alpha1, out_packed=a2, out_sf=sa2, out_layout=lay,
+                                         workspace=wspace)
 
         def g2(a2=a2, sa2=sa2, out2=out2, it=it, alpha2=alpha2):
             b, sfb = w2[it["i"] % len(w2)]
             it["i"] += 1
             lb.lowbit_gemm_bf16(a2, b, sa2, sfb, fmt=lb.NVFP4, sfa_layout=lay, sfb_layout=lay, alpha=alpha2,
-                                out=out2)
+                                out=out2, workspace=wspace)
 
-        stages.append(Stage(f"chain_m{M}_add_rmsnorm_nvfp4_{M}x{H}", prod, "hbm", producer_bytes(M, H, 16), "B",
-                            HBM_PEAK))
-        stages.append(Stage(f"chain_m{M}_nvfp4_gemm_gelu_fp4_{M}x{N1}x{H}", g1, "hbm",
-                            gemm_bytes(M, N1, H, 16, epi_bias=True, out_fp4=True), "B", HBM_PEAK))
-        stages.append(Stage(f"chain_m{M}_nvfp4_gemm_{M}x{H}x{N1}", g2, "hbm", gemm_bytes(M, H, N1, 16), "B",
-                            HBM_PEAK))
+        stages.append(graphed(Stage(f"chain_m{M}_add_rmsnorm_nvfp4_{M}x{H}", prod, "hbm", producer_bytes(M, H, 16),
+                                    "B", HBM_PEAK)))
+        stages.append(graphed(Stage(f"chain_m{M}_nvfp4_gemm_gelu_fp4_{M}x{N1}x{H}", g1, "hbm",
+                                    gemm_bytes(M, N1, H, 16, epi_bias=True, out_fp4=True), "B", HBM_PEAK)))
+        stages.append(graphed(Stage(f"chain_m{M}_nvfp4_gemm_{M}x{H}x{N1}", g2, "hbm", gemm_bytes(M, H, N1, 16),
+                                    "B", HBM_PEAK)))
     return stages
 
 

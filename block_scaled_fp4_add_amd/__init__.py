@@ -16,7 +16,7 @@ import torch
 NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: producer / quantizer / dequantizer, LINEAR scales
 NVFP4_B32 = 3                   # the NVFP4 rule on 32-blocks: the same three calls, LINEAR scales
 LINEAR, TILED, SWZ128 = 0, 1, 2   # SWZ128: the 128 x 4 swizzle, quantization side only
-VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = -1, 0, 1
+VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL, VARIANT_SPLITK = -1, 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowbit.so")
 
@@ -30,7 +30,7 @@ EXPORTS = (
     "lowbit_add_rmsnorm_quant_both_sf", "lowbit_add_rmsnorm_quant_both_sf_fp16",
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
-    "lowbit_gemm_pick_variant",
+    "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes",
 )
 
 
@@ -41,7 +41,7 @@ class LowbitError(RuntimeError):
 
 
 _lib = None
-_vp, _i64, _int, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+_vp, _i64, _int, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
 
 def lib():
@@ -69,18 +69,21 @@ def lib():
         L.lowbit_dequantize.restype = _int
         L.lowbit_dequantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
         head = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f32]
-        L.lowbit_gemm_bf16.argtypes = head + [_vp, _int, _vp]
-        L.lowbit_gemm_bias_bf16.argtypes = head + [_vp, _vp, _int, _vp]
-        L.lowbit_gemm_residual_bf16.argtypes = head + [_vp, _vp, _int, _vp]
-        L.lowbit_gemm_bias_residual_bf16.argtypes = head + [_vp, _vp, _vp, _int, _vp]
-        L.lowbit_gemm_bias_gelu_bf16.argtypes = head + [_vp, _vp, _int, _vp]
-        L.lowbit_gemm_bias_gelu_fp4.argtypes = head + [_vp, _vp, _vp, _vp, _int, _int, _vp]
+        tail = [_int, _vp, _sz, _vp]   # variant, workspace, workspace_bytes, stream
+        L.lowbit_gemm_bf16.argtypes = head + [_vp] + tail
+        L.lowbit_gemm_bias_bf16.argtypes = head + [_vp, _vp] + tail
+        L.lowbit_gemm_residual_bf16.argtypes = head + [_vp, _vp] + tail
+        L.lowbit_gemm_bias_residual_bf16.argtypes = head + [_vp, _vp, _vp] + tail
+        L.lowbit_gemm_bias_gelu_bf16.argtypes = head + [_vp, _vp] + tail
+        L.lowbit_gemm_bias_gelu_fp4.argtypes = head + [_vp, _vp, _vp, _vp, _int] + tail
         for n in ("lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
                   "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16",
                   "lowbit_gemm_bias_gelu_fp4"):
             getattr(L, n).restype = _int
         L.lowbit_gemm_pick_variant.restype = _int
-        L.lowbit_gemm_pick_variant.argtypes = [_i64, _i64, _i64, _int, _int]
+        L.lowbit_gemm_pick_variant.argtypes = [_i64, _i64, _i64, _int, _int, _sz]
+        L.lowbit_gemm_workspace_bytes.restype = _sz
+        L.lowbit_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
         _lib = L
     return _lib
 
@@ -293,6 +296,19 @@ def _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha):
                      float(alpha)]
 
 
+def _ws(workspace):
+    """(pointer, bytes) of an optional uint8 device workspace for split-K."""
+    if workspace is None:
+        return None, 0
+    _need(workspace, torch.uint8, "workspace")
+    return _ptr(workspace), workspace.numel()
+
+
+def lowbit_gemm_workspace_bytes(M, N, K, fmt=NVFP4, variant=VARIANT_AUTO):
+    """Workspace bytes the split-K schedule needs (0: it would not run)."""
+    return int(lib().lowbit_gemm_workspace_bytes(M, N, K, fmt, variant))
+
+
 def _out_bf16(out, a, M, N):
     if out is None:
         out = torch.empty(tuple(a.shape[:-1]) + (N,), dtype=torch.bfloat16, device=a.device)
@@ -315,58 +331,59 @@ def _residual(residual, M, N):
 
 
 def lowbit_gemm_bf16(a, b, sfa, sfb, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR, alpha=1.0,
-                     out=None, variant=VARIANT_AUTO, stream=None):
+                     out=None, variant=VARIANT_AUTO, workspace=None, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     out = _out_bf16(out, a, M, N)
-    _check("lowbit_gemm_bf16", lib().lowbit_gemm_bf16(*head, _ptr(out), variant, _stream(stream)))
+    _check("lowbit_gemm_bf16", lib().lowbit_gemm_bf16(*head, _ptr(out), variant, *_ws(workspace), _stream(stream)))
     return out
 
 
 def lowbit_gemm_bias_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
-                          alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
+                          alpha=1.0, out=None, variant=VARIANT_AUTO, workspace=None, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     _bias(bias, N)
     out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bias_bf16",
-           lib().lowbit_gemm_bias_bf16(*head, _ptr(bias), _ptr(out), variant, _stream(stream)))
+           lib().lowbit_gemm_bias_bf16(*head, _ptr(bias), _ptr(out), variant, *_ws(workspace), _stream(stream)))
     return out
 
 
 def lowbit_gemm_residual_bf16(a, b, sfa, sfb, residual, fmt=NVFP4, sfa_layout=LINEAR,
-                              sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
+                              sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO, workspace=None,
+                              stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     _residual(residual, M, N)
     out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_residual_bf16",
-           lib().lowbit_gemm_residual_bf16(*head, _ptr(residual), _ptr(out), variant, _stream(stream)))
+           lib().lowbit_gemm_residual_bf16(*head, _ptr(residual), _ptr(out), variant, *_ws(workspace), _stream(stream)))
     return out
 
 
 def lowbit_gemm_bias_residual_bf16(a, b, sfa, sfb, bias, residual, fmt=NVFP4, sfa_layout=LINEAR,
                                    sfb_layout=LINEAR, alpha=1.0, out=None, variant=VARIANT_AUTO,
-                                   stream=None):
+                                   workspace=None, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     _bias(bias, N)
     _residual(residual, M, N)
     out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bias_residual_bf16", lib().lowbit_gemm_bias_residual_bf16(
-        *head, _ptr(bias), _ptr(residual), _ptr(out), variant, _stream(stream)))
+        *head, _ptr(bias), _ptr(residual), _ptr(out), variant, *_ws(workspace), _stream(stream)))
     return out
 
 
 def lowbit_gemm_bias_gelu_bf16(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
-                               alpha=1.0, out=None, variant=VARIANT_AUTO, stream=None):
+                               alpha=1.0, out=None, variant=VARIANT_AUTO, workspace=None, stream=None):
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     _bias(bias, N)
     out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bias_gelu_bf16",
-           lib().lowbit_gemm_bias_gelu_bf16(*head, _ptr(bias), _ptr(out), variant, _stream(stream)))
+           lib().lowbit_gemm_bias_gelu_bf16(*head, _ptr(bias), _ptr(out), variant, *_ws(workspace), _stream(stream)))
     return out
 
 
 def lowbit_gemm_bias_gelu_fp4(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR,
                               alpha=1.0, out_global_scale=None, out_packed=None, out_sf=None,
-                              out_layout=LINEAR, variant=VARIANT_AUTO, stream=None):
+                              out_layout=LINEAR, variant=VARIANT_AUTO, workspace=None, stream=None):
     """GELU(alpha * A.B^T + bias) quantized to NVFP4 along N.  Returns (packed, scales)."""
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     _bias(bias, N)
@@ -378,9 +395,9 @@ def lowbit_gemm_bias_gelu_fp4(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR
     _check_q_out(out_packed, out_sf, M, N, NVFP4, out_layout)
     _check("lowbit_gemm_bias_gelu_fp4", lib().lowbit_gemm_bias_gelu_fp4(
         *head, _ptr(bias), _ptr(out_global_scale), _ptr(out_packed), _ptr(out_sf), out_layout, variant,
-        _stream(stream)))
+        *_ws(workspace), _stream(stream)))
     return out_packed, out_sf
 
 
-def lowbit_gemm_pick_variant(M, N, K, fmt=NVFP4, variant=VARIANT_AUTO):
-    return int(lib().lowbit_gemm_pick_variant(M, N, K, fmt, variant))
+def lowbit_gemm_pick_variant(M, N, K, fmt=NVFP4, variant=VARIANT_AUTO, workspace_bytes=0):
+    return int(lib().lowbit_gemm_pick_variant(M, N, K, fmt, variant, workspace_bytes))

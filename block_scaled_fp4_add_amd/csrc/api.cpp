@@ -70,12 +70,13 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
                           int64_t M, int64_t N, int64_t K, int fmt, int la, int lb, float alpha,
                           int epi, const void* bias, const void* residual, void* out,
                           const float* gs_out, uint8_t* out_packed, uint8_t* out_sf, int out_layout,
-                          int variant, hipStream_t stream) {
+                          int variant, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const bool fp4_out = epi == lowbit::kEpiBiasGeluFp4;
   // EINVAL: enums and pointers
   if (!fmt_ok(fmt) || !layout_ok(la) || !layout_ok(lb)) return LOWBIT_EINVAL;
   if (fp4_out && !layout_ok(out_layout)) return LOWBIT_EINVAL;
-  if (variant < -1 || variant > 1) return LOWBIT_EINVAL;
+  if (variant < -1 || variant > lowbit::kVariantSplitK) return LOWBIT_EINVAL;
+  if (workspace_bytes > 0 && !workspace) return LOWBIT_EINVAL;
   if (M < 0 || N < 0 || K < 0) return LOWBIT_ESHAPE;
   const bool empty = (M == 0 || N == 0);
   if (!empty) {
@@ -91,8 +92,11 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   const int64_t B = block_of(fmt);
   if (K < B || K % B != 0) return LOWBIT_ESHAPE;
   if (fp4_out && N % 16 != 0) return LOWBIT_ESHAPE;
-  const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant);
+  const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, workspace ? workspace_bytes : 0);
   if (v < 0) return LOWBIT_ESHAPE;
+  // split-K asked for explicitly needs the workspace it documents
+  const lowbit::SplitPlan plan = lowbit::gemm_splitk_plan(M, N, K, variant == lowbit::kVariantSplitK);
+  if (v == lowbit::kVariantSplitK && !empty && (!workspace || workspace_bytes < plan.bytes)) return LOWBIT_EINVAL;
   // the prefill schedule addresses each operand through a 32-bit buffer offset
   if (v == 1 && (M * (K / 2) >= (int64_t(1) << 30) || N * (K / 2) >= (int64_t(1) << 30)))
     return LOWBIT_ESHAPE;
@@ -109,6 +113,7 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   } else if (!aligned(out, 16)) {
     return LOWBIT_EALIGN;
   }
+  if (v == lowbit::kVariantSplitK && !aligned(workspace, 16)) return LOWBIT_EALIGN;
   // EDEVICE
   if (lowbit_status d = device_check()) return d;
   GemmArgs g{};
@@ -131,6 +136,11 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   g.out_packed = out_packed;
   g.out_sf = out_sf;
   g.out_layout = out_layout;
+  if (v == lowbit::kVariantSplitK) {
+    g.ws = static_cast<float*>(workspace);
+    g.splits = plan.splits;
+    g.per = plan.per;
+  }
   if (getenv("LOWBIT_LOG"))
     fprintf(stderr, "[lowbit] gemm M=%lld N=%lld K=%lld fmt=%d epi=%d variant=%d\n", (long long)M,
             (long long)N, (long long)K, fmt, epi, v);
@@ -261,46 +271,53 @@ lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_
 lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
                                int64_t M, int64_t N, int64_t K, lowbit_format fmt,
                                lowbit_sf_layout sfa_layout, lowbit_sf_layout sfb_layout, float alpha,
-                               void* out, int variant, hipStream_t stream) {
+                               void* out, int variant, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiNone,
-                     nullptr, nullptr, out, nullptr, nullptr, nullptr, 0, variant, stream);
+                     nullptr, nullptr, out, nullptr, nullptr, nullptr, 0, variant, workspace, workspace_bytes,
+                     stream);
 }
 
 lowbit_status lowbit_gemm_bias_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                     const uint8_t* sfb, int64_t M, int64_t N, int64_t K, lowbit_format fmt,
                                     lowbit_sf_layout sfa_layout, lowbit_sf_layout sfb_layout, float alpha,
-                                    const void* bias, void* out, int variant, hipStream_t stream) {
+                                    const void* bias, void* out, int variant, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiBias, bias,
-                     nullptr, out, nullptr, nullptr, nullptr, 0, variant, stream);
+                     nullptr, out, nullptr, nullptr, nullptr, 0, variant, workspace, workspace_bytes, stream);
 }
 
 lowbit_status lowbit_gemm_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                         const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                         lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                         lowbit_sf_layout sfb_layout, float alpha, const void* residual,
-                                        void* out, int variant, hipStream_t stream) {
+                                        void* out, int variant, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiResidual,
-                     nullptr, residual, out, nullptr, nullptr, nullptr, 0, variant, stream);
+                     nullptr, residual, out, nullptr, nullptr, nullptr, 0, variant, workspace, workspace_bytes,
+                     stream);
 }
 
 lowbit_status lowbit_gemm_bias_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                              const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                              lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                              lowbit_sf_layout sfb_layout, float alpha, const void* bias,
-                                             const void* residual, void* out, int variant,
-                                             hipStream_t stream) {
+                                             const void* residual, void* out, int variant, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha,
                      lowbit::kEpiBiasResidual, bias, residual, out, nullptr, nullptr, nullptr, 0, variant,
-                     stream);
+                     workspace, workspace_bytes, stream);
 }
 
 lowbit_status lowbit_gemm_bias_gelu_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                          const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                          lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                          lowbit_sf_layout sfb_layout, float alpha, const void* bias,
-                                         void* out, int variant, hipStream_t stream) {
+                                         void* out, int variant, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiBiasGelu,
-                     bias, nullptr, out, nullptr, nullptr, nullptr, 0, variant, stream);
+                     bias, nullptr, out, nullptr, nullptr, nullptr, 0, variant, workspace, workspace_bytes,
+                     stream);
 }
 
 lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
@@ -309,15 +326,23 @@ lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, cons
                                         lowbit_sf_layout sfb_layout, float alpha, const void* bias,
                                         const float* out_global_scale, uint8_t* out_packed,
                                         uint8_t* out_sf, lowbit_sf_layout out_layout, int variant,
-                                        hipStream_t stream) {
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha,
                      lowbit::kEpiBiasGeluFp4, bias, nullptr, nullptr, out_global_scale, out_packed, out_sf,
-                     out_layout, variant, stream);
+                     out_layout, variant, workspace, workspace_bytes, stream);
 }
 
-int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant) {
+int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant,
+                             size_t workspace_bytes) {
   if (!fmt_ok(fmt) || M < 0 || N < 0 || K < block_of(fmt) || K % block_of(fmt) != 0) return -1;
-  return lowbit::gemm_pick_variant(M, N, K, fmt, variant);
+  if (variant < -1 || variant > lowbit::kVariantSplitK) return -1;
+  return lowbit::gemm_pick_variant(M, N, K, fmt, variant, workspace_bytes);
+}
+
+size_t lowbit_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant) {
+  if (!fmt_ok(fmt) || M < 0 || N < 0 || K < block_of(fmt) || K % block_of(fmt) != 0) return 0;
+  if (variant != -1 && variant != lowbit::kVariantSplitK) return 0;
+  return lowbit::gemm_splitk_plan(M, N, K, variant == lowbit::kVariantSplitK).bytes;
 }
 
 }  // extern "C"

@@ -9,31 +9,69 @@ namespace lowbit {
 namespace gk {
 template <int FMT, int EPI>
 hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s);
+template <int FMT, int EPI>
+hipError_t launch_splitk(const GemmArgs& g, hipStream_t s);
 }  // namespace gk
 
 namespace {
 using gk::launch_fmt_epi;
 
+template <int FMT, int EPI>
+hipError_t launch_one(const GemmArgs& g, int variant, hipStream_t s) {
+  return variant == kVariantSplitK ? gk::launch_splitk<FMT, EPI>(g, s) : launch_fmt_epi<FMT, EPI>(g, variant, s);
+}
+
 template <int FMT>
 hipError_t launch_fmt(const GemmArgs& g, int variant, hipStream_t s) {
   switch (g.epi) {
-    case kEpiNone: return launch_fmt_epi<FMT, kEpiNone>(g, variant, s);
-    case kEpiBias: return launch_fmt_epi<FMT, kEpiBias>(g, variant, s);
-    case kEpiResidual: return launch_fmt_epi<FMT, kEpiResidual>(g, variant, s);
-    case kEpiBiasResidual: return launch_fmt_epi<FMT, kEpiBiasResidual>(g, variant, s);
-    case kEpiBiasGelu: return launch_fmt_epi<FMT, kEpiBiasGelu>(g, variant, s);
-    case kEpiBiasGeluFp4: return launch_fmt_epi<FMT, kEpiBiasGeluFp4>(g, variant, s);
+    case kEpiNone: return launch_one<FMT, kEpiNone>(g, variant, s);
+    case kEpiBias: return launch_one<FMT, kEpiBias>(g, variant, s);
+    case kEpiResidual: return launch_one<FMT, kEpiResidual>(g, variant, s);
+    case kEpiBiasResidual: return launch_one<FMT, kEpiBiasResidual>(g, variant, s);
+    case kEpiBiasGelu: return launch_one<FMT, kEpiBiasGelu>(g, variant, s);
+    case kEpiBiasGeluFp4: return launch_one<FMT, kEpiBiasGeluFp4>(g, variant, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant) {
-  (void)N;
-  // NVFP4 rows of K % 32 == 16 elements: decode schedule only, any M (in
+// Split-K targets twice as many workgroups as the chip has CUs, each split
+// holding at least four supersteps of K (one per wave).  Its second launch
+// costs about as much as one round trip of loads, so the automatic choice
+// splits only K of 16 supersteps or more (measured: (41, 1536, 6144) MXFP4
+// 13.7 -> 10.7 us split; (41, 4608, 1536) 6.8 -> 9.4 us, so not split).
+constexpr int64_t kSplitTargetWorkgroups = 512;
+constexpr int64_t kSplitMinSupersteps = 16;
+
+SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, bool force) {
+  const int64_t nss = (K + 255) / 256;
+  SplitPlan none{1, (int)nss, 0};
+  if (M <= 0 || M > 128 || N <= 0 || K <= 0) return none;
+  const int64_t tiles = (N + 31) / 32, mt = (M + 31) / 32;
+  int64_t S = (kSplitTargetWorkgroups + tiles - 1) / tiles;
+  if (S > nss / 4) S = nss / 4;
+  if (!force && nss < kSplitMinSupersteps) S = 1;
+  if (force && S < 2 && nss >= 2) S = 2;
+  if (S <= 1) return none;
+  const int64_t per = (nss + S - 1) / S;
+  S = (nss + per - 1) / per;
+  return SplitPlan{(int)S, (int)per, (size_t)(S * tiles * mt * 1024 * 4)};
+}
+
+int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, size_t ws_bytes) {
+  // NVFP4 rows of K % 32 == 16 elements: decode schedules only, any M (in
   // 128-row slices past 128 rows); an explicit prefill request is refused
   const bool half_k = fmt == kNVFP4 && (K / 2) % 16 != 0;
+  if (variant == kVariantSplitK) {
+    // the caller asked for split-K: M <= 128 and a K of two supersteps at least
+    if (M == 0 || N == 0) return kVariantSplitK;   // nothing to run
+    return gemm_splitk_plan(M, N, K, true).splits > 1 ? kVariantSplitK : -1;
+  }
+  if (variant == -1 && M <= 128) {
+    const SplitPlan p = gemm_splitk_plan(M, N, K, false);
+    if (p.splits > 1 && ws_bytes >= p.bytes) return kVariantSplitK;
+  }
   if (half_k) return (variant == -1 || variant == 0) ? 0 : -1;
   if (variant == -1) return M <= 128 ? 0 : 1;
   if (variant == 0) return M <= 128 ? 0 : -1;   // the decode tile holds at most 128 tokens

@@ -1185,17 +1185,24 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 // ===========================================================================
 // Decode schedule (weights as the MFMA row operand, K split across waves)
 // ===========================================================================
-template <int FMT, int MT, int W, int EPI, bool DB = true, bool HALF = false>
+// Decode schedule.  SPLIT: split-K -- workgroup (tile, y) takes supersteps
+// [y * g.per, (y + 1) * g.per) of K and writes its partial C^T tiles, in the
+// MFMA accumulator layout (lane-major, 16 floats a lane), to the workspace
+// at g.ws + ((y * tiles + tile) * MT + i) * 1024; gemm_splitk_reduce_kernel
+// sums the partials and applies the epilogue.
+template <int FMT, int MT, int W, int EPI, bool DB = true, bool HALF = false, bool SPLIT = false>
 __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float red[W * MT * 64 * 16];
-  __shared__ __attribute__((aligned(16))) float tile[MT * 32 * kEpiPitch];
+  __shared__ __attribute__((aligned(16))) float tile[SPLIT ? 1 : MT * 32 * kEpiPitch];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, c = lane >> 5;
   const int64_t n0 = (int64_t)blockIdx.x * 32;
   const int64_t kbytes = g.K / 2;
   const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
-  const int64_t nss = (g.K + 255) / 256;
+  const int64_t nss_all = (g.K + 255) / 256;
+  const int64_t s_begin = SPLIT ? (int64_t)blockIdx.y * g.per : 0;
+  const int64_t nss = SPLIT ? (s_begin + g.per < nss_all ? s_begin + g.per : nss_all) : nss_all;
 
   v16f acc[1][MT];
 #pragma unroll
@@ -1223,7 +1230,7 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  int64_t ss = wave;
+  int64_t ss = s_begin + wave;
   if constexpr (DB) {
     if (ss < nss) load(B0{}, ss);
     for (; ss < nss; ss += 2 * W) {
@@ -1240,28 +1247,75 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
     }
   }
 
-  // cross-wave sum of the partial C^T tiles
+  // cross-wave sum of the partial C^T tiles: every wave writes its
+  // accumulators, then thread t sums element e = t, t + 64 W, .. over the W
+  // waves in wave order (one barrier; element e = (i * 64 + l) * 16 + k is
+  // accumulator k of lane l for M-tile i)
 #pragma unroll
   for (int i = 0; i < MT; i++)
 #pragma unroll
     for (int k = 0; k < 16; k++) red[((wave * MT + i) * 64 + lane) * 16 + k] = acc[0][i][k];
   __syncthreads();
-  for (int e = tid; e < MT * 64 * 16; e += W * 64) {
-    float s = 0.0f;
+  if constexpr (SPLIT) {
+    // the partial goes out in the accumulator layout, consecutive threads
+    // writing consecutive floats
+    float* dst = g.ws + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * MT * 1024;
+    for (int e = tid; e < MT * 64 * 16; e += W * 64) {
+      float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; w++) s += red[w * MT * 64 * 16 + e];
-    // e = (i * 64 + l) * 16 + k: C^T row n = (k/4)*8 + (l/32)*4 + k%4, column m = l % 32
-    const int i = e / 1024, l = (e / 16) % 64, k = e % 16;
-    const int nl = (k >> 2) * 8 + (l >> 5) * 4 + (k & 3), ml = l & 31;
-    tile[(i * 32 + ml) * kEpiPitch + nl] = s;
+      for (int w = 0; w < W; w++) s += red[w * MT * 64 * 16 + e];
+      dst[e] = s;
+    }
+  } else {
+    for (int e = tid; e < MT * 64 * 16; e += W * 64) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; w++) s += red[w * MT * 64 * 16 + e];
+      // C^T row n = (k/4)*8 + (l/32)*4 + k%4, column m = l % 32
+      const int i = e / 1024, l = (e / 16) % 64, k = e % 16;
+      const int nl = (k >> 2) * 8 + (l >> 5) * 4 + (k & 3), ml = l & 31;
+      tile[(i * 32 + ml) * kEpiPitch + nl] = s;
+    }
+    __syncthreads();
+    if (wave < MT) {
+      const int er = lane & 31, ec = (lane >> 5) * 16;
+      epi_run16<EPI>(tile + (wave * 32 + er) * kEpiPitch + ec, wave * 32 + er, n0 + ec, g);
+    }
+    if constexpr (EPI == kEpiBiasGeluFp4)
+      fp4_out_padding(g, 0, (g.M + 31) / 32 * 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, tid, W * 64);
   }
+}
+
+// Split-K second pass: one wave per (32-column tile, M-tile): the partials
+// of the g.splits workgroups are summed in split order (the result does not
+// depend on timing), transposed through LDS, and the epilogue applied.
+template <int EPI>
+__global__ __launch_bounds__(64) void gemm_splitk_reduce_kernel(GemmArgs g, int MT) {
+  __shared__ __attribute__((aligned(16))) float t[32 * kEpiPitch];
+  const int lane = threadIdx.x, r = lane & 31, c = lane >> 5;
+  const int64_t tiles = gridDim.x, tile = blockIdx.x, i = blockIdx.y;
+  const int64_t n0 = tile * 32;
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) v[k] = 0.0f;
+  for (int y = 0; y < g.splits; y++) {
+    const float4* p = reinterpret_cast<const float4*>(g.ws + ((y * tiles + tile) * MT + i) * 1024 + lane * 16);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float4 w = p[q];
+      v[4 * q] += w.x;
+      v[4 * q + 1] += w.y;
+      v[4 * q + 2] += w.z;
+      v[4 * q + 3] += w.w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 16; k++) t[r * kEpiPitch + (k >> 2) * 8 + c * 4 + (k & 3)] = v[k];
   __syncthreads();
-  if (wave < MT) {
-    const int er = lane & 31, ec = (lane >> 5) * 16;
-    epi_run16<EPI>(tile + (wave * 32 + er) * kEpiPitch + ec, wave * 32 + er, n0 + ec, g);
-  }
+  const int ec = c * 16;
+  epi_run16<EPI>(t + r * kEpiPitch + ec, i * 32 + r, n0 + ec, g);
   if constexpr (EPI == kEpiBiasGeluFp4)
-    fp4_out_padding(g, 0, (g.M + 31) / 32 * 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, tid, W * 64);
+    fp4_out_padding(g, i * 32, i * 32 + 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, lane, 64);
 }
 
 template <int FMT, int EPI>

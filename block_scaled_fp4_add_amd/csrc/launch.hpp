@@ -38,10 +38,28 @@ struct GemmArgs {
   uint8_t* out_packed;        // FP4 output: (M, N/2)
   uint8_t* out_sf;            // FP4 output scales
   int out_layout;
+  float* ws;                  // split-K: fp32 partial tiles (device), else nullptr
+  int splits;                 // split-K: workgroups along K per 32-column tile
+  int per;                    // split-K: supersteps (256 elements of K) per split
 };
 
-// Schedule resolution shared by the launcher and lowbit_gemm_pick_variant.
-int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant);
+// Schedules: 0 decode, 1 prefill, 2 split-K decode (needs a workspace).
+constexpr int kVariantSplitK = 2;
+
+// Split-K plan of a GEMM with M <= 128: `splits` workgroups along K per
+// 32-column tile (1: no split), `per` supersteps each, `bytes` of workspace
+// for the partials.  force: at least two splits whenever K has two supersteps.
+struct SplitPlan {
+  int splits;
+  int per;
+  size_t bytes;
+};
+SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, bool force);
+
+// Schedule resolution shared by the launcher, lowbit_gemm_pick_variant and
+// lowbit_gemm_workspace_bytes: -1 resolves by shape and by the workspace the
+// caller offers (ws_bytes); returns -1 for a variant that cannot run the shape.
+int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, size_t ws_bytes);
 hipError_t launch_gemm(const GemmArgs& g, int variant, hipStream_t s);
 
 }  // namespace lowbit

@@ -92,12 +92,19 @@ typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2, LOWBIT_NVFP
  * only; the GEMMs return LOWBIT_EINVAL for it. */
 typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1, LOWBIT_SF_SWZ128 = 2 } lowbit_sf_layout;
 
-/* GEMM schedule: -1 picks by shape; 0 = decode (weights as the MFMA row
- * operand, K split across the waves of a workgroup, for small M); 1 = prefill
- * (LDS-staged macro tiles, for large M).  Cf. [FRT] `variant`. */
+/* GEMM schedule: -1 picks by shape (and by the workspace offered); 0 =
+ * decode (weights as the MFMA row operand, K split across the waves of a
+ * workgroup, for small M); 1 = prefill (LDS-staged macro tiles, for large M);
+ * 2 = split-K decode ([FRT] "Available Functions": the stream-K
+ * down-projection functions nvfp4_gemm_streamk_bf16 / _streamk_bias_bf16):
+ * M <= 128, K split across workgroups as well, each writing fp32 partial
+ * tiles into the caller's workspace, which a second kernel sums in a fixed
+ * order (the result does not depend on timing) before the epilogue.
+ * Cf. [FRT] `variant`. */
 #define LOWBIT_VARIANT_AUTO (-1)
 #define LOWBIT_VARIANT_DECODE 0
 #define LOWBIT_VARIANT_PREFILL 1
+#define LOWBIT_VARIANT_SPLITK 2
 
 /* Human-readable name of a status. */
 const char* lowbit_status_str(lowbit_status s);
@@ -189,36 +196,48 @@ lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_
  * variant: LOWBIT_VARIANT_*; an explicit variant that cannot run the shape
  * returns LOWBIT_ESHAPE instead of silently picking another schedule.
  * NVFP4 with K % 32 == 16 (packed rows of 8 mod 16 bytes) runs on the decode
- * schedule only, at any M (more than 128 rows go as consecutive launches
- * over 128-row slices); LOWBIT_VARIANT_PREFILL returns LOWBIT_ESHAPE for it. */
+ * schedules only, at any M (more than 128 rows go as consecutive launches
+ * over 128-row slices); LOWBIT_VARIANT_PREFILL returns LOWBIT_ESHAPE for it.
+ * workspace, workspace_bytes: device scratch for the split-K partials
+ * (16-byte aligned), owned by the caller; NULL / 0 = none.  With
+ * LOWBIT_VARIANT_AUTO the split-K schedule runs only when it is offered at
+ * least lowbit_gemm_workspace_bytes(M, N, K, fmt, LOWBIT_VARIANT_AUTO) bytes
+ * (and that is non-zero); LOWBIT_VARIANT_SPLITK needs
+ * lowbit_gemm_workspace_bytes(M, N, K, fmt, LOWBIT_VARIANT_SPLITK) bytes
+ * (LOWBIT_EINVAL with less), M <= 128 and K of at least 512 elements
+ * (LOWBIT_ESHAPE otherwise).  The workspace contents need no initialisation
+ * and are left undefined; two launches in flight on different streams must
+ * not share one. */
 lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                lowbit_sf_layout sfb_layout, float alpha, void* out, int variant,
-                               hipStream_t stream);
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 lowbit_status lowbit_gemm_bias_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                     const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                     lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                     lowbit_sf_layout sfb_layout, float alpha, const void* bias,
-                                    void* out, int variant, hipStream_t stream);
+                                    void* out, int variant, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 lowbit_status lowbit_gemm_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                         const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                         lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                         lowbit_sf_layout sfb_layout, float alpha,
                                         const void* residual, void* out, int variant,
-                                        hipStream_t stream);
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 lowbit_status lowbit_gemm_bias_residual_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                              const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                              lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                              lowbit_sf_layout sfb_layout, float alpha,
                                              const void* bias, const void* residual, void* out,
-                                             int variant, hipStream_t stream);
+                                             int variant, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
 lowbit_status lowbit_gemm_bias_gelu_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                          const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                          lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                          lowbit_sf_layout sfb_layout, float alpha,
                                          const void* bias, void* out, int variant,
-                                         hipStream_t stream);
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* GEMM + bias + GELU emitting NVFP4 for the next projection ([FRT]
  * nvfp4_gemm_bias_gelu_nvfp4: packed FP4 plus scales, no bf16 tensor in
@@ -233,11 +252,21 @@ lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, cons
                                         const void* bias, const float* out_global_scale,
                                         uint8_t* out_packed, uint8_t* out_sf,
                                         lowbit_sf_layout out_layout, int variant,
-                                        hipStream_t stream);
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Which schedule a GEMM call with these sizes would run (-1 auto resolved),
- * or -1 if the sizes are invalid.  Host-only, launches nothing. */
-int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant);
+/* Which schedule a GEMM call with these sizes and this much workspace would
+ * run (-1 auto resolved), or -1 if the sizes or the variant are invalid.
+ * Host-only, launches nothing. */
+int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant,
+                             size_t workspace_bytes);
+
+/* Workspace bytes the split-K schedule needs for these sizes: variant
+ * LOWBIT_VARIANT_AUTO gives the amount that lets the automatic choice split
+ * K (0 when it would not split: M > 128, or K too short for the tile count),
+ * LOWBIT_VARIANT_SPLITK the amount an explicit split-K call needs (0 when it
+ * cannot run); 0 for every other variant and for invalid sizes (cf. [FRT]
+ * sfa_size_bytes, a size query beside the kernels).  Host-only. */
+size_t lowbit_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant);
 
 #ifdef __cplusplus
 }

@@ -66,12 +66,52 @@ def test_sf_bytes_matches_the_oracle(orc):
 
 def test_pick_variant():
     L = lb.lib()
-    assert L.lowbit_gemm_pick_variant(41, 4608, 1536, 1, -1) == 0      # small M: decode schedule
-    assert L.lowbit_gemm_pick_variant(128, 4608, 1536, 1, -1) == 0
-    assert L.lowbit_gemm_pick_variant(129, 4608, 1536, 1, -1) == 1     # prefill schedule
-    assert L.lowbit_gemm_pick_variant(8192, 4096, 14336, 0, -1) == 1
-    assert L.lowbit_gemm_pick_variant(8192, 4096, 14336, 1, 0) < 0     # decode needs M <= 128
-    assert L.lowbit_gemm_pick_variant(1, 17408, 5120, 1, 1) == 1       # prefill accepts any M
+    assert L.lowbit_gemm_pick_variant(41, 4608, 1536, 1, -1, 0) == 0      # small M: decode schedule
+    assert L.lowbit_gemm_pick_variant(128, 4608, 1536, 1, -1, 0) == 0
+    assert L.lowbit_gemm_pick_variant(129, 4608, 1536, 1, -1, 0) == 1     # prefill schedule
+    assert L.lowbit_gemm_pick_variant(8192, 4096, 14336, 0, -1, 0) == 1
+    assert L.lowbit_gemm_pick_variant(8192, 4096, 14336, 1, 0, 0) < 0     # decode needs M <= 128
+    assert L.lowbit_gemm_pick_variant(1, 17408, 5120, 1, 1, 0) == 1       # prefill accepts any M
+    assert L.lowbit_gemm_pick_variant(300, 64, 48, 0, -1, 0) == 0         # NVFP4, K % 32 == 16: decode
+    assert L.lowbit_gemm_pick_variant(300, 64, 48, 0, 1, 0) < 0           # ... and never prefill
+    assert L.lowbit_gemm_pick_variant(8, 128, 256, 1, 3, 0) < 0           # no such variant
+
+
+def splitk_plan(M, N, K):
+    """The split-K plan the library documents, written out: twice as many
+    workgroups as CUs, at least four supersteps (1024 elements) per split,
+    K of at least 16 supersteps, no empty split; bytes = splits x 32-column
+    tiles x M-tiles x 32 x 32 floats."""
+    nss = -(-K // 256)
+    tiles, mt = -(-N // 32), -(-M // 32)
+    S = min(-(-512 // tiles), nss // 4)
+    if nss < 16:
+        S = 1
+    if S <= 1:
+        return 1, 0
+    per = -(-nss // S)
+    S = -(-nss // per)
+    return S, S * tiles * mt * 1024 * 4
+
+
+@pytest.mark.parametrize("M,N,K", [(41, 4608, 1536), (41, 6144, 1536), (41, 1536, 6144), (1, 17408, 5120),
+                                   (1, 5120, 17408), (128, 5120, 17408), (128, 17408, 5120), (5, 40, 512), (2, 64, 4096)])
+def test_splitk_workspace_and_choice(M, N, K):
+    L = lb.lib()
+    for fmt in (0, 1):
+        S, need = splitk_plan(M, N, K)
+        assert L.lowbit_gemm_workspace_bytes(M, N, K, fmt, -1) == need
+        if need:
+            assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, need) == 2       # offered enough: split
+            assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, need - 1) == 0   # too little: decode
+        else:
+            assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, 1 << 30) == 0
+        forced = L.lowbit_gemm_workspace_bytes(M, N, K, fmt, 2)
+        assert forced >= need and forced > 0
+        assert L.lowbit_gemm_pick_variant(M, N, K, fmt, 2, 0) == 2
+    assert L.lowbit_gemm_workspace_bytes(M, N, K, 1, 0) == 0 and L.lowbit_gemm_workspace_bytes(M, N, K, 1, 1) == 0
+    assert L.lowbit_gemm_workspace_bytes(200, N, K, 1, 2) == 0             # split-K needs M <= 128
+    assert L.lowbit_gemm_pick_variant(200, N, K, 1, 2, 1 << 30) < 0
 
 
 class Buf:
@@ -161,14 +201,21 @@ def test_gemm_argument_order(buf):
     L = lb.lib()
     a, b, sa, sb, out = buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288), buf.at(16384)
 
-    def call(M, N, K, fmt=1, la=0, lb_=0, variant=-1, o=out, a_=a):
-        return L.lowbit_gemm_bf16(a_, b, sa, sb, M, N, K, fmt, la, lb_, 1.0, o, variant, None)
+    def call(M, N, K, fmt=1, la=0, lb_=0, variant=-1, o=out, a_=a, ws=None, wsb=0):
+        return L.lowbit_gemm_bf16(a_, b, sa, sb, M, N, K, fmt, la, lb_, 1.0, o, variant, ws, wsb, None)
 
     assert call(8, 128, 256, fmt=3) == EINVAL                # 32-block NVFP4: no GEMM
     assert call(8, 128, 256, fmt=4) == EINVAL
     assert call(8, 128, 256, la=2) == EINVAL                 # 128 x 4 swizzle: no GEMM
     assert call(8, 128, 256, fmt=2) == EINVAL                # MXFP8: no GEMM
-    assert call(8, 128, 256, variant=2) == EINVAL
+    assert call(8, 128, 256, variant=3) == EINVAL
+    assert call(8, 128, 256, wsb=64) == EINVAL               # workspace bytes without a workspace
+    assert call(8, 128, 1024, variant=2) == EINVAL           # split-K without its workspace
+    assert call(8, 128, 1024, variant=2, ws=buf.at(32768), wsb=100) == EINVAL
+    assert call(8, 128, 256, variant=2, ws=buf.at(32768), wsb=1 << 20) == ESHAPE   # one superstep: no split
+    assert call(200, 128, 1024, variant=2, ws=buf.at(32768), wsb=1 << 20) == ESHAPE  # M > 128
+    assert call(8, 128, 1024, variant=2, ws=buf.at(32772), wsb=1 << 15) == EALIGN   # workspace alignment
+    assert call(0, 128, 1024, variant=2) == OK               # empty: nothing to run
     assert call(8, 128, 256, o=None) == EINVAL
     assert call(-1, 128, 256) == ESHAPE
     assert call(8, 128, 48) == ESHAPE                        # K % 32
@@ -177,13 +224,15 @@ def test_gemm_argument_order(buf):
     assert call(0, 128, 256) == OK
     if NO_DEVICE:
         assert call(8, 128, 256) == EDEVICE
+        assert call(8, 128, 1024, variant=2, ws=buf.at(32768), wsb=1 << 15) == EDEVICE
     # epilogues that need an operand reject its absence
-    assert L.lowbit_gemm_bias_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1, None) == EINVAL
+    assert L.lowbit_gemm_bias_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1, None, 0,
+                                   None) == EINVAL
     assert L.lowbit_gemm_residual_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1,
-                                       None) == EINVAL
+                                       None, 0, None) == EINVAL
     # FP4 out: N must be a multiple of the NVFP4 block
     assert L.lowbit_gemm_bias_gelu_fp4(a, b, sa, sb, 8, 120, 256, 1, 0, 0, 1.0, buf.at(20480), None,
-                                       buf.at(24576), buf.at(28672), 0, -1, None) == ESHAPE
+                                       buf.at(24576), buf.at(28672), 0, -1, None, 0, None) == ESHAPE
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

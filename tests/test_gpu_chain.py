@@ -123,3 +123,92 @@ def test_nvfp4_chain(orc, weights, M):
     ok, worst = checkers.gemm_within_tolerance(got, ref2d, l12d)
     banner(f"  gemm2 at the full launch: worst {worst:.3g}, violations {int((~ok).sum())}")
     assert ok.all(), f"{int((~ok).sum())} outputs out of tolerance (worst ratio {worst})"
+
+
+@pytest.mark.parametrize("M", [1, 128])
+def test_nvfp4_chain_splitk(orc, weights, M):
+    """The decode chain with a workspace offered to both GEMMs (split-K where
+    the plan splits: GEMM2, K = 17408), checked like the launches above on
+    sampled rows and every column against the oracle fed with the device's
+    own bytes."""
+    W = weights
+    H, N1 = W["H"], W["N1"]
+    x, r, w = synth.producer_inputs(M, H, synth.NVFP4_CHAIN["seed"] + M, outliers=True)
+    y = orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4, orc.LINEAR,
+                              diag=True)["y"]
+    gsA = float(np.float32(2688.0 / np.abs(y).max()))
+    a1, sfa1 = lb.lowbit_add_rmsnorm_quant(dev_bf16(x), dev_bf16(r), dev_bf16(w), EPS, lb.NVFP4, lb.TILED,
+                                           global_scale=dev_f32(gsA))
+    alpha1, alpha2 = 1.0 / (gsA * W["gs1"]), 1.0 / W["gs2"]
+    n1 = lb.lowbit_gemm_workspace_bytes(M, N1, H, 0, -1)
+    n2 = lb.lowbit_gemm_workspace_bytes(M, H, N1, 0, -1)
+    assert n2 > 0, "the down-projection splits K"
+    ws = torch.empty(max(n1, n2), dtype=torch.uint8, device="cuda")
+    p1, s1 = lb.lowbit_gemm_bias_gelu_fp4(a1, W["d_b1"], sfa1, W["d_sfb1"], W["d_bias1"], fmt=0, sfa_layout=1,
+                                          sfb_layout=1, alpha=alpha1, out_layout=lb.TILED, workspace=ws)
+    out = lb.lowbit_gemm_bf16(p1, W["d_b2"], s1, W["d_sfb2"], fmt=0, sfa_layout=1, sfb_layout=1, alpha=alpha2,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 4 else np.unique(np.r_[0, 31, 32, 64, 100, M - 1])
+    a_dev, sfa_dev = linear_rows(orc, host_u8(a1), host_u8(sfa1), rows, H, 0, orc.TILED)
+    g1d = orc.gemm_gelu_fp4(a_dev, W["b1"], sfa_dev, W["sfb1"], len(rows), N1, H, 0, 0, 1, alpha1,
+                            synth.bits(W["bias1"]), 1.0, orc.LINEAR, diag=True)
+    gp, gsf = linear_rows(orc, host_u8(p1), host_u8(s1), rows, N1, 0, orc.TILED)
+    ce, se = checkers.fp4_out_windows(g1d, 1.0, len(rows), N1)
+    rep = checkers.compare_quantized(
+        orc, 0, 1.0, gp, gsf, g1d["packed"], g1d["sf"], g1d["y"], g1d["v"], g1d["spre"], len(rows), N1,
+        orc.LINEAR, code_extra=ce, scale_extra=se)
+    banner(f"  split-K chain gemm1 {dict(rep)}")
+    assert rep.ok(), rep
+    ref2, l12 = orc.gemm(gp, W["b2"], gsf, W["sfb2"], len(rows), H, N1, 0, 0, 1, alpha=alpha2)
+    ok, worst = checkers.gemm_within_tolerance(host_f64(out)[rows], ref2, l12)
+    banner(f"  split-K chain gemm2 worst {worst:.3g}")
+    assert ok.all()
+
+
+def test_decode_chain_graph_replays(orc, weights):
+    """The decode chain at M = 128 (producer, GEMM1 -> FP4, split-K GEMM2)
+    captured in a HIP graph and replayed three times, with eager work and
+    synchronisations between the replays: every replay matches the eager
+    result bit for bit (the library allocates nothing and never
+    synchronizes, so its calls capture as they are)."""
+    W = weights
+    M, H, N1 = 128, W["H"], W["N1"]
+    x, r, w = synth.producer_inputs(M, H, 4242, outliers=True)
+    xd, wd, r0 = dev_bf16(x), dev_bf16(w), dev_bf16(r)
+    a1 = torch.empty((M, H // 2), dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(lb.lowbit_sf_bytes(M, H, 0, 1), dtype=torch.uint8, device="cuda")
+    a2 = torch.empty((M, N1 // 2), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty(lb.lowbit_sf_bytes(M, N1, 0, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lb.lowbit_gemm_workspace_bytes(M, H, N1, 0, -1), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    rd = r0.clone()
+    gs = dev_f32(2.0)
+
+    def step():
+        lb.lowbit_add_rmsnorm_quant(xd, rd, wd, EPS, lb.NVFP4, lb.TILED, global_scale=gs, out_packed=a1,
+                                    out_sf=s1)
+        lb.lowbit_gemm_bias_gelu_fp4(a1, W["d_b1"], s1, W["d_sfb1"], W["d_bias1"], fmt=0, sfa_layout=1,
+                                     sfb_layout=1, alpha=1e-3, out_packed=a2, out_sf=s2, out_layout=1)
+        lb.lowbit_gemm_bf16(a2, W["d_b2"], s2, W["d_sfb2"], fmt=0, sfa_layout=1, sfb_layout=1, alpha=0.01,
+                            out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = (rd.clone(), a1.clone(), s1.clone(), a2.clone(), s2.clone(), out.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for k in range(3):
+        # eager work between the replays: the residual back to its input
+        # value (the producer updates it in place) and the outputs cleared
+        rd.copy_(r0)
+        for t in (a1, s1, a2, s2, out, ws):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (rd, a1, s1, a2, s2, out)
+        banner(f"  graph replay {k}")
+        assert all(torch.equal(a, b) for a, b in zip(got, want)), f"replay {k} differs from the eager run"

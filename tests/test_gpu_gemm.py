@@ -32,13 +32,23 @@ def operands(orc, M, N, K, fmt, la, lb_, seed, outliers=False):
     return a, sfa, b, sfb
 
 
-def run_gemm(orc, M, N, K, fmt, la, lb_, epi, variant, seed, alpha=1.0, sample=None, outliers=False):
-    banner(f"gemm M={M} N={N} K={K} fmt={fmt} la={la} lb={lb_} epi={epi} variant={variant} seed={seed}")
+def split_workspace(M, N, K, fmt, variant):
+    """A workspace of the size the split-K schedule asks for, filled with NaN
+    bytes (its contents need no initialisation), or None."""
+    n = lb.lowbit_gemm_workspace_bytes(M, N, K, fmt, variant)
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda") if n else None
+
+
+def run_gemm(orc, M, N, K, fmt, la, lb_, epi, variant, seed, alpha=1.0, sample=None, outliers=False,
+             workspace=False):
+    banner(f"gemm M={M} N={N} K={K} fmt={fmt} la={la} lb={lb_} epi={epi} variant={variant} seed={seed}"
+           f" workspace={workspace}")
     a, sfa, b, sfb = operands(orc, M, N, K, fmt, la, lb_, seed, outliers)
     bias = synth.bias(N, seed)
     res = synth.residual(M, N, seed)
+    ws = split_workspace(M, N, K, fmt, variant) if (workspace or variant == 2) else None
     out = EPI_FN[epi](dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb), bias=dev_bf16(bias), res=dev_bf16(res),
-                      fmt=fmt, sfa_layout=la, sfb_layout=lb_, alpha=alpha, variant=variant)
+                      fmt=fmt, sfa_layout=la, sfb_layout=lb_, alpha=alpha, variant=variant, workspace=ws)
     torch.cuda.synchronize()
     got = host_f64(out)
     assert np.all(np.isfinite(got))
@@ -183,6 +193,7 @@ def test_gemm_empty_and_errors(orc):
 
 def run_gelu_fp4(orc, M, N, K, fmt, variant, out_layout, seed, gs_out=1.0):
     banner(f"gelu_fp4 M={M} N={N} K={K} fmt={fmt} variant={variant} out_layout={out_layout}")
+    ws = split_workspace(M, N, K, fmt, variant) if variant == 2 else None
     a, sfa, b, sfb = operands(orc, M, N, K, fmt, 0, 1, seed)
     bias = synth.bias(N, seed)
     alpha = 1.0
@@ -191,7 +202,7 @@ def run_gelu_fp4(orc, M, N, K, fmt, variant, out_layout, seed, gs_out=1.0):
     p, s = lb.lowbit_gemm_bias_gelu_fp4(dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb), dev_bf16(bias),
                                         fmt=fmt, sfa_layout=0, sfb_layout=1, alpha=alpha,
                                         out_global_scale=dev_f32(gs_out), out_layout=out_layout,
-                                        variant=variant)
+                                        variant=variant, workspace=ws)
     torch.cuda.synchronize()
     code_extra, scale_extra = checkers.fp4_out_windows(ref, gs_out, M, N)
     rep = checkers.compare_quantized(orc, orc.NVFP4, gs_out, host_u8(p), host_u8(s), ref["packed"],
@@ -212,3 +223,71 @@ def test_gemm_gelu_fp4(orc, M, N, K, fmt, out_layout):
         if variant == 0 and M > 128:
             continue
         run_gelu_fp4(orc, M, N, K, fmt, variant, out_layout, seed=M + N)
+
+
+# --- split-K (decode schedule with K also split across workgroups) ---------------------------
+
+SPLITK_SHAPES = [(1, 32, 512), (5, 40, 768), (33, 70, 2048), (64, 96, 4352), (100, 48, 4608), (128, 264, 1536),
+                 (17, 1000, 3072), (3, 96, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_gemm_splitk_plain(orc, M, N, K, fmt):
+    run_gemm(orc, M, N, K, fmt, 0, 1, 0, 2, seed=M + N + K + 5, alpha=0.5)
+
+
+@pytest.mark.parametrize("epi", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("la,lb_", [(0, 0), (1, 1)])
+def test_gemm_splitk_epilogues(orc, epi, fmt, la, lb_):
+    run_gemm(orc, 97, 264, 2304, fmt, la, lb_, epi, 2, seed=epi * 10 + fmt + la)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (96, 272, 2560), (128, 160, 4096)])
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out_layout", [0, 1])
+def test_gemm_splitk_gelu_fp4(orc, M, N, K, fmt, out_layout):
+    run_gelu_fp4(orc, M, N, K, fmt, 2, out_layout, seed=M + N + 3)
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 96, 1552), (128, 200, 4112), (3, 64, 2064)])
+def test_gemm_splitk_nvfp4_half_chunk_k(orc, M, N, K):
+    assert K % 32 == 16
+    run_gemm(orc, M, N, K, 0, 1, 1, 3, 2, seed=M + K)
+
+
+@pytest.mark.parametrize("shape", synth.MXFP4_DECODE["shapes"])
+def test_gemm_splitk_mxfp4_decode_shapes_full(orc, shape):
+    """The decode workloads with a workspace offered (the automatic choice
+    splits K where its plan says so) and with split-K forced, every output
+    checked."""
+    M, N, K = shape
+    run_gemm(orc, M, N, K, orc.MXFP4, 1, 1, 0, -1, seed=synth.MXFP4_DECODE["seed"], workspace=True)
+    run_gemm(orc, M, N, K, orc.MXFP4, 1, 1, 0, 2, seed=synth.MXFP4_DECODE["seed"])
+
+
+def test_gemm_splitk_repeatable(orc):
+    """The partials are summed in split order: two launches give identical
+    bits whatever the workspace held before."""
+    M, N, K = 41, 1536, 6144
+    a, sfa, b, sfb = operands(orc, M, N, K, 1, 1, 1, 17)
+    args = (dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb))
+    ws = split_workspace(M, N, K, 1, 2)
+    o1 = lb.lowbit_gemm_bf16(*args, fmt=1, sfa_layout=1, sfb_layout=1, variant=2, workspace=ws)
+    ws.fill_(0x7F)
+    o2 = lb.lowbit_gemm_bf16(*args, fmt=1, sfa_layout=1, sfb_layout=1, variant=2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_gemm_splitk_errors(orc):
+    a, sfa, b, sfb = operands(orc, 8, 64, 1024, 1, 0, 0, 1)
+    args = (dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb))
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_gemm_bf16(*args, fmt=1, variant=2)                      # no workspace
+    assert e.value.status == 1
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_gemm_bf16(*args, fmt=1, variant=2, workspace=small)     # too small
+    assert e.value.status == 1
