@@ -30,8 +30,9 @@ EXPORTS = (
     "lowbit_add_rmsnorm_quant_both_sf", "lowbit_add_rmsnorm_quant_both_sf_fp16",
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
-    "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes",
+    "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes", "lowbit_gemm_bf16_noalloc",
 )
+STATIC_SCRATCH_BYTES = 16 << 20   # LOWBIT_STATIC_SCRATCH_BYTES
 
 
 class LowbitError(RuntimeError):
@@ -72,11 +73,12 @@ def lib():
         tail = [_int, _vp, _sz, _vp]   # variant, workspace, workspace_bytes, stream
         L.lowbit_gemm_bf16.argtypes = head + [_vp] + tail
         L.lowbit_gemm_bias_bf16.argtypes = head + [_vp, _vp] + tail
+        L.lowbit_gemm_bf16_noalloc.argtypes = head + [_vp, _int, _vp]
         L.lowbit_gemm_residual_bf16.argtypes = head + [_vp, _vp] + tail
         L.lowbit_gemm_bias_residual_bf16.argtypes = head + [_vp, _vp, _vp] + tail
         L.lowbit_gemm_bias_gelu_bf16.argtypes = head + [_vp, _vp] + tail
         L.lowbit_gemm_bias_gelu_fp4.argtypes = head + [_vp, _vp, _vp, _vp, _int] + tail
-        for n in ("lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
+        for n in ("lowbit_gemm_bf16", "lowbit_gemm_bf16_noalloc", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
                   "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16",
                   "lowbit_gemm_bias_gelu_fp4"):
             getattr(L, n).restype = _int
@@ -335,6 +337,18 @@ def lowbit_gemm_bf16(a, b, sfa, sfb, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LI
     M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
     out = _out_bf16(out, a, M, N)
     _check("lowbit_gemm_bf16", lib().lowbit_gemm_bf16(*head, _ptr(out), variant, *_ws(workspace), _stream(stream)))
+    return out
+
+
+def lowbit_gemm_bf16_noalloc(a, b, sfa, sfb, fmt=NVFP4, sfa_layout=LINEAR, sfb_layout=LINEAR, alpha=1.0,
+                             out=None, variant=VARIANT_AUTO, stream=None):
+    """lowbit_gemm_bf16 with its split-K workspace in the library's static
+    device array (nothing allocated by the call; pass `out` to allocate
+    nothing here either).  Calls overlapping on one device race on the array."""
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    out = _out_bf16(out, a, M, N)
+    _check("lowbit_gemm_bf16_noalloc",
+           lib().lowbit_gemm_bf16_noalloc(*head, _ptr(out), variant, _stream(stream)))
     return out
 
 

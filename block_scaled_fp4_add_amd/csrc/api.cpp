@@ -18,6 +18,15 @@
 #include "launch.hpp"
 #include "lowbit.h"
 
+// Split-K workspace of lowbit_gemm_bf16_noalloc: a file-scope device array,
+// one copy per device, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device memory: its device address is
+// looked up per device with hipGetSymbolAddress and only that address is
+// handed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static_assert(kStaticScratchBytes == LOWBIT_STATIC_SCRATCH_BYTES, "header and library disagree");
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
 namespace {
 
 using lowbit::GemmArgs;
@@ -61,6 +70,29 @@ lowbit_status device_check() {
 
 lowbit_status from_hip(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_EHIP; }
 
+// Device address of `scratch` on the current device, resolved on the first
+// call on that device (with it current) and kept per device.
+lowbit_status static_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return LOWBIT_EHIP;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return LOWBIT_EHIP;
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return LOWBIT_OK;
+}
+
 lowbit_status check_sf_ptr(const void* sf, int layout) {
   if (layout == LOWBIT_SF_TILED && !aligned(sf, 4)) return LOWBIT_EALIGN;
   return LOWBIT_OK;
@@ -70,7 +102,8 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
                           int64_t M, int64_t N, int64_t K, int fmt, int la, int lb, float alpha,
                           int epi, const void* bias, const void* residual, void* out,
                           const float* gs_out, uint8_t* out_packed, uint8_t* out_sf, int out_layout,
-                          int variant, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          int variant, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          bool static_ws = false) {
   const bool fp4_out = epi == lowbit::kEpiBiasGeluFp4;
   // EINVAL: enums and pointers
   if (!fmt_ok(fmt) || !layout_ok(la) || !layout_ok(lb)) return LOWBIT_EINVAL;
@@ -92,11 +125,15 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   const int64_t B = block_of(fmt);
   if (K < B || K % B != 0) return LOWBIT_ESHAPE;
   if (fp4_out && N % 16 != 0) return LOWBIT_ESHAPE;
-  const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, workspace ? workspace_bytes : 0);
+  // workspace on offer: the caller's, or the static scratch
+  const size_t ws_avail = static_ws ? kStaticScratchBytes : (workspace ? workspace_bytes : 0);
+  const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, ws_avail);
   if (v < 0) return LOWBIT_ESHAPE;
-  // split-K asked for explicitly needs the workspace it documents
+  // split-K asked for explicitly needs the workspace it documents; beyond
+  // the static scratch that is a size the entry point does not take
   const lowbit::SplitPlan plan = lowbit::gemm_splitk_plan(M, N, K, variant == lowbit::kVariantSplitK);
-  if (v == lowbit::kVariantSplitK && !empty && (!workspace || workspace_bytes < plan.bytes)) return LOWBIT_EINVAL;
+  if (v == lowbit::kVariantSplitK && !empty && ws_avail < plan.bytes)
+    return static_ws ? LOWBIT_ESHAPE : LOWBIT_EINVAL;
   // the prefill schedule addresses each operand through a 32-bit buffer offset
   if (v == 1 && (M * (K / 2) >= (int64_t(1) << 30) || N * (K / 2) >= (int64_t(1) << 30)))
     return LOWBIT_ESHAPE;
@@ -113,9 +150,12 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   } else if (!aligned(out, 16)) {
     return LOWBIT_EALIGN;
   }
-  if (v == lowbit::kVariantSplitK && !aligned(workspace, 16)) return LOWBIT_EALIGN;
+  if (v == lowbit::kVariantSplitK && !static_ws && !aligned(workspace, 16)) return LOWBIT_EALIGN;
   // EDEVICE
   if (lowbit_status d = device_check()) return d;
+  if (v == lowbit::kVariantSplitK && static_ws) {
+    if (lowbit_status e = static_scratch(&workspace)) return e;
+  }
   GemmArgs g{};
   g.a = a;
   g.b = b;
@@ -276,6 +316,14 @@ lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t
   return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiNone,
                      nullptr, nullptr, out, nullptr, nullptr, nullptr, 0, variant, workspace, workspace_bytes,
                      stream);
+}
+
+lowbit_status lowbit_gemm_bf16_noalloc(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                       const uint8_t* sfb, int64_t M, int64_t N, int64_t K, lowbit_format fmt,
+                                       lowbit_sf_layout sfa_layout, lowbit_sf_layout sfb_layout, float alpha,
+                                       void* out, int variant, hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiNone,
+                     nullptr, nullptr, out, nullptr, nullptr, nullptr, 0, variant, nullptr, 0, stream, true);
 }
 
 lowbit_status lowbit_gemm_bias_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,

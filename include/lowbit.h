@@ -254,6 +254,27 @@ lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, cons
                                         lowbit_sf_layout out_layout, int variant,
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* lowbit_gemm_bf16 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same GEMM and arguments, without a workspace: split-K partials go to a
+ * static device array of LOWBIT_STATIC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends; the call allocates
+ * nothing.  The array is shared by every call on a device and keeps the last
+ * call's contents (the split-K partials need no initialisation), so calls
+ * that overlap on one device -- on different streams, or from other
+ * threads -- race on it and must be serialised by the caller.  The automatic
+ * choice splits K only when its plan fits the array; LOWBIT_VARIANT_SPLITK
+ * whose plan needs more (lowbit_gemm_workspace_bytes(M, N, K, fmt,
+ * LOWBIT_VARIANT_SPLITK) > LOWBIT_STATIC_SCRATCH_BYTES) returns
+ * LOWBIT_ESHAPE.  The first call on a device looks the array's address up
+ * there (LOWBIT_EHIP if that fails); every other check is lowbit_gemm_bf16's. */
+#define LOWBIT_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+lowbit_status lowbit_gemm_bf16_noalloc(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                                       const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                                       lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                                       lowbit_sf_layout sfb_layout, float alpha, void* out,
+                                       int variant, hipStream_t stream);
+
 /* Which schedule a GEMM call with these sizes and this much workspace would
  * run (-1 auto resolved), or -1 if the sizes or the variant are invalid.
  * Host-only, launches nothing. */
