@@ -14,6 +14,10 @@
  *     AddRMSNormFP4QuantKernel.kernel, phases 1-3 (add + residual write-back,
  *     sum of squares / rstd, per-block scale, FP4 quantize-and-pack), with the
  *     readings listed under each function below.
+ *   - The inverse-RoPE + MX quantizer follows the vLLM page
+ *     "deepseek_v41/nvidia/ops/fused_wo_a", FusedWoAKernel.device_kernel,
+ *     its activation quant stage (inverse RoPE on the rope slice, a 32-element
+ *     block maximum floored at 1e-10, an MX scale, FP8 elements).
  *   - The FP4 GEMM follows the FlashRT "fp4-gemm" README: "Tensor Contract"
  *     (A (M,K/2), B (N,K/2) packed, out (M,N) = alpha * A . B^T) and its
  *     "Validation" paragraph (dequantize exactly the bytes the kernel used,
@@ -525,6 +529,100 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Inverse RoPE + MX quantization (vLLM page deepseek_v41/nvidia/ops/          */
+/* fused_wo_a, FusedWoAKernel.device_kernel, the activation quant stage)       */
+/* ------------------------------------------------------------------------- */
+/*
+ * x: bf16 (T, heads, D), one row of D elements per (token, head); the last R
+ * elements of a row (from nope = D - R on) carry RoPE.  positions: (T) table
+ * rows; rope: fp32 (P, R), each row cos[0 .. R/2) followed by sin[0 .. R/2).
+ * For row (t, h), with pos = positions[t] (held to [0, P) -- the table is
+ * never read outside) and each pair p of the rope slice, elements
+ * k = nope + 2p and k + 1, c = rope[pos][p], s = rope[pos][p + R/2]:
+ *     even' = even * c + odd * s          (the inverse rotation)
+ *     odd'  = odd * c - even * s
+ * each taken as the page's _rope_fma reads most plainly: the second product
+ * rounded to fp32, then one fused multiply-add with the first.  Then each
+ * 32-element block of the fp32 row is quantized with the page's floor on the
+ * block maximum, amax' = max(amax, fl32(1e-10)), and the OCP MX rule on
+ * amax' (the page's _scale is off-page; the same reading as the MX formats
+ * elsewhere): e = clamp(floor(log2 amax') - emax, -127, 127), emax = 8 for
+ * MXFP8 (E4M3 elements) and 2 for MXFP4 (E2M1), byte e + 127, elements
+ * encode(y * 2^-e).  An all-zero block therefore gets e = -34 - emax, not the
+ * zero byte of the other producers.  Diagnostics (optional): the rotated fp32
+ * row values y (rows * D) and the floored block maxima (rows * D / 32).
+ */
+static float rope_term(float a, float c, float b, float s, int subtract) {
+    volatile float bs = b * s;                   /* fl32(b * s) */
+    return fmaf(a, c, subtract ? -bs : bs);      /* one rounding of a*c +- bs */
+}
+
+int orc_rope_quant(const uint16_t* x, const int64_t* positions, const float* rope, int64_t T,
+                   int64_t heads, int64_t D, int64_t R, int64_t P, int fmt, int layout,
+                   uint8_t* out_packed, uint8_t* out_sf, float* diag_y, float* diag_amax) {
+    if (T < 0 || heads <= 0 || D <= 0 || D % 32 != 0 || R < 0 || R > D || R % 2 != 0) return 1;
+    if (R > 0 && P <= 0) return 1;
+    if (fmt != ORC_MXFP8 && fmt != ORC_MXFP4) return 1;
+    if (check_common(T * heads, D, fmt, layout)) return 1;
+    const int64_t rows = T * heads, nope = D - R, nblk = D / 32;
+    const float floor_amax = 1e-10f;
+    const int emax = (fmt == ORC_MXFP8) ? 8 : 2;
+    memset(out_sf, 0, (size_t)orc_sf_bytes(rows, D, fmt, layout));
+    int err = 0;
+#pragma omp parallel
+    {
+        float* y = (float*)malloc(sizeof(float) * (size_t)D);
+        uint8_t* codes = (uint8_t*)malloc((size_t)D);
+        if (!y || !codes) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t row = 0; row < rows; row++) {
+                const int64_t t = row / heads;
+                for (int64_t k = 0; k < D; k++) y[k] = orc_bf16_to_f32(x[row * D + k]);
+                if (R > 0) {
+                    int64_t pos = positions[t];
+                    if (pos < 0) pos = 0;
+                    if (pos >= P) pos = P - 1;
+                    for (int64_t p = 0; p < R / 2; p++) {
+                        const int64_t k = nope + 2 * p;
+                        const float c = rope[pos * R + p], s = rope[pos * R + p + R / 2];
+                        const float even = y[k], odd = y[k + 1];
+                        y[k] = rope_term(even, c, odd, s, 0);
+                        y[k + 1] = rope_term(odd, c, even, s, 1);
+                    }
+                }
+                if (diag_y) memcpy(diag_y + row * D, y, sizeof(float) * (size_t)D);
+                for (int64_t b = 0; b < nblk; b++) {
+                    float amax = 0.0f;
+                    for (int i = 0; i < 32; i++) {
+                        const float a = fabsf(y[b * 32 + i]);
+                        if (a > amax) amax = a;
+                    }
+                    if (amax < floor_amax) amax = floor_amax;   /* the page's max(amax, 1e-10) */
+                    if (diag_amax) diag_amax[row * nblk + b] = amax;
+                    int E;
+                    (void)frexp((double)amax, &E);              /* amax = f * 2^E, f in [0.5, 1) */
+                    int e = (E - 1) - emax;                     /* floor(log2 amax) - emax */
+                    if (e < -127) e = -127;
+                    if (e > 127) e = 127;
+                    out_sf[orc_sf_offset(row, b, nblk, fmt, layout)] = (uint8_t)(e + 127);
+                    for (int i = 0; i < 32; i++) {
+                        const float v = ldexpf(y[b * 32 + i], -e);
+                        codes[b * 32 + i] = (fmt == ORC_MXFP8) ? orc_e4m3_encode(v) : orc_e2m1_encode(v);
+                    }
+                }
+                pack_row(codes, D, fmt, out_packed + row * row_bytes(fmt, D));
+            }
+        }
+        free(y);
+        free(codes);
+    }
+    return err;
 }
 
 /* ------------------------------------------------------------------------- */

@@ -100,6 +100,9 @@ def lib():
     L.orc_gemm_gelu_fp4.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _int, _int, _int,
                                     ctypes.c_double, _u16p, ctypes.c_float, _int, _u8p, _u8p,
                                     _vp, _vp, _vp, _vp, _vp]
+    L.orc_rope_quant.restype = _int
+    L.orc_rope_quant.argtypes = [_u16p, _i64p, _f32p, _i64, _i64, _i64, _i64, _i64, _int, _int, _u8p, _u8p,
+                                 _vp, _vp]
     L.orc_num_threads.restype = _int
     L.orc_num_threads.argtypes = []
     L.orc_set_num_threads.restype = None
@@ -212,6 +215,30 @@ def quantize(x, fmt, layout, gs=1.0, diag=False, dtype=BF16):
     if rc:
         raise ValueError(f"oracle quantize rejected its arguments (rc={rc})")
     return (packed, sf, spre) if diag else (packed, sf)
+
+
+def rope_quant(x, positions, rope, heads, fmt, layout, diag=False):
+    """Inverse RoPE + MX quantization (the vLLM fused_wo_a page's activation
+    quant stage).  x: uint16 bf16 bits (T, heads, D); positions: int64 (T);
+    rope: fp32 (P, R), each row cos || sin.  Returns packed (T*heads, D or
+    D/2), scales, and with diag the rotated fp32 rows and the floored block
+    maxima."""
+    x = _c(x, np.uint16)
+    positions = _c(positions, np.int64)
+    rope = _c(rope, np.float32)
+    T, H, D = x.shape
+    assert H == heads
+    P, R = rope.shape if rope.size else (0, 0)
+    rows = T * heads
+    packed = np.zeros((rows, row_bytes(fmt, D)), np.uint8)
+    sf = np.zeros(sf_bytes(rows, D, fmt, layout), np.uint8)
+    y = np.zeros((rows, D), np.float32) if diag else None
+    am = np.zeros((rows, D // 32), np.float32) if diag else None
+    rc = lib().orc_rope_quant(x, positions, rope if rope.size else np.zeros(1, np.float32), T, heads, D, R,
+                              P, fmt, layout, packed, sf, _ptr(y), _ptr(am))
+    if rc:
+        raise ValueError(f"oracle rope_quant rejected its arguments (rc={rc})")
+    return (packed, sf, y, am) if diag else (packed, sf)
 
 
 def dequantize(packed, sf, rows, K, fmt, layout, gs=1.0):
