@@ -52,6 +52,32 @@ def producer_bytes(M, H, B, elem_bytes=0.5):
     return M * H * 6 + int(M * H * elem_bytes) + M * H // B + 2 * H + 4
 
 
+def rope_bytes(T, heads, D, R, elem_bytes):
+    # x read (bf16) + the elements (one byte MXFP8, half a byte MXFP4) + a scale
+    # byte per 32, per element; each token's table row and position once
+    return T * heads * D * 2 + int(T * heads * D * elem_bytes) + T * heads * D // 32 + T * (R * 4 + 8)
+
+
+ROPE_D, ROPE_R, ROPE_P = 512, 64, 4096   # head, rotary slice, table rows of the RoPE workloads
+
+
+def rope_stage(name, T, heads, fmt, dev):
+    """The inverse-RoPE + MX quantizer over T tokens of `heads` heads."""
+    x = synth.activation(T * heads, ROPE_D, 77, outliers=True).reshape(T, heads, ROPE_D).to(dev)
+    inv = 10000.0 ** (-np.arange(0, ROPE_R, 2, dtype=np.float64) / ROPE_R)
+    ang = np.arange(ROPE_P, dtype=np.float64)[:, None] * inv[None, :]
+    tab = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)).to(dev)
+    pos = torch.from_numpy(np.random.default_rng(7).integers(0, ROPE_P, T).astype(np.int64)).to(dev)
+    pk = torch.empty((T * heads, ROPE_D if fmt == lb.MXFP8 else ROPE_D // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty(lb.lowbit_sf_bytes(T * heads, ROPE_D, fmt, lb.LINEAR), dtype=torch.uint8, device=dev)
+
+    def fn(x=x, pos=pos, tab=tab, pk=pk, sf=sf):
+        lb.lowbit_rope_quant(x, pos, tab, fmt, lb.LINEAR, out_packed=pk, out_sf=sf)
+
+    return Stage(name, fn, "hbm", rope_bytes(T, heads, ROPE_D, ROPE_R, 1.0 if fmt == lb.MXFP8 else 0.5), "B",
+                 HBM_PEAK)
+
+
 def gemm_bytes(M, N, K, B, epi_bias=False, epi_res=False, out_fp4=False):
     b = (M + N) * (K // 2 + K // B)
     b += 2 * N if epi_bias else 0
@@ -248,7 +274,10 @@ def build_variant_stages():
     reported apart from `value`, at the 4096 x 4096 producer workload with 4
     rotating input sets like the bf16 stage: the NVFP4 producer on fp16
     tensors (same draws, rounded to fp16), the producer with MXFP8 output, and
-    the NVFP4 producer writing both scale layouts in one pass."""
+    the NVFP4 producer writing both scale layouts in one pass; then the
+    inverse-RoPE + MX quantizer at a prefill size.  Each is replayed from a
+    HIP graph of DECODE_REPS launches, so that the binding's per-call host
+    work does not stand in for these 20-30 us kernels."""
     dev = "cuda"
     c = synth.NVFP4_PRODUCER
     M, H = c["M"], c["H"]
@@ -270,7 +299,8 @@ def build_variant_stages():
         lb.lowbit_add_rmsnorm_quant_fp16(x, r, w, EPS, lb.NVFP4, lb.LINEAR, global_scale=gs, out_packed=pk,
                                          out_sf=sf)
 
-    stages = [Stage(f"add_rmsnorm_nvfp4_fp16_{M}x{H}", producer, "hbm", producer_bytes(M, H, 16), "B", HBM_PEAK)]
+    stages = [graphed(Stage(f"add_rmsnorm_nvfp4_fp16_{M}x{H}", producer, "hbm", producer_bytes(M, H, 16), "B",
+                            HBM_PEAK))]
 
     # the same bf16 workload quantized to MXFP8 (E4M3 elements, one byte each)
     bsets = []
@@ -286,8 +316,8 @@ def build_variant_stages():
         it8["i"] += 1
         lb.lowbit_add_rmsnorm_quant(x, r, w, EPS, lb.MXFP8, lb.LINEAR, out_packed=pk8, out_sf=sf8)
 
-    stages.append(Stage(f"add_rmsnorm_mxfp8_{M}x{H}", producer8, "hbm", producer_bytes(M, H, 32, 1.0), "B",
-                        HBM_PEAK))
+    stages.append(graphed(Stage(f"add_rmsnorm_mxfp8_{M}x{H}", producer8, "hbm", producer_bytes(M, H, 32, 1.0), "B",
+                                HBM_PEAK)))
 
     # the bf16 NVFP4 producer writing TILED and LINEAR scales in one pass: one
     # more scale byte per block (4096 rows and 256 blocks per row: no padding)
@@ -302,8 +332,11 @@ def build_variant_stages():
         lb.lowbit_add_rmsnorm_quant_both_sf(x, r, w, EPS, lb.NVFP4, global_scale=gs, out_packed=pkb,
                                             out_sf_tiled=sft, out_sf_linear=sfl)
 
-    stages.append(Stage(f"add_rmsnorm_nvfp4_both_sf_{M}x{H}", producer_both, "hbm",
-                        producer_bytes(M, H, 16) + M * H // 16, "B", HBM_PEAK))
+    stages.append(graphed(Stage(f"add_rmsnorm_nvfp4_both_sf_{M}x{H}", producer_both, "hbm",
+                                producer_bytes(M, H, 16) + M * H // 16, "B", HBM_PEAK)))
+    # inverse RoPE + MX quantization at a prefill size: 4096 tokens x 16 heads of 512
+    stages.append(graphed(rope_stage("rope_quant_mxfp8_4096x16x512", 4096, 16, lb.MXFP8, dev)))
+    stages.append(graphed(rope_stage("rope_quant_mxfp4_4096x16x512", 4096, 16, lb.MXFP4, dev)))
     return stages
 
 
@@ -434,6 +467,8 @@ def build_decode_stages():
                                     gemm_bytes(M, N1, H, 16, epi_bias=True, out_fp4=True), "B", HBM_PEAK)))
         stages.append(graphed(Stage(f"chain_m{M}_nvfp4_gemm_{M}x{H}x{N1}", g2, "hbm", gemm_bytes(M, H, N1, 16),
                                     "B", HBM_PEAK)))
+    # inverse RoPE + MXFP8 at the page's decode size: 96 tokens x 16 heads of 512
+    stages.append(graphed(rope_stage("rope_quant_mxfp8_96x16x512", 96, 16, lb.MXFP8, dev)))
     return stages
 
 

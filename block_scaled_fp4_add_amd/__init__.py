@@ -31,6 +31,7 @@ EXPORTS = (
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
     "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes", "lowbit_gemm_bf16_noalloc",
+    "lowbit_rope_quant",
 )
 STATIC_SCRATCH_BYTES = 16 << 20   # LOWBIT_STATIC_SCRATCH_BYTES
 
@@ -67,6 +68,8 @@ def lib():
             getattr(L, name).argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _int, _vp, _vp, _vp, _vp, _vp]
         L.lowbit_quantize_fp16.restype = _int
         L.lowbit_quantize_fp16.argtypes = L.lowbit_quantize.argtypes
+        L.lowbit_rope_quant.restype = _int
+        L.lowbit_rope_quant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]
         L.lowbit_dequantize.restype = _int
         L.lowbit_dequantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
         head = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f32]
@@ -258,6 +261,35 @@ def lowbit_quantize_fp16(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_pac
     """The fp16 quantizer by name (lowbit_quantize dispatches on dtype)."""
     _need(x, torch.float16, "x")
     return lowbit_quantize(x, fmt, layout, global_scale, out_packed, out_sf, stream)
+
+
+def lowbit_rope_quant(x, positions, rope, fmt=MXFP8, layout=LINEAR, out_packed=None, out_sf=None, stream=None):
+    """Inverse RoPE on the last R elements of each head row, then MX
+    quantization with the 1e-10 floor on the block maximum.  x: bf16
+    (T, heads, D); positions: int64 (T); rope: fp32 (P, R), each row
+    cos || sin (R = 0: pass an empty (P, 0) tensor or None).  Returns
+    (packed (T*heads, D) for MXFP8 or (T*heads, D/2) for MXFP4, scales)."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 3:
+        raise ValueError(f"x must be (tokens, heads, head_dim), got {tuple(x.shape)}")
+    T, heads, D = (int(v) for v in x.shape)
+    if rope is None or rope.numel() == 0:
+        R, P, rope, positions = 0, 0, None, None
+    else:
+        _need(rope, torch.float32, "rope")
+        if rope.dim() != 2:
+            raise ValueError(f"rope must be (positions, rope_dim), got {tuple(rope.shape)}")
+        P, R = (int(v) for v in rope.shape)
+        _need(positions, torch.int64, "positions")
+        if positions.numel() != T:
+            raise ValueError(f"positions has {positions.numel()} entries for {T} tokens")
+    rows = T * heads
+    out_packed, out_sf = _alloc_q(rows, D, fmt, layout, x.device, out_packed, out_sf)
+    _check_q_out(out_packed, out_sf, rows, D, fmt, layout)
+    _check("lowbit_rope_quant", lib().lowbit_rope_quant(
+        _ptr(x), _ptr(positions), _ptr(rope), T, heads, D, R, P, fmt, layout, _ptr(out_packed), _ptr(out_sf),
+        _stream(stream)))
+    return out_packed, out_sf
 
 
 def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):

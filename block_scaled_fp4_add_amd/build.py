@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblowbit.so")
 SOURCES = ["gemm_inst_splitk.hip", "gemm_inst_nv2.hip", "gemm_inst_nv1.hip", "gemm_inst_nv0.hip", "gemm_inst_mx2.hip",
-           "gemm_inst_mx1.hip", "gemm_inst_mx0.hip", "quant.hip", "gemm.hip", "api.cpp"]
+           "gemm_inst_mx1.hip", "gemm_inst_mx0.hip", "quant.hip", "rope.hip", "gemm.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -292,6 +292,40 @@ lowbit_status lowbit_quantize_fp16(const void* x, int64_t rows, int64_t K, lowbi
   return quantize(x, rows, K, fmt, layout, global_scale, out_packed, out_sf, 1, stream);
 }
 
+lowbit_status lowbit_rope_quant(const void* x, const int64_t* positions, const float* rope, int64_t T,
+                                int64_t heads, int64_t D, int64_t R, int64_t P, lowbit_format fmt,
+                                lowbit_sf_layout layout, uint8_t* out_packed, uint8_t* out_sf,
+                                hipStream_t stream) {
+  // EINVAL: formats (MXFP8 with LINEAR scales, MXFP4 with any FP4 layout) and pointers
+  if (fmt != LOWBIT_MXFP8 && fmt != LOWBIT_MXFP4) return LOWBIT_EINVAL;
+  if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
+  const bool empty = T == 0;
+  if (!empty && (!x || !out_packed || !out_sf)) return LOWBIT_EINVAL;
+  if (!empty && R > 0 && (!positions || !rope)) return LOWBIT_EINVAL;
+  // ESHAPE
+  if (T < 0 || heads < 1 || D < 32 || D % 32 != 0 || D > kMaxRowElems) return LOWBIT_ESHAPE;
+  if (R < 0 || R > D || R % 2 != 0 || (R > 0 && P < 1)) return LOWBIT_ESHAPE;
+  // the kernel indexes 8-element units in 32 bits (rows padded to 128 at most)
+  if (T > 0 && ((T * heads + 127) / 128 * 128) * (D / 8) >= (int64_t(1) << 31)) return LOWBIT_ESHAPE;
+  if (empty) return LOWBIT_OK;
+  // EALIGN
+  if (!aligned(x, 16) || !aligned(out_packed, 16)) return LOWBIT_EALIGN;
+  if (R > 0 && (!aligned(positions, 8) || !aligned(rope, 4))) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  lowbit::RopeArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.positions = positions;
+  a.rope = rope;
+  a.rows = T * heads;
+  a.heads = heads;
+  a.D = D;
+  a.R = R;
+  a.P = P;
+  a.out_packed = out_packed;
+  a.out_sf = out_sf;
+  return from_hip(lowbit::launch_rope_quant(a, fmt, layout, stream));
+}
+
 lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
                                 lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
                                 void* out, hipStream_t stream) {

@@ -21,6 +21,18 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, 
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
                              int layout, const float* gs, uint16_t* out, hipStream_t s);
 
+// Inverse RoPE + MX quantization of (T, heads, D) bf16 rows (rows = T * heads).
+struct RopeArgs {
+  const uint16_t* x;          // bf16 (rows, D)
+  const int64_t* positions;   // (T) table rows; nullptr when R == 0
+  const float* rope;          // fp32 (P, R): cos || sin per row; nullptr when R == 0
+  int64_t rows, heads, D, R, P;
+  int64_t rows_grid;          // rows the grid covers (padded scale layouts pad the rows)
+  uint8_t* out_packed;        // MXFP8 (rows, D) / MXFP4 (rows, D/2)
+  uint8_t* out_sf;
+};
+hipError_t launch_rope_quant(const RopeArgs& a, int fmt, int layout, hipStream_t s);
+
 struct GemmArgs {
   const uint8_t* a;
   const uint8_t* b;

@@ -12,6 +12,9 @@
  *         kernel phases 1-3, API asserts and output allocation).
  *   [FRT] FlashRT fp4-gemm README: "Available Functions", "Tensor Contract",
  *         the variant list, and the "Validation" paragraph.
+ *   [WOA] vLLM API docs, deepseek_v41/nvidia/ops/fused_wo_a: FusedWoAKernel
+ *         (device_kernel: the activation quant stage with inverse RoPE; the
+ *         MXFP8 format of its operands).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
@@ -176,6 +179,35 @@ lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_for
 lowbit_status lowbit_quantize_fp16(const void* x, int64_t rows, int64_t K, lowbit_format fmt,
                                    lowbit_sf_layout layout, const float* global_scale,
                                    uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
+
+/* Inverse RoPE + MX quantization of attention rows ([WOA] FusedWoAKernel
+ * device_kernel, its activation quant stage: the rotary part of each head
+ * rotated back, 32-element blocks with an MX scale).  x: bf16 (T, heads, D),
+ * row (t, h) of D elements; its last R elements (from nope = D - R on) carry
+ * RoPE.  positions: int64 (T), the table row of each token; rope: fp32 (P, R),
+ * each row cos[0 .. R/2) then sin[0 .. R/2).  For each pair p of the rotary
+ * slice, elements k = nope + 2p and k + 1, c = rope[pos][p],
+ * s = rope[pos][p + R/2]:
+ *   even' = fma(even, c, fl32(odd * s)),  odd' = fma(odd, c, -fl32(even * s))
+ * (the inverse rotation, the second product rounded to fp32 first).  Each
+ * 32-element block of the fp32 row then takes amax' = max(amax, fl32(1e-10))
+ * (the page's floor, so an all-zero block is not scale byte 0 here) and the
+ * OCP MX rule on it: e = clamp(floor(log2 amax') - emax, -127, 127), byte
+ * e + 127, elements encode(y * 2^-e), nearest-even and saturating with the
+ * sign kept.  fmt LOWBIT_MXFP8 (the page's: E4M3 elements, emax 8, packed
+ * (T*heads, D), LINEAR scales) or LOWBIT_MXFP4 (E2M1, emax 2, packed
+ * (T*heads, D/2), any FP4 scale layout, for the FP4 GEMM).  out_sf:
+ * lowbit_sf_bytes(T*heads, D, fmt, layout) bytes (padding written zero).
+ * Requires D % 32 == 0 (32 <= D <= 32768), 0 <= R <= D with R even, P >= 1
+ * when R > 0, heads >= 1, T >= 0 (T == 0 is a no-op), and T * heads * D / 8
+ * below 2^31 (with the rows rounded up to 128); positions and rope may
+ * be NULL when R == 0.  A position outside [0, P) reads the nearest end row
+ * of the table (the table is never read outside).  Alignment: x and
+ * out_packed 16 bytes, positions 8, rope 4. */
+lowbit_status lowbit_rope_quant(const void* x, const int64_t* positions, const float* rope, int64_t T,
+                                int64_t heads, int64_t D, int64_t R, int64_t P, lowbit_format fmt,
+                                lowbit_sf_layout layout, uint8_t* out_packed, uint8_t* out_sf,
+                                hipStream_t stream);
 
 /* Dequantize to bf16: x = bf16(fl32(E2M1 * scale / gs)) (NVFP4, gs from
  * global_scale or 1.0) or bf16(E2M1 * 2^(b-127)) (MXFP4; global_scale NULL)

@@ -235,6 +235,34 @@ def test_gemm_argument_order(buf):
                                        buf.at(24576), buf.at(28672), 0, -1, None, 0, None) == ESHAPE
 
 
+def test_rope_quant_argument_order(buf):
+    L = lb.lib()
+
+    def call(T=2, heads=4, D=512, R=64, P=16, fmt=2, layout=0, x=0, pos=True, rope=True, p=4096):
+        return L.lowbit_rope_quant(buf.at(x), buf.at(8192) if pos else None, buf.at(12288) if rope else None,
+                                   T, heads, D, R, P, fmt, layout, buf.at(p), buf.at(16384), None)
+
+    assert call(fmt=0) == EINVAL                      # NVFP4: not an MX format
+    assert call(fmt=3) == EINVAL
+    assert call(fmt=2, layout=1) == EINVAL            # MXFP8: LINEAR scales only
+    assert call(pos=False) == EINVAL                  # rope without positions
+    assert call(rope=False) == EINVAL
+    assert call(T=-1) == ESHAPE
+    assert call(heads=0) == ESHAPE
+    assert call(D=100) == ESHAPE                      # D % 32
+    assert call(R=63) == ESHAPE                       # odd rotary slice
+    assert call(R=576) == ESHAPE                      # R > D
+    assert call(P=0) == ESHAPE
+    assert call(x=4) == EALIGN
+    assert call(p=8) == EALIGN
+    assert call(T=0) == OK
+    assert call(R=0, pos=False, rope=False, T=0) == OK
+    if NO_DEVICE:
+        assert call() == EDEVICE
+        assert call(fmt=1, layout=2) == EDEVICE       # MXFP4 takes the FP4 layouts
+        assert call(R=0, pos=False, rope=False) == EDEVICE
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(lb, "LIB_PATH", "/nonexistent/liblowbit.so")
     monkeypatch.setattr(lb, "_lib", None)
