@@ -772,6 +772,80 @@ int orc_gemm_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, co
     return err;
 }
 
+/* ------------------------------------------------------------------------- */
+/* GEMM with FP8 output quantization (vLLM page deepseek_v41/nvidia/ops/       */
+/* fused_wo_a, FusedWoAKernel.device_kernel, its output epilogue)             */
+/* ------------------------------------------------------------------------- */
+/* Round a binary64 to bf16 (8 significant bits, binary32's exponent range),
+ * nearest-even, in one step from the exact value: count the value in steps
+ * of its binade's bf16 grid (2^(E-7), 2^-133 below 2^-126) and round the
+ * count.  Returns the bf16 value as a binary32 (exact). */
+static float f64_to_bf16_value(double v) {
+    double a = fabs(v);
+    if (a == 0.0) return (float)v;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                          /* floor(log2 a) */
+    if (E < -126) E = -126;                  /* subnormal grid: 2^-133 */
+    double q = rint(ldexp(a, 7 - E));        /* count of 2^(E-7) steps, ties to even */
+    double r = ldexp(q, E - 7);
+    return (float)(v < 0 ? -r : r);
+}
+
+/* value[m,n] = bf16(alpha * acc[m,n]) -- the page rounds the reduced sum to
+ * bf16 before quantizing -- then each 32-run of a row along n is quantized as
+ * MXFP8 (the MX rule of quant_block: OCP scale with emax 8, an all-zero block
+ * gets byte 0; E4M3 elements nearest-even, saturating, sign kept), one byte
+ * an element into out_packed (M, N) and the scale bytes in out_layout:
+ * LINEAR, or the page's 128 x 4 swizzle (its F8_128x4 scale bytes).
+ * Diagnostics (optional): the unrounded binary64 values and their L1 budget. */
+int orc_gemm_fp8_out(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                     int64_t M, int64_t N, int64_t K, int fmt, int layout_a, int layout_b,
+                     double alpha, int out_layout, uint8_t* out_packed, uint8_t* out_sf,
+                     double* diag_ref, double* diag_l1) {
+    if (check_common(M, K, fmt, layout_a) || check_common(N, K, fmt, layout_b)) return 1;
+    if (N % 32 != 0) return 1;
+    if (out_layout != ORC_SF_LINEAR && out_layout != ORC_SF_SWZ128) return 1;
+    double* ref = (double*)malloc(sizeof(double) * (size_t)(M * N));
+    double* l1 = (double*)malloc(sizeof(double) * (size_t)(M * N));
+    if (!ref || !l1) { free(ref); free(l1); return 2; }
+    int rc = orc_gemm(a, b, sfa, sfb, M, N, K, fmt, layout_a, layout_b, alpha, ORC_EPI_NONE, NULL, NULL,
+                      ref, l1);
+    if (rc) { free(ref); free(l1); return rc; }
+    memset(out_sf, 0, (size_t)orc_sf_bytes(M, N, ORC_MXFP8, out_layout));
+    int err = 0;
+#pragma omp parallel
+    {
+        float* y = (float*)malloc(sizeof(float) * (size_t)N);
+        uint8_t* codes = (uint8_t*)malloc((size_t)N);
+        if (!y || !codes) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t m = 0; m < M; m++) {
+                for (int64_t n = 0; n < N; n++) y[n] = f64_to_bf16_value(ref[m * N + n]);
+                quant_row(y, m, N, ORC_MXFP8, 1.0f, out_layout, out_packed + m * N, out_sf, codes, NULL, NULL,
+                          NULL);
+            }
+        }
+        free(y);
+        free(codes);
+    }
+    if (diag_ref) memcpy(diag_ref, ref, sizeof(double) * (size_t)(M * N));
+    if (diag_l1) memcpy(diag_l1, l1, sizeof(double) * (size_t)(M * N));
+    free(ref);
+    free(l1);
+    return err;
+}
+
+/* E4M3 codes of MX blocks of 32 values under given scale bytes (the parity
+ * checker's re-encoding of candidate values, one call for many blocks). */
+void orc_mxfp8_encode_blocks(const float* y, int64_t nblocks, const uint8_t* sbytes, uint8_t* codes) {
+    for (int64_t b = 0; b < nblocks; b++)
+        orc_encode_with_scale(y + b * 32, 32, ORC_MXFP8, 1.0f, sbytes[b], codes + b * 32, NULL);
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -103,6 +103,11 @@ def lib():
     L.orc_rope_quant.restype = _int
     L.orc_rope_quant.argtypes = [_u16p, _i64p, _f32p, _i64, _i64, _i64, _i64, _i64, _int, _int, _u8p, _u8p,
                                  _vp, _vp]
+    L.orc_gemm_fp8_out.restype = _int
+    L.orc_gemm_fp8_out.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _int, _int, _int,
+                                   ctypes.c_double, _int, _u8p, _u8p, _vp, _vp]
+    L.orc_mxfp8_encode_blocks.restype = None
+    L.orc_mxfp8_encode_blocks.argtypes = [_f32p, _i64, _u8p, _u8p]
     L.orc_num_threads.restype = _int
     L.orc_num_threads.argtypes = []
     L.orc_set_num_threads.restype = None
@@ -303,6 +308,31 @@ def gemm_gelu_fp4(a, b, sfa, sfb, M, N, K, fmt, layout_a, layout_b, alpha, bias,
     out = dict(packed=packed, sf=sf)
     out.update(d)
     return out
+
+
+def gemm_fp8_out(a, b, sfa, sfb, M, N, K, fmt, layout_a, layout_b, alpha, out_layout, diag=False):
+    """GEMM with the FP8 output epilogue: bf16(alpha * A.B^T) quantized as
+    MXFP8 along N.  Returns packed (M, N), scales, and with diag the
+    unrounded binary64 values and their L1 budget."""
+    a, b, sfa, sfb = (_c(t, np.uint8) for t in (a, b, sfa, sfb))
+    packed = np.zeros((M, N), np.uint8)
+    sf = np.zeros(sf_bytes(M, N, MXFP8, out_layout), np.uint8)
+    ref = np.zeros((M, N), np.float64) if diag else None
+    l1 = np.zeros((M, N), np.float64) if diag else None
+    rc = lib().orc_gemm_fp8_out(a, b, sfa, sfb, M, N, K, fmt, layout_a, layout_b, alpha, out_layout, packed, sf,
+                                _ptr(ref), _ptr(l1))
+    if rc:
+        raise ValueError(f"oracle gemm_fp8_out rejected its arguments (rc={rc})")
+    return (packed, sf, ref, l1) if diag else (packed, sf)
+
+
+def mxfp8_encode_blocks(y, sbytes):
+    """E4M3 codes of 32-value blocks y (nblocks, 32) under the scale bytes."""
+    y = _c(y, np.float32)
+    sbytes = _c(sbytes, np.uint8)
+    codes = np.zeros(y.shape, np.uint8)
+    lib().orc_mxfp8_encode_blocks(y, sbytes.size, sbytes, codes)
+    return codes
 
 
 def num_threads() -> int:
