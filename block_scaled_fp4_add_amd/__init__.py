@@ -13,9 +13,9 @@ import os
 import numpy as np
 import torch
 
-NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: producer / quantizer / dequantizer, LINEAR scales
+NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: LINEAR scales (its GEMM output also takes SWZ128)
 NVFP4_B32 = 3                   # the NVFP4 rule on 32-blocks: the same three calls, LINEAR scales
-LINEAR, TILED, SWZ128 = 0, 1, 2   # SWZ128: the 128 x 4 swizzle, quantization side only
+LINEAR, TILED, SWZ128 = 0, 1, 2   # SWZ128: the 128 x 4 swizzle (quantizer outputs, FP8 GEMM output)
 VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL, VARIANT_SPLITK = -1, 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowbit.so")
@@ -31,7 +31,7 @@ EXPORTS = (
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
     "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes", "lowbit_gemm_bf16_noalloc",
-    "lowbit_rope_quant",
+    "lowbit_rope_quant", "lowbit_gemm_fp8",
 )
 STATIC_SCRATCH_BYTES = 16 << 20   # LOWBIT_STATIC_SCRATCH_BYTES
 
@@ -81,9 +81,10 @@ def lib():
         L.lowbit_gemm_bias_residual_bf16.argtypes = head + [_vp, _vp, _vp] + tail
         L.lowbit_gemm_bias_gelu_bf16.argtypes = head + [_vp, _vp] + tail
         L.lowbit_gemm_bias_gelu_fp4.argtypes = head + [_vp, _vp, _vp, _vp, _int] + tail
+        L.lowbit_gemm_fp8.argtypes = head + [_vp, _vp, _int] + tail
         for n in ("lowbit_gemm_bf16", "lowbit_gemm_bf16_noalloc", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
                   "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16",
-                  "lowbit_gemm_bias_gelu_fp4"):
+                  "lowbit_gemm_bias_gelu_fp4", "lowbit_gemm_fp8"):
             getattr(L, n).restype = _int
         L.lowbit_gemm_pick_variant.restype = _int
         L.lowbit_gemm_pick_variant.argtypes = [_i64, _i64, _i64, _int, _int, _sz]
@@ -318,12 +319,14 @@ def _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha):
         _need(t, torch.uint8, n)
     _, M, ka = _rows_of(a)
     _, N, kb = _rows_of(b)
-    K = ka * 2
-    if kb * 2 != K:
+    per = 1 if fmt == MXFP8 else 2     # elements per packed byte
+    K = ka * per
+    if kb * per != K:
         raise ValueError("a and b disagree on K")
     # sizes are checked for the layouts the GEMM takes; any other layout or
     # format is the C ABI's to refuse (LOWBIT_EINVAL)
-    if fmt in (NVFP4, MXFP4) and sfa_layout in (LINEAR, TILED) and sfb_layout in (LINEAR, TILED):
+    if (fmt in (NVFP4, MXFP4) and sfa_layout in (LINEAR, TILED) and sfb_layout in (LINEAR, TILED)) or \
+            (fmt == MXFP8 and sfa_layout == LINEAR and sfb_layout == LINEAR):
         _at_least(sfa, lowbit_sf_bytes(M, K, fmt, sfa_layout), "sfa")
         _at_least(sfb, lowbit_sf_bytes(N, K, fmt, sfb_layout), "sfb")
     return M, N, K, [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), M, N, K, fmt, sfa_layout, sfb_layout,
@@ -442,6 +445,19 @@ def lowbit_gemm_bias_gelu_fp4(a, b, sfa, sfb, bias, fmt=NVFP4, sfa_layout=LINEAR
     _check("lowbit_gemm_bias_gelu_fp4", lib().lowbit_gemm_bias_gelu_fp4(
         *head, _ptr(bias), _ptr(out_global_scale), _ptr(out_packed), _ptr(out_sf), out_layout, variant,
         *_ws(workspace), _stream(stream)))
+    return out_packed, out_sf
+
+
+def lowbit_gemm_fp8(a, b, sfa, sfb, fmt=MXFP8, sfa_layout=LINEAR, sfb_layout=LINEAR, alpha=1.0,
+                    out_packed=None, out_sf=None, out_layout=LINEAR, variant=VARIANT_AUTO, workspace=None,
+                    stream=None):
+    """bf16(alpha * A.B^T) quantized to MXFP8 along N (E4M3 bytes (M, N) and
+    UE8M0 scales in out_layout: LINEAR or SWZ128).  Returns (packed, scales)."""
+    M, N, K, head = _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha)
+    out_packed, out_sf = _alloc_q(M, N, MXFP8, out_layout, a.device, out_packed, out_sf, tuple(a.shape[:-1]))
+    _check_q_out(out_packed, out_sf, M, N, MXFP8, out_layout)
+    _check("lowbit_gemm_fp8", lib().lowbit_gemm_fp8(
+        *head, _ptr(out_packed), _ptr(out_sf), out_layout, variant, *_ws(workspace), _stream(stream)))
     return out_packed, out_sf
 
 

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblowbit.so")
-SOURCES = ["gemm_inst_splitk.hip", "gemm_inst_nv2.hip", "gemm_inst_nv1.hip", "gemm_inst_nv0.hip", "gemm_inst_mx2.hip",
+SOURCES = ["gemm_inst_splitk.hip", "gemm_inst_splitk8.hip", "gemm_inst_f80.hip", "gemm_inst_f81.hip",
+           "gemm_inst_f82.hip", "gemm_inst_f83.hip", "gemm_inst_nv3.hip", "gemm_inst_mx3.hip", "gemm_inst_nv2.hip", "gemm_inst_nv1.hip", "gemm_inst_nv0.hip", "gemm_inst_mx2.hip",
            "gemm_inst_mx1.hip", "gemm_inst_mx0.hip", "quant.hip", "rope.hip", "gemm.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
@@ -24,7 +25,7 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
-    jobs = jobs or max(1, min(9, os.cpu_count() or 1))
+    jobs = jobs or max(1, min(8, os.cpu_count() or 1))
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
     procs = []

@@ -33,13 +33,18 @@ using lowbit::GemmArgs;
 
 constexpr int64_t kMaxRowElems = 32768;  // 4 waves x 64 lanes x 128 elements per lane
 
-bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }   // GEMM operands
+// GEMM operand formats (MXFP8 operands take LINEAR scales only)
+bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4 || f == LOWBIT_MXFP8; }
+bool fp4_fmt(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }
 bool layout_ok(int l) { return l == LOWBIT_SF_LINEAR || l == LOWBIT_SF_TILED; }
+bool gemm_layout_ok(int f, int l) { return f == LOWBIT_MXFP8 ? l == LOWBIT_SF_LINEAR : layout_ok(l); }
+// packed bytes of a row of k elements: one per MXFP8 element, else two codes a byte
+int64_t packed_row_bytes(int f, int64_t k) { return f == LOWBIT_MXFP8 ? k : k / 2; }
 // producer / quantizer / dequantizer: MXFP8 and 32-block NVFP4 as well, with
 // LINEAR scales only; the FP4 GEMM formats also take the 128 x 4 swizzle
 bool qfmt_layout_ok(int f, int l) {
   if (f == LOWBIT_MXFP8 || f == LOWBIT_NVFP4_B32) return l == LOWBIT_SF_LINEAR;
-  return fmt_ok(f) && (layout_ok(l) || l == LOWBIT_SF_SWZ128);
+  return fp4_fmt(f) && (layout_ok(l) || l == LOWBIT_SF_SWZ128);
 }
 
 int64_t block_of(int f) { return f == LOWBIT_NVFP4 ? 16 : 32; }
@@ -105,9 +110,12 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
                           int variant, void* workspace, size_t workspace_bytes, hipStream_t stream,
                           bool static_ws = false) {
   const bool fp4_out = epi == lowbit::kEpiBiasGeluFp4;
+  const bool fp8_out = epi == lowbit::kEpiFp8;
+  const bool q_out = fp4_out || fp8_out;   // packed output plus scales
   // EINVAL: enums and pointers
-  if (!fmt_ok(fmt) || !layout_ok(la) || !layout_ok(lb)) return LOWBIT_EINVAL;
+  if (!fmt_ok(fmt) || !gemm_layout_ok(fmt, la) || !gemm_layout_ok(fmt, lb)) return LOWBIT_EINVAL;
   if (fp4_out && !layout_ok(out_layout)) return LOWBIT_EINVAL;
+  if (fp8_out && out_layout != LOWBIT_SF_LINEAR && out_layout != LOWBIT_SF_SWZ128) return LOWBIT_EINVAL;
   if (variant < -1 || variant > lowbit::kVariantSplitK) return LOWBIT_EINVAL;
   if (workspace_bytes > 0 && !workspace) return LOWBIT_EINVAL;
   if (M < 0 || N < 0 || K < 0) return LOWBIT_ESHAPE;
@@ -119,23 +127,25 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
     const bool needs_res = epi == lowbit::kEpiResidual || epi == lowbit::kEpiBiasResidual;
     if (needs_bias && !bias) return LOWBIT_EINVAL;
     if (needs_res && !residual) return LOWBIT_EINVAL;
-    if (fp4_out ? (!out_packed || !out_sf) : !out) return LOWBIT_EINVAL;
+    if (q_out ? (!out_packed || !out_sf) : !out) return LOWBIT_EINVAL;
   }
   // ESHAPE
   const int64_t B = block_of(fmt);
   if (K < B || K % B != 0) return LOWBIT_ESHAPE;
   if (fp4_out && N % 16 != 0) return LOWBIT_ESHAPE;
+  if (fp8_out && N % 32 != 0) return LOWBIT_ESHAPE;
   // workspace on offer: the caller's, or the static scratch
   const size_t ws_avail = static_ws ? kStaticScratchBytes : (workspace ? workspace_bytes : 0);
   const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, ws_avail);
   if (v < 0) return LOWBIT_ESHAPE;
   // split-K asked for explicitly needs the workspace it documents; beyond
   // the static scratch that is a size the entry point does not take
-  const lowbit::SplitPlan plan = lowbit::gemm_splitk_plan(M, N, K, variant == lowbit::kVariantSplitK);
+  const lowbit::SplitPlan plan = lowbit::gemm_splitk_plan(M, N, K, fmt, variant == lowbit::kVariantSplitK);
   if (v == lowbit::kVariantSplitK && !empty && ws_avail < plan.bytes)
     return static_ws ? LOWBIT_ESHAPE : LOWBIT_EINVAL;
   // the prefill schedule addresses each operand through a 32-bit buffer offset
-  if (v == 1 && (M * (K / 2) >= (int64_t(1) << 30) || N * (K / 2) >= (int64_t(1) << 30)))
+  if (v == 1 && (M * packed_row_bytes(fmt, K) >= (int64_t(1) << 30) ||
+                 N * packed_row_bytes(fmt, K) >= (int64_t(1) << 30)))
     return LOWBIT_ESHAPE;
   if (empty) return LOWBIT_OK;
   // EALIGN
@@ -147,6 +157,8 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
     if (!aligned(out_packed, 8) || (out_layout == LOWBIT_SF_TILED && !aligned(out_sf, 4)))
       return LOWBIT_EALIGN;
     if (gs_out && !aligned(gs_out, 4)) return LOWBIT_EALIGN;
+  } else if (fp8_out) {
+    if (!aligned(out_packed, 16)) return LOWBIT_EALIGN;
   } else if (!aligned(out, 16)) {
     return LOWBIT_EALIGN;
   }
@@ -241,7 +253,9 @@ const char* lowbit_status_str(lowbit_status s) {
 }
 
 size_t lowbit_sf_bytes(int64_t rows, int64_t k, lowbit_format fmt, lowbit_sf_layout layout) {
-  if (!qfmt_layout_ok(fmt, layout) || rows < 0 || k < 0 || k % block_of(fmt) != 0) return 0;
+  // the quantization formats and layouts, and the FP8 GEMM output's 128 x 4 layout
+  const bool ok = qfmt_layout_ok(fmt, layout) || (fmt == LOWBIT_MXFP8 && layout == LOWBIT_SF_SWZ128);
+  if (!ok || rows < 0 || k < 0 || k % block_of(fmt) != 0) return 0;
   return (size_t)lowbit::sf_bytes_of(layout, rows, k / block_of(fmt));
 }
 
@@ -402,6 +416,16 @@ lowbit_status lowbit_gemm_bias_gelu_bf16(const uint8_t* a, const uint8_t* b, con
                      stream);
 }
 
+lowbit_status lowbit_gemm_fp8(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
+                              int64_t M, int64_t N, int64_t K, lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                              lowbit_sf_layout sfb_layout, float alpha, uint8_t* out_packed, uint8_t* out_sf,
+                              lowbit_sf_layout out_layout, int variant, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return gemm_common(a, b, sfa, sfb, M, N, K, fmt, sfa_layout, sfb_layout, alpha, lowbit::kEpiFp8, nullptr,
+                     nullptr, nullptr, nullptr, out_packed, out_sf, out_layout, variant, workspace,
+                     workspace_bytes, stream);
+}
+
 lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                         const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                         lowbit_format fmt, lowbit_sf_layout sfa_layout,
@@ -424,7 +448,7 @@ int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt,
 size_t lowbit_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, lowbit_format fmt, int variant) {
   if (!fmt_ok(fmt) || M < 0 || N < 0 || K < block_of(fmt) || K % block_of(fmt) != 0) return 0;
   if (variant != -1 && variant != lowbit::kVariantSplitK) return 0;
-  return lowbit::gemm_splitk_plan(M, N, K, variant == lowbit::kVariantSplitK).bytes;
+  return lowbit::gemm_splitk_plan(M, N, K, fmt, variant == lowbit::kVariantSplitK).bytes;
 }
 
 }  // extern "C"

@@ -12,12 +12,12 @@ namespace lowbit {
 
 constexpr int kWave = 64;
 
-// MXFP8 and kNV32 (the NVFP4 rule on 32-blocks): quantization only, no GEMM
+// kNV32 (the NVFP4 rule on 32-blocks): quantization only, no GEMM
 enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2, kNV32 = 3 };
 // kSwz128: the producer page's 128 x 4 swizzled layout (quantization side only)
 enum Layout : int { kLinear = 0, kTiled = 1, kSwz128 = 2 };
 enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual = 3, kEpiBiasGelu = 4,
-                 kEpiBiasGeluFp4 = 5 };
+                 kEpiBiasGeluFp4 = 5, kEpiFp8 = 6 };
 
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<kNVFP4> { static constexpr int B = 16; };

@@ -30,6 +30,7 @@ hipError_t launch_fmt(const GemmArgs& g, int variant, hipStream_t s) {
     case kEpiBiasResidual: return launch_one<FMT, kEpiBiasResidual>(g, variant, s);
     case kEpiBiasGelu: return launch_one<FMT, kEpiBiasGelu>(g, variant, s);
     case kEpiBiasGeluFp4: return launch_one<FMT, kEpiBiasGeluFp4>(g, variant, s);
+    case kEpiFp8: return launch_one<FMT, kEpiFp8>(g, variant, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -37,15 +38,17 @@ hipError_t launch_fmt(const GemmArgs& g, int variant, hipStream_t s) {
 }  // namespace
 
 // Split-K targets twice as many workgroups as the chip has CUs, each split
-// holding at least four supersteps of K (one per wave).  Its second launch
+// holding at least four supersteps of K (one per wave; a superstep is 256
+// FP4 or 128 FP8 elements).  Its second launch
 // costs about as much as one round trip of loads, so the automatic choice
 // splits only K of 16 supersteps or more (measured: (41, 1536, 6144) MXFP4
 // 13.7 -> 10.7 us split; (41, 4608, 1536) 6.8 -> 9.4 us, so not split).
 constexpr int64_t kSplitTargetWorkgroups = 512;
 constexpr int64_t kSplitMinSupersteps = 16;
 
-SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, bool force) {
-  const int64_t nss = (K + 255) / 256;
+SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force) {
+  const int64_t ss = fmt == kMXFP8 ? 128 : 256;   // K elements of a superstep
+  const int64_t nss = (K + ss - 1) / ss;
   SplitPlan none{1, (int)nss, 0};
   if (M <= 0 || M > 128 || N <= 0 || K <= 0) return none;
   const int64_t tiles = (N + 31) / 32, mt = (M + 31) / 32;
@@ -66,10 +69,10 @@ int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, siz
   if (variant == kVariantSplitK) {
     // the caller asked for split-K: M <= 128 and a K of two supersteps at least
     if (M == 0 || N == 0) return kVariantSplitK;   // nothing to run
-    return gemm_splitk_plan(M, N, K, true).splits > 1 ? kVariantSplitK : -1;
+    return gemm_splitk_plan(M, N, K, fmt, true).splits > 1 ? kVariantSplitK : -1;
   }
   if (variant == -1 && M <= 128) {
-    const SplitPlan p = gemm_splitk_plan(M, N, K, false);
+    const SplitPlan p = gemm_splitk_plan(M, N, K, fmt, false);
     if (p.splits > 1 && ws_bytes >= p.bytes) return kVariantSplitK;
   }
   if (half_k) return (variant == -1 || variant == 0) ? 0 : -1;
@@ -81,7 +84,12 @@ int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, siz
 
 hipError_t launch_gemm(const GemmArgs& g, int variant, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  return g.fmt == kMXFP4 ? launch_fmt<kMXFP4>(g, variant, s) : launch_fmt<kNVFP4>(g, variant, s);
+  switch (g.fmt) {
+    case kNVFP4: return launch_fmt<kNVFP4>(g, variant, s);
+    case kMXFP4: return launch_fmt<kMXFP4>(g, variant, s);
+    case kMXFP8: return launch_fmt<kMXFP8>(g, variant, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lowbit

@@ -52,7 +52,10 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSSBytes = 128;   // packed bytes per row per superstep (256 elements)
+constexpr int kSSBytes = 128;   // packed bytes per row per superstep (256 FP4 / 128 FP8 elements)
+// elements of K in one superstep, and packed bytes per K element times 2
+template <int FMT> constexpr int ss_elems() { return FMT == kMXFP8 ? 128 : 256; }
+template <int FMT> constexpr int64_t row_bytes(int64_t K) { return FMT == kMXFP8 ? K : K / 2; }
 constexpr int kEpiPitch = 36;   // fp32 pitch of a 32x32 epilogue tile in LDS
 
 // 64 bytes of one row held by one lane for one superstep.
@@ -67,12 +70,16 @@ struct Frag {
 template <int FMT> struct SfWord;
 template <> struct SfWord<kMXFP4> { uint32_t w; };
 template <> struct SfWord<kNVFP4> { uint32_t w[2]; };
+// MXFP8: a 128-element superstep holds four 32-blocks; lane half c takes
+// blocks c (bytes 0..31 of its 64) and 2 + c (bytes 64..95): byte h of the
+// word is the UE8M0 scale of block 2h + c (LINEAR scales only)
+template <> struct SfWord<kMXFP8> { uint32_t w; };
 
 // byte-select pattern of v_perm picking bytes {2c, 2c+1} of two words
 __device__ __forceinline__ uint32_t pair_sel(int c) { return c ? 0x07060302u : 0x05040100u; }
 
 template <int FMT>
-__device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int layout, int64_t row,
+__device__ __forceinline__ void load_sf_fp4(SfWord<FMT>& out, const uint8_t* sf, int layout, int64_t row,
                                         int64_t R, int64_t nblk, int64_t ss, int c) {
   // absent rows / blocks carry no data; give them a harmless finite scale
   constexpr uint32_t kPad = (FMT == kMXFP4) ? 0x7F7F7F7Fu : 0u;
@@ -112,6 +119,35 @@ __device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int
   } else {
     out.w[0] = w[0];
     out.w[1] = w[1];
+  }
+}
+
+// MXFP8 (LINEAR scales): byte h of the lane's word is the scale of block
+// 2h + c of superstep ss; absent rows / blocks get 2^0
+__device__ __forceinline__ void load_sf_f8(SfWord<kMXFP8>& out, const uint8_t* sf, int64_t row, int64_t R,
+                                           int64_t nblk, int64_t ss, int c) {
+  uint32_t w = 0x7F7Fu;
+  if (row < R) {
+    const uint8_t* p = sf + row * nblk;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int64_t kb = 4 * ss + 2 * h + c;
+      const uint32_t byte = (kb < nblk) ? (uint32_t)p[kb] : 0x7Fu;
+      w = (w & ~(0xFFu << (8 * h))) | (byte << (8 * h));
+    }
+  }
+  out.w = w;
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_sf(SfWord<FMT>& out, const uint8_t* sf, int layout, int64_t row,
+                                        int64_t R, int64_t nblk, int64_t ss, int c) {
+  if constexpr (FMT == kMXFP8) {
+    (void)layout;
+    load_sf_f8(out, sf, row, R, nblk, ss, c);
+    return;
+  } else {
+    load_sf_fp4<FMT>(out, sf, layout, row, R, nblk, ss, c);
   }
 }
 
@@ -184,6 +220,48 @@ __device__ __forceinline__ v8h dq8(uint32_t w, NvPart sc) {
   return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// MXFP8 dequantization to bf16, exact while the product is a normal bf16:
+// an E4M3 value has 4 significant bits and the UE8M0 scale is a power of two
+// 2^e, so E4M3 * 2^e is exact for e in [-117, 119] (bf16 has binary32's
+// exponent range).  Eight elements (two dwords, element i in byte i).
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8bf dq8_f8(uint32_t lo, uint32_t hi, float scale) {
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, scale, false);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, scale, true);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, scale, false);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, scale, true);
+  return v8bf{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+// UE8M0 scale byte h of an MXFP8 scale word as an fp32 power of two
+__device__ __forceinline__ float f8_scale(const SfWord<kMXFP8>& sw, int h) {
+  return ue8m0_to_f32((sw.w >> (8 * h)) & 0xFFu);
+}
+// acc[i][j] += quarter S of an MXFP8 superstep: 16 elements of block 2(S/2) + c
+// per lane, two bf16 MFMA steps of 8
+template <int S, int TI, int TJ>
+__device__ __forceinline__ void quarter_f8(v16f (&acc)[TI][TJ], const u32x4 (&qa)[TI], const u32x4 (&qb)[TJ],
+                                           const SfWord<kMXFP8> (&sa)[TI], const SfWord<kMXFP8> (&sb)[TJ]) {
+  float fa[TI], fb[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; i++) fa[i] = f8_scale(sa[i], S >> 1);
+#pragma unroll
+  for (int j = 0; j < TJ; j++) fb[j] = f8_scale(sb[j], S >> 1);
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    v8bf va[TI], vb[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; i++) va[i] = dq8_f8(qa[i][2 * t], qa[i][2 * t + 1], fa[i]);
+#pragma unroll
+    for (int j = 0; j < TJ; j++) vb[j] = dq8_f8(qb[j][2 * t], qb[j][2 * t + 1], fb[j]);
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], vb[j], acc[i][j], 0, 0, 0);
+  }
+}
+
 __device__ __forceinline__ uint32_t frag_dword(const Frag& f, int t) {
   const u32x4 q = f.q[t >> 2];
   switch (t & 3) {
@@ -198,7 +276,15 @@ __device__ __forceinline__ uint32_t frag_dword(const Frag& f, int t) {
 template <int FMT, int TI, int TJ>
 __device__ __forceinline__ void superstep_mma(v16f (&acc)[TI][TJ], const Frag (&fa)[TI], const Frag (&fb)[TJ],
                                               const SfWord<FMT> (&sa)[TI], const SfWord<FMT> (&sb)[TJ]) {
-  if constexpr (FMT == kMXFP4) {
+  if constexpr (FMT == kMXFP8) {
+    u32x4 qa[TI], qb[TJ];
+#define LB_F8(S)                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < TI; i++) qa[i] = fa[i].q[S];                              \
+    _Pragma("unroll") for (int j = 0; j < TJ; j++) qb[j] = fb[j].q[S];                              \
+    quarter_f8<S, TI, TJ>(acc, qa, qb, sa, sb);
+    LB_F8(0) LB_F8(1) LB_F8(2) LB_F8(3)
+#undef LB_F8
+  } else if constexpr (FMT == kMXFP4) {
 #define LB_SLICE(S)                                                                                  \
     _Pragma("unroll") for (int i = 0; i < TI; i++)                                                   \
     _Pragma("unroll") for (int j = 0; j < TJ; j++)                                                   \
@@ -228,7 +314,9 @@ __device__ __forceinline__ void superstep_mma(v16f (&acc)[TI][TJ], const Frag (&
 template <int FMT, int S, int TI, int TJ>
 __device__ __forceinline__ void quarter_mma(v16f (&acc)[TI][TJ], const u32x4 (&qa)[TI], const u32x4 (&qb)[TJ],
                                             const SfWord<FMT> (&sa)[TI], const SfWord<FMT> (&sb)[TJ]) {
-  if constexpr (FMT == kMXFP4) {
+  if constexpr (FMT == kMXFP8) {
+    quarter_f8<S, TI, TJ>(acc, qa, qb, sa, sb);
+  } else if constexpr (FMT == kMXFP4) {
 #pragma unroll
     for (int i = 0; i < TI; i++)
 #pragma unroll
@@ -319,7 +407,28 @@ template <int EPI>
 __device__ __forceinline__ void epi_run16(const float* t, int64_t m, int64_t n, const GemmArgs& g) {
   if (m >= g.M || n >= g.N) return;
   const float alpha = g.alpha;
-  if constexpr (EPI == kEpiBiasGeluFp4) {
+  if constexpr (EPI == kEpiFp8) {
+    // FP8 output ([WOA] FusedWoAKernel epilogue): bf16(alpha * acc) first, then
+    // the 32-column MX block: this lane's 16 columns and its partner's (lane
+    // ^ 32, the same row and the other half of the block: every caller maps
+    // the two halves of a 32-column tile onto lanes l and l + 32, and N % 32
+    // == 0 keeps both halves live together) share one OCP MX scale (emax 8)
+    float y[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      y[k] = bf16_to_f32(f32_to_bf16(alpha * t[k]));
+      amax = fmaxf(amax, fabsf(y[k]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    float inv;
+    const uint32_t sb = mx_block_scale_e<8>(amax, &inv);
+#pragma unroll
+    for (int k = 0; k < 16; k++) y[k] = __fmul_rn(y[k], inv);   // exact: a power of two
+    const uint2 lo = e4m3x8(y), hi = e4m3x8(y + 8);
+    *reinterpret_cast<uint4*>(g.out_packed + m * g.N + n) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    if ((n & 31) == 0) g.out_sf[sf_offset(kMXFP8, g.out_layout, m, n / 32, g.N / 32)] = (uint8_t)sb;
+  } else if constexpr (EPI == kEpiBiasGeluFp4) {
     // N % 16 == 0, so the whole block is in range
     float z[16];
 #pragma unroll
@@ -371,6 +480,32 @@ __device__ __forceinline__ void epi_run16(const float* t, int64_t m, int64_t n, 
         }
       }
     }
+  }
+}
+
+// Zero the padding of the FP8 output's 128 x 4 scale layout that this
+// workgroup owns: rows [max(M, r0), min(rows_pad, r1)) x blocks [b0, b1), and,
+// for the workgroup holding the last column block, blocks [nblk, nblk_pad)
+// of rows [r0, min(rows_pad, r1)).
+__device__ __forceinline__ void fp8_out_padding(const GemmArgs& g, int64_t r0, int64_t r1, int64_t b0,
+                                                int64_t b1, bool last_col_tile, int tid, int nthreads) {
+  if (g.out_layout != kSwz128) return;
+  const int64_t nblk = g.N / 32;
+  const int64_t nblk_pad = sf_pad_blocks(kSwz128, nblk);
+  const int64_t rows_pad = sf_pad_rows(kSwz128, g.M);
+  const int64_t re = r1 < rows_pad ? r1 : rows_pad;
+  const int64_t be = b1 < nblk ? b1 : nblk;
+  const int64_t rs = r0 > g.M ? r0 : g.M;
+  if (rs < re && b0 < be) {
+    const int64_t cnt = (re - rs) * (be - b0);
+    for (int64_t i = tid; i < cnt; i += nthreads)
+      g.out_sf[sf_offset(kMXFP8, kSwz128, rs + i / (be - b0), b0 + i % (be - b0), nblk)] = 0;
+  }
+  if (last_col_tile && nblk_pad > nblk && r0 < re) {
+    const int64_t w = nblk_pad - nblk;
+    const int64_t cnt = (re - r0) * w;
+    for (int64_t i = tid; i < cnt; i += nthreads)
+      g.out_sf[sf_offset(kMXFP8, kSwz128, r0 + i / w, nblk + i % w, nblk)] = 0;
   }
 }
 
@@ -608,9 +743,9 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_v2_kernel(GemmArgs 
   const int64_t tn = (t % group) / gsz;
   const int64_t m0 = tm * kPBM, n0 = tn * kPBN;
 
-  const int64_t kbytes = g.K / 2;
-  const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
-  const int64_t nss = (g.K + 255) / 256;
+  const int64_t kbytes = row_bytes<FMT>(g.K);
+  const int64_t nblk = g.K / FmtTraits<FMT>::B;
+  const int64_t nss = (g.K + ss_elems<FMT>() - 1) / ss_elems<FMT>();
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.M * kbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb =
@@ -753,6 +888,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_v2_kernel(GemmArgs 
   }
   if constexpr (EPI == kEpiBiasGeluFp4)
     fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + kPBN) / 16, n0 + kPBN >= g.N, tid, kPThreads);
+  if constexpr (EPI == kEpiFp8)
+    fp8_out_padding(g, m0, m0 + kPBM, n0 / 32, (n0 + kPBN) / 32, n0 + kPBN >= g.N, tid, kPThreads);
 }
 
 // s_waitcnt: vmcnt <= N (N < 64), lgkmcnt 0
@@ -1198,9 +1335,9 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, c = lane >> 5;
   const int64_t n0 = (int64_t)blockIdx.x * 32;
-  const int64_t kbytes = g.K / 2;
-  const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
-  const int64_t nss_all = (g.K + 255) / 256;
+  const int64_t kbytes = row_bytes<FMT>(g.K);
+  const int64_t nblk = g.K / FmtTraits<FMT>::B;
+  const int64_t nss_all = (g.K + ss_elems<FMT>() - 1) / ss_elems<FMT>();
   const int64_t s_begin = SPLIT ? (int64_t)blockIdx.y * g.per : 0;
   const int64_t nss = SPLIT ? (s_begin + g.per < nss_all ? s_begin + g.per : nss_all) : nss_all;
 
@@ -1283,6 +1420,8 @@ __global__ __launch_bounds__(W * 64) void gemm_decode_kernel(GemmArgs g) {
     }
     if constexpr (EPI == kEpiBiasGeluFp4)
       fp4_out_padding(g, 0, (g.M + 31) / 32 * 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, tid, W * 64);
+    if constexpr (EPI == kEpiFp8)
+      fp8_out_padding(g, 0, 128, n0 / 32, n0 / 32 + 1, n0 + 32 >= g.N, tid, W * 64);
   }
 }
 
@@ -1316,6 +1455,8 @@ __global__ __launch_bounds__(64) void gemm_splitk_reduce_kernel(GemmArgs g, int 
   epi_run16<EPI>(t + r * kEpiPitch + ec, i * 32 + r, n0 + ec, g);
   if constexpr (EPI == kEpiBiasGeluFp4)
     fp4_out_padding(g, i * 32, i * 32 + 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, lane, 64);
+  if constexpr (EPI == kEpiFp8)   // the last M-tile also owns the padding rows up to 128
+    fp8_out_padding(g, i * 32, (i + 1 == MT) ? 128 : i * 32 + 32, n0 / 32, n0 / 32 + 1, n0 + 32 >= g.N, lane, 64);
 }
 
 template <int FMT, int EPI>
@@ -1350,7 +1491,7 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
   }
   if constexpr (FMT == kNVFP4) {
     LB_DEC(1, 8, false) LB_DEC(2, 8, true) LB_DEC(3, 8, false) LB_DEC(4, 8, false)
-  } else {
+  } else {   // MXFP4, and MXFP8 (its dequantization is half an instruction an element)
     LB_DEC(1, 8, true) LB_DEC(2, 8, true) LB_DEC(3, 4, true) LB_DEC(4, 4, true)
   }
 #undef LB_DEC
@@ -1364,10 +1505,11 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t s) {
 // and output), each slice starting on a 32-row scale group.
 template <int FMT, int EPI>
 hipError_t launch_decode_rows(const GemmArgs& g, hipStream_t s) {
-  const bool half = (g.K / 2) % 16 != 0;
+  const bool half = FMT == kNVFP4 && (g.K / 2) % 16 != 0;
   if (g.M <= 128)
-    return half ? launch_decode<FMT, EPI, true>(g, s) : launch_decode<FMT, EPI, false>(g, s);
-  const int64_t kbytes = g.K / 2, nblk = g.K / FmtTraits<FMT>::B, nblk_out = g.N / 16;
+    return half ? launch_decode<FMT, EPI, FMT == kNVFP4>(g, s) : launch_decode<FMT, EPI, false>(g, s);
+  const int64_t kbytes = row_bytes<FMT>(g.K), nblk = g.K / FmtTraits<FMT>::B;
+  const int64_t nblk_out = g.N / (EPI == kEpiFp8 ? 32 : 16);
   for (int64_t m0 = 0; m0 < g.M; m0 += 128) {
     GemmArgs q = g;
     q.M = (g.M - m0) < 128 ? (g.M - m0) : 128;
@@ -1375,11 +1517,12 @@ hipError_t launch_decode_rows(const GemmArgs& g, hipStream_t s) {
     q.sfa = g.sfa + (g.la == kTiled ? (m0 / 32) * ((nblk + 7) / 8) * 256 : m0 * nblk);
     if (g.residual) q.residual = g.residual + m0 * g.N;
     if (g.out) q.out = g.out + m0 * g.N;
-    if (g.out_packed) q.out_packed = g.out_packed + m0 * (g.N / 2);
-    if (g.out_sf)
-      q.out_sf = g.out_sf + (g.out_layout == kTiled ? (m0 / 32) * ((nblk_out + 7) / 8) * 256 : m0 * nblk_out);
+    if (g.out_packed) q.out_packed = g.out_packed + m0 * (EPI == kEpiFp8 ? g.N : g.N / 2);
+    // m0 is a multiple of 128: the scale bytes of rows < m0 come first in
+    // every layout, whole 32-row (TILED) and 128-row (128 x 4) groups
+    if (g.out_sf) q.out_sf = g.out_sf + sf_bytes_of(g.out_layout, m0, nblk_out);
     const hipError_t e =
-        half ? launch_decode<FMT, EPI, true>(q, s) : launch_decode<FMT, EPI, false>(q, s);
+        half ? launch_decode<FMT, EPI, FMT == kNVFP4>(q, s) : launch_decode<FMT, EPI, false>(q, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1389,18 +1532,56 @@ template <int FMT, int EPI>
 hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   if (variant == 0) return launch_decode_rows<FMT, EPI>(g, s);
   const int64_t T = ((g.M + kPBM - 1) / kPBM) * ((g.N + kPBN - 1) / kPBN);
-  // the stage pipeline fetches LINEAR scales with dword DMA: that needs the
-  // blocks per row to be a multiple of 4 and a 4-byte aligned base
-  const int64_t nblk = g.K / (FMT == kMXFP4 ? 32 : 16);
-  auto dword_ok = [&](const uint8_t* p, int lay) {
-    return lay == kTiled || (nblk % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3) == 0);
-  };
-  if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
-    const dim3 grid((unsigned)T), block(kPThreads);
-    launch_w<FMT, EPI>(g, block, s);
-  } else
+  // MXFP8 operands and the FP8 output run the 64-byte-stage prefill kernel;
+  // the 128-byte-stage one fetches LINEAR scales with dword DMA, which needs
+  // the blocks per row to be a multiple of 4 and a 4-byte aligned base
+  if constexpr (FMT == kMXFP8 || EPI == kEpiFp8) {
     hipLaunchKernelGGL((gemm_prefill_v2_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
+  } else {
+    const int64_t nblk = g.K / FmtTraits<FMT>::B;
+    auto dword_ok = [&](const uint8_t* p, int lay) {
+      return lay == kTiled || (nblk % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3) == 0);
+    };
+    if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
+      const dim3 grid((unsigned)T), block(kPThreads);
+      launch_w<FMT, EPI>(g, block, s);
+    } else
+      hipLaunchKernelGGL((gemm_prefill_v2_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
+  }
   return hipGetLastError();
+}
+
+// Split-K launch: the partial pass (decode kernel with SPLIT; one
+// instantiation per format, M-tiles, waves and half-chunk flag, shared by
+// the epilogues) and the reduce pass with the epilogue.
+template <int FMT, int EPI, int MT, bool HALF>
+hipError_t launch_splitk_mt(const GemmArgs& g, hipStream_t s) {
+  // MXFP4 and MXFP8 keep two supersteps in flight per wave, NVFP4 (bound by
+  // its dequantization work) one, as in the decode schedule
+  constexpr bool DB = FMT != kNVFP4;
+  const unsigned tiles = (unsigned)((g.N + 31) / 32);
+  const dim3 grid(tiles, (unsigned)g.splits);
+  if (g.per >= 4)
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, MT, 4, kEpiNone, DB, HALF, true>), grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<FMT, MT, 2, kEpiNone, DB, HALF, true>), grid, dim3(128), 0, s, g);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<EPI>), dim3(tiles, (unsigned)MT), dim3(64), 0, s, g, MT);
+  return hipGetLastError();
+}
+
+template <int FMT, int EPI>
+hipError_t launch_splitk(const GemmArgs& g, hipStream_t s) {
+  const int mt = (int)((g.M + 31) / 32);
+  const bool half = FMT == kNVFP4 && (g.K / 2) % 16 != 0;
+#define LB_SPLIT(MT)                                                                        \
+  if (mt == MT)                                                                             \
+    return half ? launch_splitk_mt<FMT, EPI, MT, (FMT == kNVFP4)>(g, s)                   \
+                : launch_splitk_mt<FMT, EPI, MT, false>(g, s);
+  LB_SPLIT(1) LB_SPLIT(2) LB_SPLIT(3) LB_SPLIT(4)
+#undef LB_SPLIT
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gk

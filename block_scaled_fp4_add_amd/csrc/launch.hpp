@@ -47,8 +47,8 @@ struct GemmArgs {
   const uint16_t* residual;   // (M, N) or nullptr
   uint16_t* out;              // bf16 (M, N)
   const float* gs_out;        // FP4 output: global scale or nullptr
-  uint8_t* out_packed;        // FP4 output: (M, N/2)
-  uint8_t* out_sf;            // FP4 output scales
+  uint8_t* out_packed;        // FP4 output: (M, N/2); FP8 output: (M, N)
+  uint8_t* out_sf;            // FP4 / FP8 output scales
   int out_layout;
   float* ws;                  // split-K: fp32 partial tiles (device), else nullptr
   int splits;                 // split-K: workgroups along K per 32-column tile
@@ -66,7 +66,7 @@ struct SplitPlan {
   int per;
   size_t bytes;
 };
-SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, bool force);
+SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force);
 
 // Schedule resolution shared by the launcher, lowbit_gemm_pick_variant and
 // lowbit_gemm_workspace_bytes: -1 resolves by shape and by the workspace the

@@ -77,10 +77,11 @@ typedef enum {
  * MXFP4: 32-element blocks, UE8M0 scales.  Both pack two E2M1 codes per byte:
  *        packed (rows, K/2), element 2j in the low nibble of byte j.
  * MXFP8: 32-element blocks, UE8M0 scales, E4M3 elements, one byte each:
- *        packed (rows, K).  Scale rule e = clamp(floor(log2 amax) - 8, -127,
- *        127) (OCP MX, emax 8 for E4M3); elements nearest-even, saturating at
- *        448, sign kept.  Producer, quantizer and dequantizer only, LINEAR
- *        scales only; the GEMMs return LOWBIT_EINVAL for it.
+ *        packed (rows, K) ([WOA]'s format).  Scale rule e = clamp(floor(log2
+ *        amax) - 8, -127, 127) (OCP MX, emax 8 for E4M3); elements
+ *        nearest-even, saturating at 448, sign kept.  LINEAR scales for the
+ *        producer, quantizer, dequantizer and GEMM operands; the FP8 GEMM
+ *        output (lowbit_gemm_fp8) also takes the 128 x 4 layout.
  * NVFP4_B32: the NVFP4 rule (E4M3 scales, optional global scale, clamp at
  *        448) on 32-element blocks ([FI] add_rmsnorm_fp4quant's E4M3 scale
  *        format at block size 32); packed like NVFP4.  Producer, quantizer and
@@ -91,8 +92,9 @@ typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2, LOWBIT_NVFP
  * contiguous bytes, tiles row-tile major with ceil(K/B/4) tiles per row tile;
  * inside a tile row r and block kb sit at byte 16*(r%32) + 4*((r%128)/32) +
  * kb%4.  lowbit_sf_bytes = ceil(rows/128) * ceil(K/B/4) * 512; padding bytes
- * are written zero.  Producer, quantizer and dequantizer with NVFP4 or MXFP4
- * only; the GEMMs return LOWBIT_EINVAL for it. */
+ * are written zero.  Producer, quantizer and dequantizer with NVFP4 or MXFP4,
+ * and the MXFP8 output of lowbit_gemm_fp8 ([WOA]'s F8_128x4 scale bytes);
+ * GEMM operands do not take it (LOWBIT_EINVAL). */
 typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1, LOWBIT_SF_SWZ128 = 2 } lowbit_sf_layout;
 
 /* GEMM schedule: -1 picks by shape (and by the workspace offered); 0 =
@@ -216,11 +218,16 @@ lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_
                                 lowbit_format fmt, lowbit_sf_layout layout,
                                 const float* global_scale, void* out, hipStream_t stream);
 
-/* Block-scaled A4W4 GEMM ([FRT] nvfp4_gemm_bf16 and its epilogue family).
+/* Block-scaled GEMM ([FRT] nvfp4_gemm_bf16 and its epilogue family).
  * a: packed (M, K/2); b: packed (N, K/2) (the weight, "B^T" row-major);
  * sfa / sfb: their scales in sfa_layout / sfb_layout; both operands use `fmt`.
  * acc[m,n] = sum_k Ahat[m,k] * Bhat[n,k] with Ahat = E2M1 * scale (no global
  * scale: pass alpha = 1/(gsA*gsB) for NVFP4 operands), accumulated in fp32.
+ * MXFP8 operands ([WOA]'s format: a (M, K), b (N, K), one E4M3 byte an
+ * element, LINEAR UE8M0 scales) are dequantized to bf16 -- exact while
+ * E4M3 * 2^e is a normal bf16, i.e. scale bytes 10..246 -- and accumulated in
+ * fp32 by the bf16 MFMA; they run the decode, split-K and 64-byte-stage
+ * prefill schedules.
  * out: bf16 (M, N) = bf16(alpha*acc [+ bias[n]] [+ residual[m,n]]) or
  * bf16(GELU(alpha*acc + bias[n])), GELU(t) = 0.5 t (1 + erf(t/sqrt 2)).
  * bias: bf16 (N); residual: bf16 (M, N) (may alias out).
@@ -306,6 +313,22 @@ lowbit_status lowbit_gemm_bf16_noalloc(const uint8_t* a, const uint8_t* b, const
                                        lowbit_format fmt, lowbit_sf_layout sfa_layout,
                                        lowbit_sf_layout sfb_layout, float alpha, void* out,
                                        int variant, hipStream_t stream);
+
+/* GEMM with FP8 output ([WOA] FusedWoAKernel.device_kernel output epilogue:
+ * the reduced sum rounded to bf16, a 32-column block maximum, an MX scale,
+ * FP8 elements).  value = bf16(alpha * acc), then each 32-run of an output row
+ * is quantized as MXFP8 (the rule above; an all-zero block gets scale byte 0)
+ * into out_packed: uint8 (M, N), one E4M3 byte an element, and out_sf:
+ * lowbit_sf_bytes(M, N, LOWBIT_MXFP8, out_layout) bytes, out_layout
+ * LOWBIT_SF_LINEAR or LOWBIT_SF_SWZ128 (the page's 128 x 4 scale bytes,
+ * padding written zero).  Operands in any GEMM format; requires N % 32 == 0;
+ * out_packed 16-byte aligned.  Other arguments as lowbit_gemm_bf16. */
+lowbit_status lowbit_gemm_fp8(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
+                              const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
+                              lowbit_format fmt, lowbit_sf_layout sfa_layout,
+                              lowbit_sf_layout sfb_layout, float alpha, uint8_t* out_packed,
+                              uint8_t* out_sf, lowbit_sf_layout out_layout, int variant,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Which schedule a GEMM call with these sizes and this much workspace would
  * run (-1 auto resolved), or -1 if the sizes or the variant are invalid.

@@ -165,3 +165,78 @@ def gemm_within_tolerance(gpu, ref, l1):
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(tol > 0, err / tol, np.where(err > 0, np.inf, 0.0))
     return ok, float(np.max(ratio)) if ratio.size else 0.0
+
+
+# --- FP8-output epilogue ---------------------------------------------------------------------
+# The device rounds its fp32 sum alpha * t to bf16 and quantizes the bf16
+# values; the oracle does the same from the binary64 sum.  t differs from the
+# exact sum by the fp32 accumulation (<= 1e-6 L1) and alpha * t by one more fp32
+# rounding, so the device's bf16 value is one of the bf16 roundings of
+# [ref - e, ref + e], e = 2^-22 |ref| + 1e-6 L1.  Rounding is monotone, so
+# the block maximum, the scale byte (a function of the binade of the block
+# maximum) and each code (under the device's scale byte) must lie between
+# those of the interval's ends.
+
+def bf16_of_f32(x):
+    """Round-to-nearest-even bf16 value (as float64) of float32 values."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def mx8_scale_byte(amax):
+    """Scale byte of an MXFP8 block maximum: max(biased exponent - 8, 0)."""
+    eb = (np.ascontiguousarray(amax, dtype=np.float32).view(np.uint32) >> 23) & 0xFF
+    return np.maximum(eb.astype(np.int64) - 8, 0)
+
+
+def gather_mx8_scales(orc, sf, rows, nblk, layout):
+    sf = np.asarray(sf, dtype=np.uint8)
+    off = np.array([[orc.sf_offset(m, kb, nblk, orc.MXFP8, layout) for kb in range(nblk)] for m in range(rows)],
+                   dtype=np.int64).reshape(rows, nblk)
+    return sf[off], off
+
+
+def compare_fp8_out(orc, gpu_packed, gpu_sf, orc_packed, orc_sf, ref, l1, rows, N, layout):
+    """Device FP8-output codes and scales against the oracle's under the
+    interval rule above; reports exact matches and hard failures, and (for a
+    padded layout) that every byte outside the covered blocks is zero."""
+    nblk = N // 32
+    ref = np.asarray(ref, dtype=np.float64)
+    e = 2.0 ** -22 * np.abs(ref) + 1e-6 * np.asarray(l1, dtype=np.float64)
+    lo = bf16_of_f32((ref - e).astype(np.float32))
+    hi = bf16_of_f32((ref + e).astype(np.float32))
+    straddle = (lo <= 0) & (hi >= 0)
+    amin = np.where(straddle, 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    amax = np.maximum(np.abs(lo), np.abs(hi))
+    b_lo = mx8_scale_byte(amin.reshape(rows, nblk, 32).max(axis=2))
+    b_hi = mx8_scale_byte(amax.reshape(rows, nblk, 32).max(axis=2))
+    gs, off = gather_mx8_scales(orc, gpu_sf, rows, nblk, layout)
+    os_, _ = gather_mx8_scales(orc, orc_sf, rows, nblk, layout)
+    gs = gs.astype(np.int64)
+    rep = Report(blocks=rows * nblk, scale_diff=int((gs != os_).sum()), code_diff=0, hard_failures=0,
+                 padding_nonzero=0, examples=[])
+    bad_s = (gs < b_lo) | (gs > b_hi)
+    rep["hard_failures"] += int(bad_s.sum())
+    for m, kb in list(zip(*np.nonzero(bad_s)))[:5]:
+        rep["examples"].append(("scale", int(m), int(kb), int(gs[m, kb]), int(os_[m, kb]), int(b_lo[m, kb]),
+                                int(b_hi[m, kb])))
+    gp = np.asarray(gpu_packed, dtype=np.uint8).reshape(rows, N)
+    op = np.asarray(orc_packed, dtype=np.uint8).reshape(rows, N)
+    rep["code_diff"] = int((gp != op).sum())
+    sb = gs.astype(np.uint8).reshape(-1)
+    c_lo = orc.mxfp8_encode_blocks(lo.reshape(-1, 32).astype(np.float32), sb).reshape(rows, N)
+    c_hi = orc.mxfp8_encode_blocks(hi.reshape(-1, 32).astype(np.float32), sb).reshape(rows, N)
+    table = np.array([orc.e4m3_value(c) for c in range(256)])
+    v_dev, v_lo, v_hi = table[gp], table[c_lo], table[c_hi]
+    bad_c = ~((v_dev >= np.minimum(v_lo, v_hi)) & (v_dev <= np.maximum(v_lo, v_hi)))
+    bad_c &= ~np.repeat(bad_s, 32, axis=1)            # a wrong scale is already counted
+    rep["hard_failures"] += int(bad_c.sum())
+    for m, k in np.argwhere(bad_c)[:5]:
+        rep["examples"].append(("code", int(m), int(k), int(gp[m, k]), int(op[m, k]), float(ref[m, k])))
+    if layout != orc.LINEAR:
+        used = np.zeros(np.asarray(gpu_sf).size, bool)
+        used[off.ravel()] = True
+        rep["padding_nonzero"] = int(np.count_nonzero(np.asarray(gpu_sf)[~used]))
+        rep["hard_failures"] += rep["padding_nonzero"]
+    return rep

@@ -52,13 +52,14 @@ def test_sf_bytes_matches_the_oracle(orc):
                 continue
             for layout in (0, 1):
                 assert L.lowbit_sf_bytes(rows, K, fmt, layout) == orc.sf_bytes(rows, K, fmt, layout)
-    # MXFP8: 32-blocks, LINEAR only
+    # MXFP8: 32-blocks, LINEAR and (for the FP8 GEMM output) the 128 x 4 swizzle
     assert L.lowbit_sf_bytes(33, 5120, 2, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 2, 0)
     assert L.lowbit_sf_bytes(33, 5120, 2, 1) == 0
+    assert L.lowbit_sf_bytes(33, 5120, 2, 2) == 128 * 160 == orc.sf_bytes(33, 5120, 2, 2)
     # the 128 x 4 swizzle: FP4 GEMM formats, quantization side
     for rows, K, fmt in ((1, 64, 0), (129, 1120, 1), (300, 5120, 0)):
         assert L.lowbit_sf_bytes(rows, K, fmt, 2) == orc.sf_bytes(rows, K, fmt, 2)
-    assert L.lowbit_sf_bytes(33, 5120, 2, 2) == 0 and L.lowbit_sf_bytes(33, 5120, 3, 2) == 0
+    assert L.lowbit_sf_bytes(33, 5120, 3, 2) == 0
     # the NVFP4 rule on 32-blocks: LINEAR only
     assert L.lowbit_sf_bytes(33, 5120, 3, 0) == 33 * 160 == orc.sf_bytes(33, 5120, 3, 0)
     assert L.lowbit_sf_bytes(33, 5120, 3, 1) == 0
@@ -207,7 +208,9 @@ def test_gemm_argument_order(buf):
     assert call(8, 128, 256, fmt=3) == EINVAL                # 32-block NVFP4: no GEMM
     assert call(8, 128, 256, fmt=4) == EINVAL
     assert call(8, 128, 256, la=2) == EINVAL                 # 128 x 4 swizzle: no GEMM
-    assert call(8, 128, 256, fmt=2) == EINVAL                # MXFP8: no GEMM
+    assert call(8, 128, 256, fmt=2, la=1) == EINVAL          # MXFP8 operands: LINEAR scales only
+    assert call(8, 128, 256, fmt=2, lb_=1) == EINVAL
+    assert call(8, 128, 48, fmt=2) == ESHAPE                 # MXFP8: K % 32
     assert call(8, 128, 256, variant=3) == EINVAL
     assert call(8, 128, 256, wsb=64) == EINVAL               # workspace bytes without a workspace
     assert call(8, 128, 1024, variant=2) == EINVAL           # split-K without its workspace
@@ -224,6 +227,7 @@ def test_gemm_argument_order(buf):
     assert call(0, 128, 256) == OK
     if NO_DEVICE:
         assert call(8, 128, 256) == EDEVICE
+        assert call(8, 128, 256, fmt=2) == EDEVICE
         assert call(8, 128, 1024, variant=2, ws=buf.at(32768), wsb=1 << 15) == EDEVICE
     # epilogues that need an operand reject its absence
     assert L.lowbit_gemm_bias_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1, None, 0,
@@ -233,6 +237,29 @@ def test_gemm_argument_order(buf):
     # FP4 out: N must be a multiple of the NVFP4 block
     assert L.lowbit_gemm_bias_gelu_fp4(a, b, sa, sb, 8, 120, 256, 1, 0, 0, 1.0, buf.at(20480), None,
                                        buf.at(24576), buf.at(28672), 0, -1, None, 0, None) == ESHAPE
+
+
+def test_gemm_fp8_argument_order(buf):
+    L = lb.lib()
+    a, b, sa, sb = buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288)
+
+    def call(M=8, N=128, K=256, fmt=2, ol=0, p=16384, sf=True, variant=-1):
+        return L.lowbit_gemm_fp8(a, b, sa, sb, M, N, K, fmt, 0, 0, 1.0, buf.at(p),
+                                 buf.at(20480) if sf else None, ol, variant, None, 0, None)
+
+    assert call(ol=1) == EINVAL                       # output scales: LINEAR or the 128 x 4 swizzle
+    assert call(ol=3) == EINVAL
+    assert call(sf=False) == EINVAL
+    assert call(fmt=3) == EINVAL
+    assert call(N=112) == ESHAPE                      # N % 32
+    assert call(K=48) == ESHAPE
+    assert call(variant=2) == EINVAL                  # split-K without its workspace
+    assert call(p=16392) == EALIGN                    # packed output 16-byte aligned
+    assert call(M=0) == OK
+    if NO_DEVICE:
+        for fmt in (0, 1, 2):
+            for ol in (0, 2):
+                assert call(fmt=fmt, ol=ol) == EDEVICE
 
 
 def test_rope_quant_argument_order(buf):
