@@ -329,8 +329,8 @@ def build_variant_stages():
     def producer_both():
         x, r, w = bsets[itb["i"] % 4]
         itb["i"] += 1
-        lb.lowbit_add_rmsnorm_quant_both_sf(x, r, w, EPS, lb.NVFP4, global_scale=gs, out_packed=pkb,
-                                            out_sf_tiled=sft, out_sf_linear=sfl)
+        lb.lowbit_add_rmsnorm_quant_both_sf(x, r, w, EPS, lb.NVFP4, lb.TILED, global_scale=gs, out_packed=pkb,
+                                            out_sf=sft, out_sf_linear=sfl)
 
     stages.append(graphed(Stage(f"add_rmsnorm_nvfp4_both_sf_{M}x{H}", producer_both, "hbm",
                                 producer_bytes(M, H, 16) + M * H // 16, "B", HBM_PEAK)))

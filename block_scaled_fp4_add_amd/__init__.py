@@ -65,7 +65,7 @@ def lib():
         L.lowbit_add_rmsnorm_quant_fp16.argtypes = L.lowbit_add_rmsnorm_quant.argtypes
         for name in ("lowbit_add_rmsnorm_quant_both_sf", "lowbit_add_rmsnorm_quant_both_sf_fp16"):
             getattr(L, name).restype = _int
-            getattr(L, name).argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _int, _vp, _vp, _vp, _vp, _vp]
+            getattr(L, name).argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _vp, _vp, _vp, _vp]
         L.lowbit_quantize_fp16.restype = _int
         L.lowbit_quantize_fp16.argtypes = L.lowbit_quantize.argtypes
         L.lowbit_rope_quant.restype = _int
@@ -201,11 +201,13 @@ def lowbit_add_rmsnorm_quant_fp16(input, residual, weight, eps=1e-6, fmt=NVFP4, 
                                     out_sf, stream)
 
 
-def lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps=1e-6, fmt=NVFP4, global_scale=None,
-                                     out_packed=None, out_sf_tiled=None, out_sf_linear=None, stream=None):
-    """The producer with its scales in both layouts, one pass: bf16 tensors
-    call lowbit_add_rmsnorm_quant_both_sf, fp16 ones the _fp16 entry point.
-    Returns (packed uint8, TILED scales uint8, LINEAR scales uint8)."""
+def lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps=1e-6, fmt=NVFP4, layout=TILED,
+                                     global_scale=None, out_packed=None, out_sf=None, out_sf_linear=None,
+                                     stream=None):
+    """The producer with its scales in two layouts, one pass: `layout`
+    (TILED or SWZ128) and a LINEAR copy.  bf16 tensors call
+    lowbit_add_rmsnorm_quant_both_sf, fp16 ones the _fp16 entry point.
+    Returns (packed uint8, scales in `layout` uint8, LINEAR scales uint8)."""
     dt = _in_dtype(input, "input")
     _need(input, dt, "input")
     _need(residual, dt, "residual")
@@ -218,25 +220,26 @@ def lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps=1e-6, fmt=NVFP
     lead, M, H = _rows_of(input)
     if weight.numel() != H:
         raise ValueError(f"weight has {weight.numel()} elements, the rows have {H}")
-    out_packed, out_sf_tiled = _alloc_q(M, H, fmt, TILED, input.device, out_packed, out_sf_tiled, lead)
+    out_packed, out_sf = _alloc_q(M, H, fmt, layout, input.device, out_packed, out_sf, lead)
     if out_sf_linear is None:
         out_sf_linear = torch.empty(lowbit_sf_bytes(M, H, fmt, LINEAR), dtype=torch.uint8, device=input.device)
-    _check_q_out(out_packed, out_sf_tiled, M, H, fmt, TILED)
+    _check_q_out(out_packed, out_sf, M, H, fmt, layout)
     _need(out_sf_linear, torch.uint8, "out_sf_linear")
     _at_least(out_sf_linear, lowbit_sf_bytes(M, H, fmt, LINEAR), "out_sf_linear")
     name = "lowbit_add_rmsnorm_quant_both_sf" + ("" if dt == torch.bfloat16 else "_fp16")
     _check(name, getattr(lib(), name)(
-        _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, _ptr(global_scale),
-        _ptr(out_packed), _ptr(out_sf_tiled), _ptr(out_sf_linear), _stream(stream)))
-    return out_packed, out_sf_tiled, out_sf_linear
+        _ptr(input), _ptr(residual), _ptr(weight), M, H, eps, fmt, layout, _ptr(global_scale),
+        _ptr(out_packed), _ptr(out_sf), _ptr(out_sf_linear), _stream(stream)))
+    return out_packed, out_sf, out_sf_linear
 
 
-def lowbit_add_rmsnorm_quant_both_sf_fp16(input, residual, weight, eps=1e-6, fmt=NVFP4, global_scale=None,
-                                          out_packed=None, out_sf_tiled=None, out_sf_linear=None, stream=None):
+def lowbit_add_rmsnorm_quant_both_sf_fp16(input, residual, weight, eps=1e-6, fmt=NVFP4, layout=TILED,
+                                          global_scale=None, out_packed=None, out_sf=None, out_sf_linear=None,
+                                          stream=None):
     """The fp16 form by name (lowbit_add_rmsnorm_quant_both_sf dispatches on dtype)."""
     _need(input, torch.float16, "input")
-    return lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps, fmt, global_scale, out_packed,
-                                            out_sf_tiled, out_sf_linear, stream)
+    return lowbit_add_rmsnorm_quant_both_sf(input, residual, weight, eps, fmt, layout, global_scale, out_packed,
+                                            out_sf, out_sf_linear, stream)
 
 
 def lowbit_quantize(x, fmt=NVFP4, layout=LINEAR, global_scale=None, out_packed=None, out_sf=None,

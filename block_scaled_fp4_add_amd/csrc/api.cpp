@@ -205,7 +205,9 @@ static lowbit_status producer(const void* input, void* residual, const void* wei
                               hipStream_t stream) {
   if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
   if (!takes_gs(fmt) && global_scale) return LOWBIT_EINVAL;
-  if (out_sf_lin && layout != LOWBIT_SF_TILED) return LOWBIT_EINVAL;
+  // the second copy of the scales sits beside a padded layout of an FP4 format
+  if (out_sf_lin && (!fp4_fmt(fmt) || (layout != LOWBIT_SF_TILED && layout != LOWBIT_SF_SWZ128)))
+    return LOWBIT_EINVAL;
   if (M < 0) return LOWBIT_ESHAPE;
   if (M > 0 && (!input || !residual || !weight || !out_packed || !out_sf)) return LOWBIT_EINVAL;
   if (H < 64 || H % block_of(fmt) != 0 || H > kMaxRowElems) return LOWBIT_ESHAPE;
@@ -276,22 +278,22 @@ lowbit_status lowbit_add_rmsnorm_quant_fp16(const void* input, void* residual, c
 }
 
 lowbit_status lowbit_add_rmsnorm_quant_both_sf(const void* input, void* residual, const void* weight, int64_t M,
-                                               int64_t H, float eps, lowbit_format fmt, const float* global_scale,
-                                               uint8_t* out_packed, uint8_t* out_sf_tiled, uint8_t* out_sf_linear,
-                                               hipStream_t stream) {
+                                               int64_t H, float eps, lowbit_format fmt, lowbit_sf_layout layout,
+                                               const float* global_scale, uint8_t* out_packed, uint8_t* out_sf,
+                                               uint8_t* out_sf_linear, hipStream_t stream) {
   if (M > 0 && !out_sf_linear) return LOWBIT_EINVAL;
-  return producer(input, residual, weight, M, H, eps, fmt, LOWBIT_SF_TILED, global_scale, out_packed,
-                  out_sf_tiled, out_sf_linear, 0, stream);
+  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf,
+                  out_sf_linear, 0, stream);
 }
 
 lowbit_status lowbit_add_rmsnorm_quant_both_sf_fp16(const void* input, void* residual, const void* weight,
                                                     int64_t M, int64_t H, float eps, lowbit_format fmt,
-                                                    const float* global_scale, uint8_t* out_packed,
-                                                    uint8_t* out_sf_tiled, uint8_t* out_sf_linear,
+                                                    lowbit_sf_layout layout, const float* global_scale,
+                                                    uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_linear,
                                                     hipStream_t stream) {
   if (M > 0 && !out_sf_linear) return LOWBIT_EINVAL;
-  return producer(input, residual, weight, M, H, eps, fmt, LOWBIT_SF_TILED, global_scale, out_packed,
-                  out_sf_tiled, out_sf_linear, 1, stream);
+  return producer(input, residual, weight, M, H, eps, fmt, layout, global_scale, out_packed, out_sf,
+                  out_sf_linear, 1, stream);
 }
 
 lowbit_status lowbit_quantize(const void* x, int64_t rows, int64_t K, lowbit_format fmt,

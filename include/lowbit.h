@@ -147,27 +147,28 @@ lowbit_status lowbit_add_rmsnorm_quant_fp16(const void* input, void* residual, c
                                             lowbit_sf_layout layout, const float* global_scale,
                                             uint8_t* out_packed, uint8_t* out_sf, hipStream_t stream);
 
-/* The fused producer writing its block scales in both layouts in one pass
- * ([FI] AddRMSNormFP4QuantKernel's option to emit the swizzled scale tensor
- * and an unswizzled copy together; the swizzled one is LOWBIT_SF_TILED here).
- * Same arithmetic, checks and outputs as lowbit_add_rmsnorm_quant with layout
- * LOWBIT_SF_TILED into out_sf_tiled (lowbit_sf_bytes(M, H, fmt, TILED) bytes,
- * padding bytes zero), and the same scale bytes row-major into out_sf_linear
- * (lowbit_sf_bytes(M, H, fmt, LINEAR) bytes).  NVFP4 and MXFP4 only (MXFP8
- * has no TILED layout: EINVAL); out_sf_linear NULL with M > 0: EINVAL.  The
- * two scale buffers must not overlap each other or the other outputs. */
+/* The fused producer writing its block scales in two layouts in one pass
+ * ([FI] AddRMSNormFP4QuantKernel's option to emit the 128 x 4 swizzled scale
+ * tensor and an unswizzled copy together).  Same arithmetic, checks and
+ * outputs as lowbit_add_rmsnorm_quant with layout `layout` (LOWBIT_SF_TILED,
+ * the GEMM's own layout, or LOWBIT_SF_SWZ128, the page's) into out_sf
+ * (lowbit_sf_bytes(M, H, fmt, layout) bytes, padding bytes zero), and the
+ * same scale bytes row-major into out_sf_linear (lowbit_sf_bytes(M, H, fmt,
+ * LOWBIT_SF_LINEAR) bytes).  NVFP4 and MXFP4 only (EINVAL otherwise, and for
+ * layout LOWBIT_SF_LINEAR); out_sf_linear NULL with M > 0: EINVAL.  The two
+ * scale buffers must not overlap each other or the other outputs. */
 lowbit_status lowbit_add_rmsnorm_quant_both_sf(const void* input, void* residual, const void* weight,
                                                int64_t M, int64_t H, float eps, lowbit_format fmt,
-                                               const float* global_scale, uint8_t* out_packed,
-                                               uint8_t* out_sf_tiled, uint8_t* out_sf_linear,
+                                               lowbit_sf_layout layout, const float* global_scale,
+                                               uint8_t* out_packed, uint8_t* out_sf, uint8_t* out_sf_linear,
                                                hipStream_t stream);
 
 /* The same with fp16 input, residual and weight, as lowbit_add_rmsnorm_quant_fp16. */
 lowbit_status lowbit_add_rmsnorm_quant_both_sf_fp16(const void* input, void* residual, const void* weight,
                                                     int64_t M, int64_t H, float eps, lowbit_format fmt,
-                                                    const float* global_scale, uint8_t* out_packed,
-                                                    uint8_t* out_sf_tiled, uint8_t* out_sf_linear,
-                                                    hipStream_t stream);
+                                                    lowbit_sf_layout layout, const float* global_scale,
+                                                    uint8_t* out_packed, uint8_t* out_sf,
+                                                    uint8_t* out_sf_linear, hipStream_t stream);
 
 /* Quantize a bf16 (rows, K) tensor: the per-block rule above with y = x
  * ([FRT] quantize_fp4_sfa_bf16; used for activations and prepacked weights).

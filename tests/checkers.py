@@ -54,11 +54,20 @@ def tiled_in_group(fmt, r, j):
     return (((j // 2) % 2) * 32 + r % 32) * 4 + (j % 2) + 2 * (j // 4)
 
 
+def swz_offsets(orc, rows, nblk, fmt):
+    """Byte offsets of the (rows, nblk) scales in the 128 x 4 swizzle, from
+    the oracle's layout function."""
+    return np.array([[orc.sf_offset(m, kb, nblk, fmt, orc.SWZ128) for kb in range(nblk)] for m in range(rows)],
+                    dtype=np.int64).reshape(rows, nblk)
+
+
 def gather_scales(orc, sf, rows, nblk, fmt, layout):
-    """(rows, nblk) scale bytes from a buffer in either layout."""
+    """(rows, nblk) scale bytes from a buffer in any layout."""
     sf = np.asarray(sf, dtype=np.uint8)
     if layout == orc.LINEAR:
         return sf[: rows * nblk].reshape(rows, nblk)
+    if layout == orc.SWZ128:
+        return sf[swz_offsets(orc, rows, nblk, fmt)]
     r = np.arange(rows)[:, None]
     kb = np.arange(nblk)[None, :]
     ktiles = (nblk + 7) // 8
@@ -76,6 +85,13 @@ def tiled_padding_is_zero(orc, sf, rows, nblk, fmt):
     j = kb % 8
     off = ((r // 32) * ktiles + kb // 8) * 256 + tiled_in_group(fmt, r, j)
     used[off.ravel()] = True
+    return not np.any(sf[~used])
+
+
+def swz_padding_is_zero(orc, sf, rows, nblk, fmt):
+    sf = np.asarray(sf, dtype=np.uint8)
+    used = np.zeros(sf.size, bool)
+    used[swz_offsets(orc, rows, nblk, fmt).ravel()] = True
     return not np.any(sf[~used])
 
 
@@ -192,8 +208,8 @@ def mx8_scale_byte(amax):
 
 def gather_mx8_scales(orc, sf, rows, nblk, layout):
     sf = np.asarray(sf, dtype=np.uint8)
-    off = np.array([[orc.sf_offset(m, kb, nblk, orc.MXFP8, layout) for kb in range(nblk)] for m in range(rows)],
-                   dtype=np.int64).reshape(rows, nblk)
+    off = (np.arange(rows * nblk, dtype=np.int64).reshape(rows, nblk) if layout == orc.LINEAR
+           else swz_offsets(orc, rows, nblk, orc.MXFP8))
     return sf[off], off
 
 

@@ -179,13 +179,16 @@ def test_producer_argument_order(buf):
 def test_producer_both_sf_argument_order(buf):
     L = lb.lib()
 
-    def call(M, H, fmt=1, gs=None, lin=True, x=0, fp16=False):
+    def call(M, H, fmt=1, gs=None, lin=True, x=0, fp16=False, layout=1):
         fn = L.lowbit_add_rmsnorm_quant_both_sf_fp16 if fp16 else L.lowbit_add_rmsnorm_quant_both_sf
-        return fn(buf.at(x), buf.at(), buf.at(), M, H, 1e-6, fmt, gs, buf.at(), buf.at(),
+        return fn(buf.at(x), buf.at(), buf.at(), M, H, 1e-6, fmt, layout, gs, buf.at(), buf.at(),
                   buf.at() if lin else None, None)
 
     for fp16 in (False, True):
         assert call(4, 256, fmt=2, fp16=fp16) == EINVAL            # MXFP8: no TILED layout
+        assert call(4, 256, fmt=2, layout=2, fp16=fp16) == EINVAL  # nor a second copy beside LINEAR scales
+        assert call(4, 256, layout=0, fp16=fp16) == EINVAL         # the first layout must be a padded one
+        assert call(4, 256, layout=3, fp16=fp16) == EINVAL
         assert call(4, 256, fmt=7, fp16=fp16) == EINVAL
         assert call(4, 256, fmt=3, fp16=fp16) == EINVAL            # 32-block NVFP4: no TILED layout
         assert call(4, 256, fmt=1, gs=buf.at(), fp16=fp16) == EINVAL
@@ -196,6 +199,7 @@ def test_producer_both_sf_argument_order(buf):
         if NO_DEVICE:
             assert call(4, 256, fp16=fp16) == EDEVICE
             assert call(4, 256, fmt=0, gs=buf.at(), fp16=fp16) == EDEVICE
+            assert call(4, 256, fmt=0, gs=buf.at(), layout=2, fp16=fp16) == EDEVICE
 
 
 def test_gemm_argument_order(buf):

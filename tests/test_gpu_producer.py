@@ -176,6 +176,28 @@ def test_quantize_fp16_bit_exact(orc, rows, K, fmt, layout):
     assert np.array_equal(host_u8(s), ref_s)
 
 
+@pytest.mark.parametrize("rows", [1, 41, 128])
+@pytest.mark.parametrize("K", [5120, 6144, 17408])
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1, 2])
+def test_bf16_entry_matches_the_fp16_chain(rows, K, fmt, layout):
+    """The FlashRT README's validation gate at the decode widths: quantizing a
+    bf16 tensor directly gives, byte for byte, what converting it to fp16 and
+    quantizing that gives.  Values below fp16's normal range (|x| < 2^-14),
+    which the conversion would round, are set to zero first, so the two
+    inputs hold the same numbers."""
+    banner(f"bf16 entry vs fp16 chain rows={rows} K={K} fmt={fmt} layout={layout}")
+    x = synth.activation(rows, K, seed=rows * 7 + K, outliers=True)
+    x = torch.where(x.float().abs() < 2.0 ** -14, torch.zeros_like(x), x)
+    x16 = x.half()
+    assert torch.equal(x16.float(), x.float())
+    gs = dev_f32(5.5) if fmt == 0 else None
+    p, s = lb.lowbit_quantize(dev_bf16(x), fmt, layout, global_scale=gs)
+    p16, s16 = lb.lowbit_quantize_fp16(dev_bf16(x16), fmt, layout, global_scale=gs)
+    torch.cuda.synchronize()
+    assert torch.equal(p, p16) and torch.equal(s, s16)
+
+
 def test_quantize_hand_blocks(orc):
     with open(os.path.join(GOLDEN, "hand_blocks.json")) as f:
         blocks = json.load(f)["blocks"]
