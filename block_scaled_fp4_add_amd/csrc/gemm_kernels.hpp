@@ -1459,6 +1459,8 @@ __global__ __launch_bounds__(64) void gemm_splitk_reduce_kernel(GemmArgs g, int 
     fp8_out_padding(g, i * 32, (i + 1 == MT) ? 128 : i * 32 + 32, n0 / 32, n0 / 32 + 1, n0 + 32 >= g.N, lane, 64);
 }
 
+#include "gemm_nv.hpp"
+
 template <int FMT, int EPI>
 void launch_w(const GemmArgs& g, dim3 block, hipStream_t s) {
   constexpr int BN = PrefillTileN<FMT>::kCols;
@@ -1542,7 +1544,9 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
     auto dword_ok = [&](const uint8_t* p, int lay) {
       return lay == kTiled || (nblk % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3) == 0);
     };
-    if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
+    if (FMT == kNVFP4 && prefill_nv_ok(g)) {
+      launch_prefill_nv<EPI>(g, s);
+    } else if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
       const dim3 grid((unsigned)T), block(kPThreads);
       launch_w<FMT, EPI>(g, block, s);
     } else

@@ -101,6 +101,25 @@ def test_gemm_layouts(orc, la, lb_, fmt):
     run_gemm(orc, 20, 96, 544, fmt, la, lb_, 0, -1, seed=la * 2 + lb_ + 7)
 
 
+# NVFP4 prefill with K % 64 == 0 runs the 128 x 384 schedule that converts the
+# activation fragments once per workgroup: full and half final stages
+# (K % 128 == 0 and 64), M and N off the tile sizes, every scale layout pair,
+# more than one tile in each direction
+NV_PREFILL_SHAPES = [(129, 400, 512), (300, 1000, 576), (257, 770, 1088), (128, 384, 128), (5, 48, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", NV_PREFILL_SHAPES)
+@pytest.mark.parametrize("la,lb_", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_nvfp4_prefill_schedule(orc, M, N, K, la, lb_):
+    assert K % 64 == 0
+    run_gemm(orc, M, N, K, 0, la, lb_, 0, 1, seed=M + N + K + 3 * la + lb_, alpha=0.5, outliers=True)
+
+
+@pytest.mark.parametrize("epi", [1, 2, 3, 4])
+def test_gemm_nvfp4_prefill_schedule_epilogues(orc, epi):
+    run_gemm(orc, 200, 800, 576, 0, 0, 1, epi, 1, seed=epi + 40, outliers=True)
+
+
 def test_gemm_tiny_mxfp4_workload(orc):
     c = synth.TINY_MXFP4
     run_gemm(orc, c["M"], c["N"], c["H"], orc.MXFP4, 0, 0, 0, -1, seed=c["seed"])
