@@ -192,6 +192,7 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
     g.ws = static_cast<float*>(workspace);
     g.splits = plan.splits;
     g.per = plan.per;
+    g.split_nv = plan.nv ? 1 : 0;
   }
   if (getenv("LOWBIT_LOG"))
     fprintf(stderr, "[lowbit] gemm M=%lld N=%lld K=%lld fmt=%d epi=%d variant=%d\n", (long long)M,

@@ -45,13 +45,30 @@ hipError_t launch_fmt(const GemmArgs& g, int variant, hipStream_t s) {
 // 13.7 -> 10.7 us split; (41, 4608, 1536) 6.8 -> 9.4 us, so not split).
 constexpr int64_t kSplitTargetWorkgroups = 512;
 constexpr int64_t kSplitMinSupersteps = 16;
+// the NVFP4 128 x 384 split: one workgroup a CU (256 CUs)
+constexpr int64_t kSplitNvWorkgroups = 256;
 
 SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force) {
   const int64_t ss = fmt == kMXFP8 ? 128 : 256;   // K elements of a superstep
   const int64_t nss = (K + ss - 1) / ss;
-  SplitPlan none{1, (int)nss, 0};
+  SplitPlan none{1, (int)nss, 0, false};
   if (M <= 0 || M > 128 || N <= 0 || K <= 0) return none;
   const int64_t tiles = (N + 31) / 32, mt = (M + 31) / 32;
+  if (fmt == kNVFP4 && M > 64 && K % 64 == 0) {
+    // NVFP4 with 3-4 M-tiles: the decode schedule converts every activation
+    // fragment in every workgroup (1.25 fragments per MFMA); the 128 x 384
+    // schedule converts 1/3 of one.  About one workgroup per CU along K.
+    const int64_t nst = (K + 127) / 128, tiles_nv = (N + 383) / 384;
+    int64_t S = kSplitNvWorkgroups / tiles_nv;
+    if (S > nst / 2) S = nst / 2;
+    if (!force && nst < 2 * kSplitMinSupersteps) S = 1;
+    if (force && S < 2 && nst >= 2) S = 2;
+    if (S > 1) {
+      const int64_t per = (nst + S - 1) / S;
+      S = (nst + per - 1) / per;
+      if (S > 1) return SplitPlan{(int)S, (int)per, (size_t)(S * tiles * mt * 1024 * 4), true};
+    }
+  }
   int64_t S = (kSplitTargetWorkgroups + tiles - 1) / tiles;
   if (S > nss / 4) S = nss / 4;
   if (!force && nss < kSplitMinSupersteps) S = 1;
@@ -59,7 +76,7 @@ SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force)
   if (S <= 1) return none;
   const int64_t per = (nss + S - 1) / S;
   S = (nss + per - 1) / per;
-  return SplitPlan{(int)S, (int)per, (size_t)(S * tiles * mt * 1024 * 4)};
+  return SplitPlan{(int)S, (int)per, (size_t)(S * tiles * mt * 1024 * 4), false};
 }
 
 int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, size_t ws_bytes) {

@@ -1578,6 +1578,17 @@ hipError_t launch_splitk_mt(const GemmArgs& g, hipStream_t s) {
 template <int FMT, int EPI>
 hipError_t launch_splitk(const GemmArgs& g, hipStream_t s) {
   const int mt = (int)((g.M + 31) / 32);
+  if constexpr (FMT == kNVFP4) {
+    if (g.split_nv) {   // partials from the 128 x 384 schedule, same reduce
+      if (!prefill_nv_ok(g) || mt > 4) return hipErrorInvalidValue;
+      launch_prefill_nv<kEpiNone, true>(g, s);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((gemm_splitk_reduce_kernel<EPI>), dim3((unsigned)((g.N + 31) / 32), (unsigned)mt),
+                         dim3(64), 0, s, g, mt);
+      return hipGetLastError();
+    }
+  }
   const bool half = FMT == kNVFP4 && (g.K / 2) % 16 != 0;
 #define LB_SPLIT(MT)                                                                        \
   if (mt == MT)                                                                             \

@@ -70,7 +70,13 @@ __device__ __forceinline__ NvPart nv_part_word(uint32_t word) {
   return NvPart{__uint_as_float(u & 0x7F800000u), v2h{h, h}};
 }
 
-template <int EPI, bool LA_TILED, bool LB_TILED>
+// SPLIT: split-K -- workgroup (tile, y) takes stages [y * g.per, (y + 1) * g.per)
+// of K and writes its fp32 partial 32 x 32 tiles to the workspace in the
+// decode schedule's partial layout (lane (r, c) holds output row r and
+// columns 8(k / 4) + 4c + k % 4, 16 floats a lane, tile (y, n / 32, m / 32) at
+// ((y * ceil(N / 32) + n / 32) * ceil(M / 32) + m / 32) * 1024 floats), which
+// gemm_splitk_reduce_kernel sums in split order before the epilogue.
+template <int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   constexpr int TI = kNvTI, TJ = kNvTJ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kNvLds];
@@ -96,7 +102,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   const int kbytes = (int)(g.K / 2);
   const int nblk = (int)(g.K / 16);
   const int ktiles = (nblk + 7) >> 3;
-  const int nst = (int)((g.K + 127) / 128);
+  const int nst_all = (int)((g.K + 127) / 128);
+  const int s0 = SPLIT ? (int)blockIdx.y * g.per : 0;                        // this workgroup's stages
+  const int nst = SPLIT ? min(g.per, nst_all - s0) : nst_all;                  // (count)
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, M * kbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, N * kbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rssa = __builtin_amdgcn_make_buffer_rsrc(
@@ -197,9 +205,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   // prologue: stages 0 and 1 in flight; stage 0's A fragment converted and
   // published; step 0 of stage 0 ready in registers
 #pragma unroll
-  for (int p = 0; p < 4; p++) issue(0, p, B0, A0);
+  for (int p = 0; p < 4; p++) issue(s0, p, B0, A0);
 #pragma unroll
-  for (int p = 0; p < 4; p++) issue(1, p, B1, A1);
+  for (int p = 0; p < 4; p++) issue(s0 + 1, p, B1, A1);
 #pragma unroll
   for (int t = 0; t < kNvSteps; t++) unit(A0, t, smem);
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -207,11 +215,13 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   read_a(va, smem, 0);
   conv_b(vb, B0, 0);
 
-  // stage s from register sets (bc: stage s, bn: stage s + 1, bf: the load
-  // target for stage s + 2; an: A of stage s + 1, af: A load target)
-  auto stage = [&](int s, const NvB& bc, const NvB& bn, NvB& bf, const NvA& an, NvA& af) {
-    uint8_t* cur = smem + (s & 1) * kNvStageLds;
-    uint8_t* nxt = smem + ((s & 1) ^ 1) * kNvStageLds;
+  // the workgroup's stage ls (K stage s0 + ls) from register sets (bc: that
+  // stage, bn: the next, bf: the load target two ahead; an: A of the next
+  // stage, af: A load target); LDS buffer ls % 2 holds its converted A
+  auto stage = [&](int ls, const NvB& bc, const NvB& bn, NvB& bf, const NvA& an, NvA& af) {
+    const int s = s0 + ls;
+    uint8_t* cur = smem + (ls & 1) * kNvStageLds;
+    uint8_t* nxt = smem + ((ls & 1) ^ 1) * kNvStageLds;
 #pragma unroll
     for (int st = 0; st < kNvSteps - 1; st++) {
       __builtin_amdgcn_sched_barrier(0);
@@ -244,22 +254,54 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TJ; j++) vb[j] = nb[j];
   };
-  int s = 0;
-  for (; s + 3 <= nst; s += 3) {
-    stage(s, B0, B1, B2, A1, A2);
-    stage(s + 1, B1, B2, B0, A2, A0);
-    stage(s + 2, B2, B0, B1, A0, A1);
+  int ls = 0;
+  for (; ls + 3 <= nst; ls += 3) {
+    stage(ls, B0, B1, B2, A1, A2);
+    stage(ls + 1, B1, B2, B0, A2, A0);
+    stage(ls + 2, B2, B0, B1, A0, A1);
   }
-  if (s < nst) stage(s, B0, B1, B2, A1, A2);
-  if (s + 1 < nst) stage(s + 1, B1, B2, B0, A2, A0);
+  if (ls < nst) stage(ls, B0, B1, B2, A1, A2);
+  if (ls + 1 < nst) stage(ls + 1, B1, B2, B0, A2, A0);
   // the loads issued past the end land before the epilogue reuses LDS
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
   __syncthreads();
 
-  epi_wave<EPI, TI, TJ>(acc, reinterpret_cast<float*>(smem) + wave * 32 * kEpiRowPitch, m0,
-                        n0 + wave * TJ * 32, g, lane);
-  if constexpr (EPI == kEpiBiasGeluFp4)
-    fp4_out_padding(g, m0, m0 + kNvBM, n0 / 16, (n0 + kNvBN) / 16, n0 + kNvBN >= g.N, tid, 256);
+  float* const et = reinterpret_cast<float*>(smem) + wave * 32 * kEpiRowPitch;
+  if constexpr (SPLIT) {
+    // each row block through LDS, read back transposed into the partial layout
+    const int64_t tiles32 = (g.N + 31) / 32, mt = (g.M + 31) / 32;
+    auto fence = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+      if (m0 / 32 + i >= mt) break;   // uniform: M-tiles past M hold no rows
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+#pragma unroll
+        for (int k = 0; k < 16; k++)
+          et[((k >> 2) * 8 + c * 4 + (k & 3)) * kEpiRowPitch + j * 32 + r] = acc[i][j][k];
+      fence();
+#pragma unroll
+      for (int j = 0; j < TJ; j++) {
+        const int64_t t32 = (n0 + wave * TJ * 32 + j * 32) / 32;
+        if (t32 < tiles32) {
+          float4* dst = reinterpret_cast<float4*>(
+              g.ws + (((int64_t)blockIdx.y * tiles32 + t32) * mt + m0 / 32 + i) * 1024 + lane * 16);
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            dst[q] = *reinterpret_cast<const float4*>(et + r * kEpiRowPitch + j * 32 + q * 8 + c * 4);
+        }
+      }
+      fence();
+    }
+  } else {
+    epi_wave<EPI, TI, TJ>(acc, et, m0, n0 + wave * TJ * 32, g, lane);
+    if constexpr (EPI == kEpiBiasGeluFp4)
+      fp4_out_padding(g, m0, m0 + kNvBM, n0 / 16, (n0 + kNvBN) / 16, n0 + kNvBN >= g.N, tid, 256);
+  }
 }
 
 // The schedule's conditions: NVFP4, K % 64 == 0 (whole scale words), LINEAR
@@ -271,16 +313,18 @@ inline bool prefill_nv_ok(const GemmArgs& g) {
   return g.K % 64 == 0 && word_ok(g.sfa, g.la) && word_ok(g.sfb, g.lb);
 }
 
-template <int EPI>
+template <int EPI, bool SPLIT = false>
 void launch_prefill_nv(const GemmArgs& g, hipStream_t s) {
-  const dim3 grid((unsigned)(((g.M + kNvBM - 1) / kNvBM) * ((g.N + kNvBN - 1) / kNvBN))), block(256);
+  const dim3 grid((unsigned)(((g.M + kNvBM - 1) / kNvBM) * ((g.N + kNvBN - 1) / kNvBN)),
+                  SPLIT ? (unsigned)g.splits : 1u),
+      block(256);
   if (g.la == kTiled && g.lb == kTiled)
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, true, true>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, true, true, SPLIT>), grid, block, 0, s, g);
   else if (g.la == kTiled)
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, true, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, true, false, SPLIT>), grid, block, 0, s, g);
   else if (g.lb == kTiled)
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, false, true>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, false, true, SPLIT>), grid, block, 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, false, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, false, false, SPLIT>), grid, block, 0, s, g);
 }
 

@@ -51,20 +51,26 @@ struct GemmArgs {
   uint8_t* out_sf;            // FP4 / FP8 output scales
   int out_layout;
   float* ws;                  // split-K: fp32 partial tiles (device), else nullptr
-  int splits;                 // split-K: workgroups along K per 32-column tile
-  int per;                    // split-K: supersteps (256 elements of K) per split
+  int splits;                 // split-K: workgroups along K per output tile
+  int per;                    // split-K: K units per split (supersteps, or NVFP4 stages: split_nv)
+  int split_nv;               // split-K on the NVFP4 128 x 384 schedule (units: 128-element stages)
 };
 
 // Schedules: 0 decode, 1 prefill, 2 split-K decode (needs a workspace).
 constexpr int kVariantSplitK = 2;
 
 // Split-K plan of a GEMM with M <= 128: `splits` workgroups along K per
-// 32-column tile (1: no split), `per` supersteps each, `bytes` of workspace
-// for the partials.  force: at least two splits whenever K has two supersteps.
+// output tile (1: no split), `per` K units each, `bytes` of workspace for the
+// partials.  force: at least two splits whenever K has two units.  nv: the
+// NVFP4 128 x 384 schedule does the partial pass (NVFP4, 64 < M <= 128,
+// K % 64 == 0; units of 128 elements), else the decode schedule (units of
+// one superstep).  Either way the partials are 32 x 32 fp32 tiles in one
+// layout, summed by the same reduce pass.
 struct SplitPlan {
   int splits;
   int per;
   size_t bytes;
+  bool nv;
 };
 SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force);
 

@@ -78,13 +78,26 @@ def test_pick_variant():
     assert L.lowbit_gemm_pick_variant(8, 128, 256, 1, 3, 0) < 0           # no such variant
 
 
-def splitk_plan(M, N, K):
-    """The split-K plan the library documents, written out: twice as many
-    workgroups as CUs, at least four supersteps (1024 elements) per split,
-    K of at least 16 supersteps, no empty split; bytes = splits x 32-column
-    tiles x M-tiles x 32 x 32 floats."""
-    nss = -(-K // 256)
+def splitk_plan(M, N, K, fmt=1):
+    """The split-K plan the library documents, written out.  NVFP4 with
+    64 < M <= 128 and K % 64 == 0 splits the 128 x 384 schedule: about one
+    workgroup per CU (256 over the 384-column tiles), at least two
+    128-element stages per split, K of at least 32 stages.  Otherwise the
+    decode schedule: twice as many workgroups as CUs, at least four
+    supersteps (1024 elements) per split, K of at least 16 supersteps.  No
+    empty split; bytes = splits x 32-column tiles x M-tiles x 32 x 32 floats."""
     tiles, mt = -(-N // 32), -(-M // 32)
+    if fmt == 0 and 64 < M <= 128 and K % 64 == 0:
+        nst = -(-K // 128)
+        S = min(256 // -(-N // 384), nst // 2)
+        if nst < 32:
+            S = 1
+        if S > 1:
+            per = -(-nst // S)
+            S = -(-nst // per)
+            if S > 1:
+                return S, S * tiles * mt * 1024 * 4
+    nss = -(-K // 256)
     S = min(-(-512 // tiles), nss // 4)
     if nss < 16:
         S = 1
@@ -95,12 +108,20 @@ def splitk_plan(M, N, K):
     return S, S * tiles * mt * 1024 * 4
 
 
+def test_splitk_nvfp4_chain_plans():
+    """The chain's 128-token GEMMs split the NVFP4 128 x 384 schedule: 46
+    column tiles x 5 splits of 8 stages, and 14 x 17 splits of 8 stages."""
+    assert splitk_plan(128, 17408, 5120, 0)[0] == 5 and splitk_plan(128, 5120, 17408, 0)[0] == 17
+    assert lb.lib().lowbit_gemm_workspace_bytes(128, 17408, 5120, 0, -1) == 5 * 544 * 4 * 4096
+
+
 @pytest.mark.parametrize("M,N,K", [(41, 4608, 1536), (41, 6144, 1536), (41, 1536, 6144), (1, 17408, 5120),
-                                   (1, 5120, 17408), (128, 5120, 17408), (128, 17408, 5120), (5, 40, 512), (2, 64, 4096)])
+                                   (1, 5120, 17408), (128, 5120, 17408), (128, 17408, 5120), (5, 40, 512), (2, 64, 4096),
+                                   (100, 264, 1536), (65, 400, 4096), (97, 96, 2304)])
 def test_splitk_workspace_and_choice(M, N, K):
     L = lb.lib()
     for fmt in (0, 1):
-        S, need = splitk_plan(M, N, K)
+        S, need = splitk_plan(M, N, K, fmt)
         assert L.lowbit_gemm_workspace_bytes(M, N, K, fmt, -1) == need
         if need:
             assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, need) == 2       # offered enough: split
