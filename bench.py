@@ -35,6 +35,7 @@ from block_scaled_fp4_add_amd import synth  # noqa: E402
 HBM_PEAK = 8.0e12          # B/s, MI355X published
 FP4_PEAK = 10.1e15         # FLOP/s dense FP4/FP6 MFMA, published
 FP16_PEAK = 2.5e15         # FLOP/s dense fp16/bf16 MFMA, published
+FP8_PEAK = 5.0e15          # FLOP/s dense FP8 MFMA, published
 EPS = 1e-6
 COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -76,6 +77,40 @@ def rope_stage(name, T, heads, fmt, dev):
 
     return Stage(name, fn, "hbm", rope_bytes(T, heads, ROPE_D, ROPE_R, 1.0 if fmt == lb.MXFP8 else 0.5), "B",
                  HBM_PEAK)
+
+
+WOA_N = 1024   # output columns of the MXFP8 GEMM workloads (synthetic: the page gives no head geometry)
+
+
+def mxfp8_gemm_stage(name, M, N, K, dev, bound, workspace=None):
+    """MXFP8 operands (E4M3 elements, UE8M0 scales per 32) through the GEMM
+    with the FP8 output epilogue: bf16(A.B^T) quantized to MXFP8 along N,
+    scale bytes in the 128 x 4 layout.  The operands are dequantized exactly
+    to bf16 and contracted on bf16 MFMAs, so the executed peak is bf16's;
+    the roofline prices the format at the FP8 peak (MFMA-bound) or its bytes
+    at HBM (decode)."""
+    A = synth.activation(M, K, 79, outliers=True).to(dev)
+    a, sa = lb.lowbit_quantize(A, lb.MXFP8, lb.LINEAR)
+    # decode: one weight copy per launch of a graph replay, so that the
+    # last-level cache does not serve the weights
+    wsets = []
+    for i in range(DECODE_REPS if bound == "hbm" else 1):
+        W = synth.weight(N, K, 79 + i).to(dev)
+        wsets.append(lb.lowbit_quantize(W, lb.MXFP8, lb.LINEAR))
+    pk = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sf = torch.empty(lb.lowbit_sf_bytes(M, N, lb.MXFP8, lb.SWZ128), dtype=torch.uint8, device=dev)
+    it = {"i": 0}
+
+    def fn(a=a, sa=sa, pk=pk, sf=sf, wsets=wsets, it=it, ws=workspace):
+        b, sb = wsets[it["i"] % len(wsets)]
+        it["i"] += 1
+        lb.lowbit_gemm_fp8(a, b, sa, sb, fmt=lb.MXFP8, out_packed=pk, out_sf=sf, out_layout=lb.SWZ128,
+                           workspace=ws)
+
+    if bound == "mfma":
+        return Stage(name, fn, "mfma", 2.0 * M * N * K, "FLOP", FP8_PEAK, own_peak=FP16_PEAK, own_dtype="bf16")
+    nbytes = (M + N) * (K + K // 32) + M * N + M * N // 32
+    return Stage(name, fn, "hbm", nbytes, "B", HBM_PEAK)
 
 
 def gemm_bytes(M, N, K, B, epi_bias=False, epi_res=False, out_fp4=False):
@@ -337,6 +372,8 @@ def build_variant_stages():
     # inverse RoPE + MX quantization at a prefill size: 4096 tokens x 16 heads of 512
     stages.append(graphed(rope_stage("rope_quant_mxfp8_4096x16x512", 4096, 16, lb.MXFP8, dev)))
     stages.append(graphed(rope_stage("rope_quant_mxfp4_4096x16x512", 4096, 16, lb.MXFP4, dev)))
+    # the MXFP8 GEMM with FP8 output on the RoPE workload's rows: 4096 tokens x 16 heads of 512
+    stages.append(graphed(mxfp8_gemm_stage(f"mxfp8_gemm_fp8out_4096x{WOA_N}x8192", 4096, WOA_N, 8192, dev, "mfma")))
     return stages
 
 
@@ -398,6 +435,7 @@ def build_decode_stages():
     need += [lb.lowbit_gemm_workspace_bytes(M, N, K, lb.NVFP4, lb.VARIANT_AUTO)
              for M in (1, 128) for (N, K) in ((synth.NVFP4_CHAIN["N1"], synth.NVFP4_CHAIN["H"]),
                                               (synth.NVFP4_CHAIN["H"], synth.NVFP4_CHAIN["N1"]))]
+    need += [lb.lowbit_gemm_workspace_bytes(96, WOA_N, 8192, lb.MXFP8, lb.VARIANT_AUTO)]
     wspace = torch.empty(max(need + [16]), dtype=torch.uint8, device=dev)
     for (M, N, K) in c["shapes"]:
         A = synth.activation(M, K, c["seed"]).to(dev)
@@ -469,6 +507,8 @@ def build_decode_stages():
                                     "B", HBM_PEAK)))
     # inverse RoPE + MXFP8 at the page's decode size: 96 tokens x 16 heads of 512
     stages.append(graphed(rope_stage("rope_quant_mxfp8_96x16x512", 96, 16, lb.MXFP8, dev)))
+    stages.append(graphed(mxfp8_gemm_stage(f"mxfp8_gemm_fp8out_96x{WOA_N}x8192", 96, WOA_N, 8192, dev, "hbm",
+                                           workspace=wspace)))
     return stages
 
 
