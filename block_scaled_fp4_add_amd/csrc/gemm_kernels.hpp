@@ -608,7 +608,7 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
     }
     return;
   }
-  if ((g.N % 8) != 0) {
+  if (EPI == kEpiFp8 || (g.N % 8) != 0) {   // FP8 out and ragged N: tile by tile
     const int er = lane & 31, ec = (lane >> 5) * 16;
 #pragma unroll
     for (int i = 0; i < TI; i++)
@@ -622,7 +622,7 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
       }
     return;
   }
-  if constexpr (EPI != kEpiBiasGeluFp4) {
+  if constexpr (EPI != kEpiBiasGeluFp4 && EPI != kEpiFp8) {
     constexpr int kQ = 32 / 4;   // row groups of 4 per row block
     const int cl = (lane & 15) * 8, rl = lane >> 4;
     const int64_t n = nb + cl;
@@ -1534,9 +1534,17 @@ template <int FMT, int EPI>
 hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   if (variant == 0) return launch_decode_rows<FMT, EPI>(g, s);
   const int64_t T = ((g.M + kPBM - 1) / kPBM) * ((g.N + kPBN - 1) / kPBN);
-  // MXFP8 operands and the FP8 output run the 64-byte-stage prefill kernel;
-  // the 128-byte-stage one fetches LINEAR scales with dword DMA, which needs
-  // the blocks per row to be a multiple of 4 and a 4-byte aligned base
+  // NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) operands run the 128 x 384
+  // schedule (every epilogue); otherwise MXFP8 operands and the FP8 output
+  // run the 64-byte-stage prefill kernel; the 128-byte-stage one fetches
+  // LINEAR scales with dword DMA, which needs the blocks per row to be a
+  // multiple of 4 and a 4-byte aligned base
+  if constexpr (FMT == kNVFP4 || FMT == kMXFP8) {
+    if (prefill_nv_ok<FMT>(g)) {
+      launch_prefill_nv<FMT, EPI>(g, s);
+      return hipGetLastError();
+    }
+  }
   if constexpr (FMT == kMXFP8 || EPI == kEpiFp8) {
     hipLaunchKernelGGL((gemm_prefill_v2_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
   } else {
@@ -1544,9 +1552,7 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
     auto dword_ok = [&](const uint8_t* p, int lay) {
       return lay == kTiled || (nblk % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3) == 0);
     };
-    if (FMT == kNVFP4 && prefill_nv_ok(g)) {
-      launch_prefill_nv<EPI>(g, s);
-    } else if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
+    if (dword_ok(g.sfa, g.la) && dword_ok(g.sfb, g.lb)) {
       const dim3 grid((unsigned)T), block(kPThreads);
       launch_w<FMT, EPI>(g, block, s);
     } else
@@ -1580,8 +1586,8 @@ hipError_t launch_splitk(const GemmArgs& g, hipStream_t s) {
   const int mt = (int)((g.M + 31) / 32);
   if constexpr (FMT == kNVFP4) {
     if (g.split_nv) {   // partials from the 128 x 384 schedule, same reduce
-      if (!prefill_nv_ok(g) || mt > 4) return hipErrorInvalidValue;
-      launch_prefill_nv<kEpiNone, true>(g, s);
+      if (!prefill_nv_ok<kNVFP4>(g) || mt > 4) return hipErrorInvalidValue;
+      launch_prefill_nv<kNVFP4, kEpiNone, true>(g, s);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((gemm_splitk_reduce_kernel<EPI>), dim3((unsigned)((g.N + 31) / 32), (unsigned)mt),

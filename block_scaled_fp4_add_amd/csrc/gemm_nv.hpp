@@ -76,9 +76,21 @@ __device__ __forceinline__ NvPart nv_part_word(uint32_t word) {
 // columns 8(k / 4) + 4c + k % 4, 16 floats a lane, tile (y, n / 32, m / 32) at
 // ((y * ceil(N / 32) + n / 32) * ceil(M / 32) + m / 32) * 1024 floats), which
 // gemm_splitk_reduce_kernel sums in split order before the epilogue.
-template <int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false>
+//
+// MXFP8 (FMT == kMXFP8, LINEAR scales, K % 128 == 0) runs the same schedule:
+// a 64-byte row stage then holds 64 elements, 4 K16 steps (step t: the lane's
+// dwords 2t, 2t + 1), and lane half c covers exactly 32-element block
+// 2s + c, whose UE8M0 byte is byte 2(s % 2) + c of the row's scale word at
+// 4 * (s / 2).  The dequantization is E4M3 x 2^e -> bf16 (exact while that is
+// a normal bf16), with no mantissa multiply, into bf16 MFMAs.
+template <int FMT, int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   constexpr int TI = kNvTI, TJ = kNvTJ;
+  constexpr bool F8 = FMT == kMXFP8;
+  static_assert(FMT == kNVFP4 || FMT == kMXFP8, "NVFP4 or MXFP8 operands");
+  constexpr int kSteps = F8 ? 4 : kNvSteps;                 // K16 steps of a 64-byte row stage
+  constexpr int kStageLds = kSteps * TI * kNvUnit;           // converted A of one stage
+  using VT = typename std::conditional<F8, v8bf, v8h>::type;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kNvLds];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -99,10 +111,10 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   const int m0 = (int)(tm * kNvBM), n0 = (int)(tn * kNvBN);
 
   const int M = (int)g.M, N = (int)g.N;
-  const int kbytes = (int)(g.K / 2);
-  const int nblk = (int)(g.K / 16);
+  const int kbytes = (int)(F8 ? g.K : g.K / 2);             // packed bytes of a row
+  const int nblk = (int)(g.K / (F8 ? 32 : 16));
   const int ktiles = (nblk + 7) >> 3;
-  const int nst_all = (int)((g.K + 127) / 128);
+  const int nst_all = (kbytes + 63) / 64;                    // 64-byte row stages
   const int s0 = SPLIT ? (int)blockIdx.y * g.per : 0;                        // this workgroup's stages
   const int nst = SPLIT ? min(g.per, nst_all - s0) : nst_all;                  // (count)
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, M * kbytes, 0x00020000);
@@ -116,6 +128,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   // per-lane offsets; the stage advance goes into the scalar offset
   auto sf_base = [&](int row, int R, bool tiled) {
     if (row >= R) return kAbsent;
+    if (F8) return row * nblk;   // the word holding stages 2k and 2k + 1
     return tiled ? (((row >> 5) * ktiles) << 8) + ((c * 32 + (row & 31)) << 2) : row * nblk + 4 * c;
   };
   int ob[TJ], sb_[TJ];
@@ -137,14 +150,15 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   // turn half-rows beyond K into absent ones (zero bytes, zero scales).  The
   // choice is a select, not a branch: loads in one basic block keep the
   // compiler's waits on their registers exact.
-  const int nfull = (int)(g.K / 128);   // stages wholly inside K
+  const int nfull = kbytes / 64;   // stages wholly inside K
   auto issue = [&](int s, int p, NvB& b, NvA& a) {
     const bool fast = s < nfull;                       // uniform
     const int so = s * 64;
-    const int ssf = (p == 0 ? LA_TILED : LB_TILED) ? (s << 8) : (s << 3);
+    const int ssf = F8 ? 4 * (s >> 1) : ((p == 0 ? LA_TILED : LB_TILED) ? (s << 8) : (s << 3));
     const int sd = fast ? so : 0, ss = fast ? ssf : 0;   // scalar parts
     const int vd = fast ? 0 : so, vs = fast ? 0 : ssf;   // lane parts
-    const bool in = fast || so + 32 * c < kbytes;     // K % 64 == 0: a lane half is wholly in or out
+    // NVFP4 K % 64 == 0, MXFP8 K % 128 == 0: a lane half is wholly in or out
+    const bool in = fast || so + 32 * c < kbytes;
     auto voff = [&](int base, int add) { return in ? base + add : kAbsent; };
     if (p == 0) {
       a.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rsa, voff(oa, vd), sd, 0);
@@ -164,25 +178,39 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TJ; j++) acc[i][j] = v16f{};
 
-  // step t of this wave's A fragment, dequantized into LDS unit (t, w)
-  auto unit = [&](const NvA& a, int t, uint8_t* buf) {
-    const v8h v = dq8(a.q[t >> 2][t & 3], nv_part_word(a.s >> (8 * (t >> 1))));
-    *reinterpret_cast<v8h*>(buf + (t * TI + wave) * kNvUnit + lane * 16) = v;
+  // step t of a lane's 32 bytes, dequantized: NVFP4 dword t with the E4M3
+  // scale of block t / 2 (byte t / 2 of the word); MXFP8 dwords 2t, 2t + 1 with
+  // the UE8M0 scale of the lane's block (byte 2(s % 2) + c of the word)
+  auto deq = [&](const u32x4 (&q)[2], uint32_t sw, int t, int s) -> VT {
+    if constexpr (F8) {
+      const uint32_t b = (sw >> (8 * (2 * (s & 1) + c))) & 0xFFu;
+      return dq8_f8(q[t >> 1][2 * (t & 1)], q[t >> 1][2 * (t & 1) + 1], ue8m0_to_f32(b));
+    } else {
+      return dq8(q[t >> 2][t & 3], nv_part_word(sw >> (8 * (t >> 1))));
+    }
   };
-  auto read_a = [&](v8h (&va)[TI], const uint8_t* buf, int step) {
+  // step t of this wave's A fragment of stage s, dequantized into LDS unit (t, w)
+  auto unit = [&](const NvA& a, int t, int s, uint8_t* buf) {
+    *reinterpret_cast<VT*>(buf + (t * TI + wave) * kNvUnit + lane * 16) = deq(a.q, a.s, t, s);
+  };
+  auto read_a = [&](VT (&va)[TI], const uint8_t* buf, int step) {
 #pragma unroll
-    for (int i = 0; i < TI; i++) va[i] = *reinterpret_cast<const v8h*>(buf + (step * TI + i) * kNvUnit + lane * 16);
+    for (int i = 0; i < TI; i++) va[i] = *reinterpret_cast<const VT*>(buf + (step * TI + i) * kNvUnit + lane * 16);
   };
-  auto conv_b = [&](v8h (&vb)[TJ], const NvB& b, int step) {
+  auto conv_b = [&](VT (&vb)[TJ], const NvB& b, int step, int s) {
 #pragma unroll
-    for (int j = 0; j < TJ; j++)
-      vb[j] = dq8(b.q[j][step >> 2][step & 3], nv_part_word(b.s[j] >> (8 * (step >> 1))));
+    for (int j = 0; j < TJ; j++) vb[j] = deq(b.q[j], b.s[j], step, s);
   };
-  auto mma = [&](const v8h (&va)[TI], const v8h (&vb)[TJ]) {
+  auto mma = [&](const VT (&va)[TI], const VT (&vb)[TJ]) {
 #pragma unroll
     for (int i = 0; i < TI; i++)
 #pragma unroll
-      for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TJ; j++) {
+        if constexpr (F8)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], vb[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
+      }
   };
   // one MFMA, then a share of the VALU work, then one LDS access (the first
   // NDS MFMAs) or one load (the next NVM)
@@ -201,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
 
   NvB B0, B1, B2;
   NvA A0, A1, A2;
-  v8h va[TI], vb[TJ], na[TI], nb[TJ];
+  VT va[TI], vb[TJ], na[TI], nb[TJ];
   // prologue: stages 0 and 1 in flight; stage 0's A fragment converted and
   // published; step 0 of stage 0 ready in registers
 #pragma unroll
@@ -209,31 +237,47 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
 #pragma unroll
   for (int p = 0; p < 4; p++) issue(s0 + 1, p, B1, A1);
 #pragma unroll
-  for (int t = 0; t < kNvSteps; t++) unit(A0, t, smem);
+  for (int t = 0; t < kSteps; t++) unit(A0, t, s0, smem);
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   read_a(va, smem, 0);
-  conv_b(vb, B0, 0);
+  conv_b(vb, B0, 0, s0);
 
   // the workgroup's stage ls (K stage s0 + ls) from register sets (bc: that
   // stage, bn: the next, bf: the load target two ahead; an: A of the next
   // stage, af: A load target); LDS buffer ls % 2 holds its converted A
   auto stage = [&](int ls, const NvB& bc, const NvB& bn, NvB& bf, const NvA& an, NvA& af) {
     const int s = s0 + ls;
-    uint8_t* cur = smem + (ls & 1) * kNvStageLds;
-    uint8_t* nxt = smem + ((ls & 1) ^ 1) * kNvStageLds;
+    uint8_t* cur = smem + (ls & 1) * kStageLds;
+    uint8_t* nxt = smem + ((ls & 1) ^ 1) * kStageLds;
+    // the four load parts of stage s + 2 go out over the first steps, at most
+    // one part (three loads) per step where there are steps enough
+    constexpr int kLoadSteps = kSteps - 1 < 4 ? kSteps - 1 : 4;
 #pragma unroll
-    for (int st = 0; st < kNvSteps - 1; st++) {
+    for (int st = 0; st < kSteps - 1; st++) {
       __builtin_amdgcn_sched_barrier(0);
       read_a(na, cur, st + 1);
-      conv_b(nb, bc, st + 1);
-      unit(an, st, nxt);
-      if (st == kNvSteps - 2) unit(an, st + 1, nxt);
-      if (st < 4) issue(s + 2, st, bf, af);
+      conv_b(nb, bc, st + 1, s);
+      unit(an, st, s + 1, nxt);
+      if (st == kSteps - 2) unit(an, st + 1, s + 1, nxt);
+      int nparts = 0;
+#pragma unroll
+      for (int p = 0; p < 4; p++)
+        if (p * kLoadSteps / 4 == st) {
+          issue(s + 2, p, bf, af);
+          nparts++;
+        }
       mma(va, vb);
-      if (st == kNvSteps - 2) interleave(std::integral_constant<int, TI + 2>{}, I0{});
-      else if (st < 4) interleave(std::integral_constant<int, TI + 1>{}, I3{});
-      else interleave(std::integral_constant<int, TI + 1>{}, I0{});
+      if (st == kSteps - 2) {
+        if (nparts == 1) interleave(std::integral_constant<int, TI + 2>{}, I3{});
+        else interleave(std::integral_constant<int, TI + 2>{}, I0{});
+      } else if (nparts == 2) {
+        interleave(std::integral_constant<int, TI + 1>{}, std::integral_constant<int, 6>{});
+      } else if (nparts == 1) {
+        interleave(std::integral_constant<int, TI + 1>{}, I3{});
+      } else {
+        interleave(std::integral_constant<int, TI + 1>{}, I0{});
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TI; i++) va[i] = na[i];
@@ -245,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_a(na, nxt, 0);
-    conv_b(nb, bn, 0);
+    conv_b(nb, bn, 0, s + 1);
     mma(va, vb);
     interleave(std::integral_constant<int, TI>{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
@@ -301,30 +345,36 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
     epi_wave<EPI, TI, TJ>(acc, et, m0, n0 + wave * TJ * 32, g, lane);
     if constexpr (EPI == kEpiBiasGeluFp4)
       fp4_out_padding(g, m0, m0 + kNvBM, n0 / 16, (n0 + kNvBN) / 16, n0 + kNvBN >= g.N, tid, 256);
+    if constexpr (EPI == kEpiFp8)
+      fp8_out_padding(g, m0, m0 + kNvBM, n0 / 32, (n0 + kNvBN) / 32, n0 + kNvBN >= g.N, tid, 256);
   }
 }
 
-// The schedule's conditions: NVFP4, K % 64 == 0 (whole scale words), LINEAR
-// scale buffers 4-byte aligned.
+// The schedule's conditions: NVFP4 with K % 64 == 0, or MXFP8 with
+// K % 128 == 0 (whole scale words), LINEAR scale buffers 4-byte aligned.
+template <int FMT>
 inline bool prefill_nv_ok(const GemmArgs& g) {
   auto word_ok = [&](const uint8_t* p, int lay) {
     return lay == kTiled || (reinterpret_cast<uintptr_t>(p) & 3) == 0;
   };
-  return g.K % 64 == 0 && word_ok(g.sfa, g.la) && word_ok(g.sfb, g.lb);
+  const int64_t kmod = FMT == kMXFP8 ? 128 : 64;
+  return (FMT == kNVFP4 || FMT == kMXFP8) && g.K % kmod == 0 && word_ok(g.sfa, g.la) && word_ok(g.sfb, g.lb);
 }
 
-template <int EPI, bool SPLIT = false>
+template <int FMT, int EPI, bool SPLIT = false>
 void launch_prefill_nv(const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)(((g.M + kNvBM - 1) / kNvBM) * ((g.N + kNvBN - 1) / kNvBN)),
                   SPLIT ? (unsigned)g.splits : 1u),
       block(256);
-  if (g.la == kTiled && g.lb == kTiled)
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, true, true, SPLIT>), grid, block, 0, s, g);
-  else if (g.la == kTiled)
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, true, false, SPLIT>), grid, block, 0, s, g);
-  else if (g.lb == kTiled)
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, false, true, SPLIT>), grid, block, 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<EPI, false, false, SPLIT>), grid, block, 0, s, g);
+  if constexpr (FMT == kMXFP8) {   // LINEAR scales only
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, false, false, SPLIT>), grid, block, 0, s, g);
+  } else if (g.la == kTiled && g.lb == kTiled) {
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, true, true, SPLIT>), grid, block, 0, s, g);
+  } else if (g.la == kTiled) {
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, true, false, SPLIT>), grid, block, 0, s, g);
+  } else if (g.lb == kTiled) {
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, false, true, SPLIT>), grid, block, 0, s, g);
+  } else {
+    hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, false, false, SPLIT>), grid, block, 0, s, g);
+  }
 }
-
