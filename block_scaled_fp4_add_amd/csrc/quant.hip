@@ -222,10 +222,12 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
 
 // ---------------------------------------------------------------------------
 // Row-per-workgroup form for many rows of at most 16384 elements.  A row is
-// H/8 vectors of 8 bf16 (16 B); the workgroup has T = 64 * NW threads, NW =
-// ceil(H / 1024), and thread t owns vectors t and t + T, so that every load
-// and store instruction of a wave covers one contiguous 1 KiB span (256 B of
-// codes) and each thread keeps four 16-byte loads of x and r in flight.
+// H/8 vectors of 8 bf16 (16 B); the workgroup has T = 64 * NW threads and
+// thread t owns vectors t + jT, j < V, so that every load and store
+// instruction of a wave covers one contiguous 1 KiB span (256 B of codes) and
+// each thread keeps 2V 16-byte loads of x and r in flight.  V = 2, NW =
+// ceil(H / 1024); for 4096 < H <= 6144 over more than 1280 rows, V = 3 and
+// NW = 4 instead of 5 or 6.
 // Resident workgroups (up to eight 4-wave ones per CU) are what keeps enough
 // bytes in flight to stream HBM: measured 20.5 us on 4096 x 4096 NVFP4 against
 // 25.3 us for a form with persistent waves carrying several rows, and 18 us for
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(RowArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kWgMinRows = 256;     // fewer rows: the row-split form has more parallelism
 constexpr int kWgMaxWaves = 16;     // H <= 16384
-constexpr int kWgVecs = 2;          // 16-byte vectors per thread and tensor
+constexpr int kWgVecs = 2;          // 16-byte vectors per thread and tensor (3 for 4096 < H <= 6144)
 
 // TILED: the row of workgroup b.  Workgroups start on XCD b % 8; this order
 // puts the 32 rows of each 32-row scale group on one XCD, whose L2 then
@@ -252,12 +254,11 @@ __device__ __forceinline__ int64_t tiled_row_of_block(int64_t b, int64_t G) {
   return ((x + 8 * (i >> 5)) << 5) + (i & 31);
 }
 
-template <int FMT, int NW, bool FUSED, bool F16>
+template <int FMT, int NW, int V, bool FUSED, bool F16>
 __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   constexpr int B = FmtTraits<FMT>::B;
   constexpr int LPB = B / 8;   // lanes per block
   constexpr int T = NW * kWave;
-  constexpr int V = kWgVecs;
   __shared__ double part[NW];
   const int t = threadIdx.x, lane = t % kWave;
   const int64_t row = (a.layout == kTiled) ? tiled_row_of_block(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
@@ -366,10 +367,11 @@ __global__ __launch_bounds__(NW * kWave) void row_wg_kernel(RowArgs a) {
   if (a.layout != kLinear && t < nblk_pad - nblk) a.out_sf[sf_offset(FMT, a.layout, row, nblk + t, nblk)] = 0;
 }
 
-template <int FMT, int NW, bool FUSED, bool F16>
+template <int FMT, int NW, bool FUSED, bool F16, int V = kWgVecs>
 hipError_t launch_wg(const RowArgs& a, hipStream_t s) {
   if (a.rows_grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((row_wg_kernel<FMT, NW, FUSED, F16>), dim3((unsigned)a.rows_grid), dim3(NW * kWave), 0, s, a);
+  hipLaunchKernelGGL((row_wg_kernel<FMT, NW, V, FUSED, F16>), dim3((unsigned)a.rows_grid), dim3(NW * kWave), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -392,6 +394,13 @@ hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
   const int64_t nblk = a.H / FmtTraits<FMT>::B;
   const int64_t nw = (a.H + kWgVecs * 8 * kWave - 1) / (kWgVecs * 8 * kWave);
   if (a.M >= kWgMinRows && nw <= kWgMaxWaves && a.rows_grid <= 0x7FFFFFFF) {
+    // 4096 < H <= 6144: three vectors per thread make the workgroup 4 waves
+    // wide instead of 5 or 6, so eight of them (32 waves) stay resident per
+    // CU.  Only for more rows than the wider workgroups keep resident in one
+    // pass (five per CU): with fewer, the narrower form only loses threads
+    // (measured 2048 x 5120: 16.1 -> 15.3 us, 2048 x 6144: 19.2 -> 17.7 us;
+    // 300 x 5632: 13.5 -> 14.0 us)
+    if ((nw == 5 || nw == 6) && a.rows_grid > 5 * 256) return launch_wg<FMT, 4, FUSED, F16, 3>(a, s);
     switch (nw) {
       case 1: return launch_wg<FMT, 1, FUSED, F16>(a, s);
       case 2: return launch_wg<FMT, 2, FUSED, F16>(a, s);

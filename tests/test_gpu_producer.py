@@ -69,9 +69,11 @@ def test_producer_small(orc, M, H, fmt, layout):
 # Many rows: one workgroup per row (NW = ceil(H/1024) waves, two 16-byte
 # vectors per thread).  Rows of 1..6 waves, with H % 1024 != 0 so that the
 # second vector of some threads lies past the row's end; M % 32 != 0 for the
-# TILED padding rows.
+# TILED padding rows.  More than 1280 rows of 4096 < H <= 6144 take three
+# vectors per thread in 4 waves: (4200, 6144), (1300, 4160) (the third vector
+# of most threads past the row's end), (1281, 5632); (520, 5632) keeps two.
 MANY_ROWS = [(256, 64), (300, 1536), (257, 2560), (2100, 3584), (520, 5632), (4200, 6144), (2049, 512),
-         (4500, 4096), (256, 16384), (300, 11264)]
+         (4500, 4096), (256, 16384), (300, 11264), (1300, 4160), (1281, 5632)]
 
 
 @pytest.mark.parametrize("M,H", MANY_ROWS)
