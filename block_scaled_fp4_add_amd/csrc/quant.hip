@@ -399,7 +399,9 @@ hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
     // CU.  Only for more rows than the wider workgroups keep resident in one
     // pass (five per CU): with fewer, the narrower form only loses threads
     // (measured 2048 x 5120: 16.1 -> 15.3 us, 2048 x 6144: 19.2 -> 17.7 us;
-    // 300 x 5632: 13.5 -> 14.0 us)
+    // 300 x 5632: 13.5 -> 14.0 us).  Rows of 4096 keep V = 2 in 4 waves: all
+    // 4096 rows of 4096 x 4096 resident at once, as 2 waves with V = 4 or one
+    // with V = 8, measured 23.2 and 28.6 us against 21.1 us.
     if ((nw == 5 || nw == 6) && a.rows_grid > 5 * 256) return launch_wg<FMT, 4, FUSED, F16, 3>(a, s);
     switch (nw) {
       case 1: return launch_wg<FMT, 1, FUSED, F16>(a, s);
