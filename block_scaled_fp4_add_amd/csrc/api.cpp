@@ -136,16 +136,24 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   if (fp8_out && N % 32 != 0) return LOWBIT_ESHAPE;
   // workspace on offer: the caller's, or the static scratch
   const size_t ws_avail = static_ws ? kStaticScratchBytes : (workspace ? workspace_bytes : 0);
-  const int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, ws_avail);
+  int v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, ws_avail);
   if (v < 0) return LOWBIT_ESHAPE;
   // split-K asked for explicitly needs the workspace it documents; beyond
   // the static scratch that is a size the entry point does not take
   const lowbit::SplitPlan plan = lowbit::gemm_splitk_plan(M, N, K, fmt, variant == lowbit::kVariantSplitK);
   if (v == lowbit::kVariantSplitK && !empty && ws_avail < plan.bytes)
     return static_ws ? LOWBIT_ESHAPE : LOWBIT_EINVAL;
-  // the prefill schedule addresses each operand through a 32-bit buffer offset
-  if (v == 1 && (M * packed_row_bytes(fmt, K) >= (int64_t(1) << 30) ||
-                 N * packed_row_bytes(fmt, K) >= (int64_t(1) << 30)))
+  // the 128 x 384 schedule reads LINEAR scales as aligned words: an automatic
+  // split on it falls back to the unsplit schedule, an explicit one is refused
+  if (v == lowbit::kVariantSplitK && plan.nv &&
+      ((la == LOWBIT_SF_LINEAR && !aligned(sfa, 4)) || (lb == LOWBIT_SF_LINEAR && !aligned(sfb, 4)))) {
+    if (variant == lowbit::kVariantSplitK) return LOWBIT_EALIGN;
+    v = lowbit::gemm_pick_variant(M, N, K, fmt, variant, 0);
+  }
+  // the prefill schedules (and the split of the 128 x 384 one) address each
+  // operand through a 32-bit buffer offset
+  if ((v == 1 || (v == lowbit::kVariantSplitK && plan.nv)) &&
+      (M * packed_row_bytes(fmt, K) >= (int64_t(1) << 30) || N * packed_row_bytes(fmt, K) >= (int64_t(1) << 30)))
     return LOWBIT_ESHAPE;
   if (empty) return LOWBIT_OK;
   // EALIGN

@@ -45,15 +45,37 @@ hipError_t launch_fmt(const GemmArgs& g, int variant, hipStream_t s) {
 // 13.7 -> 10.7 us split; (41, 4608, 1536) 6.8 -> 9.4 us, so not split).
 constexpr int64_t kSplitTargetWorkgroups = 512;
 constexpr int64_t kSplitMinSupersteps = 16;
-// the NVFP4 128 x 384 split: one workgroup a CU (256 CUs)
+// the 128 x 384 split: one workgroup a CU (256 CUs)
 constexpr int64_t kSplitNvWorkgroups = 256;
+// more than 128 rows: at least 16 stages a split (the partial tiles then
+// cost a few percent of the contraction)
+constexpr int64_t kSplitNvMinStagesPrefill = 16;
 
 SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force) {
   const int64_t ss = fmt == kMXFP8 ? 128 : 256;   // K elements of a superstep
   const int64_t nss = (K + ss - 1) / ss;
   SplitPlan none{1, (int)nss, 0, false};
-  if (M <= 0 || M > 128 || N <= 0 || K <= 0) return none;
+  if (M <= 0 || N <= 0 || K <= 0) return none;
   const int64_t tiles = (N + 31) / 32, mt = (M + 31) / 32;
+  if (M > 128) {
+    // Prefill shapes with at most half the CUs' worth of 128 x 384 tiles (few
+    // columns, long K): that schedule split along K, about one workgroup per
+    // CU.  NVFP4 with K % 64 == 0 and MXFP8 with K % 128 == 0 (its stages:
+    // 128 and 64 elements).  Other formats and shapes do not split.
+    const bool nv_ok = (fmt == kNVFP4 && K % 64 == 0) || (fmt == kMXFP8 && K % 128 == 0);
+    if (!nv_ok) return none;
+    const int64_t nst = fmt == kMXFP8 ? K / 64 : (K + 127) / 128;   // the last NVFP4 stage may be half
+    const int64_t tiles_nv = ((M + 127) / 128) * ((N + 383) / 384);
+    int64_t S = kSplitNvWorkgroups / tiles_nv;
+    if (S > nst / kSplitNvMinStagesPrefill) S = nst / kSplitNvMinStagesPrefill;
+    if (2 * tiles_nv > kSplitNvWorkgroups && !force) S = 1;
+    if (force && S < 2 && nst >= 2) S = 2;
+    if (S <= 1) return none;
+    const int64_t per = (nst + S - 1) / S;
+    S = (nst + per - 1) / per;
+    if (S <= 1) return none;
+    return SplitPlan{(int)S, (int)per, (size_t)(S * tiles * mt * 1024 * 4), true};
+  }
   if (fmt == kNVFP4 && M > 64 && K % 64 == 0) {
     // NVFP4 with 3-4 M-tiles: the decode schedule converts every activation
     // fragment in every workgroup (1.25 fragments per MFMA); the 128 x 384
@@ -84,11 +106,12 @@ int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, siz
   // 128-row slices past 128 rows); an explicit prefill request is refused
   const bool half_k = fmt == kNVFP4 && (K / 2) % 16 != 0;
   if (variant == kVariantSplitK) {
-    // the caller asked for split-K: M <= 128 and a K of two supersteps at least
+    // the caller asked for split-K: a K of two supersteps (stages) at least;
+    // above 128 rows NVFP4 with K % 64 == 0 or MXFP8 with K % 128 == 0
     if (M == 0 || N == 0) return kVariantSplitK;   // nothing to run
     return gemm_splitk_plan(M, N, K, fmt, true).splits > 1 ? kVariantSplitK : -1;
   }
-  if (variant == -1 && M <= 128) {
+  if (variant == -1) {
     const SplitPlan p = gemm_splitk_plan(M, N, K, fmt, false);
     if (p.splits > 1 && ws_bytes >= p.bytes) return kVariantSplitK;
   }

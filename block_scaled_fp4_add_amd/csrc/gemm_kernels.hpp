@@ -1455,8 +1455,9 @@ __global__ __launch_bounds__(64) void gemm_splitk_reduce_kernel(GemmArgs g, int 
   epi_run16<EPI>(t + r * kEpiPitch + ec, i * 32 + r, n0 + ec, g);
   if constexpr (EPI == kEpiBiasGeluFp4)
     fp4_out_padding(g, i * 32, i * 32 + 32, n0 / 16, (n0 + 32) / 16, n0 + 32 >= g.N, lane, 64);
-  if constexpr (EPI == kEpiFp8)   // the last M-tile also owns the padding rows up to 128
-    fp8_out_padding(g, i * 32, (i + 1 == MT) ? 128 : i * 32 + 32, n0 / 32, n0 / 32 + 1, n0 + 32 >= g.N, lane, 64);
+  if constexpr (EPI == kEpiFp8)   // the last M-tile also owns the padding rows (to a multiple of 128)
+    fp8_out_padding(g, i * 32, (i + 1 == MT) ? sf_pad_rows(kSwz128, g.M) : i * 32 + 32, n0 / 32, n0 / 32 + 1,
+                    n0 + 32 >= g.N, lane, 64);
 }
 
 #include "gemm_nv.hpp"
@@ -1584,10 +1585,10 @@ hipError_t launch_splitk_mt(const GemmArgs& g, hipStream_t s) {
 template <int FMT, int EPI>
 hipError_t launch_splitk(const GemmArgs& g, hipStream_t s) {
   const int mt = (int)((g.M + 31) / 32);
-  if constexpr (FMT == kNVFP4) {
+  if constexpr (FMT == kNVFP4 || FMT == kMXFP8) {
     if (g.split_nv) {   // partials from the 128 x 384 schedule, same reduce
-      if (!prefill_nv_ok<kNVFP4>(g) || mt > 4) return hipErrorInvalidValue;
-      launch_prefill_nv<kNVFP4, kEpiNone, true>(g, s);
+      if (!prefill_nv_ok<FMT>(g)) return hipErrorInvalidValue;
+      launch_prefill_nv<FMT, kEpiNone, true>(g, s);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((gemm_splitk_reduce_kernel<EPI>), dim3((unsigned)((g.N + 31) / 32), (unsigned)mt),

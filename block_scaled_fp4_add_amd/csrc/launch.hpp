@@ -52,20 +52,22 @@ struct GemmArgs {
   int out_layout;
   float* ws;                  // split-K: fp32 partial tiles (device), else nullptr
   int splits;                 // split-K: workgroups along K per output tile
-  int per;                    // split-K: K units per split (supersteps, or NVFP4 stages: split_nv)
-  int split_nv;               // split-K on the NVFP4 128 x 384 schedule (units: 128-element stages)
+  int per;                    // split-K: K units per split (supersteps, or the stages of split_nv)
+  int split_nv;               // split-K on the 128 x 384 schedule (units: its 64-byte row stages)
 };
 
 // Schedules: 0 decode, 1 prefill, 2 split-K decode (needs a workspace).
 constexpr int kVariantSplitK = 2;
 
-// Split-K plan of a GEMM with M <= 128: `splits` workgroups along K per
-// output tile (1: no split), `per` K units each, `bytes` of workspace for the
-// partials.  force: at least two splits whenever K has two units.  nv: the
-// NVFP4 128 x 384 schedule does the partial pass (NVFP4, 64 < M <= 128,
-// K % 64 == 0; units of 128 elements), else the decode schedule (units of
-// one superstep).  Either way the partials are 32 x 32 fp32 tiles in one
-// layout, summed by the same reduce pass.
+// Split-K plan of a GEMM: `splits` workgroups along K per output tile (1: no
+// split), `per` K units each, `bytes` of workspace for the partials.  force:
+// at least two splits whenever K has two units.  nv: the 128 x 384 schedule
+// does the partial pass (units: its stages of 64 bytes of a row, 128 NVFP4 or
+// 64 MXFP8 elements) -- NVFP4 with 64 < M <= 128 and K % 64 == 0, and above
+// 128 rows NVFP4 (K % 64 == 0) or MXFP8 (K % 128 == 0) shapes with at most
+// 128 such tiles; else the decode schedule (M <= 128, units of one
+// superstep).  Either way the partials are 32 x 32 fp32 tiles in one layout,
+// summed by the same reduce pass.
 struct SplitPlan {
   int splits;
   int per;

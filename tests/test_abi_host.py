@@ -79,7 +79,8 @@ def test_pick_variant():
 
 
 def splitk_plan(M, N, K, fmt=1):
-    """The split-K plan the library documents, written out.  NVFP4 with
+    """The split-K plan the library documents, written out.  Above 128
+    rows see below.  NVFP4 with
     64 < M <= 128 and K % 64 == 0 splits the 128 x 384 schedule: about one
     workgroup per CU (256 over the 384-column tiles), at least two
     128-element stages per split, K of at least 32 stages.  Otherwise the
@@ -87,6 +88,21 @@ def splitk_plan(M, N, K, fmt=1):
     supersteps (1024 elements) per split, K of at least 16 supersteps.  No
     empty split; bytes = splits x 32-column tiles x M-tiles x 32 x 32 floats."""
     tiles, mt = -(-N // 32), -(-M // 32)
+    if M > 128:
+        # above 128 rows: NVFP4 (K % 64 == 0, 128-element stages) or MXFP8
+        # (K % 128 == 0, 64-element stages) with at most 128 tiles of
+        # 128 x 384 split those, about one workgroup per CU, 16 stages or
+        # more each
+        if not ((fmt == 0 and K % 64 == 0) or (fmt == 2 and K % 128 == 0)):
+            return 1, 0
+        nst = K // 64 if fmt == 2 else -(-K // 128)
+        tnv = -(-M // 128) * -(-N // 384)
+        S = 1 if 2 * tnv > 256 else min(256 // tnv, nst // 16)
+        if S <= 1:
+            return 1, 0
+        per = -(-nst // S)
+        S = -(-nst // per)
+        return (S, S * tiles * mt * 1024 * 4) if S > 1 else (1, 0)
     if fmt == 0 and 64 < M <= 128 and K % 64 == 0:
         nst = -(-K // 128)
         S = min(256 // -(-N // 384), nst // 2)
@@ -97,7 +113,7 @@ def splitk_plan(M, N, K, fmt=1):
             S = -(-nst // per)
             if S > 1:
                 return S, S * tiles * mt * 1024 * 4
-    nss = -(-K // 256)
+    nss = -(-K // (128 if fmt == 2 else 256))
     S = min(-(-512 // tiles), nss // 4)
     if nss < 16:
         S = 1
@@ -132,8 +148,38 @@ def test_splitk_workspace_and_choice(M, N, K):
         assert forced >= need and forced > 0
         assert L.lowbit_gemm_pick_variant(M, N, K, fmt, 2, 0) == 2
     assert L.lowbit_gemm_workspace_bytes(M, N, K, 1, 0) == 0 and L.lowbit_gemm_workspace_bytes(M, N, K, 1, 1) == 0
-    assert L.lowbit_gemm_workspace_bytes(200, N, K, 1, 2) == 0             # split-K needs M <= 128
+    assert L.lowbit_gemm_workspace_bytes(200, N, K, 1, 2) == 0             # MXFP4 split-K needs M <= 128
     assert L.lowbit_gemm_pick_variant(200, N, K, 1, 2, 1 << 30) < 0
+
+
+@pytest.mark.parametrize("M,N,K,fmt", [(4096, 1024, 8192, 2), (4096, 1024, 8192, 0), (600, 1000, 4096, 0),
+                                       (300, 770, 2048, 2), (2048, 5120, 17408, 0), (2048, 17408, 5120, 0),
+                                       (8192, 4096, 14336, 1), (129, 96, 8192, 0), (4096, 1024, 8160, 2),
+                                       (1000, 400, 4096 + 32, 0), (200, 384, 1024, 0), (257, 400, 4160, 0),
+                                       (300, 400, 1984, 0)])
+def test_splitk_above_128_rows(M, N, K, fmt):
+    """Above 128 rows only NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0)
+    split, on the 128 x 384 tiles, and the automatic choice only with at most
+    128 such tiles: (4096, 1024, 8192) has 96 tiles and splits in two, the
+    chain's 2048-token GEMMs (224 and 736 tiles) and MXFP4 never do."""
+    L = lb.lib()
+    S, need = splitk_plan(M, N, K, fmt)
+    assert L.lowbit_gemm_workspace_bytes(M, N, K, fmt, -1) == need
+    if need:
+        assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, need) == 2
+        assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, need - 1) == 1   # too little: prefill
+    else:
+        assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, 1 << 30) == 1
+    nv_ok = (fmt == 0 and K % 64 == 0) or (fmt == 2 and K % 128 == 0)
+    forced = L.lowbit_gemm_workspace_bytes(M, N, K, fmt, 2)
+    assert (forced > 0) == nv_ok and forced >= need
+    assert (L.lowbit_gemm_pick_variant(M, N, K, fmt, 2, 0) == 2) == nv_ok
+    if (M, N, K) == (4096, 1024, 8192):
+        assert S == 2 and need == 2 * 32 * 128 * 4096
+    if (M, N, K) == (257, 400, 4160):   # 33 stages, the last a half one: 2 splits of 17 and 16
+        assert S == 2
+    if (M, N) in ((2048, 5120), (2048, 17408)) or fmt == 1:
+        assert need == 0
 
 
 class Buf:
@@ -241,7 +287,15 @@ def test_gemm_argument_order(buf):
     assert call(8, 128, 1024, variant=2) == EINVAL           # split-K without its workspace
     assert call(8, 128, 1024, variant=2, ws=buf.at(32768), wsb=100) == EINVAL
     assert call(8, 128, 256, variant=2, ws=buf.at(32768), wsb=1 << 20) == ESHAPE   # one superstep: no split
-    assert call(200, 128, 1024, variant=2, ws=buf.at(32768), wsb=1 << 20) == ESHAPE  # M > 128
+    assert call(200, 128, 1024, variant=2, ws=buf.at(32768), wsb=1 << 20) == ESHAPE  # MXFP4 above 128 rows
+    assert call(200, 128, 1056, fmt=2, variant=2, ws=buf.at(32768), wsb=1 << 30) == ESHAPE  # MXFP8: K % 128
+    assert call(200, 128, 1040, fmt=0, variant=2, ws=buf.at(32768), wsb=1 << 30) == ESHAPE  # NVFP4: K % 64
+    # above 64 NVFP4 rows the split runs the 128 x 384 schedule, which reads
+    # LINEAR scales as aligned words
+    assert L.lowbit_gemm_bf16(a, b, buf.at(8193), sb, 300, 400, 4096, 0, 0, 0, 1.0, out, 2, buf.at(32768),
+                              1 << 30, None) == EALIGN
+    assert L.lowbit_gemm_bf16(a, b, sa, buf.at(12290), 100, 400, 4096, 0, 0, 0, 1.0, out, 2, buf.at(32768),
+                              1 << 30, None) == EALIGN
     assert call(8, 128, 1024, variant=2, ws=buf.at(32772), wsb=1 << 15) == EALIGN   # workspace alignment
     assert call(0, 128, 1024, variant=2) == OK               # empty: nothing to run
     assert call(8, 128, 256, o=None) == EINVAL
@@ -254,6 +308,11 @@ def test_gemm_argument_order(buf):
         assert call(8, 128, 256) == EDEVICE
         assert call(8, 128, 256, fmt=2) == EDEVICE
         assert call(8, 128, 1024, variant=2, ws=buf.at(32768), wsb=1 << 15) == EDEVICE
+        assert call(300, 400, 4096, fmt=0, variant=2, ws=buf.at(32768), wsb=1 << 30) == EDEVICE
+        assert call(300, 400, 4096, fmt=2, variant=2, ws=buf.at(32768), wsb=1 << 30) == EDEVICE
+        # the automatic split with misaligned LINEAR scales runs unsplit instead
+        assert L.lowbit_gemm_bf16(a, b, buf.at(8193), sb, 300, 400, 4096, 0, 0, 0, 1.0, out, -1,
+                                  buf.at(32768), 1 << 30, None) == EDEVICE
     # epilogues that need an operand reject its absence
     assert L.lowbit_gemm_bias_bf16(a, b, sa, sb, 8, 128, 256, 1, 0, 0, 1.0, None, out, -1, None, 0,
                                    None) == EINVAL

@@ -270,6 +270,34 @@ def test_gemm_splitk_gelu_fp4(orc, M, N, K, fmt, out_layout):
     run_gelu_fp4(orc, M, N, K, fmt, 2, out_layout, seed=M + N + 3)
 
 
+# Above 128 rows NVFP4 with K % 64 == 0 splits the 128 x 384 schedule along
+# K: ragged M (129: a one-row second M-tile) and N, a last stage of half
+# length (4160 = 32.5 stages of 128), every layout pair and epilogue;
+# explicit, and automatic with the workspace offered (all but the 16-stage
+# shape have few tiles and K enough for the automatic choice to split)
+PREFILL_SPLIT_SHAPES = [(300, 770, 4096), (600, 1000, 2048), (129, 96, 8192), (257, 400, 4160)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL_SPLIT_SHAPES)
+@pytest.mark.parametrize("la,lb_", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_nvfp4_prefill_splitk(orc, M, N, K, la, lb_):
+    run_gemm(orc, M, N, K, 0, la, lb_, 0, 2, seed=M + N + K + la, alpha=0.5, outliers=True)
+    auto = lb.lowbit_gemm_workspace_bytes(M, N, K, 0, -1)
+    assert (auto > 0) == (K >= 4096)
+    if auto:
+        run_gemm(orc, M, N, K, 0, la, lb_, 0, -1, seed=M + N + K + lb_ + 7, workspace=True)
+
+
+@pytest.mark.parametrize("epi", [1, 2, 3, 4])
+def test_gemm_nvfp4_prefill_splitk_epilogues(orc, epi):
+    run_gemm(orc, 300, 400, 4096, 0, 1, 1, epi, 2, seed=epi + 40, outliers=True)
+
+
+@pytest.mark.parametrize("out_layout", [0, 1])
+def test_gemm_nvfp4_prefill_splitk_gelu_fp4(orc, out_layout):
+    run_gelu_fp4(orc, 300, 400, 4096, 0, 2, out_layout, seed=301)
+
+
 @pytest.mark.parametrize("M,N,K", [(40, 96, 1552), (128, 200, 4112), (3, 64, 2064)])
 def test_gemm_splitk_nvfp4_half_chunk_k(orc, M, N, K):
     assert K % 32 == 16
