@@ -30,10 +30,18 @@
 //            buffers, 16-byte chunks XOR-swizzled by row so the 32-row
 //            fragment reads are bank-conflict free); tiles are mapped so that
 //            consecutive tiles share an XCD's L2.
+//            NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) run the 128 x 384
+//            schedule of gemm_nv.hpp instead, which converts each activation
+//            fragment once per workgroup.
 //   decode:  the weights are the MFMA row operand (32 weight rows per
 //            workgroup, all <= 128 tokens as the column operand, so each weight
 //            byte is read once); the K supersteps are dealt round-robin to the
 //            workgroup's waves and the partial tiles summed through LDS.
+//   split-K: the decode schedule (<= 128 tokens) or the 128 x 384 one
+//            (NVFP4 above 64 tokens; NVFP4 / MXFP8 prefill shapes with few
+//            tiles) with K split across workgroups, fp32 partials in a
+//            workspace, summed in a fixed order by gemm_splitk_reduce_kernel,
+//            which applies the epilogue.
 // Epilogues run per 32x32 tile through LDS so that every global access is a
 // contiguous 16-element run of a row: bf16 out with alpha, bias, residual,
 // GELU; or GELU followed by NVFP4 quantization along N (FP4 output for the
