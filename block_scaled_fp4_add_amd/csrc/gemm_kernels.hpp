@@ -690,8 +690,10 @@ __device__ __forceinline__ void epi_wave(const v16f (&acc)[TI][TJ], float* et, i
         if (col_ok && m < g.M) {
           const u32x4 o = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]), pack_bf16x2(z[4], z[5]),
                            pack_bf16x2(z[6], z[7])};
+          // nontemporal: written once, not read back by this kernel (MXFP4
+          // (8192, 14336, 4096) + bias + residual: 370.6 -> 361.6 us)
           uint16_t* base = g.out + (mb + i * 32 + q * 4) * g.N + nb;
-          *reinterpret_cast<u32x4*>(base + loff) = o;
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(base + loff));
         }
       }
       fence();
