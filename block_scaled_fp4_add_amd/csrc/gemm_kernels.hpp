@@ -1008,10 +1008,15 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   constexpr int kPf = 2;   // prefetch instructions per wave per superstep
   const int pf_a = (m0 + wave * 64 + lane < M) ? (m0 + wave * 64 + lane) * kbytes : kAbsent;
   const int pf_b = (wave * 64 + lane < BN && n0 + wave * 64 + lane < N) ? (n0 + wave * 64 + lane) * kbytes : kAbsent;
+  // Past the last superstep the instruction still goes out (the wait counts
+  // assume kPf of them) but with the out-of-range lane offset: only that one
+  // is range-checked, and the superstep's advance in the scalar offset would
+  // otherwise reach past the end of the buffer on its last row.
   auto prefetch = [&](int k) {
-    const int so = k * kSSBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)pf_lds, 4, pf_a, so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)pf_lds, 4, pf_b, so, 0, 0);
+    const bool ok = k < nss;   // uniform
+    const int so = ok ? k * kSSBytes : 0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)pf_lds, 4, ok ? pf_a : kAbsent, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)pf_lds, 4, ok ? pf_b : kAbsent, so, 0, 0);
   };
 
   // superstep k -> ring slot k % 2 (and, with_sf, its scales -> scale slot
