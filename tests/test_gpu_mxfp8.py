@@ -161,6 +161,15 @@ def test_gemm_fp8_out_splitk(orc, M, N, K, fmt, out_layout):
     run_fp8_out(orc, M, N, K, fmt, 2, out_layout, seed=M + K + fmt)
 
 
+def test_mxfp8_fp8_out_prefill_workload_full(orc):
+    """The MXFP8 prefill workload the benchmark times, (4096, 1024, 8192) with
+    FP8 output and 128 x 4 scales, in its launch configuration (the 128 x 384
+    schedule split in two along K), every output compared."""
+    assert lb.lowbit_gemm_workspace_bytes(4096, 1024, 8192, F8, -1) == lb.lowbit_gemm_workspace_bytes(
+        4096, 1024, 8192, F8, 2) > 0
+    run_fp8_out(orc, 4096, 1024, 8192, F8, 2, 2, seed=79, alpha=1.0)
+
+
 @pytest.mark.parametrize("M", [5, 200])
 def test_gemm_fp8_out_nvfp4_half_chunk_k(orc, M):
     """NVFP4 with K % 32 == 16 runs the decode schedule in 128-row slices."""
