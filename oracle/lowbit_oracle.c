@@ -229,6 +229,20 @@ int64_t orc_sf_offset(int64_t row, int64_t kb, int64_t nblk, int fmt, int layout
     return tile * 256 + (((j / 2) % 2) * 32 + row % 32) * 4 + (j % 2) + 2 * (j / 4);
 }
 
+/* The scale bytes of a (rows, k) operand moved from one layout to another:
+ * the byte of each (row, block) goes to the same (row, block) of the
+ * destination, whose padding is zero.  The FlashRT page's GEMM takes its
+ * operand scales in the 128 x 4 layout (its "Tensor Contract"); this is the
+ * definition the library's relayout is checked against. */
+void orc_sf_convert(const uint8_t* src, int src_layout, uint8_t* dst, int dst_layout, int64_t rows,
+                    int64_t k, int fmt) {
+    int64_t nblk = k / block_of(fmt);
+    memset(dst, 0, (size_t)orc_sf_bytes(rows, k, fmt, dst_layout));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t kb = 0; kb < nblk; ++kb)
+            dst[orc_sf_offset(r, kb, nblk, fmt, dst_layout)] = src[orc_sf_offset(r, kb, nblk, fmt, src_layout)];
+}
+
 /* ------------------------------------------------------------------------- */
 /* One quantization block (FlashInfer page, kernel Phase 3)                    */
 /* ------------------------------------------------------------------------- */

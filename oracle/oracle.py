@@ -72,6 +72,8 @@ def lib():
     L.orc_sf_bytes.argtypes = [_i64, _i64, _int, _int]
     L.orc_sf_offset.restype = _i64
     L.orc_sf_offset.argtypes = [_i64, _i64, _i64, _int, _int]
+    L.orc_sf_convert.restype = None
+    L.orc_sf_convert.argtypes = [_u8p, _int, _u8p, _int, _i64, _i64, _int]
     L.orc_encode_with_scale.restype = None
     L.orc_encode_with_scale.argtypes = [_f32p, _int, _int, ctypes.c_float, ctypes.c_uint8, _u8p, _vp]
     L.orc_add_rmsnorm_quant.restype = _int
@@ -168,6 +170,15 @@ def sf_bytes(rows: int, k: int, fmt: int, layout: int) -> int:
 
 def sf_offset(row: int, kb: int, nblk: int, fmt: int, layout: int) -> int:
     return lib().orc_sf_offset(row, kb, nblk, fmt, layout)
+
+
+def sf_convert(sf, rows: int, k: int, fmt: int, src_layout: int, dst_layout: int):
+    """Scale bytes of a (rows, k) operand in dst_layout, from src_layout."""
+    src = _c(sf, np.uint8)
+    assert src.size >= sf_bytes(rows, k, fmt, src_layout)
+    out = np.empty(sf_bytes(rows, k, fmt, dst_layout), dtype=np.uint8)
+    lib().orc_sf_convert(src, src_layout, out, dst_layout, rows, k, fmt)
+    return out
 
 
 def encode_with_scale(y, fmt: int, gs: float, sbyte: int, with_v: bool = False):
