@@ -31,7 +31,7 @@ EXPORTS = (
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
     "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes", "lowbit_gemm_bf16_noalloc",
-    "lowbit_rope_quant", "lowbit_gemm_fp8",
+    "lowbit_rope_quant", "lowbit_gemm_fp8", "lowbit_sf_convert",
 )
 STATIC_SCRATCH_BYTES = 16 << 20   # LOWBIT_STATIC_SCRATCH_BYTES
 
@@ -72,6 +72,8 @@ def lib():
         L.lowbit_rope_quant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]
         L.lowbit_dequantize.restype = _int
         L.lowbit_dequantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
+        L.lowbit_sf_convert.restype = _int
+        L.lowbit_sf_convert.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _int, _vp]
         head = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f32]
         tail = [_int, _vp, _sz, _vp]   # variant, workspace, workspace_bytes, stream
         L.lowbit_gemm_bf16.argtypes = head + [_vp] + tail
@@ -312,6 +314,21 @@ def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, o
     _at_least(out, rows * K, "out")
     _check("lowbit_dequantize", lib().lowbit_dequantize(
         _ptr(packed), _ptr(sf), rows, K, fmt, layout, _ptr(global_scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def lowbit_sf_convert(sf, rows, k, fmt=NVFP4, src_layout=SWZ128, dst_layout=TILED, out=None, stream=None):
+    """Scale bytes of a (rows, k) operand rewritten from src_layout into
+    dst_layout (destination padding zero), e.g. 128 x 4 weight scales into the
+    TILED layout the GEMM reads."""
+    _need(sf, torch.uint8, "sf")
+    _at_least(sf, lowbit_sf_bytes(rows, k, fmt, src_layout), "sf")
+    if out is None:
+        out = torch.empty(lowbit_sf_bytes(rows, k, fmt, dst_layout), dtype=torch.uint8, device=sf.device)
+    _need(out, torch.uint8, "out")
+    _at_least(out, lowbit_sf_bytes(rows, k, fmt, dst_layout), "out")
+    _check("lowbit_sf_convert", lib().lowbit_sf_convert(
+        _ptr(sf), src_layout, _ptr(out), dst_layout, rows, k, fmt, _stream(stream)))
     return out
 
 

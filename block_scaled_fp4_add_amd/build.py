@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblowbit.so")
 SOURCES = ["gemm_inst_splitk.hip", "gemm_inst_splitk8.hip", "gemm_inst_f80.hip", "gemm_inst_f81.hip",
            "gemm_inst_f82.hip", "gemm_inst_f83.hip", "gemm_inst_nv3.hip", "gemm_inst_mx3.hip", "gemm_inst_nv2.hip", "gemm_inst_nv1.hip", "gemm_inst_nv0.hip", "gemm_inst_mx2.hip",
-           "gemm_inst_mx1.hip", "gemm_inst_mx0.hip", "quant.hip", "rope.hip", "gemm.hip", "api.cpp"]
+           "gemm_inst_mx1.hip", "gemm_inst_mx0.hip", "quant.hip", "rope.hip", "sf_layout.hip", "gemm.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -367,6 +367,27 @@ lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_
                                             static_cast<uint16_t*>(out), stream));
 }
 
+lowbit_status lowbit_sf_convert(const uint8_t* src, lowbit_sf_layout src_layout, uint8_t* dst,
+                                lowbit_sf_layout dst_layout, int64_t rows, int64_t k, lowbit_format fmt,
+                                hipStream_t stream) {
+  // every (format, layout) pair that has a scale buffer size
+  if (lowbit_sf_bytes(1, block_of(fmt), fmt, src_layout) == 0 ||
+      lowbit_sf_bytes(1, block_of(fmt), fmt, dst_layout) == 0)
+    return LOWBIT_EINVAL;
+  if (rows < 0) return LOWBIT_ESHAPE;
+  if (rows > 0 && (!src || !dst)) return LOWBIT_EINVAL;
+  if (k < block_of(fmt) || k % block_of(fmt) != 0) return LOWBIT_ESHAPE;
+  if (rows == 0) return LOWBIT_OK;
+  const size_t sbytes = lowbit_sf_bytes(rows, k, fmt, src_layout);
+  const size_t dbytes = lowbit_sf_bytes(rows, k, fmt, dst_layout);
+  if ((int64_t)dbytes > lowbit::kRelayoutMaxBytes) return LOWBIT_ESHAPE;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + dbytes && d0 < s0 + sbytes) return LOWBIT_EINVAL;   // the buffers overlap
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_sf_relayout(src, src_layout, dst, dst_layout, rows, k / block_of(fmt), fmt,
+                                             stream));
+}
+
 lowbit_status lowbit_gemm_bf16(const uint8_t* a, const uint8_t* b, const uint8_t* sfa, const uint8_t* sfb,
                                int64_t M, int64_t N, int64_t K, lowbit_format fmt,
                                lowbit_sf_layout sfa_layout, lowbit_sf_layout sfb_layout, float alpha,

@@ -21,6 +21,12 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, 
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
                              int layout, const float* gs, uint16_t* out, hipStream_t s);
 
+// Scale bytes of a (rows, nblk blocks) operand rewritten from layout ls into
+// layout ld, destination padding zero; at most kRelayoutMaxBytes of output.
+constexpr int64_t kRelayoutMaxBytes = int64_t(1) << 33;
+hipError_t launch_sf_relayout(const uint8_t* src, int ls, uint8_t* dst, int ld, int64_t rows, int64_t nblk,
+                              int fmt, hipStream_t s);
+
 // Inverse RoPE + MX quantization of (T, heads, D) bf16 rows (rows = T * heads).
 struct RopeArgs {
   const uint16_t* x;          // bf16 (rows, D)

@@ -94,7 +94,8 @@ typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2, LOWBIT_NVFP
  * kb%4.  lowbit_sf_bytes = ceil(rows/128) * ceil(K/B/4) * 512; padding bytes
  * are written zero.  Producer, quantizer and dequantizer with NVFP4 or MXFP4,
  * and the MXFP8 output of lowbit_gemm_fp8 ([WOA]'s F8_128x4 scale bytes);
- * GEMM operands do not take it (LOWBIT_EINVAL). */
+ * GEMM operands do not take it (LOWBIT_EINVAL): lowbit_sf_convert rewrites it
+ * into a layout they take. */
 typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1, LOWBIT_SF_SWZ128 = 2 } lowbit_sf_layout;
 
 /* GEMM schedule: -1 picks by shape (and by the workspace offered); 0 =
@@ -221,6 +222,24 @@ lowbit_status lowbit_rope_quant(const void* x, const int64_t* positions, const f
 lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
                                 lowbit_format fmt, lowbit_sf_layout layout,
                                 const float* global_scale, void* out, hipStream_t stream);
+
+/* Scale bytes rewritten from one layout into another: for every row r < rows
+ * and block kb < k/B, the byte of (r, kb) in src_layout is written at (r, kb)
+ * of dst_layout; the destination's padding bytes (TILED, SWZ128) are written
+ * zero, the source's are not read.  [FRT] "Tensor Contract" hands its GEMM
+ * the operand scales in the 128 x 4 layout (CUTLASS SFA / SFB), which the
+ * GEMMs below do not read: rewritten as TILED (FP4 formats) or LINEAR they
+ * can be, once, for prepacked weights.  Likewise the 128 x 4 scales of
+ * lowbit_gemm_fp8 become the LINEAR ones an MXFP8 GEMM operand takes.
+ * src: lowbit_sf_bytes(rows, k, fmt, src_layout) bytes; dst:
+ * lowbit_sf_bytes(rows, k, fmt, dst_layout) bytes, at most 8 GiB (ESHAPE);
+ * device pointers, any alignment, the two buffers must not overlap
+ * (LOWBIT_EINVAL).  Every (format, layout) pair that lowbit_sf_bytes sizes is
+ * taken (TILED: NVFP4 and MXFP4 only; equal layouts copy).  Requires
+ * k % B == 0, k >= B and rows >= 0 (rows == 0 is a no-op). */
+lowbit_status lowbit_sf_convert(const uint8_t* src, lowbit_sf_layout src_layout, uint8_t* dst,
+                                lowbit_sf_layout dst_layout, int64_t rows, int64_t k, lowbit_format fmt,
+                                hipStream_t stream);
 
 /* Block-scaled GEMM ([FRT] nvfp4_gemm_bf16 and its epilogue family).
  * a: packed (M, K/2); b: packed (N, K/2) (the weight, "B^T" row-major);

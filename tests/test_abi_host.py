@@ -225,6 +225,36 @@ def test_quantize_argument_order(buf):
         assert quant(L, buf, 4, 64, fmt=3, gs=buf.at()) == EDEVICE         # 32-block NVFP4 takes gs
 
 
+def conv(L, buf, rows, k, fmt=0, ls=2, ld=1, s=0, d=4096):
+    return L.lowbit_sf_convert(buf.at(s), ls, buf.at(d), ld, rows, k, fmt, None)
+
+
+def test_sf_convert_argument_order(buf):
+    L = lb.lib()
+    assert conv(L, buf, 4, 64, fmt=4) == EINVAL                  # format
+    assert conv(L, buf, 4, 64, ls=3) == EINVAL                   # layout
+    assert conv(L, buf, 4, 64, fmt=2, ld=1) == EINVAL            # MXFP8 has no TILED layout
+    assert conv(L, buf, 4, 64, fmt=3, ls=2, ld=0) == EINVAL      # 32-block NVFP4: LINEAR only
+    assert conv(L, buf, -1, 64) == ESHAPE
+    assert L.lowbit_sf_convert(None, 2, buf.at(), 1, 4, 64, 0, None) == EINVAL
+    assert L.lowbit_sf_convert(buf.at(), 2, None, 1, 4, 64, 0, None) == EINVAL
+    assert conv(L, buf, 4, 40) == ESHAPE                         # k % 16
+    assert conv(L, buf, 4, 0) == ESHAPE                          # k below one block
+    assert conv(L, buf, 4, 48, fmt=1, ls=0) == ESHAPE            # MXFP4: k % 32
+    assert conv(L, buf, 1 << 40, 64) == ESHAPE                   # more than 8 GiB of output
+    # overlapping buffers: the 512-byte 128 x 4 source and the 256-byte TILED output
+    assert conv(L, buf, 4, 64, s=0, d=256) == EINVAL
+    assert conv(L, buf, 4, 64, s=128, d=0) == EINVAL
+    if NO_DEVICE:
+        assert conv(L, buf, 4, 64, s=256, d=0) == EDEVICE        # adjacent the other way
+    assert conv(L, buf, 0, 64) == OK                             # empty: nothing to do
+    if NO_DEVICE:
+        assert conv(L, buf, 4, 64, s=0, d=512) == EDEVICE        # adjacent, not overlapping
+        assert conv(L, buf, 4, 64, fmt=2, ls=2, ld=0) == EDEVICE  # MXFP8 128 x 4 -> LINEAR
+        assert conv(L, buf, 4, 64, fmt=3, ls=0, ld=0) == EDEVICE  # 32-block NVFP4 copy
+        assert conv(L, buf, 4, 64, s=1, d=4097) == EDEVICE       # any alignment
+
+
 def test_producer_argument_order(buf):
     L = lb.lib()
 
