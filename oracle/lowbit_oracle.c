@@ -511,16 +511,20 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout
 }
 
 /* ------------------------------------------------------------------------- */
-/* Dequantize (FlashRT README: dequantize_fp4_sfa_fp16, here to bf16)          */
+/* Dequantize (FlashRT README: dequantize_fp4_sfa_fp16)                       */
 /* ------------------------------------------------------------------------- */
 /* x_hat = fl32(E2M1(code) * scale / gs) for NVFP4 (gs divides: it was folded
  * into the block scale on the way in), E2M1(code) * 2^(b-127) for MXFP4,
  * E4M3(byte) * 2^(b-127) for MXFP8, then
- * stored as bf16 (nearest-even).  Also returns the binary64 values when
- * out_f64 is non-NULL. */
-int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
-                   int layout, float gs, uint16_t* out_bf16, double* out_f64) {
+ * stored as bf16, or as fp16 with dtype ORC_IN_F16 (the README's fp16
+ * output), nearest-even either way (fp16: values from 65520 up become
+ * infinity, small ones fp16 subnormals).  Also returns the binary64 values
+ * when out_f64 is non-NULL. */
+int orc_dequantize_dt(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
+                      int layout, float gs, uint16_t* out16, double* out_f64, int dtype) {
     if (check_common(rows, K, fmt, layout)) return 1;
+    if (dtype != ORC_IN_BF16 && dtype != ORC_IN_F16) return 1;
+    const orc_narrow_fn nar = narrow_of(dtype);
     int64_t B = block_of(fmt), nblk = K / B;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < rows; m++) {
@@ -539,10 +543,15 @@ int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64
              * binary32 equals the correctly rounded binary32 quotient */
             if (e4m3_scaled(fmt)) v = v / (double)gs;
             if (out_f64) out_f64[m * K + i] = v;
-            if (out_bf16) out_bf16[m * K + i] = orc_f32_to_bf16((float)v);
+            if (out16) out16[m * K + i] = nar((float)v);
         }
     }
     return 0;
+}
+
+int orc_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
+                   int layout, float gs, uint16_t* out_bf16, double* out_f64) {
+    return orc_dequantize_dt(packed, sf, rows, K, fmt, layout, gs, out_bf16, out_f64, ORC_IN_BF16);
 }
 
 /* ------------------------------------------------------------------------- */

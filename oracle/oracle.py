@@ -92,6 +92,8 @@ def lib():
     L.orc_quantize.argtypes = [_u16p, _i64, _i64, _int, _int, ctypes.c_float, _u8p, _u8p, _vp]
     L.orc_dequantize.restype = _int
     L.orc_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp]
+    L.orc_dequantize_dt.restype = _int
+    L.orc_dequantize_dt.argtypes = [_u8p, _u8p, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp, _int]
     L.orc_gemm.restype = _int
     L.orc_gemm.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _int, _int, _int,
                            ctypes.c_double, _int, _vp, _vp, _f64p, _vp]
@@ -257,12 +259,13 @@ def rope_quant(x, positions, rope, heads, fmt, layout, diag=False):
     return (packed, sf, y, am) if diag else (packed, sf)
 
 
-def dequantize(packed, sf, rows, K, fmt, layout, gs=1.0):
+def dequantize(packed, sf, rows, K, fmt, layout, gs=1.0, dtype=BF16):
+    """Dequantizer: bf16 bits (fp16 bits with dtype F16) and the binary64 values."""
     packed = _c(packed, np.uint8)
     sf = _c(sf, np.uint8)
     out = np.zeros((rows, K), dtype=np.uint16)
     f64 = np.zeros((rows, K), dtype=np.float64)
-    rc = lib().orc_dequantize(packed, sf, rows, K, fmt, layout, gs, _ptr(out), _ptr(f64))
+    rc = lib().orc_dequantize_dt(packed, sf, rows, K, fmt, layout, gs, _ptr(out), _ptr(f64), dtype)
     if rc:
         raise ValueError(f"oracle dequantize rejected its arguments (rc={rc})")
     return out, f64

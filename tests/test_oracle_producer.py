@@ -174,6 +174,33 @@ def test_nvfp4_dequantize_divides_by_global_scale(orc):
     assert np.array_equal(bits, synth.bits(torch.from_numpy(want).to(torch.bfloat16)))
 
 
+@pytest.mark.parametrize("fmt,gs", [(0, 1.0), (0, 0.3), (1, 1.0), (2, 1.0), (3, 7.0)])
+def test_dequantize_fp16_output_is_numpys_rounding(orc, fmt, gs):
+    """The fp16 output of the dequantizer (the README's dequantize_fp4_sfa_fp16)
+    is numpy's IEEE rounding of the binary32 value, for every code under scale
+    bytes that reach fp16 overflow (infinity) and its subnormals."""
+    rows, K = 64, 256
+    B = orc.block_size(fmt)
+    rng = np.random.default_rng(fmt * 10 + int(gs))
+    width = K if fmt == orc.MXFP8 else K // 2
+    packed = rng.integers(0, 256, size=(rows, width), dtype=np.uint8)
+    if fmt == orc.MXFP8:
+        packed[(packed & 0x7F) == 0x7F] = 0x7E           # no E4M3 NaN codes
+    if fmt in (orc.MXFP4, orc.MXFP8):
+        # UE8M0 bytes from 2^-40 to 2^25: fp16 subnormals, zeros and overflow to infinity
+        sf = rng.integers(127 - 40, 127 + 26, size=rows * (K // B), dtype=np.uint8)
+    else:
+        sf = rng.integers(0, 0x7F, size=rows * (K // B), dtype=np.uint8)   # every E4M3 scale but NaN
+    bits, f64 = orc.dequantize(packed, sf, rows, K, fmt, orc.LINEAR, gs=gs, dtype=orc.F16)
+    with np.errstate(over="ignore"):   # overflow to infinity is the case under test
+        want = f64.astype(np.float32).astype(np.float16).view(np.uint16)
+    assert np.array_equal(bits, want)
+    if fmt in (orc.MXFP4, orc.MXFP8):
+        assert (want & 0x7FFF == 0x7C00).any() and ((want & 0x7C00) == 0).any()   # both ends reached
+    bf, f64b = orc.dequantize(packed, sf, rows, K, fmt, orc.LINEAR, gs=gs)
+    assert np.array_equal(f64b, f64)
+
+
 # --- fp16 tensors ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt", [0, 1])
