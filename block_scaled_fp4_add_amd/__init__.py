@@ -31,7 +31,7 @@ EXPORTS = (
     "lowbit_dequantize", "lowbit_gemm_bf16", "lowbit_gemm_bias_bf16", "lowbit_gemm_residual_bf16",
     "lowbit_gemm_bias_residual_bf16", "lowbit_gemm_bias_gelu_bf16", "lowbit_gemm_bias_gelu_fp4",
     "lowbit_gemm_pick_variant", "lowbit_gemm_workspace_bytes", "lowbit_gemm_bf16_noalloc",
-    "lowbit_rope_quant", "lowbit_gemm_fp8", "lowbit_sf_convert",
+    "lowbit_rope_quant", "lowbit_gemm_fp8", "lowbit_sf_convert", "lowbit_dequantize_fp16",
 )
 STATIC_SCRATCH_BYTES = 16 << 20   # LOWBIT_STATIC_SCRATCH_BYTES
 
@@ -72,6 +72,8 @@ def lib():
         L.lowbit_rope_quant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]
         L.lowbit_dequantize.restype = _int
         L.lowbit_dequantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
+        L.lowbit_dequantize_fp16.restype = _int
+        L.lowbit_dequantize_fp16.argtypes = L.lowbit_dequantize.argtypes
         L.lowbit_sf_convert.restype = _int
         L.lowbit_sf_convert.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _int, _vp]
         head = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f32]
@@ -300,6 +302,15 @@ def lowbit_rope_quant(x, positions, rope, fmt=MXFP8, layout=LINEAR, out_packed=N
 
 def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):
     """packed (..., K/2) (MXFP8: (..., K)) + scales -> bf16 (..., K)."""
+    return _dequantize("lowbit_dequantize", torch.bfloat16, packed, sf, fmt, layout, global_scale, out, stream)
+
+
+def lowbit_dequantize_fp16(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, out=None, stream=None):
+    """packed (..., K/2) (MXFP8: (..., K)) + scales -> fp16 (..., K)."""
+    return _dequantize("lowbit_dequantize_fp16", torch.float16, packed, sf, fmt, layout, global_scale, out, stream)
+
+
+def _dequantize(fn, dtype, packed, sf, fmt, layout, global_scale, out, stream):
     _need(packed, torch.uint8, "packed")
     _need(sf, torch.uint8, "sf")
     lead, rows, kb = _rows_of(packed)
@@ -309,10 +320,10 @@ def lowbit_dequantize(packed, sf, fmt=NVFP4, layout=LINEAR, global_scale=None, o
         _need(global_scale, torch.float32, "global_scale")
         _at_least(global_scale, 1, "global_scale")
     if out is None:
-        out = torch.empty(lead + (K,), dtype=torch.bfloat16, device=packed.device)
-    _need(out, torch.bfloat16, "out")
+        out = torch.empty(lead + (K,), dtype=dtype, device=packed.device)
+    _need(out, dtype, "out")
     _at_least(out, rows * K, "out")
-    _check("lowbit_dequantize", lib().lowbit_dequantize(
+    _check(fn, getattr(lib(), fn)(
         _ptr(packed), _ptr(sf), rows, K, fmt, layout, _ptr(global_scale), _ptr(out), _stream(stream)))
     return out
 

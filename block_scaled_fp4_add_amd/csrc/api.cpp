@@ -247,6 +247,22 @@ static lowbit_status quantize(const void* x, int64_t rows, int64_t K, lowbit_for
                                           global_scale, out_packed, out_sf, in_f16, stream));
 }
 
+static lowbit_status dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
+                                int layout, const float* global_scale, void* out, int out_f16,
+                                hipStream_t stream) {
+  if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
+  if (!takes_gs(fmt) && global_scale) return LOWBIT_EINVAL;
+  if (rows < 0) return LOWBIT_ESHAPE;
+  if (rows > 0 && (!packed || !sf || !out)) return LOWBIT_EINVAL;
+  if (K < block_of(fmt) || K % block_of(fmt) != 0) return LOWBIT_ESHAPE;
+  if (rows == 0) return LOWBIT_OK;
+  if (!aligned(packed, 16) || !aligned(out, 16)) return LOWBIT_EALIGN;
+  if (global_scale && !aligned(global_scale, 4)) return LOWBIT_EALIGN;
+  if (lowbit_status d = device_check()) return d;
+  return from_hip(lowbit::launch_dequantize(packed, sf, rows, K, fmt, layout, global_scale,
+                                            static_cast<uint16_t*>(out), out_f16, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,17 +370,13 @@ lowbit_status lowbit_rope_quant(const void* x, const int64_t* positions, const f
 lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
                                 lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
                                 void* out, hipStream_t stream) {
-  if (!qfmt_layout_ok(fmt, layout)) return LOWBIT_EINVAL;
-  if (!takes_gs(fmt) && global_scale) return LOWBIT_EINVAL;
-  if (rows < 0) return LOWBIT_ESHAPE;
-  if (rows > 0 && (!packed || !sf || !out)) return LOWBIT_EINVAL;
-  if (K < block_of(fmt) || K % block_of(fmt) != 0) return LOWBIT_ESHAPE;
-  if (rows == 0) return LOWBIT_OK;
-  if (!aligned(packed, 16) || !aligned(out, 16)) return LOWBIT_EALIGN;
-  if (global_scale && !aligned(global_scale, 4)) return LOWBIT_EALIGN;
-  if (lowbit_status d = device_check()) return d;
-  return from_hip(lowbit::launch_dequantize(packed, sf, rows, K, fmt, layout, global_scale,
-                                            static_cast<uint16_t*>(out), stream));
+  return dequantize(packed, sf, rows, K, fmt, layout, global_scale, out, 0, stream);
+}
+
+lowbit_status lowbit_dequantize_fp16(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
+                                     lowbit_format fmt, lowbit_sf_layout layout, const float* global_scale,
+                                     void* out, hipStream_t stream) {
+  return dequantize(packed, sf, rows, K, fmt, layout, global_scale, out, 1, stream);
 }
 
 lowbit_status lowbit_sf_convert(const uint8_t* src, lowbit_sf_layout src_layout, uint8_t* dst,

@@ -18,8 +18,9 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* x, uint16_t* residual, const
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, int layout,
                            const float* gs, uint8_t* out_packed, uint8_t* out_sf, int in_f16, hipStream_t s);
 
+// out: bf16, or fp16 with out_f16
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
-                             int layout, const float* gs, uint16_t* out, hipStream_t s);
+                             int layout, const float* gs, uint16_t* out, int out_f16, hipStream_t s);
 
 // Scale bytes of a (rows, nblk blocks) operand rewritten from layout ls into
 // layout ld, destination padding zero; at most kRelayoutMaxBytes of output.

@@ -442,9 +442,10 @@ hipError_t dispatch_row(const RowArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: one lane per block.
+// Dequantize: one lane per block; bf16 output, or fp16 with F16 (both
+// nearest-even from the binary32 value; fp16 overflows to infinity).
 // ---------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, bool F16>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed, const uint8_t* sf,
                                                            int64_t rows, int64_t K, int layout,
                                                            const float* gsp, uint16_t* out) {
@@ -468,8 +469,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
 #pragma unroll
       for (int j = 0; j < 8; j++) {
         const uint32_t wd = w4[j >> 1], sh = 16 * (j & 1);
-        o[j] = pack_bf16x2(__fmul_rn(e4m3_to_f32((wd >> sh) & 0xFF), scale),
-                           __fmul_rn(e4m3_to_f32((wd >> (sh + 8)) & 0xFF), scale));
+        o[j] = pack_in2<F16>(__fmul_rn(e4m3_to_f32((wd >> sh) & 0xFF), scale),
+                             __fmul_rn(e4m3_to_f32((wd >> (sh + 8)) & 0xFF), scale));
       }
       uint4* d4 = reinterpret_cast<uint4*>(dst + h * 16);
       d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* packed
       float v0 = __fmul_rn(e2m1_to_f32(byte & 15), scale);   // exact
       float v1 = __fmul_rn(e2m1_to_f32(byte >> 4), scale);
       if (e4m3_scaled(FMT)) { v0 = __fdiv_rn(v0, gs); v1 = __fdiv_rn(v1, gs); }
-      o[j] = pack_bf16x2(v0, v1);
+      o[j] = pack_in2<F16>(v0, v1);
     }
     uint4* d4 = reinterpret_cast<uint4*>(dst + q * 16);
     d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -520,24 +521,31 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int fmt, 
   return fmt == kNVFP4 ? dispatch_row<kNVFP4, false, false>(a, s) : dispatch_row<kMXFP4, false, false>(a, s);
 }
 
+template <bool F16>
+static void dequant_fmt(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt, int layout,
+                        const float* gs, uint16_t* out, unsigned grid, hipStream_t s) {
+  if (fmt == kNVFP4)
+    hipLaunchKernelGGL((dequant_kernel<kNVFP4, F16>), dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K,
+                       layout, gs, out);
+  else if (fmt == kNV32)
+    hipLaunchKernelGGL((dequant_kernel<kNV32, F16>), dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K,
+                       layout, gs, out);
+  else if (fmt == kMXFP8)
+    hipLaunchKernelGGL((dequant_kernel<kMXFP8, F16>), dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K,
+                       layout, gs, out);
+  else
+    hipLaunchKernelGGL((dequant_kernel<kMXFP4, F16>), dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K,
+                       layout, gs, out);
+}
+
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K, int fmt,
-                             int layout, const float* gs, uint16_t* out, hipStream_t s) {
+                             int layout, const float* gs, uint16_t* out, int out_f16, hipStream_t s) {
   const int64_t nblk = K / (fmt == kNVFP4 ? 16 : 32);
   const int64_t n = rows * nblk;
   if (n == 0) return hipSuccess;
   const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
-  if (fmt == kNVFP4)
-    hipLaunchKernelGGL(dequant_kernel<kNVFP4>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
-                       gs, out);
-  else if (fmt == kNV32)
-    hipLaunchKernelGGL(dequant_kernel<kNV32>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
-                       gs, out);
-  else if (fmt == kMXFP8)
-    hipLaunchKernelGGL(dequant_kernel<kMXFP8>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
-                       gs, out);
-  else
-    hipLaunchKernelGGL(dequant_kernel<kMXFP4>, dim3(grid), dim3(kThreads), 0, s, packed, sf, rows, K, layout,
-                       gs, out);
+  if (out_f16) dequant_fmt<true>(packed, sf, rows, K, fmt, layout, gs, out, grid, s);
+  else dequant_fmt<false>(packed, sf, rows, K, fmt, layout, gs, out, grid, s);
   return hipGetLastError();
 }
 

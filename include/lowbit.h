@@ -218,10 +218,20 @@ lowbit_status lowbit_rope_quant(const void* x, const int64_t* positions, const f
 
 /* Dequantize to bf16: x = bf16(fl32(E2M1 * scale / gs)) (NVFP4, gs from
  * global_scale or 1.0) or bf16(E2M1 * 2^(b-127)) (MXFP4; global_scale NULL)
- * ([FRT] dequantize_fp4_sfa_fp16, here with bf16 output). */
+ * ([FRT] dequantize_fp4_sfa_fp16 with bf16 output; lowbit_dequantize_fp16
+ * below gives its fp16 output). */
 lowbit_status lowbit_dequantize(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
                                 lowbit_format fmt, lowbit_sf_layout layout,
                                 const float* global_scale, void* out, hipStream_t stream);
+
+/* lowbit_dequantize with fp16 output ([FRT] dequantize_fp4_sfa_fp16): the
+ * same binary32 values rounded to IEEE binary16, nearest-even (values from
+ * 65520 up in magnitude become infinity; small ones fp16 subnormals or
+ * zero).  out: fp16 (rows, K); arguments, checks and errors as
+ * lowbit_dequantize. */
+lowbit_status lowbit_dequantize_fp16(const uint8_t* packed, const uint8_t* sf, int64_t rows, int64_t K,
+                                     lowbit_format fmt, lowbit_sf_layout layout,
+                                     const float* global_scale, void* out, hipStream_t stream);
 
 /* Scale bytes rewritten from one layout into another: for every row r < rows
  * and block kb < k/B, the byte of (r, kb) in src_layout is written at (r, kb)

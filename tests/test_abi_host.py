@@ -255,6 +255,26 @@ def test_sf_convert_argument_order(buf):
         assert conv(L, buf, 4, 64, s=1, d=4097) == EDEVICE       # any alignment
 
 
+def test_dequantize_argument_order(buf):
+    """Both dequantizers (bf16 and fp16 output) check their arguments alike."""
+    L = lb.lib()
+    for fn in (L.lowbit_dequantize, L.lowbit_dequantize_fp16):
+        def dq(rows, K, fmt=1, layout=0, gs=None, p=0, s=0, o=0):
+            return fn(buf.at(p), buf.at(s), rows, K, fmt, layout, gs, buf.at(o), None)
+        assert dq(4, 64, fmt=5) == EINVAL                           # format
+        assert dq(4, 64, fmt=2, layout=1) == EINVAL                 # MXFP8: LINEAR scales only
+        assert dq(4, 64, gs=buf.at()) == EINVAL                     # MXFP4 has no global scale
+        assert dq(-1, 64) == ESHAPE
+        assert fn(None, buf.at(), 4, 64, 1, 0, None, buf.at(), None) == EINVAL
+        assert dq(4, 48) == ESHAPE                                  # K % 32
+        assert dq(0, 64) == OK                                      # empty: nothing to do
+        assert dq(4, 64, o=2) == EALIGN                             # output 16 bytes
+        assert dq(4, 64, p=8) == EALIGN                             # packed 16 bytes
+        if NO_DEVICE:
+            assert dq(4, 64) == EDEVICE
+            assert dq(4, 64, fmt=0, layout=2, gs=buf.at()) == EDEVICE   # NVFP4, 128 x 4, global scale
+
+
 def test_producer_argument_order(buf):
     L = lb.lib()
 

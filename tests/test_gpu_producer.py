@@ -233,6 +233,32 @@ def test_dequantize_bit_exact(orc, fmt, layout):
     assert np.array_equal(host_bits(out), want)
 
 
+@pytest.mark.parametrize("fmt,layout,gs", [(0, 0, 0.75), (0, 1, 0.01), (0, 2, 1.0), (1, 0, 1.0), (1, 1, 1.0),
+                                           (1, 2, 1.0), (2, 0, 1.0), (3, 0, 3.0)])
+@pytest.mark.parametrize("rows,K", [(37, 512), (300, 1024)])
+def test_dequantize_fp16_bit_exact(orc, fmt, layout, gs, rows, K):
+    """fp16 output ([FRT] dequantize_fp4_sfa_fp16) against the oracle, every
+    value, with scales that take the results past fp16's largest value
+    (infinity) and into its subnormals."""
+    banner(f"dequantize fp16 fmt={fmt} layout={layout} gs={gs} rows={rows} K={K}")
+    rng = np.random.default_rng(fmt * 8 + layout + rows)
+    width = K if fmt == 2 else K // 2
+    packed = rng.integers(0, 256, (rows, width), dtype=np.uint8)
+    if fmt == 2:
+        packed[(packed & 0x7F) == 0x7F] = 0x7E           # no E4M3 NaN codes
+    nb = orc.sf_bytes(rows, K, fmt, layout)
+    if fmt in (0, 3):
+        sf = rng.integers(0, 0x7F, nb, dtype=np.uint8)   # finite E4M3 (no NaN code)
+    else:
+        sf = rng.integers(127 - 40, 127 + 26, nb, dtype=np.uint8)
+    want, _ = orc.dequantize(packed, sf, rows, K, fmt, layout, gs=gs, dtype=orc.F16)
+    out = lb.lowbit_dequantize_fp16(dev_u8(packed), dev_u8(sf), fmt, layout,
+                                    global_scale=dev_f32(gs) if fmt in (0, 3) else None)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16
+    assert np.array_equal(host_bits(out), want)
+
+
 def test_argument_errors_on_device():
     x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
     p = torch.empty((4, 50), dtype=torch.uint8, device="cuda")
