@@ -82,13 +82,15 @@ def rope_stage(name, T, heads, fmt, dev):
 WOA_N = 1024   # output columns of the MXFP8 GEMM workloads (synthetic: the page gives no head geometry)
 
 
-def mxfp8_gemm_stage(name, M, N, K, dev, bound, workspace=None):
+def mxfp8_gemm_stage(name, M, N, K, dev, bound, workspace=None, fmt=None):
     """MXFP8 operands (E4M3 elements, UE8M0 scales per 32) through the GEMM
     with the FP8 output epilogue: bf16(A.B^T) quantized to MXFP8 along N,
-    scale bytes in the 128 x 4 layout.  The operands are dequantized exactly
-    to bf16 and contracted on bf16 MFMAs, so the executed peak is bf16's;
-    the roofline prices the format at the FP8 peak (MFMA-bound) or its bytes
-    at HBM (decode)."""
+    scale bytes in the 128 x 4 layout.  With fmt MXFP8 the operands are
+    dequantized exactly to bf16 and contracted on bf16 MFMAs, so the executed
+    peak is bf16's; with MXFP8_MMA they run on the scaled FP8 MFMA.  The
+    roofline prices the format at the FP8 peak (MFMA-bound) or its bytes at
+    HBM (decode)."""
+    fmt = lb.MXFP8 if fmt is None else fmt
     A = synth.activation(M, K, 79, outliers=True).to(dev)
     a, sa = lb.lowbit_quantize(A, lb.MXFP8, lb.LINEAR)
     # decode: one weight copy per launch of a graph replay, so that the
@@ -104,9 +106,11 @@ def mxfp8_gemm_stage(name, M, N, K, dev, bound, workspace=None):
     def fn(a=a, sa=sa, pk=pk, sf=sf, wsets=wsets, it=it, ws=workspace):
         b, sb = wsets[it["i"] % len(wsets)]
         it["i"] += 1
-        lb.lowbit_gemm_fp8(a, b, sa, sb, fmt=lb.MXFP8, out_packed=pk, out_sf=sf, out_layout=lb.SWZ128,
+        lb.lowbit_gemm_fp8(a, b, sa, sb, fmt=fmt, out_packed=pk, out_sf=sf, out_layout=lb.SWZ128,
                            workspace=ws)
 
+    if bound == "mfma" and fmt == lb.MXFP8_MMA:
+        return Stage(name, fn, "mfma", 2.0 * M * N * K, "FLOP", FP8_PEAK)
     if bound == "mfma":
         return Stage(name, fn, "mfma", 2.0 * M * N * K, "FLOP", FP8_PEAK, own_peak=FP16_PEAK, own_dtype="bf16")
     nbytes = (M + N) * (K + K // 32) + M * N + M * N // 32
@@ -378,6 +382,11 @@ def build_variant_stages():
     ws8 = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
     stages.append(graphed(mxfp8_gemm_stage(f"mxfp8_gemm_fp8out_4096x{WOA_N}x8192", 4096, WOA_N, 8192, dev, "mfma",
                                            workspace=ws8)))
+    # the same on the scaled FP8 MFMA (LOWBIT_MXFP8_MMA: 64 tiles of 256 x 256, K split in four)
+    need = lb.lowbit_gemm_workspace_bytes(4096, WOA_N, 8192, lb.MXFP8_MMA, -1)
+    wsm = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
+    stages.append(graphed(mxfp8_gemm_stage(f"mxfp8_mma_gemm_fp8out_4096x{WOA_N}x8192", 4096, WOA_N, 8192, dev,
+                                           "mfma", workspace=wsm, fmt=lb.MXFP8_MMA)))
     return stages
 
 

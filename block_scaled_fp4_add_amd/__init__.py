@@ -15,6 +15,7 @@ import torch
 
 NVFP4, MXFP4, MXFP8 = 0, 1, 2   # MXFP8: LINEAR scales (its GEMM output also takes SWZ128)
 NVFP4_B32 = 3                   # the NVFP4 rule on 32-blocks: the same three calls, LINEAR scales
+MXFP8_MMA = 4                   # GEMM operands: MXFP8 bytes and scales, contracted on the scaled FP8 MFMA
 LINEAR, TILED, SWZ128 = 0, 1, 2   # SWZ128: the 128 x 4 swizzle (quantizer outputs, FP8 GEMM output)
 VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL, VARIANT_SPLITK = -1, 0, 1, 2
 
@@ -127,7 +128,7 @@ def block_size(fmt):
 
 def _row_bytes(fmt, k):
     """Packed bytes of a row of k elements: one per MXFP8 element, else two codes a byte."""
-    return k if fmt == MXFP8 else k // 2
+    return k if fmt in (MXFP8, MXFP8_MMA) else k // 2
 
 
 def _at_least(t, n, name):
@@ -350,14 +351,14 @@ def _gemm_head(a, b, sfa, sfb, fmt, sfa_layout, sfb_layout, alpha):
         _need(t, torch.uint8, n)
     _, M, ka = _rows_of(a)
     _, N, kb = _rows_of(b)
-    per = 1 if fmt == MXFP8 else 2     # elements per packed byte
+    per = 1 if fmt in (MXFP8, MXFP8_MMA) else 2     # elements per packed byte
     K = ka * per
     if kb * per != K:
         raise ValueError("a and b disagree on K")
     # sizes are checked for the layouts the GEMM takes; any other layout or
     # format is the C ABI's to refuse (LOWBIT_EINVAL)
     if (fmt in (NVFP4, MXFP4) and sfa_layout in (LINEAR, TILED) and sfb_layout in (LINEAR, TILED)) or \
-            (fmt == MXFP8 and sfa_layout == LINEAR and sfb_layout == LINEAR):
+            (fmt in (MXFP8, MXFP8_MMA) and sfa_layout == LINEAR and sfb_layout == LINEAR):
         _at_least(sfa, lowbit_sf_bytes(M, K, fmt, sfa_layout), "sfa")
         _at_least(sfb, lowbit_sf_bytes(N, K, fmt, sfb_layout), "sfb")
     return M, N, K, [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), M, N, K, fmt, sfa_layout, sfb_layout,

@@ -25,6 +25,7 @@
 // handed to kernels.
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 static_assert(kStaticScratchBytes == LOWBIT_STATIC_SCRATCH_BYTES, "header and library disagree");
+static_assert(LOWBIT_MXFP8_MMA == lowbit::kMXFP8Mma && LOWBIT_MXFP8 == lowbit::kMXFP8, "format ids");
 static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
 
 namespace {
@@ -34,12 +35,14 @@ using lowbit::GemmArgs;
 constexpr int64_t kMaxRowElems = 32768;  // 4 waves x 64 lanes x 128 elements per lane
 
 // GEMM operand formats (MXFP8 operands take LINEAR scales only)
-bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4 || f == LOWBIT_MXFP8; }
+bool fmt_ok(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4 || f == LOWBIT_MXFP8 || f == LOWBIT_MXFP8_MMA; }
+// MXFP8 operands, exact or on the scaled FP8 MFMA
+bool fp8_fmt(int f) { return f == LOWBIT_MXFP8 || f == LOWBIT_MXFP8_MMA; }
 bool fp4_fmt(int f) { return f == LOWBIT_NVFP4 || f == LOWBIT_MXFP4; }
 bool layout_ok(int l) { return l == LOWBIT_SF_LINEAR || l == LOWBIT_SF_TILED; }
-bool gemm_layout_ok(int f, int l) { return f == LOWBIT_MXFP8 ? l == LOWBIT_SF_LINEAR : layout_ok(l); }
+bool gemm_layout_ok(int f, int l) { return fp8_fmt(f) ? l == LOWBIT_SF_LINEAR : layout_ok(l); }
 // packed bytes of a row of k elements: one per MXFP8 element, else two codes a byte
-int64_t packed_row_bytes(int f, int64_t k) { return f == LOWBIT_MXFP8 ? k : k / 2; }
+int64_t packed_row_bytes(int f, int64_t k) { return fp8_fmt(f) ? k : k / 2; }
 // producer / quantizer / dequantizer: MXFP8 and 32-block NVFP4 as well, with
 // LINEAR scales only; the FP4 GEMM formats also take the 128 x 4 swizzle
 bool qfmt_layout_ok(int f, int l) {
@@ -184,7 +187,8 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   g.M = M;
   g.N = N;
   g.K = K;
-  g.fmt = fmt;
+  g.fmt = fmt == LOWBIT_MXFP8_MMA ? LOWBIT_MXFP8 : fmt;   // the kernels run MXFP8 operands either way
+  g.f8mma = fmt == LOWBIT_MXFP8_MMA ? 1 : 0;
   g.la = la;
   g.lb = lb;
   g.alpha = alpha;
@@ -281,6 +285,8 @@ const char* lowbit_status_str(lowbit_status s) {
 
 size_t lowbit_sf_bytes(int64_t rows, int64_t k, lowbit_format fmt, lowbit_sf_layout layout) {
   // the quantization formats and layouts, and the FP8 GEMM output's 128 x 4 layout
+  // (LOWBIT_MXFP8_MMA: the MXFP8 scale bytes it reads)
+  if (fmt == LOWBIT_MXFP8_MMA) fmt = LOWBIT_MXFP8;
   const bool ok = qfmt_layout_ok(fmt, layout) || (fmt == LOWBIT_MXFP8 && layout == LOWBIT_SF_SWZ128);
   if (!ok || rows < 0 || k < 0 || k % block_of(fmt) != 0) return 0;
   return (size_t)lowbit::sf_bytes_of(layout, rows, k / block_of(fmt));

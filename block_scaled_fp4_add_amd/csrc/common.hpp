@@ -14,6 +14,10 @@ constexpr int kWave = 64;
 
 // kNV32 (the NVFP4 rule on 32-blocks): quantization only, no GEMM
 enum Fmt : int { kNVFP4 = 0, kMXFP4 = 1, kMXFP8 = 2, kNV32 = 3 };
+// kMXFP8Mma: MXFP8 operands (kMXFP8's bytes and scales) contracted on the
+// scaled FP8 MFMA -- a GEMM format id only; its kernels run as kMXFP8 with
+// GemmArgs::f8mma set
+constexpr int kMXFP8Mma = 4;
 // kSwz128: the producer page's 128 x 4 swizzled layout (quantization side only)
 enum Layout : int { kLinear = 0, kTiled = 1, kSwz128 = 2 };
 enum Epi : int { kEpiNone = 0, kEpiBias = 1, kEpiResidual = 2, kEpiBiasResidual = 3, kEpiBiasGelu = 4,

@@ -51,23 +51,29 @@ constexpr int64_t kSplitNvWorkgroups = 256;
 // cost a few percent of the contraction)
 constexpr int64_t kSplitNvMinStagesPrefill = 16;
 
-SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force) {
+SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt_in, bool force) {
+  const bool mma = fmt_in == kMXFP8Mma;            // MXFP8 on the scaled FP8 MFMA
+  const int fmt = mma ? kMXFP8 : fmt_in;
   const int64_t ss = fmt == kMXFP8 ? 128 : 256;   // K elements of a superstep
   const int64_t nss = (K + ss - 1) / ss;
   SplitPlan none{1, (int)nss, 0, false};
   if (M <= 0 || N <= 0 || K <= 0) return none;
   const int64_t tiles = (N + 31) / 32, mt = (M + 31) / 32;
   if (M > 128) {
-    // Prefill shapes with at most half the CUs' worth of 128 x 384 tiles (few
-    // columns, long K): that schedule split along K, about one workgroup per
-    // CU.  NVFP4 with K % 64 == 0 and MXFP8 with K % 128 == 0 (its stages:
-    // 128 and 64 elements).  Other formats and shapes do not split.
+    // Prefill shapes with at most half the CUs' worth of prefill tiles (few
+    // columns, long K): the prefill schedule split along K, about one
+    // workgroup per CU.  NVFP4 with K % 64 == 0 and MXFP8 with K % 128 == 0
+    // on the 128 x 384 tiles (units: stages of 64 row bytes, 128 and 64
+    // elements, at least 16 a split); MXFP8 on the scaled FP8 MFMA on the
+    // 256 x 256 tiles (units: supersteps of 128 elements, at least 8 a split).
+    // Other formats and shapes do not split.
     const bool nv_ok = (fmt == kNVFP4 && K % 64 == 0) || (fmt == kMXFP8 && K % 128 == 0);
     if (!nv_ok) return none;
-    const int64_t nst = fmt == kMXFP8 ? K / 64 : (K + 127) / 128;   // the last NVFP4 stage may be half
-    const int64_t tiles_nv = ((M + 127) / 128) * ((N + 383) / 384);
+    const int64_t nst = mma ? K / 128 : fmt == kMXFP8 ? K / 64 : (K + 127) / 128;   // the last NVFP4 stage may be half
+    const int64_t tiles_nv = mma ? ((M + 255) / 256) * ((N + 255) / 256) : ((M + 127) / 128) * ((N + 383) / 384);
+    const int64_t min_units = mma ? kSplitNvMinStagesPrefill / 2 : kSplitNvMinStagesPrefill;
     int64_t S = kSplitNvWorkgroups / tiles_nv;
-    if (S > nst / kSplitNvMinStagesPrefill) S = nst / kSplitNvMinStagesPrefill;
+    if (S > nst / min_units) S = nst / min_units;
     if (2 * tiles_nv > kSplitNvWorkgroups && !force) S = 1;
     if (force && S < 2 && nst >= 2) S = 2;
     if (S <= 1) return none;
@@ -102,6 +108,7 @@ SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt, bool force)
 }
 
 int gemm_pick_variant(int64_t M, int64_t N, int64_t K, int fmt, int variant, size_t ws_bytes) {
+  // fmt may be kMXFP8Mma (the split plan tells the two MXFP8 contractions apart)
   // NVFP4 rows of K % 32 == 16 elements: decode schedules only, any M (in
   // 128-row slices past 128 rows); an explicit prefill request is refused
   const bool half_k = fmt == kNVFP4 && (K / 2) % 16 != 0;

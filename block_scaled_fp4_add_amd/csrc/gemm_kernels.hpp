@@ -202,6 +202,18 @@ __device__ __forceinline__ v16f mfma_mx(u32x4 a, u32x4 b, v16f acc, uint32_t sa,
                                                          (int)sb);
 }
 
+// Scaled FP8 (E4M3) MFMA: a lane's 32 bytes are the two 16-byte halves a0, a1
+// (b0, b1); scale byte S of sa / sb.  SWAP: B is the row operand, so the
+// accumulator holds the transposed tile (the split-K partial layout).
+template <int S, bool SWAP>
+__device__ __forceinline__ v16f mfma_f8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, v16f acc, uint32_t sa,
+                                        uint32_t sb) {
+  const v8i a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const v8i b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  if constexpr (SWAP) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, S, (int)sb, S, (int)sa);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, S, (int)sa, S, (int)sb);
+}
+
 // NVFP4 dequantization to fp16, exact.  An E2M1 value (2 significant bits)
 // times an E4M3 scale (4 significant bits) has at most 6 significant bits and
 // lies in [2^-10, 2688], so it is an fp16 normal number.  The E4M3 byte is
@@ -314,6 +326,26 @@ __device__ __forceinline__ void superstep_mma(v16f (&acc)[TI][TJ], const Frag (&
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
     }
   }
+}
+
+// MXFP8 on the 128-byte-stage prefill schedule: step Q of a superstep (128
+// FP8 elements of a row, 32-element blocks 4s .. 4s + 3 of superstep s) is one
+// scaled FP8 MFMA per tile pair.  The instruction's first K block is the
+// first 16 bytes (x0) of both lane halves, its second the last 16 (x1), and
+// lane half c supplies the scale of block c: so x0 of lane half c is the
+// 16 bytes [16c, 16c + 16) of block 2Q and x1 those of block 2Q + 1 (the
+// fragments of the stage's quarters 2Q and 2Q + 1), and lane half c's scale
+// word, shifted by 8c, holds block 2Q + c at byte 2Q.
+// (SW: the scale word type; only SfWord<kMXFP8> reaches a launch)
+template <int Q, bool SWAP, int TI, int TJ, class SW>
+__device__ __forceinline__ void step_f8(v16f (&acc)[TI][TJ], const u32x4 (&a0)[TI], const u32x4 (&a1)[TI],
+                                        const u32x4 (&b0)[TJ], const u32x4 (&b1)[TJ], const SW (&sa)[TI],
+                                        const SW (&sb)[TJ]) {
+#pragma unroll
+  for (int i = 0; i < TI; i++)
+#pragma unroll
+    for (int j = 0; j < TJ; j++)
+      acc[i][j] = mfma_f8<2 * Q, SWAP>(a0[i], a1[i], b0[j], b1[j], acc[i][j], sa[i].w, sb[j].w);
 }
 
 // acc[i][j] += quarter S (bytes 16S..16S+15 of each lane's 64) of a superstep:
@@ -930,16 +962,27 @@ template <int FMT> struct PrefillTileN {
 };
 __device__ __forceinline__ int w_off(int row, int chunk) { return row * kSSBytes + ((chunk ^ w_swz(row)) << 4); }
 
-template <int FMT, int EPI, bool LA_TILED, bool LB_TILED>
+// MXFP8 (LINEAR scales, K % 128 == 0): a superstep is 128 FP8 elements of a
+// row, two scaled FP8 MFMA steps (step_f8).  SPLIT (MXFP8): workgroup (tile, y)
+// runs supersteps [y * g.per, (y + 1) * g.per) with B as the MFMA row operand
+// and writes its fp32 partial tiles to the workspace in the reduce pass's
+// layout: tile (y, n / 32, m / 32) at ((y * ceil(N / 32) + n / 32) * ceil(M / 32)
+// + m / 32) * 1024 floats, lane (r, c) holding row r and columns
+// 8(k / 4) + 4c + k % 4.
+template <int FMT, int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false>
 __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g) {
+  constexpr bool F8 = FMT == kMXFP8;
+  static_assert(!F8 || (!LA_TILED && !LB_TILED), "MXFP8 operands take LINEAR scales");
+  static_assert(!SPLIT || F8, "the split form is built for MXFP8");
   constexpr int BN = PrefillTileN<FMT>::kCols;
   constexpr int TI = kPBM / kPWM / 32, TJ = BN / kPWN / 32;
   constexpr int kStage = (kPBM + BN) * kSSBytes;            // bytes of one superstep in LDS
   constexpr int kLoadsA = kPBM * kSSBytes / 16 / kPThreads;  // 16-byte DMAs per thread: A rows
   constexpr int kLoadsAB = kStage / 16 / kPThreads;            // ... A and B rows
-  // scale bytes of a superstep: one 256-byte group per 32 rows and 8 blocks
-  constexpr int kSfGrp = (FMT == kMXFP4) ? 1 : 2;            // 8-block groups per superstep
-  constexpr int SFA = kPBM / 32 * 256 * kSfGrp, SFB = SFA + BN / 32 * 256 * kSfGrp;
+  // scale bytes of a row and superstep: MXFP4 8 blocks, NVFP4 16, MXFP8 4
+  // (in the TILED layout one 256-byte group per 32 rows and 8 blocks)
+  constexpr int SFR = F8 ? 4 : (FMT == kMXFP4 ? 8 : 16);
+  constexpr int SFA = kPBM * SFR, SFB = SFA + BN * SFR;
   constexpr int SFLA = SFA / 4 / kPThreads, SFL = SFB / 4 / kPThreads;   // dword DMAs per thread
   static_assert(SFB % (4 * kPThreads) == 0 && kStage % (16 * kPThreads) == 0 && kLoadsAB <= kPLoads, "DMA split");
   // outstanding DMA instructions of one stage with its scales
@@ -965,10 +1008,14 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   const int64_t tn = (t % group) / gsz;
   const int m0 = (int)(tm * kPBM), n0 = (int)(tn * BN);
 
-  const int kbytes = (int)(g.K / 2);
-  const int nblk = (int)(g.K / (FMT == kMXFP4 ? 32 : 16));
+  const int kbytes = (int)(F8 ? g.K : g.K / 2);               // bytes of a packed row
+  const int nblk = (int)(g.K / (FMT == kNVFP4 ? 16 : 32));
   const int ktiles = (nblk + 7) >> 3;
-  const int nss = (int)((g.K + 255) / 256);
+  const int nss = (kbytes + kSSBytes - 1) / kSSBytes;          // supersteps of 128 row bytes
+  // this workgroup's supersteps [s0, send) and the row bytes they cover
+  const int s0 = SPLIT ? (int)blockIdx.y * g.per : 0;
+  const int send = SPLIT ? min(nss, s0 + g.per) : nss;
+  const int kend = min(kbytes, send * kSSBytes);
   const int M = (int)g.M, N = (int)g.N;
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, M * kbytes, 0x00020000);
@@ -1013,7 +1060,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   // is range-checked, and the superstep's advance in the scalar offset would
   // otherwise reach past the end of the buffer on its last row.
   auto prefetch = [&](int k) {
-    const bool ok = k < nss;   // uniform
+    const bool ok = k < send;   // uniform
     const int so = ok ? k * kSSBytes : 0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)pf_lds, 4, ok ? pf_a : kAbsent, so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)pf_lds, 4, ok ? pf_b : kAbsent, so, 0, 0);
@@ -1028,7 +1075,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     uint8_t* slot = smem + (k & 1) * kStage;
 #pragma unroll
     for (int i = 0; i < kLoadsAB; i++) {
-      const int voff = (so + chunk_off[i] + 16 <= kbytes) ? base_off[i] + so : kAbsent;
+      const int voff = (so + chunk_off[i] + 16 <= kend) ? base_off[i] + so : kAbsent;
       lds_ptr_t dst = (lds_ptr_t)(slot + (i * kPThreads + wave * 64) * 16);
       if (i < kLoadsA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, dst, 16, voff, 0, 0, 0);
@@ -1047,7 +1094,13 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
         const bool tiled = is_a ? la_t : lb_t;   // compile-time per q
         int vt, vl;
         bool okt, okl;
-        if constexpr (FMT == kMXFP4) {
+        if constexpr (F8) {   // LINEAR: one word (4 blocks) of a row per superstep
+          const int gr = row0 + dd;
+          okt = false;
+          vt = 0;
+          okl = ss < send && gr < R;
+          vl = gr * nblk + 4 * ss;
+        } else if constexpr (FMT == kMXFP4) {
           const int grp = (row0 >> 5) + (dd >> 6);
           okt = ss < nss && grp * 32 < R;
           vt = ((grp * ktiles + ss) << 8) + ((dd & 63) << 2);
@@ -1086,7 +1139,10 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     const int G = is_a ? kPBM / 32 : BN / 32;
     const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
     const bool tiled = is_a ? la_t : lb_t;
-    if constexpr (FMT == kMXFP4) {
+    if constexpr (F8) {
+      const int gr = row0 + dd;
+      sf_voff[q] = gr < R ? gr * nblk : kAbsent;
+    } else if constexpr (FMT == kMXFP4) {
       const int grp = (row0 >> 5) + (dd >> 6);
       const int gr = row0 + (dd >> 1);
       sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles) << 8) + ((dd & 63) << 2) : kAbsent)
@@ -1115,7 +1171,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       // scalar advance per superstep: one 256-byte group column (MXFP4) or two
       // (NVFP4) in the tiled layout, 8 or 16 bytes of a row in the linear one
       const int adv_t = (FMT == kMXFP4) ? (ss << 8) : (ss << 9);
-      const int adv_l = (FMT == kMXFP4) ? (ss << 3) : (ss << 4);
+      const int adv_l = F8 ? (ss << 2) : (FMT == kMXFP4) ? (ss << 3) : (ss << 4);
       const int soa = la_t ? adv_t : adv_l, sob = lb_t ? adv_t : adv_l;
 #pragma unroll
       for (int q = 0; q < SFL; q++) {
@@ -1145,7 +1201,13 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
         const int grp = (side ? wn * TJ : wm * TI) + i;     // 32-row group inside the tile
         const int row = grp * 32 + r;
         SfWord<FMT>& o = side ? xb[i] : xa[i];
-        if constexpr (FMT == kMXFP4) {
+        if constexpr (F8) {
+          // blocks 4ss .. 4ss + 3 of the row; lane half c takes block 2Q + c
+          // in step Q, found at byte 2Q once the word is shifted by 8c
+          // (every superstep is whole: K % 128 == 0)
+          o.w = *reinterpret_cast<const uint32_t*>(area + row * 4) >> (8 * c);
+          (void)tiled;
+        } else if constexpr (FMT == kMXFP4) {
           const int a0 = tiled ? grp * 256 + (c * 32 + r) * 4 : row * 8;
           const uint32_t lo = *reinterpret_cast<const uint32_t*>(area + a0);
           uint32_t w = lo;    // tiled: the word is the lane's four blocks
@@ -1175,10 +1237,10 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   };
 
   // quarter Q of superstep k: the lane's 16 bytes at 64(Q/2) + 32c + 16(Q%2)
-  // of each 128-byte row
+  // of each 128-byte row; MXFP8 at 64(Q/2) + 16c + 32(Q%2) (step_f8)
   auto frags = [&](int k, int s, u32x4 (&qa)[TI], u32x4 (&qb)[TJ]) {
     const uint8_t* base = smem + (k & 1) * kStage;
-    const int ch = 4 * (s >> 1) + 2 * c + (s & 1);
+    const int ch = F8 ? 4 * (s >> 1) + c + 2 * (s & 1) : 4 * (s >> 1) + 2 * c + (s & 1);
     // order of first use by quarter_mma (i outer, j inner): a0, b0..b3, a1..a3
     qa[0] = *reinterpret_cast<const u32x4*>(base + w_off(wm * TI * 32 + r, ch));
 #pragma unroll
@@ -1194,7 +1256,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   // writes (another ring slot) from the reads, so it keeps them in that order.
   auto interleave = [&](auto dsr, auto vm) {
     constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
-    if constexpr (FMT == kMXFP4) {
+    if constexpr (FMT == kMXFP4 || F8) {
       constexpr int NR = TI + TJ;                              // MFMAs carrying reads
       constexpr int NV = TI * TJ - NR;                         // MFMAs that can carry DMAs
       constexpr int PER = (VM + NV - 1) / (NV > 0 ? NV : 1);   // DMAs per such MFMA
@@ -1241,15 +1303,17 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 
   SfWord<FMT> sa[TI], sb[TJ], sa_n[TI], sb_n[TJ];
   u32x4 qa[TI], qb[TJ], na[TI], nb[TJ];
-  issue(0, kWithSf{});
-  issue(1, kWithSf{});
-  prefetch(2);   // every stage is followed by kPf prefetch instructions
+  u32x4 qa2[TI], qb2[TJ], na2[TI], nb2[TJ];   // MXFP8: quarters 2 and 3 (step 1)
+  issue(s0, kWithSf{});
+  issue(s0 + 1, kWithSf{});
+  prefetch(s0 + 2);   // every stage is followed by kPf prefetch instructions
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm_le_lgkm0<kInFlight1 + kPf>();   // superstep 0 has landed (1 may be in flight)
+  wait_vm_le_lgkm0<kInFlight1 + kPf>();   // superstep s0 has landed (s0 + 1 may be in flight)
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_sf(0, sa, sb, std::true_type{});
-  frags(0, 0, qa, qb);
+  read_sf(s0, sa, sb, std::true_type{});
+  frags(s0, 0, qa, qb);
+  if constexpr (F8) frags(s0, 1, na, nb);
   v8h va[TI], vb[TJ];   // NVFP4: the next MFMA step's dequantized operands
   if constexpr (FMT == kNVFP4) {
 #pragma unroll
@@ -1258,12 +1322,47 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][0], nv_part(sb[j], 0));
   }
   // supersteps whose refill (superstep ss + 2, scales included) lies wholly
-  // inside K: (ss + 3) * 256 <= K
-  const int nfast = max(0, min(nss, (int)(g.K / 256) - 2));
+  // inside this workgroup's K: ss + 2 < min(send, whole supersteps of K)
+  const int nfast = max(s0, min(send, kbytes / kSSBytes) - 2);
   // superstep ss from slot ss % 2: quarters 0-2, then one barrier (superstep
   // ss + 1 has landed; every wave is done with slot ss % 2, whose last
   // quarter is already in registers), then quarter 3 reads superstep ss + 1
   // and refills slot ss % 2 with superstep ss + 2
+  using I3 = std::integral_constant<int, 3>;
+  // MXFP8: on entry (qa, qb) and (na, nb) hold quarters 0 and 1 of superstep
+  // ss; step 0 runs on them while quarters 2 and 3 are read, then (after the
+  // barrier) step 1 runs on those while the next superstep's quarters 0 and 1
+  // and its scale words are read and slot ss % 2 is refilled
+  auto superstep_f8 = [&](int ss, auto fast) {
+    constexpr bool F = decltype(fast)::value;
+    frags(ss, 2, qa2, qb2);
+    frags(ss, 3, na2, nb2);
+    step_f8<0, SPLIT>(acc, qa, na, qb, nb, sa, sb);
+    interleave(I2{}, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    if (F || ss == nfast) stage_barrier(std::integral_constant<int, kPf>{});
+    else stage_barrier(std::integral_constant<int, 0>{});
+    if constexpr (F) {
+      read_sf(ss + 1, sa_n, sb_n, std::false_type{});
+      frags(ss + 1, 0, qa, qb);
+      frags(ss + 1, 1, na, nb);
+      issue_fast(ss + 2, kWithSf{});
+      prefetch(ss + 3);
+    } else {
+      issue(ss + 2, kWithSf{});
+      __builtin_amdgcn_sched_barrier(0);
+      read_sf(ss + 1, sa_n, sb_n, std::false_type{});
+      frags(ss + 1, 0, qa, qb);
+      frags(ss + 1, 1, na, nb);
+    }
+    step_f8<1, SPLIT>(acc, qa2, na2, qb2, nb2, sa, sb);
+    if constexpr (F) interleave(I3{}, ILSP{}); else interleave(I3{}, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
+#pragma unroll
+    for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
+  };
   auto superstep = [&](int ss, auto fast) {
     constexpr bool F = decltype(fast)::value;
     frags(ss, 1, na, nb);
@@ -1321,17 +1420,46 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
 #pragma unroll
     for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
   };
-  int ss = 0;
-  for (; ss < nfast; ss++) superstep(ss, std::true_type{});
-  for (; ss < nss; ss++) superstep(ss, std::false_type{});
+  int ss = s0;
+  if constexpr (F8) {
+    for (; ss < nfast; ss++) superstep_f8(ss, std::true_type{});
+    for (; ss < send; ss++) superstep_f8(ss, std::false_type{});
+  } else {
+    for (; ss < nfast; ss++) superstep(ss, std::true_type{});
+    for (; ss < nss; ss++) superstep(ss, std::false_type{});
+  }
   // the DMA issued past the end (zeros) lands before the epilogue reuses LDS
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
   __syncthreads();
 
+  if constexpr (SPLIT) {
+    // acc[i][j] is the transposed tile (B was the row operand): lane (r, c)
+    // holds row m of A tile i and columns 8(k / 4) + 4c + k % 4 of B tile j,
+    // the partial layout; tiles wholly past M or N are not part of it
+    const int64_t tn32 = (g.N + 31) / 32, tm32 = (g.M + 31) / 32;
+    const int64_t y = blockIdx.y;
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+      const int64_t mt = (m0 + wm * TI * 32) / 32 + i;
+#pragma unroll
+      for (int j = 0; j < TJ; j++) {
+        const int64_t nt = (n0 + wn * TJ * 32) / 32 + j;
+        if (mt < tm32 && nt < tn32) {
+          float4* p = reinterpret_cast<float4*>(g.ws + ((y * tn32 + nt) * tm32 + mt) * 1024 + lane * 16);
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            p[q] = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      }
+    }
+    return;
+  }
   epi_wave<EPI, TI, TJ>(acc, reinterpret_cast<float*>(smem) + wave * 32 * kEpiRowPitch, m0 + wm * TI * 32,
                         n0 + wn * TJ * 32, g, lane);
   if constexpr (EPI == kEpiBiasGeluFp4)
     fp4_out_padding(g, m0, m0 + kPBM, n0 / 16, (n0 + BN) / 16, n0 + BN >= g.N, tid, kPThreads);
+  if constexpr (EPI == kEpiFp8)
+    fp8_out_padding(g, m0, m0 + kPBM, n0 / 32, (n0 + BN) / 32, n0 + BN >= g.N, tid, kPThreads);
 }
 
 // ===========================================================================
@@ -1477,11 +1605,13 @@ __global__ __launch_bounds__(64) void gemm_splitk_reduce_kernel(GemmArgs g, int 
 
 #include "gemm_nv.hpp"
 
-template <int FMT, int EPI>
+template <int FMT, int EPI, bool SPLIT = false>
 void launch_w(const GemmArgs& g, dim3 block, hipStream_t s) {
   constexpr int BN = PrefillTileN<FMT>::kCols;
-  const dim3 grid((unsigned)(((g.M + kPBM - 1) / kPBM) * ((g.N + BN - 1) / BN)));
-  if (g.la == kTiled && g.lb == kTiled)
+  const dim3 grid((unsigned)(((g.M + kPBM - 1) / kPBM) * ((g.N + BN - 1) / BN)), SPLIT ? (unsigned)g.splits : 1u);
+  if constexpr (FMT == kMXFP8)   // LINEAR scales only
+    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, false, false, SPLIT>), grid, block, 0, s, g);
+  else if (g.la == kTiled && g.lb == kTiled)
     hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, true, true>), grid, block, 0, s, g);
   else if (g.la == kTiled)
     hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, true, false>), grid, block, 0, s, g);
@@ -1550,11 +1680,19 @@ template <int FMT, int EPI>
 hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   if (variant == 0) return launch_decode_rows<FMT, EPI>(g, s);
   const int64_t T = ((g.M + kPBM - 1) / kPBM) * ((g.N + kPBN - 1) / kPBN);
-  // NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) operands run the 128 x 384
-  // schedule (every epilogue); otherwise MXFP8 operands and the FP8 output
-  // run the 64-byte-stage prefill kernel; the 128-byte-stage one fetches
-  // LINEAR scales with dword DMA, which needs the blocks per row to be a
-  // multiple of 4 and a 4-byte aligned base
+  // MXFP8 operands on the scaled FP8 MFMA (f8mma) with K % 128 == 0 run the
+  // 128-byte-stage schedule; NVFP4 (K % 64 == 0) and exact MXFP8 (K % 128
+  // == 0) operands the 128 x 384 schedule (every epilogue); otherwise MXFP8
+  // operands and the FP8 output run the 64-byte-stage prefill kernel.  The
+  // 128-byte-stage and 128 x 384 kernels fetch LINEAR scales as aligned
+  // words, which needs the blocks per row to be a multiple of 4 and a 4-byte
+  // aligned base
+  if constexpr (FMT == kMXFP8) {
+    if (g.f8mma && prefill_nv_ok<FMT>(g)) {
+      launch_w<FMT, EPI>(g, dim3(kPThreads), s);
+      return hipGetLastError();
+    }
+  }
   if constexpr (FMT == kNVFP4 || FMT == kMXFP8) {
     if (prefill_nv_ok<FMT>(g)) {
       launch_prefill_nv<FMT, EPI>(g, s);
@@ -1601,9 +1739,14 @@ template <int FMT, int EPI>
 hipError_t launch_splitk(const GemmArgs& g, hipStream_t s) {
   const int mt = (int)((g.M + 31) / 32);
   if constexpr (FMT == kNVFP4 || FMT == kMXFP8) {
-    if (g.split_nv) {   // partials from the 128 x 384 schedule, same reduce
+    if (g.split_nv) {   // partials from a prefill schedule, same reduce
       if (!prefill_nv_ok<FMT>(g)) return hipErrorInvalidValue;
-      launch_prefill_nv<FMT, kEpiNone, true>(g, s);
+      if constexpr (FMT == kMXFP8) {
+        if (g.f8mma) launch_w<FMT, kEpiNone, true>(g, dim3(kPThreads), s);   // 256 x 256, supersteps of 128
+        else launch_prefill_nv<FMT, kEpiNone, true>(g, s);                  // 128 x 384, stages of 64 bytes
+      } else {
+        launch_prefill_nv<FMT, kEpiNone, true>(g, s);
+      }
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((gemm_splitk_reduce_kernel<EPI>), dim3((unsigned)((g.N + 31) / 32), (unsigned)mt),

@@ -60,7 +60,9 @@ struct GemmArgs {
   float* ws;                  // split-K: fp32 partial tiles (device), else nullptr
   int splits;                 // split-K: workgroups along K per output tile
   int per;                    // split-K: K units per split (supersteps, or the stages of split_nv)
-  int split_nv;               // split-K on the 128 x 384 schedule (units: its 64-byte row stages)
+  int split_nv;               // split-K on a prefill schedule: 128 x 384 (units: its 64-byte row stages),
+                              // or with f8mma 256 x 256 (units: its supersteps of 128 elements)
+  int f8mma;                  // MXFP8 operands on the scaled FP8 MFMA (kMXFP8Mma), else exact bf16 dequantization
 };
 
 // Schedules: 0 decode, 1 prefill, 2 split-K decode (needs a workspace).
@@ -68,13 +70,15 @@ constexpr int kVariantSplitK = 2;
 
 // Split-K plan of a GEMM: `splits` workgroups along K per output tile (1: no
 // split), `per` K units each, `bytes` of workspace for the partials.  force:
-// at least two splits whenever K has two units.  nv: the 128 x 384 schedule
-// does the partial pass (units: its stages of 64 bytes of a row, 128 NVFP4 or
-// 64 MXFP8 elements) -- NVFP4 with 64 < M <= 128 and K % 64 == 0, and above
-// 128 rows NVFP4 (K % 64 == 0) or MXFP8 (K % 128 == 0) shapes with at most
-// 128 such tiles; else the decode schedule (M <= 128, units of one
+// at least two splits whenever K has two units.  nv: a prefill schedule does
+// the partial pass -- NVFP4 with 64 < M <= 128 and K % 64 == 0, and above 128
+// rows NVFP4 (K % 64 == 0) or MXFP8 (K % 128 == 0), on the 128 x 384 tiles
+// (units: stages of 64 bytes of a row, 128 NVFP4 or 64 MXFP8 elements);
+// above 128 rows kMXFP8Mma (K % 128 == 0) on the 256 x 256 tiles (units:
+// supersteps of 128 elements); above 128 rows only for shapes with at most
+// 128 such tiles.  Else the decode schedule (M <= 128, units of one
 // superstep).  Either way the partials are 32 x 32 fp32 tiles in one layout,
-// summed by the same reduce pass.
+// summed by the same reduce pass.  fmt: a GEMM format, kMXFP8Mma included.
 struct SplitPlan {
   int splits;
   int per;

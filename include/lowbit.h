@@ -86,7 +86,29 @@ typedef enum {
  *        448) on 32-element blocks ([FI] add_rmsnorm_fp4quant's E4M3 scale
  *        format at block size 32); packed like NVFP4.  Producer, quantizer and
  *        dequantizer only, LINEAR scales only; the GEMMs return LOWBIT_EINVAL. */
-typedef enum { LOWBIT_NVFP4 = 0, LOWBIT_MXFP4 = 1, LOWBIT_MXFP8 = 2, LOWBIT_NVFP4_B32 = 3 } lowbit_format;
+/* MXFP8_MMA: GEMM operands in the MXFP8 format (the same bytes and LINEAR
+ *        scales as LOWBIT_MXFP8; quantize them with LOWBIT_MXFP8), contracted
+ *        on gfx950's scaled FP8 MFMA instead of the exact bf16 path -- as
+ *        [WOA]'s MMA stage runs its block-scaled MXFP8 contraction on the
+ *        hardware MMA.  That instruction adds the products of a 32-element
+ *        block in a narrower window than fp32: products far below the block's
+ *        largest lose low bits.  Measured on the MI355X, the result differs
+ *        from the exact sum by at most 2^-11.4 * sum |a_k * b_k| (random codes
+ *        over the whole E4M3 range with block scales spread over 20 binades);
+ *        the parity bound of this format is |out - exact| <= 2^-7 |exact| +
+ *        2^-10 * sum |a_k * b_k|, against 1e-6 for the other formats.  A single
+ *        product per output stays exact.  GEMM entry points only (the
+ *        quantization side, lowbit_sf_bytes aside, returns LOWBIT_EINVAL);
+ *        above 128 rows with K % 128 == 0 and 4-byte aligned scales it runs
+ *        at about 2-3x the exact path, elsewhere (the decode shapes, other K)
+ *        it runs the exact path. */
+typedef enum {
+  LOWBIT_NVFP4 = 0,
+  LOWBIT_MXFP4 = 1,
+  LOWBIT_MXFP8 = 2,
+  LOWBIT_NVFP4_B32 = 3,
+  LOWBIT_MXFP8_MMA = 4
+} lowbit_format;
 /* LOWBIT_SF_SWZ128: the 128 x 4 swizzled scale layout of [FI]'s producer
  * (its swizzled output): rows grouped by 128 and blocks by 4, each tile 512
  * contiguous bytes, tiles row-tile major with ceil(K/B/4) tiles per row tile;

@@ -172,10 +172,12 @@ def compare_quantized(orc, fmt, gs, gpu_packed, gpu_sf, orc_packed, orc_sf, y, v
     return rep
 
 
-def gemm_within_tolerance(gpu, ref, l1):
-    """Elementwise GEMM tolerance rule; returns (ok_mask, worst ratio)."""
+def gemm_within_tolerance(gpu, ref, l1, l1_coef=1e-6):
+    """Elementwise GEMM tolerance rule; returns (ok_mask, worst ratio).
+    l1_coef: the accumulation term (1e-6; the scaled FP8 MFMA format states
+    a wider one)."""
     gpu = np.asarray(gpu, dtype=np.float64)
-    tol = 2.0 ** -7 * np.abs(ref) + 1e-6 * l1
+    tol = 2.0 ** -7 * np.abs(ref) + l1_coef * l1
     err = np.abs(gpu - ref)
     ok = err <= tol
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -213,13 +215,13 @@ def gather_mx8_scales(orc, sf, rows, nblk, layout):
     return sf[off], off
 
 
-def compare_fp8_out(orc, gpu_packed, gpu_sf, orc_packed, orc_sf, ref, l1, rows, N, layout):
+def compare_fp8_out(orc, gpu_packed, gpu_sf, orc_packed, orc_sf, ref, l1, rows, N, layout, l1_coef=1e-6):
     """Device FP8-output codes and scales against the oracle's under the
     interval rule above; reports exact matches and hard failures, and (for a
     padded layout) that every byte outside the covered blocks is zero."""
     nblk = N // 32
     ref = np.asarray(ref, dtype=np.float64)
-    e = 2.0 ** -22 * np.abs(ref) + 1e-6 * np.asarray(l1, dtype=np.float64)
+    e = 2.0 ** -22 * np.abs(ref) + l1_coef * np.asarray(l1, dtype=np.float64)
     lo = bf16_of_f32((ref - e).astype(np.float32))
     hi = bf16_of_f32((ref + e).astype(np.float32))
     straddle = (lo <= 0) & (hi >= 0)

@@ -88,16 +88,20 @@ def splitk_plan(M, N, K, fmt=1):
     supersteps (1024 elements) per split, K of at least 16 supersteps.  No
     empty split; bytes = splits x 32-column tiles x M-tiles x 32 x 32 floats."""
     tiles, mt = -(-N // 32), -(-M // 32)
+    mma = fmt == 4          # MXFP8 on the scaled FP8 MFMA
+    if mma:
+        fmt = 2
     if M > 128:
-        # above 128 rows: NVFP4 (K % 64 == 0, 128-element stages) or MXFP8
-        # (K % 128 == 0, 64-element stages) with at most 128 tiles of
-        # 128 x 384 split those, about one workgroup per CU, 16 stages or
-        # more each
+        # above 128 rows: NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) with at
+        # most 128 tiles of 128 x 384 split its stages of 64 row bytes (128 and
+        # 64 elements), 16 or more each; MXFP8 on the scaled FP8 MFMA with at
+        # most 128 tiles of 256 x 256 its 128-element supersteps, 8 or more
+        # each; about one workgroup per CU
         if not ((fmt == 0 and K % 64 == 0) or (fmt == 2 and K % 128 == 0)):
             return 1, 0
-        nst = K // 64 if fmt == 2 else -(-K // 128)
-        tnv = -(-M // 128) * -(-N // 384)
-        S = 1 if 2 * tnv > 256 else min(256 // tnv, nst // 16)
+        nst = K // 128 if mma else K // 64 if fmt == 2 else -(-K // 128)
+        tnv = -(-M // 256) * -(-N // 256) if mma else -(-M // 128) * -(-N // 384)
+        S = 1 if 2 * tnv > 256 else min(256 // tnv, nst // (8 if mma else 16))
         if S <= 1:
             return 1, 0
         per = -(-nst // S)
@@ -152,16 +156,20 @@ def test_splitk_workspace_and_choice(M, N, K):
     assert L.lowbit_gemm_pick_variant(200, N, K, 1, 2, 1 << 30) < 0
 
 
-@pytest.mark.parametrize("M,N,K,fmt", [(4096, 1024, 8192, 2), (4096, 1024, 8192, 0), (600, 1000, 4096, 0),
+@pytest.mark.parametrize("M,N,K,fmt", [(4096, 1024, 8192, 2), (4096, 1024, 8192, 4), (4096, 1024, 8192, 0),
+                                       (600, 1000, 4096, 0), (300, 770, 2048, 4), (4096, 1024, 8160, 4),
+                                       (2048, 7168, 4096, 4),
                                        (300, 770, 2048, 2), (2048, 5120, 17408, 0), (2048, 17408, 5120, 0),
                                        (8192, 4096, 14336, 1), (129, 96, 8192, 0), (4096, 1024, 8160, 2),
                                        (1000, 400, 4096 + 32, 0), (200, 384, 1024, 0), (257, 400, 4160, 0),
                                        (300, 400, 1984, 0)])
 def test_splitk_above_128_rows(M, N, K, fmt):
-    """Above 128 rows only NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0)
-    split, on the 128 x 384 tiles, and the automatic choice only with at most
-    128 such tiles: (4096, 1024, 8192) has 96 tiles and splits in two, the
-    chain's 2048-token GEMMs (224 and 736 tiles) and MXFP4 never do."""
+    """Above 128 rows only NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) split,
+    on the 128 x 384 tiles (MXFP8 on the scaled FP8 MFMA: 256 x 256), and the
+    automatic choice only with at most 128 such tiles: (4096, 1024, 8192) has
+    96 tiles of 128 x 384 and splits in two, 64 of 256 x 256 and splits in
+    four; the chain's 2048-token GEMMs (224 and 736 tiles) and MXFP4 never
+    do."""
     L = lb.lib()
     S, need = splitk_plan(M, N, K, fmt)
     assert L.lowbit_gemm_workspace_bytes(M, N, K, fmt, -1) == need
@@ -170,12 +178,14 @@ def test_splitk_above_128_rows(M, N, K, fmt):
         assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, need - 1) == 1   # too little: prefill
     else:
         assert L.lowbit_gemm_pick_variant(M, N, K, fmt, -1, 1 << 30) == 1
-    nv_ok = (fmt == 0 and K % 64 == 0) or (fmt == 2 and K % 128 == 0)
+    nv_ok = (fmt == 0 and K % 64 == 0) or (fmt in (2, 4) and K % 128 == 0)
     forced = L.lowbit_gemm_workspace_bytes(M, N, K, fmt, 2)
     assert (forced > 0) == nv_ok and forced >= need
     assert (L.lowbit_gemm_pick_variant(M, N, K, fmt, 2, 0) == 2) == nv_ok
-    if (M, N, K) == (4096, 1024, 8192):
+    if (M, N, K) == (4096, 1024, 8192) and fmt in (0, 2):
         assert S == 2 and need == 2 * 32 * 128 * 4096
+    if (M, N, K, fmt) == (4096, 1024, 8192, 4):
+        assert S == 4 and need == 4 * 32 * 128 * 4096
     if (M, N, K) == (257, 400, 4160):   # 33 stages, the last a half one: 2 splits of 17 and 16
         assert S == 2
     if (M, N) in ((2048, 5120), (2048, 17408)) or fmt == 1:
@@ -327,7 +337,11 @@ def test_gemm_argument_order(buf):
         return L.lowbit_gemm_bf16(a_, b, sa, sb, M, N, K, fmt, la, lb_, 1.0, o, variant, ws, wsb, None)
 
     assert call(8, 128, 256, fmt=3) == EINVAL                # 32-block NVFP4: no GEMM
-    assert call(8, 128, 256, fmt=4) == EINVAL
+    assert call(8, 128, 256, fmt=5) == EINVAL
+    assert call(8, 128, 256, fmt=4, la=1) == EINVAL          # MXFP8 on the FP8 MFMA: LINEAR scales only
+    assert call(8, 128, 48, fmt=4) == ESHAPE                 # ... K % 32
+    assert L.lowbit_sf_bytes(33, 5120, 4, 0) == L.lowbit_sf_bytes(33, 5120, 2, 0) == 33 * 160
+    assert quant(L, buf, 4, 64, fmt=4) == EINVAL             # a GEMM format only
     assert call(8, 128, 256, la=2) == EINVAL                 # 128 x 4 swizzle: no GEMM
     assert call(8, 128, 256, fmt=2, la=1) == EINVAL          # MXFP8 operands: LINEAR scales only
     assert call(8, 128, 256, fmt=2, lb_=1) == EINVAL

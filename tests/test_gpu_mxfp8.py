@@ -120,22 +120,25 @@ def test_mxfp8_dequantization_is_exact(orc, M, N, K, variant):
 
 # --- FP8-output epilogue ---------------------------------------------------------------------
 
-def run_fp8_out(orc, M, N, K, fmt, variant, out_layout, seed, alpha=0.75):
+def run_fp8_out(orc, M, N, K, fmt, variant, out_layout, seed, alpha=0.75, l1_coef=1e-6):
     banner(f"gemm_fp8 M={M} N={N} K={K} fmt={fmt} variant={variant} out_layout={out_layout} seed={seed}")
-    la, lb_ = (0, 0) if fmt == F8 else (0, 1)
-    a, sfa, b, sfb = operands(orc, M, N, K, fmt, la, lb_, seed, outliers=True)
+    ofmt = F8 if fmt == lb.MXFP8_MMA else fmt     # the oracle's format
+    la, lb_ = (0, 0) if ofmt == F8 else (0, 1)
+    a, sfa, b, sfb = operands(orc, M, N, K, ofmt, la, lb_, seed, outliers=True)
     ws = split_workspace(M, N, K, fmt, 2) if variant == 2 else None
-    p_ref, s_ref, ref, l1 = orc.gemm_fp8_out(a, b, sfa, sfb, M, N, K, fmt, la, lb_, alpha, out_layout, diag=True)
+    p_ref, s_ref, ref, l1 = orc.gemm_fp8_out(a, b, sfa, sfb, M, N, K, ofmt, la, lb_, alpha, out_layout, diag=True)
     p, s = lb.lowbit_gemm_fp8(dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb), fmt=fmt, sfa_layout=la,
                               sfb_layout=lb_, alpha=alpha, out_layout=out_layout, variant=variant, workspace=ws)
     torch.cuda.synchronize()
     assert tuple(p.shape) == (M, N) and s.numel() == s_ref.size
-    rep = checkers.compare_fp8_out(orc, host_u8(p), host_u8(s), p_ref, s_ref, ref, l1, M, N, out_layout)
+    rep = checkers.compare_fp8_out(orc, host_u8(p), host_u8(s), p_ref, s_ref, ref, l1, M, N, out_layout, l1_coef)
     banner(f"  report {dict(rep)}")
     assert rep.ok(), rep
     # the interval rule admits a neighbour only where the fp32 sum sits next
-    # to a rounding boundary: nearly every byte matches the oracle's
-    assert rep["code_diff"] <= max(8, M * N // 500) and rep["scale_diff"] <= max(2, rep["blocks"] // 500)
+    # to a rounding boundary: nearly every byte matches the oracle's (the
+    # scaled FP8 MFMA's wider accumulation term admits more)
+    if l1_coef <= 1e-6:
+        assert rep["code_diff"] <= max(8, M * N // 500) and rep["scale_diff"] <= max(2, rep["blocks"] // 500)
 
 
 FP8_OUT_SHAPES = [(1, 64, 256), (33, 288, 512), (130, 160, 320), (96, 4096, 512), (1, 8224, 256), (128, 160, 1024),
