@@ -378,42 +378,6 @@ __device__ __forceinline__ void quarter_mma(v16f (&acc)[TI][TJ], const u32x4 (&q
   }
 }
 
-// NVFP4 quarter S, software-pipelined: on entry va / vb hold step 0 of this
-// quarter already dequantized; each step t issues its 16 MFMAs while the
-// dequantization of step t + 1 (for t = 3: step 0 of the next quarter, from
-// its fragments xa / xb and scales xsa / xsb, block 2 SN) runs beside them.
-template <int S, int SN, int TI, int TJ>
-__device__ __forceinline__ void quarter_nv(v16f (&acc)[TI][TJ], const u32x4 (&qa)[TI], const u32x4 (&qb)[TJ],
-                                           const SfWord<kNVFP4> (&sa)[TI], const SfWord<kNVFP4> (&sb)[TJ],
-                                           v8h (&va)[TI], v8h (&vb)[TJ], const u32x4 (&xa)[TI],
-                                           const u32x4 (&xb)[TJ], const SfWord<kNVFP4> (&xsa)[TI],
-                                           const SfWord<kNVFP4> (&xsb)[TJ]) {
-#pragma unroll
-  for (int t = 0; t < 4; t++) {
-    v8h na[TI], nb[TJ];
-    if (t < 3) {
-#pragma unroll
-      for (int i = 0; i < TI; i++) na[i] = dq8(qa[i][t + 1], nv_part(sa[i], 2 * S + ((t + 1) >> 1)));
-#pragma unroll
-      for (int j = 0; j < TJ; j++) nb[j] = dq8(qb[j][t + 1], nv_part(sb[j], 2 * S + ((t + 1) >> 1)));
-    } else {
-#pragma unroll
-      for (int i = 0; i < TI; i++) na[i] = dq8(xa[i][0], nv_part(xsa[i], 2 * SN));
-#pragma unroll
-      for (int j = 0; j < TJ; j++) nb[j] = dq8(xb[j][0], nv_part(xsb[j], 2 * SN));
-    }
-#pragma unroll
-    for (int i = 0; i < TI; i++)
-#pragma unroll
-      for (int j = 0; j < TJ; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < TI; i++) va[i] = na[i];
-#pragma unroll
-    for (int j = 0; j < TJ; j++) vb[j] = nb[j];
-  }
-}
-
 // ---------------------------------------------------------------------------
 // FP4-out epilogue of one 16-element NVFP4 block of output row m (columns
 // n .. n+15, n a multiple of 16): GELU of the pre-activations z, the block
@@ -953,12 +917,11 @@ __device__ __forceinline__ void wait_vm_le_lgkm0() {
 // last quarter runs.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int w_swz(int row) { return (row >> 1) & 7; }
-// tile columns: NVFP4 192 (spreads the NVFP4 chain's shapes more evenly over
-// the CUs; NVFP4 is bound by its fp16 MFMAs and dequantization, not by L2
-// traffic), MXFP4 256
+// tile columns (MXFP4 and MXFP8 operands; NVFP4 runs the 128 x 384 schedule
+// or, for K % 64 != 0, the 64-byte-stage one)
 template <int FMT> struct PrefillTileN {
-  static constexpr int kCols = (FMT == kNVFP4) ? 192 : 256;
-  static_assert(kCols % 64 == 0 && kCols <= 256, "tile width");
+  static_assert(FMT != kNVFP4, "NVFP4 prefill runs other schedules");
+  static constexpr int kCols = 256;
 };
 __device__ __forceinline__ int w_off(int row, int chunk) { return row * kSSBytes + ((chunk ^ w_swz(row)) << 4); }
 
@@ -979,9 +942,9 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   constexpr int kStage = (kPBM + BN) * kSSBytes;            // bytes of one superstep in LDS
   constexpr int kLoadsA = kPBM * kSSBytes / 16 / kPThreads;  // 16-byte DMAs per thread: A rows
   constexpr int kLoadsAB = kStage / 16 / kPThreads;            // ... A and B rows
-  // scale bytes of a row and superstep: MXFP4 8 blocks, NVFP4 16, MXFP8 4
-  // (in the TILED layout one 256-byte group per 32 rows and 8 blocks)
-  constexpr int SFR = F8 ? 4 : (FMT == kMXFP4 ? 8 : 16);
+  // scale bytes of a row and superstep: MXFP4 8 blocks, MXFP8 4 (in the
+  // TILED layout one 256-byte group per 32 rows and 8 blocks)
+  constexpr int SFR = F8 ? 4 : 8;
   constexpr int SFA = kPBM * SFR, SFB = SFA + BN * SFR;
   constexpr int SFLA = SFA / 4 / kPThreads, SFL = SFB / 4 / kPThreads;   // dword DMAs per thread
   static_assert(SFB % (4 * kPThreads) == 0 && kStage % (16 * kPThreads) == 0 && kLoadsAB <= kPLoads, "DMA split");
@@ -1009,7 +972,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   const int m0 = (int)(tm * kPBM), n0 = (int)(tn * BN);
 
   const int kbytes = (int)(F8 ? g.K : g.K / 2);               // bytes of a packed row
-  const int nblk = (int)(g.K / (FMT == kNVFP4 ? 16 : 32));
+  const int nblk = (int)(g.K / 32);
   const int ktiles = (nblk + 7) >> 3;
   const int nss = (kbytes + kSSBytes - 1) / kSSBytes;          // supersteps of 128 row bytes
   // this workgroup's supersteps [s0, send) and the row bytes they cover
@@ -1090,7 +1053,6 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
         const bool is_a = q < SFLA;              // the first SFLA dwords: A (uniform)
         const int dd = (is_a ? q : q - SFLA) * kPThreads + tid;
         const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
-        const int G = is_a ? kPBM / 32 : BN / 32;   // 32-row groups of this side
         const bool tiled = is_a ? la_t : lb_t;   // compile-time per q
         int vt, vl;
         bool okt, okl;
@@ -1100,21 +1062,13 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
           vt = 0;
           okl = ss < send && gr < R;
           vl = gr * nblk + 4 * ss;
-        } else if constexpr (FMT == kMXFP4) {
+        } else {   // MXFP4: two words (8 blocks) of a row, or a 256-byte TILED group per 32 rows
           const int grp = (row0 >> 5) + (dd >> 6);
           okt = ss < nss && grp * 32 < R;
           vt = ((grp * ktiles + ss) << 8) + ((dd & 63) << 2);
           const int gr = row0 + (dd >> 1);
           okl = ss < nss && gr < R;
           vl = gr * nblk + 8 * ss + 4 * (dd & 1);
-        } else {
-          const int tile = 2 * ss + dd / (G * 64);
-          const int grp = (row0 >> 5) + (dd % (G * 64)) / 64;
-          okt = tile < ktiles && grp * 32 < R;
-          vt = ((grp * ktiles + tile) << 8) + ((dd & 63) << 2);
-          const int gr = row0 + (dd >> 2);
-          okl = ss < nss && gr < R;
-          vl = gr * nblk + 16 * ss + 4 * (dd & 3);
         }
         const int voff = tiled ? (okt ? vt : kAbsent) : (okl ? vl : kAbsent);
         lds_ptr_t dst = (lds_ptr_t)(sfs + (q * kPThreads + wave * 64) * 4);
@@ -1136,22 +1090,16 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   for (int q = 0; q < SFL; q++) {
     const bool is_a = q < SFLA;
     const int dd = (is_a ? q : q - SFLA) * kPThreads + tid;
-    const int G = is_a ? kPBM / 32 : BN / 32;
     const int row0 = is_a ? m0 : n0, R = is_a ? M : N;
     const bool tiled = is_a ? la_t : lb_t;
     if constexpr (F8) {
       const int gr = row0 + dd;
       sf_voff[q] = gr < R ? gr * nblk : kAbsent;
-    } else if constexpr (FMT == kMXFP4) {
+    } else {
       const int grp = (row0 >> 5) + (dd >> 6);
       const int gr = row0 + (dd >> 1);
       sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles) << 8) + ((dd & 63) << 2) : kAbsent)
                          : (gr < R ? gr * nblk + 4 * (dd & 1) : kAbsent);
-    } else {
-      const int grp = (row0 >> 5) + (dd % (G * 64)) / 64;
-      const int gr = row0 + (dd >> 2);
-      sf_voff[q] = tiled ? (grp * 32 < R ? ((grp * ktiles + dd / (G * 64)) << 8) + ((dd & 63) << 2) : kAbsent)
-                         : (gr < R ? gr * nblk + 4 * (dd & 3) : kAbsent);
     }
   }
   auto issue_fast = [&](int k, auto with_sf) {
@@ -1168,10 +1116,10 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     if constexpr (decltype(with_sf)::value) {
       const int ss = k;
       uint8_t* sfs = sf_lds + (ss & 1) * SFB;
-      // scalar advance per superstep: one 256-byte group column (MXFP4) or two
-      // (NVFP4) in the tiled layout, 8 or 16 bytes of a row in the linear one
-      const int adv_t = (FMT == kMXFP4) ? (ss << 8) : (ss << 9);
-      const int adv_l = F8 ? (ss << 2) : (FMT == kMXFP4) ? (ss << 3) : (ss << 4);
+      // scalar advance per superstep: one 256-byte group column in the tiled
+      // layout, 8 (MXFP4) or 4 (MXFP8) bytes of a row in the linear one
+      const int adv_t = ss << 8;
+      const int adv_l = F8 ? (ss << 2) : (ss << 3);
       const int soa = la_t ? adv_t : adv_l, sob = lb_t ? adv_t : adv_l;
 #pragma unroll
       for (int q = 0; q < SFL; q++) {
@@ -1189,13 +1137,11 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   auto read_sf = [&](int ss, SfWord<FMT> (&xa)[TI], SfWord<FMT> (&xb)[TJ], auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     const uint8_t* sfs = sf_lds + (ss & 1) * SFB;
-    const int blk_per_ss = (FMT == kMXFP4) ? 8 : 16;
-    const int left = nblk - ss * blk_per_ss;   // blocks of this superstep that exist
+    const int left = nblk - ss * 8;   // MXFP4 blocks of this superstep that exist
 #pragma unroll
     for (int side = 0; side < 2; side++) {
       const bool tiled = side ? lb_t : la_t;
       const uint8_t* area = sfs + side * SFA;
-      const int G = side ? BN / 32 : kPBM / 32;       // 32-row groups of this side
 #pragma unroll
       for (int i = 0; i < (side ? TJ : TI); i++) {
         const int grp = (side ? wn * TJ : wm * TI) + i;     // 32-row group inside the tile
@@ -1207,7 +1153,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
           // (every superstep is whole: K % 128 == 0)
           o.w = *reinterpret_cast<const uint32_t*>(area + row * 4) >> (8 * c);
           (void)tiled;
-        } else if constexpr (FMT == kMXFP4) {
+        } else {
           const int a0 = tiled ? grp * 256 + (c * 32 + r) * 4 : row * 8;
           const uint32_t lo = *reinterpret_cast<const uint32_t*>(area + a0);
           uint32_t w = lo;    // tiled: the word is the lane's four blocks
@@ -1218,19 +1164,6 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
             w = absent ? (w & ~(0xFFu << (8 * j))) | (0x7Fu << (8 * j)) : w;
           }
           o.w = w;
-        } else {
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            // one aligned word in both layouts: no byte shuffling
-            const int a0 = tiled ? h * (G * 256) + grp * 256 + (c * 32 + r) * 4 : row * 16 + 8 * h + 4 * c;
-            uint32_t w = *reinterpret_cast<const uint32_t*>(area + a0);
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-              const bool absent = MASK && 8 * h + 4 * c + j >= left;
-              w = absent ? (w & ~(0xFFu << (8 * j))) : w;
-            }
-            o.w[h] = w;
-          }
         }
       }
     }
@@ -1271,28 +1204,10 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       }
     }
   };
-  // NVFP4: one MFMA, then a share of the dequantization VALU work (about 6.5
-  // VALU ops per MFMA in the steady state: groups of 7 measured best), and one
-  // LDS read per MFMA until DSR are issued, then one DMA per MFMA until VM
-  // are (reads before DMAs, as above)
-  auto interleave_nv = [&](auto dsr, auto vm) {
-    constexpr int DSR = decltype(dsr)::value, VM = decltype(vm)::value;
-    if constexpr (FMT == kNVFP4) {
-#pragma unroll
-      for (int k = 0; k < 4 * TI * TJ; k++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
-        if (k < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one LDS read
-        else if (k < DSR + VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one DMA
-      }
-    }
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using ILSP = std::integral_constant<int, kLoadsAB + SFL + kPf>;
-  using IF = std::integral_constant<int, TI + TJ>;           // fragment reads of a quarter
-  using IFS = std::integral_constant<int, 4 * (TI + TJ)>;    // fragment + scale reads
   // VM: DMA instructions issued after the stage being waited for (the prefetch)
   auto stage_barrier = [&](auto vm) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1314,13 +1229,6 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   read_sf(s0, sa, sb, std::true_type{});
   frags(s0, 0, qa, qb);
   if constexpr (F8) frags(s0, 1, na, nb);
-  v8h va[TI], vb[TJ];   // NVFP4: the next MFMA step's dequantized operands
-  if constexpr (FMT == kNVFP4) {
-#pragma unroll
-    for (int i = 0; i < TI; i++) va[i] = dq8(qa[i][0], nv_part(sa[i], 0));
-#pragma unroll
-    for (int j = 0; j < TJ; j++) vb[j] = dq8(qb[j][0], nv_part(sb[j], 0));
-  }
   // supersteps whose refill (superstep ss + 2, scales included) lies wholly
   // inside this workgroup's K: ss + 2 < min(send, whole supersteps of K)
   const int nfast = max(s0, min(send, kbytes / kSSBytes) - 2);
@@ -1366,31 +1274,16 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   auto superstep = [&](int ss, auto fast) {
     constexpr bool F = decltype(fast)::value;
     frags(ss, 1, na, nb);
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<0, 1>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
-      interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
-      interleave(I1{}, I0{});
-    }
+    quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
+    interleave(I1{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
     frags(ss, 2, qa, qb);
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<1, 2>(acc, na, nb, sa, sb, va, vb, qa, qb, sa, sb);
-      interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
-      interleave(I1{}, I0{});
-    }
+    quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
+    interleave(I1{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
     frags(ss, 3, na, nb);
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<2, 3>(acc, qa, qb, sa, sb, va, vb, na, nb, sa, sb);
-      interleave_nv(IF{}, I0{});
-    } else {
-      quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
-      interleave(I1{}, I0{});
-    }
+    quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
+    interleave(I1{}, I0{});
     // superstep ss + 1 was issued by the previous superstep (or the prologue)
     // and followed by kPf prefetch instructions when that one was a
     // steady-state superstep (the prologue always prefetches)
@@ -1407,13 +1300,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       read_sf(ss + 1, sa_n, sb_n, std::true_type{});
       frags(ss + 1, 0, qa, qb);
     }
-    if constexpr (FMT == kNVFP4) {
-      quarter_nv<3, 0>(acc, na, nb, sa, sb, va, vb, qa, qb, sa_n, sb_n);
-      if constexpr (F) interleave_nv(IFS{}, ILSP{}); else interleave_nv(IFS{}, I0{});
-    } else {
-      quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
-      if constexpr (F) interleave(I2{}, ILSP{}); else interleave(I2{}, I0{});
-    }
+    quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
+    if constexpr (F) interleave(I2{}, ILSP{}); else interleave(I2{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TI; i++) sa[i] = sa_n[i];
@@ -1682,11 +1570,11 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   const int64_t T = ((g.M + kPBM - 1) / kPBM) * ((g.N + kPBN - 1) / kPBN);
   // MXFP8 operands on the scaled FP8 MFMA (f8mma) with K % 128 == 0 run the
   // 128-byte-stage schedule; NVFP4 (K % 64 == 0) and exact MXFP8 (K % 128
-  // == 0) operands the 128 x 384 schedule (every epilogue); otherwise MXFP8
-  // operands and the FP8 output run the 64-byte-stage prefill kernel.  The
-  // 128-byte-stage and 128 x 384 kernels fetch LINEAR scales as aligned
-  // words, which needs the blocks per row to be a multiple of 4 and a 4-byte
-  // aligned base
+  // == 0) operands the 128 x 384 schedule (every epilogue); other NVFP4 and
+  // MXFP8 operands the 64-byte-stage prefill kernel, MXFP4 the 128-byte-stage
+  // one.  The 128-byte-stage and 128 x 384 kernels fetch LINEAR scales as
+  // aligned words, which needs the blocks per row to be a multiple of 4 and a
+  // 4-byte aligned base (else the 64-byte-stage kernel)
   if constexpr (FMT == kMXFP8) {
     if (g.f8mma && prefill_nv_ok<FMT>(g)) {
       launch_w<FMT, EPI>(g, dim3(kPThreads), s);
@@ -1699,7 +1587,10 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if constexpr (FMT == kMXFP8 || EPI == kEpiFp8) {
+  if constexpr (FMT == kMXFP8 || FMT == kNVFP4) {
+    // (NVFP4 with K % 64 == 32 and TILED scales: 4096 x 4096 x 8224 and
+    // 2048 x 8192 x 4128 ran 288-298 / 151-153 us here against 348-352 /
+    // 182-184 us on the 128-byte-stage kernel)
     hipLaunchKernelGGL((gemm_prefill_v2_kernel<FMT, EPI>), dim3((unsigned)T), dim3(kPThreads), 0, s, g);
   } else {
     const int64_t nblk = g.K / FmtTraits<FMT>::B;
