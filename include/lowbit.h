@@ -129,9 +129,10 @@ typedef enum { LOWBIT_SF_LINEAR = 0, LOWBIT_SF_TILED = 1, LOWBIT_SF_SWZ128 = 2 }
  * workspace, which a second kernel sums in a fixed order (the result does not
  * depend on timing) before the epilogue.  M <= 128 (decode tiles, or NVFP4's
  * 128 x 384 tiles above 64 rows), or, above 128 rows, NVFP4 with K % 64 == 0
- * and MXFP8 with K % 128 == 0 on the 128 x 384 tiles (the automatic choice:
- * only when those tiles number at most 128, i.e. fill at most half the CUs).
- * Cf. [FRT] `variant`. */
+ * and MXFP8 with K % 128 == 0 on the 128 x 384 tiles, LOWBIT_MXFP8_MMA with
+ * K % 128 == 0 on its 256 x 256 tiles (the automatic choice: only when those
+ * tiles number at most 128, i.e. fill at most half the CUs).  MXFP4 splits
+ * only at M <= 128.  Cf. [FRT] `variant`. */
 #define LOWBIT_VARIANT_AUTO (-1)
 #define LOWBIT_VARIANT_DECODE 0
 #define LOWBIT_VARIANT_PREFILL 1
@@ -397,7 +398,8 @@ int lowbit_gemm_pick_variant(int64_t M, int64_t N, int64_t K, lowbit_format fmt,
 /* Workspace bytes the split-K schedule needs for these sizes: variant
  * LOWBIT_VARIANT_AUTO gives the amount that lets the automatic choice split
  * K (0 when it would not split: K too short for the tile count, more than
- * 128 rows in MXFP4 or in more than 128 tiles of 128 x 384),
+ * 128 rows in MXFP4, or more than 128 prefill tiles -- 128 x 384, or 256 x
+ * 256 for LOWBIT_MXFP8_MMA),
  * LOWBIT_VARIANT_SPLITK the amount an explicit split-K call needs (0 when it
  * cannot run); 0 for every other variant and for invalid sizes (cf. [FRT]
  * sfa_size_bytes, a size query beside the kernels).  Host-only. */
