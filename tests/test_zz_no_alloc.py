@@ -46,6 +46,25 @@ def test_noalloc_matches_workspace_entry(orc, variant):
         assert ok.all()
 
 
+def test_noalloc_mxfp8_mma(orc):
+    """MXFP8 on the scaled FP8 MFMA: its 256 x 256 split through the static
+    array gives the caller-workspace result, explicitly and automatically."""
+    M, N, K = 300, 400, 4096
+    A, W = synth.activation(M, K, 9, outliers=True), synth.weight(N, K, 9)
+    a, sfa = orc.quantize(synth.bits(A), orc.MXFP8, orc.LINEAR)
+    b, sfb = orc.quantize(synth.bits(W), orc.MXFP8, orc.LINEAR)
+    args = (dev_u8(a), dev_u8(b), dev_u8(sfa), dev_u8(sfb))
+    for variant in (lb.VARIANT_SPLITK, lb.VARIANT_AUTO):
+        banner(f"noalloc mxfp8 mma M={M} N={N} K={K} variant={variant}")
+        need = lb.lowbit_gemm_workspace_bytes(M, N, K, lb.MXFP8_MMA, variant)
+        assert 0 < need <= lb.STATIC_SCRATCH_BYTES
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+        want = lb.lowbit_gemm_bf16(*args, fmt=lb.MXFP8_MMA, variant=variant, workspace=ws)
+        got = lb.lowbit_gemm_bf16_noalloc(*args, fmt=lb.MXFP8_MMA, variant=variant)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
+
+
 def test_noalloc_refuses_plans_beyond_the_array(orc):
     """Forced split-K of a product whose partials need more than the static
     array: refused with LOWBIT_ESHAPE before any launch."""
