@@ -118,6 +118,7 @@ lowbit_status gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* sfa
   // EINVAL: enums and pointers
   if (!fmt_ok(fmt) || !gemm_layout_ok(fmt, la) || !gemm_layout_ok(fmt, lb)) return LOWBIT_EINVAL;
   if (fp4_out && !layout_ok(out_layout)) return LOWBIT_EINVAL;
+  if (fp4_out && fp8_fmt(fmt)) return LOWBIT_EINVAL;   // NVFP4 output from FP4 operands only
   if (fp8_out && out_layout != LOWBIT_SF_LINEAR && out_layout != LOWBIT_SF_SWZ128) return LOWBIT_EINVAL;
   if (variant < -1 || variant > lowbit::kVariantSplitK) return LOWBIT_EINVAL;
   if (workspace_bytes > 0 && !workspace) return LOWBIT_EINVAL;

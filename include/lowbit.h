@@ -342,7 +342,9 @@ lowbit_status lowbit_gemm_bias_gelu_bf16(const uint8_t* a, const uint8_t* b, con
  * between).  y = fl32(GELU(alpha*acc + bias[n])) is quantized along N in
  * 16-blocks with E4M3 scales and global scale out_global_scale (device
  * fp32[1] or NULL = 1.0).  out_packed: uint8 (M, N/2); out_sf:
- * lowbit_sf_bytes(M, N, LOWBIT_NVFP4, out_layout) bytes.  Requires N % 16 == 0. */
+ * lowbit_sf_bytes(M, N, LOWBIT_NVFP4, out_layout) bytes.  Requires N % 16 == 0.
+ * Operands NVFP4 or MXFP4 (the page's function takes FP4 operands); MXFP8
+ * operands return LOWBIT_EINVAL. */
 lowbit_status lowbit_gemm_bias_gelu_fp4(const uint8_t* a, const uint8_t* b, const uint8_t* sfa,
                                         const uint8_t* sfb, int64_t M, int64_t N, int64_t K,
                                         lowbit_format fmt, lowbit_sf_layout sfa_layout,

@@ -387,6 +387,20 @@ def test_gemm_argument_order(buf):
                                        buf.at(24576), buf.at(28672), 0, -1, None, 0, None) == ESHAPE
 
 
+def test_gemm_fp4_out_takes_fp4_operands(buf):
+    """The GELU -> NVFP4 output GEMM takes NVFP4 or MXFP4 operands; MXFP8
+    (exact or on the FP8 MFMA) is refused before anything else is checked."""
+    L = lb.lib()
+    for fmt in (2, 4):
+        assert L.lowbit_gemm_bias_gelu_fp4(buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288), 8, 128, 256, fmt,
+                                           0, 0, 1.0, buf.at(16384), None, buf.at(20480), buf.at(24576), 0, -1,
+                                           None, 0, None) == EINVAL
+    if NO_DEVICE:
+        assert L.lowbit_gemm_bias_gelu_fp4(buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288), 8, 128, 256, 1,
+                                           0, 0, 1.0, buf.at(16384), None, buf.at(20480), buf.at(24576), 0, -1,
+                                           None, 0, None) == EDEVICE
+
+
 def test_gemm_fp8_argument_order(buf):
     L = lb.lib()
     a, b, sa, sb = buf.at(0), buf.at(4096), buf.at(8192), buf.at(12288)
