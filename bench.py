@@ -377,7 +377,7 @@ def build_variant_stages():
     stages.append(graphed(rope_stage("rope_quant_mxfp8_4096x16x512", 4096, 16, lb.MXFP8, dev)))
     stages.append(graphed(rope_stage("rope_quant_mxfp4_4096x16x512", 4096, 16, lb.MXFP4, dev)))
     # the MXFP8 GEMM with FP8 output on the RoPE workload's rows: 4096 tokens x 16 heads of 512, with
-    # the workspace its plan asks for (its 96 tiles of 128 x 384 fill 3/8 of the CUs: K splits in two)
+    # the workspace its plan asks for (its 64 tiles of 256 x 256 fill 1/4 of the CUs: K splits in four)
     need = lb.lowbit_gemm_workspace_bytes(4096, WOA_N, 8192, lb.MXFP8, -1)
     ws8 = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
     stages.append(graphed(mxfp8_gemm_stage(f"mxfp8_gemm_fp8out_4096x{WOA_N}x8192", 4096, WOA_N, 8192, dev, "mfma",

@@ -52,8 +52,8 @@ constexpr int64_t kSplitNvWorkgroups = 256;
 constexpr int64_t kSplitNvMinStagesPrefill = 16;
 
 SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt_in, bool force) {
-  const bool mma = fmt_in == kMXFP8Mma;            // MXFP8 on the scaled FP8 MFMA
-  const int fmt = mma ? kMXFP8 : fmt_in;
+  // MXFP8 on the scaled FP8 MFMA splits as exact MXFP8 does
+  const int fmt = fmt_in == kMXFP8Mma ? kMXFP8 : fmt_in;
   const int64_t ss = fmt == kMXFP8 ? 128 : 256;   // K elements of a superstep
   const int64_t nss = (K + ss - 1) / ss;
   SplitPlan none{1, (int)nss, 0, false};
@@ -62,16 +62,17 @@ SplitPlan gemm_splitk_plan(int64_t M, int64_t N, int64_t K, int fmt_in, bool for
   if (M > 128) {
     // Prefill shapes with at most half the CUs' worth of prefill tiles (few
     // columns, long K): the prefill schedule split along K, about one
-    // workgroup per CU.  NVFP4 with K % 64 == 0 and MXFP8 with K % 128 == 0
-    // on the 128 x 384 tiles (units: stages of 64 row bytes, 128 and 64
-    // elements, at least 16 a split); MXFP8 on the scaled FP8 MFMA on the
-    // 256 x 256 tiles (units: supersteps of 128 elements, at least 8 a split).
-    // Other formats and shapes do not split.
+    // workgroup per CU.  NVFP4 with K % 64 == 0 on the 128 x 384 tiles (units:
+    // stages of 128 elements, at least 16 a split); MXFP8 (exact or on the
+    // scaled FP8 MFMA) with K % 128 == 0 on the 256 x 256 tiles (units:
+    // supersteps of 128 elements, at least 8 a split).  Other formats and
+    // shapes do not split.
     const bool nv_ok = (fmt == kNVFP4 && K % 64 == 0) || (fmt == kMXFP8 && K % 128 == 0);
     if (!nv_ok) return none;
-    const int64_t nst = mma ? K / 128 : fmt == kMXFP8 ? K / 64 : (K + 127) / 128;   // the last NVFP4 stage may be half
-    const int64_t tiles_nv = mma ? ((M + 255) / 256) * ((N + 255) / 256) : ((M + 127) / 128) * ((N + 383) / 384);
-    const int64_t min_units = mma ? kSplitNvMinStagesPrefill / 2 : kSplitNvMinStagesPrefill;
+    const bool f8 = fmt == kMXFP8;
+    const int64_t nst = f8 ? K / 128 : (K + 127) / 128;   // the last NVFP4 stage may be half
+    const int64_t tiles_nv = f8 ? ((M + 255) / 256) * ((N + 255) / 256) : ((M + 127) / 128) * ((N + 383) / 384);
+    const int64_t min_units = f8 ? kSplitNvMinStagesPrefill / 2 : kSplitNvMinStagesPrefill;
     int64_t S = kSplitNvWorkgroups / tiles_nv;
     if (S > nst / min_units) S = nst / min_units;
     if (2 * tiles_nv > kSplitNvWorkgroups && !force) S = 1;

@@ -348,6 +348,35 @@ __device__ __forceinline__ void step_f8(v16f (&acc)[TI][TJ], const u32x4 (&a0)[T
       acc[i][j] = mfma_f8<2 * Q, SWAP>(a0[i], a1[i], b0[j], b1[j], acc[i][j], sa[i].w, sb[j].w);
 }
 
+// Exact MXFP8 on the 128-byte-stage prefill schedule: quarter S of a superstep
+// holds, in both lane halves, 16 bytes of its 32-element block S (bytes
+// [16c, 16c + 16)), widened exactly to bf16 with that block's power of two
+// (byte S of the unshifted scale word), two bf16 MFMA steps of 8 elements a
+// lane.  SWAP: B as the row operand (split-K partials).
+template <int S, bool SWAP, int TI, int TJ, class SW>
+__device__ __forceinline__ void quarter_f8dq(v16f (&acc)[TI][TJ], const u32x4 (&qa)[TI], const u32x4 (&qb)[TJ],
+                                             const SW (&sa)[TI], const SW (&sb)[TJ]) {
+  float fa[TI], fb[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; i++) fa[i] = ue8m0_to_f32((sa[i].w >> (8 * S)) & 0xFFu);
+#pragma unroll
+  for (int j = 0; j < TJ; j++) fb[j] = ue8m0_to_f32((sb[j].w >> (8 * S)) & 0xFFu);
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    v8bf va[TI], vb[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; i++) va[i] = dq8_f8(qa[i][2 * t], qa[i][2 * t + 1], fa[i]);
+#pragma unroll
+    for (int j = 0; j < TJ; j++) vb[j] = dq8_f8(qb[j][2 * t], qb[j][2 * t + 1], fb[j]);
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+        acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[j], va[i], acc[i][j], 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], vb[j], acc[i][j], 0, 0, 0);
+  }
+}
+
 // acc[i][j] += quarter S (bytes 16S..16S+15 of each lane's 64) of a superstep:
 // MXFP4 one scaled MFMA per tile pair (op_sel S picks the block's scale
 // byte); NVFP4 four fp16 MFMA steps (block 8c + 2S + t/2).
@@ -932,9 +961,10 @@ __device__ __forceinline__ int w_off(int row, int chunk) { return row * kSSBytes
 // layout: tile (y, n / 32, m / 32) at ((y * ceil(N / 32) + n / 32) * ceil(M / 32)
 // + m / 32) * 1024 floats, lane (r, c) holding row r and columns
 // 8(k / 4) + 4c + k % 4.
-template <int FMT, int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false>
+template <int FMT, int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false, bool DQ = false>
 __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g) {
   constexpr bool F8 = FMT == kMXFP8;
+  static_assert(!DQ || F8, "the exact bf16 form is MXFP8's");
   static_assert(!F8 || (!LA_TILED && !LB_TILED), "MXFP8 operands take LINEAR scales");
   static_assert(!SPLIT || F8, "the split form is built for MXFP8");
   constexpr int BN = PrefillTileN<FMT>::kCols;
@@ -1151,7 +1181,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
           // blocks 4ss .. 4ss + 3 of the row; lane half c takes block 2Q + c
           // in step Q, found at byte 2Q once the word is shifted by 8c
           // (every superstep is whole: K % 128 == 0)
-          o.w = *reinterpret_cast<const uint32_t*>(area + row * 4) >> (8 * c);
+          o.w = *reinterpret_cast<const uint32_t*>(area + row * 4) >> (DQ ? 0 : 8 * c);
           (void)tiled;
         } else {
           const int a0 = tiled ? grp * 256 + (c * 32 + r) * 4 : row * 8;
@@ -1228,7 +1258,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   __builtin_amdgcn_sched_barrier(0);
   read_sf(s0, sa, sb, std::true_type{});
   frags(s0, 0, qa, qb);
-  if constexpr (F8) frags(s0, 1, na, nb);
+  if constexpr (F8 && !DQ) frags(s0, 1, na, nb);
   // supersteps whose refill (superstep ss + 2, scales included) lies wholly
   // inside this workgroup's K: ss + 2 < min(send, whole supersteps of K)
   const int nfast = max(s0, min(send, kbytes / kSSBytes) - 2);
@@ -1274,15 +1304,18 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
   auto superstep = [&](int ss, auto fast) {
     constexpr bool F = decltype(fast)::value;
     frags(ss, 1, na, nb);
-    quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
+    if constexpr (DQ) quarter_f8dq<0, SPLIT>(acc, qa, qb, sa, sb);
+    else quarter_mma<FMT, 0, TI, TJ>(acc, qa, qb, sa, sb);
     interleave(I1{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
     frags(ss, 2, qa, qb);
-    quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
+    if constexpr (DQ) quarter_f8dq<1, SPLIT>(acc, na, nb, sa, sb);
+    else quarter_mma<FMT, 1, TI, TJ>(acc, na, nb, sa, sb);
     interleave(I1{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
     frags(ss, 3, na, nb);
-    quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
+    if constexpr (DQ) quarter_f8dq<2, SPLIT>(acc, qa, qb, sa, sb);
+    else quarter_mma<FMT, 2, TI, TJ>(acc, qa, qb, sa, sb);
     interleave(I1{}, I0{});
     // superstep ss + 1 was issued by the previous superstep (or the prologue)
     // and followed by kPf prefetch instructions when that one was a
@@ -1300,7 +1333,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
       read_sf(ss + 1, sa_n, sb_n, std::true_type{});
       frags(ss + 1, 0, qa, qb);
     }
-    quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
+    if constexpr (DQ) quarter_f8dq<3, SPLIT>(acc, na, nb, sa, sb);
+    else quarter_mma<FMT, 3, TI, TJ>(acc, na, nb, sa, sb);
     if constexpr (F) interleave(I2{}, ILSP{}); else interleave(I2{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1309,7 +1343,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     for (int j = 0; j < TJ; j++) sb[j] = sb_n[j];
   };
   int ss = s0;
-  if constexpr (F8) {
+  if constexpr (F8 && !DQ) {
     for (; ss < nfast; ss++) superstep_f8(ss, std::true_type{});
     for (; ss < send; ss++) superstep_f8(ss, std::false_type{});
   } else {
@@ -1493,12 +1527,12 @@ __global__ __launch_bounds__(64) void gemm_splitk_reduce_kernel(GemmArgs g, int 
 
 #include "gemm_nv.hpp"
 
-template <int FMT, int EPI, bool SPLIT = false>
+template <int FMT, int EPI, bool SPLIT = false, bool DQ = false>
 void launch_w(const GemmArgs& g, dim3 block, hipStream_t s) {
   constexpr int BN = PrefillTileN<FMT>::kCols;
   const dim3 grid((unsigned)(((g.M + kPBM - 1) / kPBM) * ((g.N + BN - 1) / BN)), SPLIT ? (unsigned)g.splits : 1u);
   if constexpr (FMT == kMXFP8)   // LINEAR scales only
-    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, false, false, SPLIT>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, false, false, SPLIT, DQ>), grid, block, 0, s, g);
   else if (g.la == kTiled && g.lb == kTiled)
     hipLaunchKernelGGL((gemm_prefill_w_kernel<FMT, EPI, true, true>), grid, block, 0, s, g);
   else if (g.la == kTiled)
@@ -1576,12 +1610,13 @@ hipError_t launch_fmt_epi(const GemmArgs& g, int variant, hipStream_t s) {
   // aligned words, which needs the blocks per row to be a multiple of 4 and a
   // 4-byte aligned base (else the 64-byte-stage kernel)
   if constexpr (FMT == kMXFP8) {
-    if (g.f8mma && prefill_nv_ok<FMT>(g)) {
-      launch_w<FMT, EPI>(g, dim3(kPThreads), s);
+    if (prefill_nv_ok<FMT>(g)) {
+      if (g.f8mma) launch_w<FMT, EPI>(g, dim3(kPThreads), s);
+      else launch_w<FMT, EPI, false, true>(g, dim3(kPThreads), s);
       return hipGetLastError();
     }
   }
-  if constexpr (FMT == kNVFP4 || FMT == kMXFP8) {
+  if constexpr (FMT == kNVFP4) {
     if (prefill_nv_ok<FMT>(g)) {
       launch_prefill_nv<FMT, EPI>(g, s);
       return hipGetLastError();
@@ -1632,10 +1667,10 @@ hipError_t launch_splitk(const GemmArgs& g, hipStream_t s) {
   if constexpr (FMT == kNVFP4 || FMT == kMXFP8) {
     if (g.split_nv) {   // partials from a prefill schedule, same reduce
       if (!prefill_nv_ok<FMT>(g)) return hipErrorInvalidValue;
-      if constexpr (FMT == kMXFP8) {
-        if (g.f8mma) launch_w<FMT, kEpiNone, true>(g, dim3(kPThreads), s);   // 256 x 256, supersteps of 128
-        else launch_prefill_nv<FMT, kEpiNone, true>(g, s);                  // 128 x 384, stages of 64 bytes
-      } else {
+      if constexpr (FMT == kMXFP8) {   // 256 x 256 tiles, supersteps of 128 elements
+        if (g.f8mma) launch_w<FMT, kEpiNone, true, false>(g, dim3(kPThreads), s);
+        else launch_w<FMT, kEpiNone, true, true>(g, dim3(kPThreads), s);
+      } else {                         // 128 x 384 tiles, stages of 64 bytes
         launch_prefill_nv<FMT, kEpiNone, true>(g, s);
       }
       const hipError_t e = hipGetLastError();

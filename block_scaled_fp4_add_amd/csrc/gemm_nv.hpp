@@ -76,21 +76,13 @@ __device__ __forceinline__ NvPart nv_part_word(uint32_t word) {
 // columns 8(k / 4) + 4c + k % 4, 16 floats a lane, tile (y, n / 32, m / 32) at
 // ((y * ceil(N / 32) + n / 32) * ceil(M / 32) + m / 32) * 1024 floats), which
 // gemm_splitk_reduce_kernel sums in split order before the epilogue.
-//
-// MXFP8 (FMT == kMXFP8, LINEAR scales, K % 128 == 0) runs the same schedule:
-// a 64-byte row stage then holds 64 elements, 4 K16 steps (step t: the lane's
-// dwords 2t, 2t + 1), and lane half c covers exactly 32-element block
-// 2s + c, whose UE8M0 byte is byte 2(s % 2) + c of the row's scale word at
-// 4 * (s / 2).  The dequantization is E4M3 x 2^e -> bf16 (exact while that is
-// a normal bf16), with no mantissa multiply, into bf16 MFMAs.
 template <int FMT, int EPI, bool LA_TILED, bool LB_TILED, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   constexpr int TI = kNvTI, TJ = kNvTJ;
-  constexpr bool F8 = FMT == kMXFP8;
-  static_assert(FMT == kNVFP4 || FMT == kMXFP8, "NVFP4 or MXFP8 operands");
-  constexpr int kSteps = F8 ? 4 : kNvSteps;                 // K16 steps of a 64-byte row stage
+  static_assert(FMT == kNVFP4, "NVFP4 operands");
+  constexpr int kSteps = kNvSteps;                           // K16 steps of a 64-byte row stage
   constexpr int kStageLds = kSteps * TI * kNvUnit;           // converted A of one stage
-  using VT = typename std::conditional<F8, v8bf, v8h>::type;
+  using VT = v8h;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kNvLds];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -111,8 +103,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   const int m0 = (int)(tm * kNvBM), n0 = (int)(tn * kNvBN);
 
   const int M = (int)g.M, N = (int)g.N;
-  const int kbytes = (int)(F8 ? g.K : g.K / 2);             // packed bytes of a row
-  const int nblk = (int)(g.K / (F8 ? 32 : 16));
+  const int kbytes = (int)(g.K / 2);                         // packed bytes of a row
+  const int nblk = (int)(g.K / 16);
   const int ktiles = (nblk + 7) >> 3;
   const int nst_all = (kbytes + 63) / 64;                    // 64-byte row stages
   const int s0 = SPLIT ? (int)blockIdx.y * g.per : 0;                        // this workgroup's stages
@@ -128,7 +120,6 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   // per-lane offsets; the stage advance goes into the scalar offset
   auto sf_base = [&](int row, int R, bool tiled) {
     if (row >= R) return kAbsent;
-    if (F8) return row * nblk;   // the word holding stages 2k and 2k + 1
     return tiled ? (((row >> 5) * ktiles) << 8) + ((c * 32 + (row & 31)) << 2) : row * nblk + 4 * c;
   };
   int ob[TJ], sb_[TJ];
@@ -154,10 +145,10 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   auto issue = [&](int s, int p, NvB& b, NvA& a) {
     const bool fast = s < nfull;                       // uniform
     const int so = s * 64;
-    const int ssf = F8 ? 4 * (s >> 1) : ((p == 0 ? LA_TILED : LB_TILED) ? (s << 8) : (s << 3));
+    const int ssf = (p == 0 ? LA_TILED : LB_TILED) ? (s << 8) : (s << 3);
     const int sd = fast ? so : 0, ss = fast ? ssf : 0;   // scalar parts
     const int vd = fast ? 0 : so, vs = fast ? 0 : ssf;   // lane parts
-    // NVFP4 K % 64 == 0, MXFP8 K % 128 == 0: a lane half is wholly in or out
+    // K % 64 == 0: a lane half is wholly in or out
     const bool in = fast || so + 32 * c < kbytes;
     auto voff = [&](int base, int add) { return in ? base + add : kAbsent; };
     if (p == 0) {
@@ -178,16 +169,11 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TJ; j++) acc[i][j] = v16f{};
 
-  // step t of a lane's 32 bytes, dequantized: NVFP4 dword t with the E4M3
-  // scale of block t / 2 (byte t / 2 of the word); MXFP8 dwords 2t, 2t + 1 with
-  // the UE8M0 scale of the lane's block (byte 2(s % 2) + c of the word)
+  // step t of a lane's 32 bytes, dequantized: dword t with the E4M3 scale of
+  // block t / 2 (byte t / 2 of the word)
   auto deq = [&](const u32x4 (&q)[2], uint32_t sw, int t, int s) -> VT {
-    if constexpr (F8) {
-      const uint32_t b = (sw >> (8 * (2 * (s & 1) + c))) & 0xFFu;
-      return dq8_f8(q[t >> 1][2 * (t & 1)], q[t >> 1][2 * (t & 1) + 1], ue8m0_to_f32(b));
-    } else {
-      return dq8(q[t >> 2][t & 3], nv_part_word(sw >> (8 * (t >> 1))));
-    }
+    (void)s;
+    return dq8(q[t >> 2][t & 3], nv_part_word(sw >> (8 * (t >> 1))));
   };
   // step t of this wave's A fragment of stage s, dequantized into LDS unit (t, w)
   auto unit = [&](const NvA& a, int t, int s, uint8_t* buf) {
@@ -205,12 +191,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < TI; i++)
 #pragma unroll
-      for (int j = 0; j < TJ; j++) {
-        if constexpr (F8)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], vb[j], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
   };
   // one MFMA, then a share of the VALU work, then one LDS access (the first
   // NDS MFMAs) or one load (the next NVM)
@@ -350,8 +331,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nv_kernel(GemmArgs g) {
   }
 }
 
-// The schedule's conditions: NVFP4 with K % 64 == 0, or MXFP8 with
-// K % 128 == 0 (whole scale words), LINEAR scale buffers 4-byte aligned.
+// The prefill schedules' conditions: NVFP4 with K % 64 == 0 (the 128 x 384
+// one), MXFP8 with K % 128 == 0 (the 256 x 256 one; whole scale words), LINEAR
+// scale buffers 4-byte aligned.
 template <int FMT>
 inline bool prefill_nv_ok(const GemmArgs& g) {
   auto word_ok = [&](const uint8_t* p, int lay) {
@@ -366,9 +348,7 @@ void launch_prefill_nv(const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)(((g.M + kNvBM - 1) / kNvBM) * ((g.N + kNvBN - 1) / kNvBN)),
                   SPLIT ? (unsigned)g.splits : 1u),
       block(256);
-  if constexpr (FMT == kMXFP8) {   // LINEAR scales only
-    hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, false, false, SPLIT>), grid, block, 0, s, g);
-  } else if (g.la == kTiled && g.lb == kTiled) {
+  if (g.la == kTiled && g.lb == kTiled) {
     hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, true, true, SPLIT>), grid, block, 0, s, g);
   } else if (g.la == kTiled) {
     hipLaunchKernelGGL((gemm_prefill_nv_kernel<FMT, EPI, true, false, SPLIT>), grid, block, 0, s, g);

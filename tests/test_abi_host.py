@@ -88,20 +88,18 @@ def splitk_plan(M, N, K, fmt=1):
     supersteps (1024 elements) per split, K of at least 16 supersteps.  No
     empty split; bytes = splits x 32-column tiles x M-tiles x 32 x 32 floats."""
     tiles, mt = -(-N // 32), -(-M // 32)
-    mma = fmt == 4          # MXFP8 on the scaled FP8 MFMA
-    if mma:
+    if fmt == 4:            # MXFP8 on the scaled FP8 MFMA splits as MXFP8 does
         fmt = 2
     if M > 128:
-        # above 128 rows: NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) with at
-        # most 128 tiles of 128 x 384 split its stages of 64 row bytes (128 and
-        # 64 elements), 16 or more each; MXFP8 on the scaled FP8 MFMA with at
-        # most 128 tiles of 256 x 256 its 128-element supersteps, 8 or more
-        # each; about one workgroup per CU
+        # above 128 rows: NVFP4 (K % 64 == 0) with at most 128 tiles of
+        # 128 x 384 splits its 128-element stages, 16 or more each; MXFP8
+        # (K % 128 == 0) with at most 128 tiles of 256 x 256 its 128-element
+        # supersteps, 8 or more each; about one workgroup per CU
         if not ((fmt == 0 and K % 64 == 0) or (fmt == 2 and K % 128 == 0)):
             return 1, 0
-        nst = K // 128 if mma else K // 64 if fmt == 2 else -(-K // 128)
-        tnv = -(-M // 256) * -(-N // 256) if mma else -(-M // 128) * -(-N // 384)
-        S = 1 if 2 * tnv > 256 else min(256 // tnv, nst // (8 if mma else 16))
+        nst = K // 128 if fmt == 2 else -(-K // 128)
+        tnv = -(-M // 256) * -(-N // 256) if fmt == 2 else -(-M // 128) * -(-N // 384)
+        S = 1 if 2 * tnv > 256 else min(256 // tnv, nst // (8 if fmt == 2 else 16))
         if S <= 1:
             return 1, 0
         per = -(-nst // S)
@@ -164,12 +162,12 @@ def test_splitk_workspace_and_choice(M, N, K):
                                        (1000, 400, 4096 + 32, 0), (200, 384, 1024, 0), (257, 400, 4160, 0),
                                        (300, 400, 1984, 0)])
 def test_splitk_above_128_rows(M, N, K, fmt):
-    """Above 128 rows only NVFP4 (K % 64 == 0) and MXFP8 (K % 128 == 0) split,
-    on the 128 x 384 tiles (MXFP8 on the scaled FP8 MFMA: 256 x 256), and the
-    automatic choice only with at most 128 such tiles: (4096, 1024, 8192) has
-    96 tiles of 128 x 384 and splits in two, 64 of 256 x 256 and splits in
-    four; the chain's 2048-token GEMMs (224 and 736 tiles) and MXFP4 never
-    do."""
+    """Above 128 rows only NVFP4 (K % 64 == 0, 128 x 384 tiles) and MXFP8
+    (K % 128 == 0, exact or on the scaled FP8 MFMA, 256 x 256 tiles) split,
+    and the automatic choice only with at most 128 such tiles: (4096, 1024,
+    8192) has 96 tiles of 128 x 384 and splits in two, 64 of 256 x 256 and
+    splits in four; the chain's 2048-token GEMMs (224 and 736 tiles) and
+    MXFP4 never do."""
     L = lb.lib()
     S, need = splitk_plan(M, N, K, fmt)
     assert L.lowbit_gemm_workspace_bytes(M, N, K, fmt, -1) == need
@@ -182,9 +180,9 @@ def test_splitk_above_128_rows(M, N, K, fmt):
     forced = L.lowbit_gemm_workspace_bytes(M, N, K, fmt, 2)
     assert (forced > 0) == nv_ok and forced >= need
     assert (L.lowbit_gemm_pick_variant(M, N, K, fmt, 2, 0) == 2) == nv_ok
-    if (M, N, K) == (4096, 1024, 8192) and fmt in (0, 2):
+    if (M, N, K, fmt) == (4096, 1024, 8192, 0):
         assert S == 2 and need == 2 * 32 * 128 * 4096
-    if (M, N, K, fmt) == (4096, 1024, 8192, 4):
+    if (M, N, K) == (4096, 1024, 8192) and fmt in (2, 4):
         assert S == 4 and need == 4 * 32 * 128 * 4096
     if (M, N, K) == (257, 400, 4160):   # 33 stages, the last a half one: 2 splits of 17 and 16
         assert S == 2

@@ -42,7 +42,7 @@ def test_mxfp8_gemm_epilogues(orc, epi, variant):
              outliers=True)
 
 
-# K % 128 == 0 runs the 128 x 384 schedule (prefill): ragged M and N, every epilogue
+# K % 128 == 0 runs the 256 x 256 schedule (prefill, exact bf16 form): ragged M and N, every epilogue
 @pytest.mark.parametrize("M,N,K", [(129, 400, 512), (300, 1000, 1152), (257, 770, 128)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
 def test_mxfp8_gemm_prefill_schedule(orc, M, N, K, epi):
@@ -56,13 +56,13 @@ def test_mxfp8_gemm_splitk(orc, M, N, K):
     run_gemm(orc, M, N, K, F8, 0, 0, 0, -1, seed=M + N + K + 9, alpha=0.25, workspace=True)
 
 
-# Above 128 rows MXFP8 with K % 128 == 0 splits the 128 x 384 schedule along
-# K (stages of 64 elements): ragged M and N, a last split shorter than the
+# Above 128 rows MXFP8 with K % 128 == 0 splits the 256 x 256 schedule along
+# K (supersteps of 128 elements): ragged M and N, a last split shorter than the
 # others (4224 = 66 stages); explicit, and automatic with the workspace offered
 @pytest.mark.parametrize("M,N,K", [(300, 770, 2048), (600, 1000, 4096), (129, 96, 8192), (257, 400, 4224)])
 def test_mxfp8_gemm_prefill_splitk(orc, M, N, K):
     run_gemm(orc, M, N, K, F8, 0, 0, 0, 2, seed=M + N + K + 11, alpha=0.5, outliers=True)
-    assert lb.lowbit_gemm_workspace_bytes(M, N, K, F8, -1) > 0      # 32 stages of 64 elements or more
+    assert lb.lowbit_gemm_workspace_bytes(M, N, K, F8, -1) > 0      # 16 supersteps of 128 elements or more
     run_gemm(orc, M, N, K, F8, 0, 0, 0, -1, seed=M + N + K + 12, workspace=True)
 
 
@@ -167,8 +167,8 @@ def test_gemm_fp8_out_splitk(orc, M, N, K, fmt, out_layout):
 
 def test_mxfp8_fp8_out_prefill_workload_full(orc):
     """The MXFP8 prefill workload the benchmark times, (4096, 1024, 8192) with
-    FP8 output and 128 x 4 scales, in its launch configuration (the 128 x 384
-    schedule split in two along K), every output compared."""
+    FP8 output and 128 x 4 scales, in its launch configuration (the 256 x 256
+    schedule split in four along K), every output compared."""
     assert lb.lowbit_gemm_workspace_bytes(4096, 1024, 8192, F8, -1) == lb.lowbit_gemm_workspace_bytes(
         4096, 1024, 8192, F8, 2) > 0
     run_fp8_out(orc, 4096, 1024, 8192, F8, 2, 2, seed=79, alpha=1.0)
