@@ -25,7 +25,7 @@
 // handed to kernels.
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 static_assert(kStaticScratchBytes == LOWBIT_STATIC_SCRATCH_BYTES, "header and library disagree");
-static_assert(LOWBIT_MXFP8_MMA == lowbit::kMXFP8Mma && LOWBIT_MXFP8 == lowbit::kMXFP8, "format ids");
+static_assert((int)LOWBIT_MXFP8_MMA == (int)lowbit::kMXFP8Mma && (int)LOWBIT_MXFP8 == (int)lowbit::kMXFP8, "format ids");
 static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
 
 namespace {

@@ -1348,7 +1348,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_prefill_w_kernel(GemmArgs g
     for (; ss < send; ss++) superstep_f8(ss, std::false_type{});
   } else {
     for (; ss < nfast; ss++) superstep(ss, std::true_type{});
-    for (; ss < nss; ss++) superstep(ss, std::false_type{});
+    for (; ss < send; ss++) superstep(ss, std::false_type{});
   }
   // the DMA issued past the end (zeros) lands before the epilogue reuses LDS
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
