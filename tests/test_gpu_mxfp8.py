@@ -58,7 +58,7 @@ def test_mxfp8_gemm_splitk(orc, M, N, K):
 
 # Above 128 rows MXFP8 with K % 128 == 0 splits the 256 x 256 schedule along
 # K (supersteps of 128 elements): ragged M and N, a last split shorter than the
-# others (4224 = 66 stages); explicit, and automatic with the workspace offered
+# others (4224 = 33 supersteps: 9, 9, 9, 6); explicit, and automatic with the workspace offered
 @pytest.mark.parametrize("M,N,K", [(300, 770, 2048), (600, 1000, 4096), (129, 96, 8192), (257, 400, 4224)])
 def test_mxfp8_gemm_prefill_splitk(orc, M, N, K):
     run_gemm(orc, M, N, K, F8, 0, 0, 0, 2, seed=M + N + K + 11, alpha=0.5, outliers=True)
