@@ -610,17 +610,27 @@ def _oracle_step_time(orc, stages, small):
     return t_step, parts
 
 
-def oracle_config_seconds(orc):
-    """Oracle seconds of each workload on all host cores: the tiny MXFP4
-    case, the 4096 x 4096 producer and the four decode GEMMs in full; the
-    prefill GEMMs and the chain's GEMMs from a timed block scaled by its share
-    of the multiply-accumulates (the chain at M = 1 and 128 in full)."""
+def oracle_config_seconds(orc, small=False):
+    """Oracle seconds of each workload on the threads the oracle is set to:
+    the tiny MXFP4 case, the 4096 x 4096 producer and the four decode GEMMs in
+    full; the prefill GEMMs and the chain's GEMMs from a timed block scaled by
+    its share of the multiply-accumulates (the chain at M = 1 and 128 in
+    full).  small: the one-core pass -- each timed call runs on one thread
+    (the inputs are prepared on all of them), the decode GEMMs on 8 rows, the
+    prefill GEMMs on 32, the chain at M = 128 and 2048 on 8, each timed also
+    on half its rows and extrapolated linearly in the row count."""
     out = {}
+    threads = orc.num_threads()
 
     def timed(fn):
-        t0 = time.perf_counter()
-        fn()
-        return time.perf_counter() - t0
+        if small:
+            orc.set_num_threads(1)
+        try:
+            t0 = time.perf_counter()
+            fn()
+            return time.perf_counter() - t0
+        finally:
+            orc.set_num_threads(threads)
 
     c = synth.TINY_MXFP4
     x, r, w = synth.producer_inputs(c["M"], c["H"], c["seed"])
@@ -645,24 +655,31 @@ def oracle_config_seconds(orc):
         b, sfb = orc.quantize(synth.bits(Wt), fmt, orc.TILED)
         bias = synth.bits(synth.bias(N, seed))
         res = synth.bits(synth.residual(Ms, N, seed))
-        if gelu_fp4:
-            dt = timed(lambda: orc.gemm_gelu_fp4(a, b, sfa, sfb, Ms, N, K, fmt, orc.TILED, orc.TILED, 1.0, bias,
-                                                 1.0, orc.TILED))
-        else:
-            dt = timed(lambda: orc.gemm(a, b, sfa, sfb, Ms, N, K, fmt, orc.TILED, orc.TILED, 1.0, epi, bias, res))
-        return dt * M / Ms
+        def run(rows):
+            if gelu_fp4:
+                return timed(lambda: orc.gemm_gelu_fp4(a, b, sfa, sfb, rows, N, K, fmt, orc.TILED, orc.TILED, 1.0,
+                                                       bias, 1.0, orc.TILED))
+            return timed(lambda: orc.gemm(a, b, sfa, sfb, rows, N, K, fmt, orc.TILED, orc.TILED, 1.0, epi, bias, res))
+        dt = run(Ms)
+        if not small or Ms == M:
+            return dt * M / Ms
+        # one-core samples are a few rows: the call's fixed cost (the B
+        # operand's decode) is counted once, the rows' cost scaled
+        half = run(Ms // 2)
+        return dt + (dt - half) * (M - Ms) / (Ms - Ms // 2)
 
     for (M, N, K) in synth.MXFP4_DECODE["shapes"]:
-        out[f"mxfp4_decode_gemm_{M}x{N}x{K}"] = round(gemm_s(M, N, K, orc.MXFP4), 3)
+        key = f"mxfp4_decode_gemm_{M}x{N}x{K}" + ("_extrapolated" if small and M > 8 else "")
+        out[key] = round(gemm_s(M, N, K, orc.MXFP4, rows=8 if small else None), 3)
     for (M, N, K) in synth.MXFP4_PREFILL["shapes"]:
         out[f"mxfp4_prefill_gemm_bias_residual_{M}x{N}x{K}_extrapolated"] = round(
-            gemm_s(M, N, K, orc.MXFP4, orc.EPI_BIAS_RESIDUAL, rows=256), 2)
+            gemm_s(M, N, K, orc.MXFP4, orc.EPI_BIAS_RESIDUAL, rows=32 if small else 256), 2)
     ch = synth.NVFP4_CHAIN
     for M in ch["Ms"]:
         x, r, w = synth.producer_inputs(M, ch["H"], ch["seed"] + M, outliers=True)
         tp = timed(lambda: orc.add_rmsnorm_quant(synth.bits(x), synth.bits(r), synth.bits(w), EPS, orc.NVFP4,
                                                  orc.TILED))
-        rows = None if M <= 128 else 64
+        rows = (None if M == 1 else 8) if small else (None if M <= 128 else 64)
         t1 = gemm_s(M, ch["N1"], ch["H"], orc.NVFP4, rows=rows, gelu_fp4=True)
         t2 = gemm_s(M, ch["H"], ch["N1"], orc.NVFP4, rows=rows)
         key = f"nvfp4_chain_m{M}" + ("_extrapolated" if rows else "")
@@ -687,13 +704,15 @@ def cpu_baseline(stages, step_ideal_s):
     finally:
         orc.set_num_threads(threads)
     configs = oracle_config_seconds(orc)
+    log("[bench] cpu baseline: workloads on one core")
+    configs1 = oracle_config_seconds(orc, small=True)
     return {"value": 100.0 * step_ideal_s / t_all, "unit": "% of 1-GPU roofline", "cores": threads,
             "kind": "oracle", "step_s": round(t_all, 2),
             "value_1core": 100.0 * step_ideal_s / t_one, "step_s_1core": round(t_one, 2),
             "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": "; ".join(parts) + f"; extrapolated step time {t_all:.1f} s on {threads} threads",
             "sample_1core": "; ".join(parts1) + f"; extrapolated step time {t_one:.1f} s on 1 thread",
-            "config_seconds": configs}
+            "config_seconds": configs, "config_seconds_1core": configs1}
 
 
 def source_digest():
